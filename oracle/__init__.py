@@ -1,0 +1,130 @@
+"""fp64 CPU oracle for sparse decode attention and the decode index builder.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package.  The GPU library
+never calls it, and it shares no code, header, table or helper with the GPU
+library.  The C source (``spd_oracle.c``) states the definition it computes and
+the page passage each step follows (sglang PR #28392 summary, "key source
+snippet": the ``paged_decode.py`` module docstring).
+
+Arrays are numpy: bf16 data travels as its raw ``uint16`` bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "spd_oracle.c")
+_BUILD_DIR = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_BUILD_DIR, "libspd_oracle.so")
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc (generic x86-64, OpenMP).  Returns the path."""
+    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    os.makedirs(_BUILD_DIR, exist_ok=True)
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c99", "-Wall", "-Wextra",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        P = ctypes.c_void_p
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        lib.spd_oracle_sparse_decode_attn.argtypes = [P, P, i64, P, P, P, ctypes.c_float, i32, i32,
+                                                      i32, P, i32, P]
+        lib.spd_oracle_sparse_decode_attn.restype = ctypes.c_int
+        lib.spd_oracle_build_decode_indices.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i32, P,
+                                                        P, i64]
+        lib.spd_oracle_build_decode_indices.restype = ctypes.c_int
+        lib.spd_oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.spd_oracle_set_threads.restype = None
+        lib.spd_oracle_get_threads.argtypes = []
+        lib.spd_oracle_get_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def set_threads(n: int) -> None:
+    _load().spd_oracle_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(_load().spd_oracle_get_threads())
+
+
+def sparse_decode_attn(q_bits: np.ndarray, kv_bits: np.ndarray, kv_indices: np.ndarray,
+                       kv_indptr: np.ndarray, attn_sink: np.ndarray, softmax_scale: float,
+                       tokens: Optional[np.ndarray] = None) -> np.ndarray:
+    """fp64 attention output ``[n, H, D]`` (n = N, or len(tokens) when given).
+
+    q_bits ``[N, H, D]`` and kv_bits ``[P, D]`` are uint16 bf16 bit patterns,
+    kv_indices / kv_indptr ``[N+1]`` int32, attn_sink ``[H]`` float32.
+    """
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    kv_bits = np.ascontiguousarray(kv_bits, dtype=np.uint16)
+    kv_indices = np.ascontiguousarray(kv_indices, dtype=np.int32)
+    kv_indptr = np.ascontiguousarray(kv_indptr, dtype=np.int32)
+    attn_sink = np.ascontiguousarray(attn_sink, dtype=np.float32)
+    N, H, D = q_bits.shape
+    assert kv_bits.ndim == 2 and kv_bits.shape[1] == D
+    assert kv_indptr.shape == (N + 1,) and attn_sink.shape == (H,)
+    if tokens is not None:
+        tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    n_out = N if tokens is None else len(tokens)
+    out = np.zeros((n_out, H, D), dtype=np.float64)
+    if kv_indices.size == 0:
+        kv_indices = np.zeros(1, dtype=np.int32)  # never read: every slice is empty
+    rc = _load().spd_oracle_sparse_decode_attn(
+        _ptr(q_bits), _ptr(kv_bits), kv_bits.shape[0], _ptr(kv_indices), _ptr(kv_indptr),
+        _ptr(attn_sink), float(np.float32(softmax_scale)), N, H, D, _ptr(tokens),
+        0 if tokens is None else len(tokens), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected its input (code %d)" % rc)
+    return out
+
+
+def build_decode_indices(state_slot: np.ndarray, swa_len: np.ndarray,
+                         comp_pos: Optional[np.ndarray], block_table: Optional[np.ndarray],
+                         win: int, k_per_block: int, swa_pages: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Ragged-packed ``(kv_indptr [N+1], kv_indices [kv_indptr[N]])``, both int32.
+
+    comp_pos ``[N, topk]`` int32 (negative = no entry) or None; block_table
+    ``[N, max_blocks]`` int32 (unused when comp_pos is None).
+    """
+    state_slot = np.ascontiguousarray(state_slot, dtype=np.int32)
+    swa_len = np.ascontiguousarray(swa_len, dtype=np.int32)
+    N = state_slot.shape[0]
+    topk, max_blocks = 0, 0
+    if comp_pos is not None:
+        comp_pos = np.ascontiguousarray(comp_pos, dtype=np.int32)
+        block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+        topk = comp_pos.shape[1]
+        max_blocks = block_table.shape[1]
+    capacity = N * (max(int(win), 0) + topk)
+    indptr = np.zeros(N + 1, dtype=np.int32)
+    indices = np.zeros(max(capacity, 1), dtype=np.int32)
+    rc = _load().spd_oracle_build_decode_indices(
+        _ptr(state_slot), _ptr(swa_len), _ptr(comp_pos), topk, _ptr(block_table), max_blocks, N,
+        int(win), int(k_per_block), int(swa_pages), _ptr(indptr), _ptr(indices), capacity)
+    if rc != 0:
+        raise ValueError("oracle builder rejected its input (code %d)" % rc)
+    return indptr, indices[: indptr[-1]].copy()
