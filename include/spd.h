@@ -1,0 +1,171 @@
+/*
+ * spd.h -- C ABI of libspd: sparse decode attention over a unified paged KV
+ * pool, and the decode index builder that feeds it, for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Source of the contract: sglang PR #28392 summary page, "key source snippet"
+ * section (the paged_decode.py module docstring), and the same page's
+ * "implementation" and "key files" sections naming the decode index builder
+ * write_v4_paged_decode_indices.
+ *
+ * Conventions for every call:
+ *   - All tensor arguments are DEVICE pointers owned by the caller, row-major
+ *     and contiguous.  The library keeps no reference after the call returns
+ *     (the work is asynchronous on `stream`; buffers must stay alive until
+ *     the stream reaches that point).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   - Calls never synchronise, never read device data on the host, never
+ *     allocate, and launch a grid that depends only on the scalar arguments,
+ *     so they may be captured in a HIP graph (the page designs the decode
+ *     kernel for graph capture).  spd_validate_indices is the one exception
+ *     (a debug call that allocates and synchronises).
+ *   - Errors are returned as spd_status; nothing is thrown or aborted across
+ *     the ABI.  Argument checks run on the host before any HIP call, so they
+ *     also work on a machine without a GPU.
+ *   - bf16 means IEEE binary32 truncated to its top 16 bits (1-8-7).
+ */
+#ifndef SPD_H_
+#define SPD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPD_API __attribute__((visibility("default")))
+
+typedef enum spd_status {
+  SPD_OK = 0,
+  SPD_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad scalar, misalignment */
+  SPD_ERR_UNSUPPORTED = 2, /* shape this library does not implement (see *_can_use) */
+  SPD_ERR_WORKSPACE = 3,   /* workspace missing or smaller than *_workspace_size */
+  SPD_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} spd_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+SPD_API const char* spd_status_string(spd_status s);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+SPD_API int spd_version(void);
+
+/*
+ * 1 when sparse_decode_attn supports heads H and head width D, else 0.
+ * Supported: D in {64, 128, 256, 512}, 1 <= H <= 1024.  Callers own the
+ * fallback for anything else (the call then returns SPD_ERR_UNSUPPORTED).
+ */
+SPD_API int sparse_decode_attn_can_use(int32_t H, int32_t D);
+
+/*
+ * Sparse decode attention (page: "key source snippet", caller contract and
+ * numerics).  For each query token t and head h:
+ *
+ *   J = kv_indices[kv_indptr[t] : kv_indptr[t+1]]          (a multiset)
+ *   s_j = softmax_scale * dot(q[t,h,:], unified_kv[J_j,:])
+ *   out[t,h,:] = sum_j e^(s_j) unified_kv[J_j,:] / (e^(attn_sink[h]) + sum_j e^(s_j))
+ *   out[t,h,:] = 0 when J is empty (also when attn_sink[h] = -inf)
+ *
+ * computed as an online softmax in the log2 domain with
+ * qk_scale = softmax_scale * log2(e); one pool row is both key and value; the
+ * sink acts as a virtual key in the denominator.  fp32 accumulation, output
+ * rounded to bf16 with round-to-nearest-even.
+ *
+ *   q            [N, H, D] bf16, 16-byte aligned
+ *   unified_kv   [num_rows, D] bf16 (page_size 1), 16-byte aligned.  Slots
+ *                [0, swa_pages) hold sliding-window entries and slots from
+ *                swa_pages on hold compressed entries; this call does not
+ *                need to know the split.
+ *   kv_indices   [kv_indptr[N]] int32: every entry must lie in [0, num_rows)
+ *   kv_indptr    [N+1] int32: kv_indptr[0] == 0, non-decreasing (true prefix
+ *                sums; a graph-padded token has kv_indptr[t+1] == kv_indptr[t])
+ *   attn_sink    [H] fp32, natural-log logit in the units of the scaled score
+ *                (-inf disables the sink)
+ *   out          [N, H, D] bf16, 16-byte aligned, must not overlap the inputs
+ *
+ * The kernel does not check the index preconditions (as on the page, there is
+ * no per-entry sentinel test); breaking them is undefined behaviour.  Use
+ * spd_validate_indices in debug builds.  N == 0 returns SPD_OK and does
+ * nothing.  This form never splits a token's slice across workgroups, so it
+ * needs no workspace; sparse_decode_attn_ex adds split-L for long slices.
+ */
+SPD_API spd_status sparse_decode_attn(const void* q, const void* unified_kv, int64_t num_rows,
+                                      const int32_t* kv_indices, const int32_t* kv_indptr,
+                                      const float* attn_sink, float softmax_scale, void* out,
+                                      int32_t N, int32_t H, int32_t D, void* stream);
+
+/*
+ * Workspace bytes that sparse_decode_attn_ex needs for (N, H, D, max_len,
+ * split_rows); 0 when the plan does not split.  Returns 0 for unsupported or
+ * invalid arguments (the call itself then reports the error).
+ */
+SPD_API size_t sparse_decode_attn_workspace_size(int32_t N, int32_t H, int32_t D, int32_t max_len,
+                                                 int32_t split_rows);
+
+/*
+ * sparse_decode_attn with a split-L plan.  max_len is a capacity bound on
+ * every slice length, used only to size the grid and the workspace (a longer
+ * slice is still computed correctly, by its last partition).  split_rows
+ * fixes the partition length (rounded up to a multiple of 32); 0 chooses it
+ * from N, H and max_len.  Partitions of one token are merged by a combine
+ * kernel (the attention sink is counted once).  workspace/workspace_bytes: a
+ * caller-owned device buffer of at least sparse_decode_attn_workspace_size
+ * bytes (may be NULL when that size is 0); no state survives between calls.
+ */
+SPD_API spd_status sparse_decode_attn_ex(const void* q, const void* unified_kv, int64_t num_rows,
+                                         const int32_t* kv_indices, const int32_t* kv_indptr,
+                                         const float* attn_sink, float softmax_scale, void* out,
+                                         int32_t N, int32_t H, int32_t D, int32_t max_len,
+                                         int32_t split_rows, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/*
+ * Decode index builder, the page's write_v4_paged_decode_indices ("paged
+ * decode index scatter kernel"): packs sliding-window ring slots and
+ * compressed paged slots into ragged CSR indices with no sentinels.
+ * For each token t, in token order:
+ *   window part:     state_slot[t] * win + r            for r = 0 .. swa_len[t]-1
+ *   compressed part: swa_pages + block_table[t][c / k_per_block] * k_per_block
+ *                              + c % k_per_block
+ *                    for each entry c of comp_pos[t][0 .. topk-1] with c >= 0,
+ *                    in row order
+ *   kv_indptr[0] = 0, kv_indptr[t+1] = kv_indptr[t] + entries of token t.
+ * A padded token (swa_len 0, no valid comp_pos) gets a zero-length slice.
+ *
+ *   state_slot   [N] int32        swa_len [N] int32, each in [0, win]
+ *   comp_pos     [N, topk] int32, negative = no entry; NULL with topk == 0
+ *   block_table  [N, max_blocks] int32 (NULL allowed when comp_pos is NULL)
+ *   kv_indptr    [N+1] int32 (out)   kv_indices [indices_capacity] int32 (out)
+ *
+ * Host checks: win > 0, k_per_block > 0, N >= 0, topk >= 0, swa_pages >= 0,
+ * indices_capacity >= N * (win + topk) and N * (win + topk) < 2^31.
+ * Device-side: swa_len is clamped to [0, win] and a comp_pos entry whose block
+ * lookup falls outside [0, max_blocks) is dropped, so bad metadata cannot
+ * make the builder read or write out of bounds.  Caller precondition (not
+ * checked): the produced slots lie inside the pool.
+ */
+SPD_API spd_status build_decode_indices(const int32_t* state_slot, const int32_t* swa_len,
+                                        const int32_t* comp_pos, int32_t topk,
+                                        const int32_t* block_table, int32_t max_blocks, int32_t N,
+                                        int32_t win, int32_t k_per_block, int32_t swa_pages,
+                                        int32_t* kv_indptr, int32_t* kv_indices,
+                                        int64_t indices_capacity, void* stream);
+
+/*
+ * Debug check of the attention call's index preconditions: kv_indptr[0] == 0,
+ * kv_indptr non-decreasing, kv_indptr[N] <= num_indices (the length of the
+ * kv_indices buffer), and every kv_indices[j], j < kv_indptr[N], in
+ * [0, num_rows).  *first_bad (host pointer) receives -1 when all hold, else
+ * the smallest offending position: t (0..N) for a kv_indptr violation, or
+ * N + 1 + j for kv_indices[j].  Allocates a few bytes of device memory and
+ * synchronises `stream`: not for the hot path and not capturable.
+ */
+SPD_API spd_status spd_validate_indices(const int32_t* kv_indices, int64_t num_indices,
+                                        const int32_t* kv_indptr, int32_t N, int64_t num_rows,
+                                        int64_t* first_bad, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPD_H_ */

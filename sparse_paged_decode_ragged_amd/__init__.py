@@ -1,0 +1,201 @@
+"""Python binding of libspd: sparse decode attention over a unified paged KV
+pool and its decode index builder, hand-written HIP for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/spd.h``.  PyTorch provides
+device memory and the current stream.  There is no fallback: if the built
+library is missing, importing this package raises.
+
+Call names follow the C ABI:
+
+* ``sparse_decode_attn(q, unified_kv, kv_indices, kv_indptr, attn_sink,
+  softmax_scale, out=None, *, max_len=0, split_rows=0, workspace=None)``
+* ``build_decode_indices(state_slot, swa_len, comp_pos, block_table, win,
+  k_per_block, swa_pages, kv_indptr=None, kv_indices=None)``
+* ``sparse_decode_attn_workspace_size``, ``sparse_decode_attn_can_use``,
+  ``validate_indices``
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libspd.so")
+
+SPD_OK = 0
+_STATUS = {0: "SPD_OK", 1: "SPD_ERR_INVALID_ARG", 2: "SPD_ERR_UNSUPPORTED", 3: "SPD_ERR_WORKSPACE",
+           4: "SPD_ERR_HIP"}
+
+EXPORTED_SYMBOLS = (
+    "spd_status_string", "spd_version", "sparse_decode_attn_can_use", "sparse_decode_attn",
+    "sparse_decode_attn_workspace_size", "sparse_decode_attn_ex", "build_decode_indices",
+    "spd_validate_indices",
+)
+
+
+class SpdError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        super().__init__("%s failed: %s" % (call, _STATUS.get(status, "status %d" % status)))
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libspd.so is not built (expected at %s); run "
+                          "sparse_paged_decode_ragged_amd/build.py" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.spd_status_string.argtypes = [ctypes.c_int]
+    lib.spd_status_string.restype = ctypes.c_char_p
+    lib.spd_version.argtypes = []
+    lib.spd_version.restype = ctypes.c_int
+    lib.sparse_decode_attn_can_use.argtypes = [i32, i32]
+    lib.sparse_decode_attn_can_use.restype = ctypes.c_int
+    lib.sparse_decode_attn.argtypes = [P, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32, P]
+    lib.sparse_decode_attn.restype = ctypes.c_int
+    lib.sparse_decode_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.sparse_decode_attn_workspace_size.restype = sz
+    lib.sparse_decode_attn_ex.argtypes = [P, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32, i32,
+                                          i32, P, sz, P]
+    lib.sparse_decode_attn_ex.restype = ctypes.c_int
+    lib.build_decode_indices.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i32, P, P, i64, P]
+    lib.build_decode_indices.restype = ctypes.c_int
+    lib.spd_validate_indices.argtypes = [P, i64, P, i32, i64, ctypes.POINTER(ctypes.c_int64), P]
+    lib.spd_validate_indices.restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: Optional[int] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims" % (name, ndim))
+
+
+def _raise_on(status: int, call: str):
+    if status != SPD_OK:
+        raise SpdError(status, call)
+
+
+def sparse_decode_attn_can_use(H: int, D: int) -> bool:
+    return bool(lib.sparse_decode_attn_can_use(int(H), int(D)))
+
+
+def sparse_decode_attn_workspace_size(N: int, H: int, D: int, max_len: int = 0,
+                                      split_rows: int = 0) -> int:
+    return int(lib.sparse_decode_attn_workspace_size(int(N), int(H), int(D), int(max_len),
+                                                     int(split_rows)))
+
+
+def sparse_decode_attn(q: torch.Tensor, unified_kv: torch.Tensor, kv_indices: torch.Tensor,
+                       kv_indptr: torch.Tensor, attn_sink: torch.Tensor, softmax_scale: float,
+                       out: Optional[torch.Tensor] = None, *, max_len: int = 0,
+                       split_rows: int = 0, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[N, H, D] (bf16) = sparse decode attention; see include/spd.h.
+
+    max_len == 0 and split_rows == 0 select the plain call (no split-L, no
+    workspace).  Otherwise the split-L form runs; ``workspace`` (a device
+    tensor of at least ``sparse_decode_attn_workspace_size`` bytes) is
+    allocated here when not given -- pass one in when capturing a graph.
+    """
+    _check(q, "q", torch.bfloat16, 3)
+    _check(unified_kv, "unified_kv", torch.bfloat16, 2)
+    _check(kv_indices, "kv_indices", torch.int32, 1)
+    _check(kv_indptr, "kv_indptr", torch.int32, 1)
+    _check(attn_sink, "attn_sink", torch.float32, 1)
+    N, H, D = q.shape
+    if unified_kv.shape[1] != D or kv_indptr.shape[0] != N + 1 or attn_sink.shape[0] != H:
+        raise ValueError("shape mismatch between q, unified_kv, kv_indptr and attn_sink")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16, 3)
+        if tuple(out.shape) != (N, H, D):
+            raise ValueError("out must be [N, H, D]")
+    idx = kv_indices if kv_indices.numel() > 0 else kv_indptr  # any valid pointer; never read
+    stream = _stream(q.device)
+    if max_len == 0 and split_rows == 0:
+        st = lib.sparse_decode_attn(_ptr(q), _ptr(unified_kv), unified_kv.shape[0], _ptr(idx),
+                                    _ptr(kv_indptr), _ptr(attn_sink), float(softmax_scale),
+                                    _ptr(out), N, H, D, stream)
+        _raise_on(st, "sparse_decode_attn")
+        return out
+    need = sparse_decode_attn_workspace_size(N, H, D, max_len, split_rows)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.sparse_decode_attn_ex(_ptr(q), _ptr(unified_kv), unified_kv.shape[0], _ptr(idx),
+                                   _ptr(kv_indptr), _ptr(attn_sink), float(softmax_scale),
+                                   _ptr(out), N, H, D, int(max_len), int(split_rows),
+                                   _ptr(workspace), ws_bytes, stream)
+    _raise_on(st, "sparse_decode_attn_ex")
+    return out
+
+
+def build_decode_indices(state_slot: torch.Tensor, swa_len: torch.Tensor,
+                         comp_pos: Optional[torch.Tensor], block_table: Optional[torch.Tensor],
+                         win: int, k_per_block: int, swa_pages: int,
+                         kv_indptr: Optional[torch.Tensor] = None,
+                         kv_indices: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Ragged-packed (kv_indptr [N+1], kv_indices [N*(win+topk)] capacity), int32 device tensors.
+
+    Only kv_indices[:kv_indptr[N]] is meaningful; reading kv_indptr[N] on the
+    host is the caller's choice (this call never synchronises).
+    """
+    _check(state_slot, "state_slot", torch.int32, 1)
+    _check(swa_len, "swa_len", torch.int32, 1)
+    N = state_slot.shape[0]
+    topk, max_blocks = 0, 0
+    if comp_pos is not None:
+        _check(comp_pos, "comp_pos", torch.int32, 2)
+        _check(block_table, "block_table", torch.int32, 2)
+        topk, max_blocks = comp_pos.shape[1], block_table.shape[1]
+        if comp_pos.shape[0] != N or block_table.shape[0] != N:
+            raise ValueError("comp_pos and block_table must have N rows")
+    cap = N * (int(win) + topk)
+    dev = state_slot.device
+    if kv_indptr is None:
+        kv_indptr = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    if kv_indices is None:
+        kv_indices = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    _check(kv_indptr, "kv_indptr", torch.int32, 1)
+    _check(kv_indices, "kv_indices", torch.int32, 1)
+    st = lib.build_decode_indices(_ptr(state_slot), _ptr(swa_len), _ptr(comp_pos), topk,
+                                  _ptr(block_table), max_blocks, N, int(win), int(k_per_block),
+                                  int(swa_pages), _ptr(kv_indptr), _ptr(kv_indices),
+                                  kv_indices.numel(), _stream(dev))
+    _raise_on(st, "build_decode_indices")
+    return kv_indptr, kv_indices
+
+
+def validate_indices(kv_indices: torch.Tensor, kv_indptr: torch.Tensor, num_rows: int) -> int:
+    """-1 when the attention preconditions hold, else the first offending position (syncs)."""
+    _check(kv_indices, "kv_indices", torch.int32, 1)
+    _check(kv_indptr, "kv_indptr", torch.int32, 1)
+    first = ctypes.c_int64(0)
+    st = lib.spd_validate_indices(_ptr(kv_indices), kv_indices.numel(), _ptr(kv_indptr),
+                                  kv_indptr.shape[0] - 1, int(num_rows), ctypes.byref(first),
+                                  _stream(kv_indptr.device))
+    _raise_on(st, "spd_validate_indices")
+    return int(first.value)

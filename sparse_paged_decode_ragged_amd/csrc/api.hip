@@ -1,0 +1,165 @@
+// api.hip -- the exported C ABI of libspd (declared in include/spd.h).
+//
+// Every argument check runs on the host before the first HIP call, so the
+// validation paths work (and are tested) on machines without a GPU.  No entry
+// point but spd_validate_indices allocates or synchronises.
+#include <math.h>
+#include <stdint.h>
+
+#include "spd.h"
+#include "spd_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+constexpr double kLog2eD = 1.4426950408889634073599;
+
+}  // namespace
+
+extern "C" {
+
+SPD_API const char* spd_status_string(spd_status s) {
+  switch (s) {
+    case SPD_OK: return "SPD_OK";
+    case SPD_ERR_INVALID_ARG: return "SPD_ERR_INVALID_ARG";
+    case SPD_ERR_UNSUPPORTED: return "SPD_ERR_UNSUPPORTED";
+    case SPD_ERR_WORKSPACE: return "SPD_ERR_WORKSPACE";
+    case SPD_ERR_HIP: return "SPD_ERR_HIP";
+  }
+  return "SPD_ERR_UNKNOWN";
+}
+
+SPD_API int spd_version(void) { return 100; }
+
+SPD_API int sparse_decode_attn_can_use(int32_t H, int32_t D) {
+  return spd::attn_supported(H, D) ? 1 : 0;
+}
+
+SPD_API size_t sparse_decode_attn_workspace_size(int32_t N, int32_t H, int32_t D, int32_t max_len,
+                                                 int32_t split_rows) {
+  spd::AttnPlan plan;
+  if (!spd::make_attn_plan(N, H, D, max_len, split_rows, &plan)) return 0;
+  return plan.workspace_bytes;
+}
+
+SPD_API spd_status sparse_decode_attn_ex(const void* q, const void* unified_kv, int64_t num_rows,
+                                         const int32_t* kv_indices, const int32_t* kv_indptr,
+                                         const float* attn_sink, float softmax_scale, void* out,
+                                         int32_t N, int32_t H, int32_t D, int32_t max_len,
+                                         int32_t split_rows, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  if (N < 0 || H <= 0 || D <= 0 || num_rows <= 0 || max_len < 0 || split_rows < 0)
+    return SPD_ERR_INVALID_ARG;
+  if (!isfinite(softmax_scale)) return SPD_ERR_INVALID_ARG;
+  if (!spd::attn_supported(H, D)) return SPD_ERR_UNSUPPORTED;
+  if (N == 0) return SPD_OK;
+  if (!q || !unified_kv || !kv_indices || !kv_indptr || !attn_sink || !out)
+    return SPD_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(unified_kv, 16) || !aligned(out, 16) || !aligned(kv_indices, 4) ||
+      !aligned(kv_indptr, 4) || !aligned(attn_sink, 4))
+    return SPD_ERR_INVALID_ARG;
+  if (num_rows > (int64_t)1 << 40) return SPD_ERR_INVALID_ARG;
+  const size_t qo_bytes = (size_t)N * H * D * 2;
+  if (overlap(out, qo_bytes, q, qo_bytes) ||
+      overlap(out, qo_bytes, unified_kv, (size_t)num_rows * D * 2) ||
+      overlap(out, qo_bytes, attn_sink, (size_t)H * 4) ||
+      overlap(out, qo_bytes, kv_indptr, (size_t)(N + 1) * 4))
+    return SPD_ERR_INVALID_ARG;
+
+  spd::AttnPlan plan;
+  if (!spd::make_attn_plan(N, H, D, max_len, split_rows, &plan)) return SPD_ERR_INVALID_ARG;
+  if (plan.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.workspace_bytes) return SPD_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return SPD_ERR_INVALID_ARG;
+  }
+
+  spd::AttnArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint16_t*>(unified_kv);
+  a.kv_indices = kv_indices;
+  a.kv_indptr = kv_indptr;
+  a.sink = attn_sink;
+  a.out = static_cast<uint16_t*>(out);
+  a.ws = static_cast<float*>(workspace);
+  a.qk_scale = (float)((double)softmax_scale * kLog2eD);
+  a.N = N;
+  a.H = H;
+  a.head_groups = plan.head_groups;
+  a.splits = plan.splits;
+  a.split_rows = plan.split_rows;
+  const hipError_t e = spd::launch_attention(a, D, plan, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPD_OK : SPD_ERR_HIP;
+}
+
+SPD_API spd_status sparse_decode_attn(const void* q, const void* unified_kv, int64_t num_rows,
+                                      const int32_t* kv_indices, const int32_t* kv_indptr,
+                                      const float* attn_sink, float softmax_scale, void* out,
+                                      int32_t N, int32_t H, int32_t D, void* stream) {
+  return sparse_decode_attn_ex(q, unified_kv, num_rows, kv_indices, kv_indptr, attn_sink,
+                               softmax_scale, out, N, H, D, 0, 0, nullptr, 0, stream);
+}
+
+SPD_API spd_status build_decode_indices(const int32_t* state_slot, const int32_t* swa_len,
+                                        const int32_t* comp_pos, int32_t topk,
+                                        const int32_t* block_table, int32_t max_blocks, int32_t N,
+                                        int32_t win, int32_t k_per_block, int32_t swa_pages,
+                                        int32_t* kv_indptr, int32_t* kv_indices,
+                                        int64_t indices_capacity, void* stream) {
+  if (N < 0 || topk < 0 || win <= 0 || k_per_block <= 0 || swa_pages < 0 || max_blocks < 0 ||
+      indices_capacity < 0)
+    return SPD_ERR_INVALID_ARG;
+  if (comp_pos == nullptr && topk > 0) return SPD_ERR_INVALID_ARG;
+  if (comp_pos != nullptr && topk > 0 && (block_table == nullptr || max_blocks <= 0))
+    return SPD_ERR_INVALID_ARG;
+  const int64_t need = (int64_t)N * ((int64_t)win + topk);
+  if (need > 0x7fffffffLL || indices_capacity < need) return SPD_ERR_INVALID_ARG;
+  if (kv_indptr == nullptr) return SPD_ERR_INVALID_ARG;
+  if (N > 0 && (state_slot == nullptr || swa_len == nullptr || kv_indices == nullptr))
+    return SPD_ERR_INVALID_ARG;
+
+  spd::BuildArgs a;
+  a.state_slot = state_slot;
+  a.swa_len = swa_len;
+  a.comp_pos = topk > 0 ? comp_pos : nullptr;
+  a.block_table = block_table;
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = kv_indices;
+  a.topk = topk;
+  a.max_blocks = max_blocks;
+  a.N = N;
+  a.win = win;
+  a.k_per_block = k_per_block;
+  a.swa_pages = swa_pages;
+  const hipError_t e = spd::launch_build_indices(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPD_OK : SPD_ERR_HIP;
+}
+
+SPD_API spd_status spd_validate_indices(const int32_t* kv_indices, int64_t num_indices,
+                                        const int32_t* kv_indptr, int32_t N, int64_t num_rows,
+                                        int64_t* first_bad, void* stream) {
+  if (N < 0 || num_indices < 0 || num_rows < 0 || !kv_indptr || !first_bad)
+    return SPD_ERR_INVALID_ARG;
+  if (num_indices > 0 && !kv_indices) return SPD_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned long long* dev = nullptr;
+  if (hipMalloc(&dev, sizeof(unsigned long long)) != hipSuccess) return SPD_ERR_HIP;
+  spd_status st = SPD_OK;
+  unsigned long long host = ~0ULL;
+  if (hipMemcpyAsync(dev, &host, sizeof host, hipMemcpyHostToDevice, s) != hipSuccess ||
+      spd::launch_validate_indices(kv_indices, num_indices, kv_indptr, N, num_rows, dev, s) !=
+          hipSuccess ||
+      hipMemcpyAsync(&host, dev, sizeof host, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    st = SPD_ERR_HIP;
+  (void)hipFree(dev);
+  if (st == SPD_OK) *first_bad = host == ~0ULL ? -1 : (int64_t)host;
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// Internal declarations shared by the host API and the kernel launchers of
+// libspd.  Not installed; the public ABI is include/spd.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace spd {
+
+// Rows of a token's slice that one workgroup stages per step (MFMA K of the
+// PV product is 32 rows).
+constexpr int kTileRows = 32;
+
+// Work decomposition of one attention call, fixed by scalar arguments only so
+// that the grid never depends on device data.
+struct AttnPlan {
+  int waves;           // waves per workgroup; each wave owns 16 heads
+  int heads_per_group; // 16 * waves
+  int head_groups;     // ceil(H / heads_per_group)
+  int splits;          // partitions of a slice (1 = no split-L)
+  int split_rows;      // rows per partition (multiple of kTileRows); huge when splits == 1
+  size_t workspace_bytes;
+};
+
+bool attn_supported(int32_t H, int32_t D);
+// Returns false when the arguments cannot form a plan.
+bool make_attn_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t split_rows,
+                    AttnPlan* plan);
+
+struct AttnArgs {
+  const uint16_t* q;         // [N][H][D] bf16 bits
+  const uint16_t* kv;        // [num_rows][D] bf16 bits
+  const int32_t* kv_indices;
+  const int32_t* kv_indptr;  // [N+1]
+  const float* sink;         // [H]
+  uint16_t* out;             // [N][H][D] bf16 bits
+  float* ws;                 // split partials (splits > 1)
+  float qk_scale;            // softmax_scale * log2(e)
+  int32_t N, H, head_groups, splits, split_rows;
+};
+
+hipError_t launch_attention(const AttnArgs& args, int D, const AttnPlan& plan, hipStream_t stream);
+
+struct BuildArgs {
+  const int32_t* state_slot;
+  const int32_t* swa_len;
+  const int32_t* comp_pos;
+  const int32_t* block_table;
+  int32_t* kv_indptr;
+  int32_t* kv_indices;
+  int32_t topk, max_blocks, N, win, k_per_block, swa_pages;
+};
+
+hipError_t launch_build_indices(const BuildArgs& args, hipStream_t stream);
+
+hipError_t launch_validate_indices(const int32_t* kv_indices, int64_t num_indices,
+                                   const int32_t* kv_indptr, int32_t N, int64_t num_rows,
+                                   unsigned long long* first_bad_dev, hipStream_t stream);
+
+}  // namespace spd

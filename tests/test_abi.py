@@ -1,0 +1,139 @@
+"""The C ABI library: it loads, exports every entry point include/spd.h
+declares, and rejects bad arguments on the host before any HIP call (so these
+run without a GPU).  No case here passes all checks, so nothing is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "sparse_paged_decode_ragged_amd", "_lib", "libspd.so")
+HEADER = os.path.join(ROOT, "include", "spd.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = 0x10000  # 64 KiB-aligned non-null pointer value; never dereferenced here
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libspd.so not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(LIB)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.sparse_decode_attn.argtypes = [P, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32, P]
+    L.sparse_decode_attn_ex.argtypes = [P, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32, i32,
+                                        i32, P, sz, P]
+    L.sparse_decode_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    L.sparse_decode_attn_workspace_size.restype = sz
+    L.sparse_decode_attn_can_use.argtypes = [i32, i32]
+    L.build_decode_indices.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i32, P, P, i64, P]
+    L.spd_validate_indices.argtypes = [P, i64, P, i32, i64, ctypes.POINTER(ctypes.c_int64), P]
+    L.spd_status_string.argtypes = [ctypes.c_int]
+    L.spd_status_string.restype = ctypes.c_char_p
+    return L
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"SPD_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_symbols()
+    assert set(names) >= {"sparse_decode_attn", "build_decode_indices", "sparse_decode_attn_ex",
+                          "sparse_decode_attn_workspace_size", "sparse_decode_attn_can_use",
+                          "spd_validate_indices", "spd_status_string", "spd_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_lists_the_same_symbols():
+    import ast
+    src = open(os.path.join(ROOT, "sparse_paged_decode_ragged_amd", "__init__.py")).read()
+    tree = ast.parse(src)
+    exported = None
+    for node in tree.body:
+        if isinstance(node, ast.Assign) and getattr(node.targets[0], "id", "") == "EXPORTED_SYMBOLS":
+            exported = ast.literal_eval(node.value)
+    assert exported is not None and set(exported) == set(declared_symbols())
+
+
+def test_status_strings(lib):
+    assert lib.spd_status_string(0) == b"SPD_OK"
+    assert lib.spd_status_string(3) == b"SPD_ERR_WORKSPACE"
+    assert lib.spd_version() >= 100
+
+
+@pytest.mark.parametrize("H,D,ok", [(64, 512, 1), (128, 512, 1), (8, 64, 1), (1, 128, 1),
+                                    (64, 576, 0), (64, 100, 0), (0, 512, 0), (2048, 512, 0)])
+def test_can_use(lib, H, D, ok):
+    assert lib.sparse_decode_attn_can_use(H, D) == ok
+
+
+def _attn(lib, q=FAKE, kv=FAKE, rows=100, idx=FAKE, ptr=FAKE, sink=FAKE, scale=0.1, out=FAKE * 4096,
+          N=2, H=8, D=64):
+    return lib.sparse_decode_attn(q, kv, rows, idx, ptr, sink, scale, out, N, H, D, None)
+
+
+def test_attn_rejects_bad_arguments(lib):
+    assert _attn(lib, q=None) == INVALID
+    assert _attn(lib, kv=None) == INVALID
+    assert _attn(lib, idx=None) == INVALID
+    assert _attn(lib, ptr=None) == INVALID
+    assert _attn(lib, sink=None) == INVALID
+    assert _attn(lib, out=None) == INVALID
+    assert _attn(lib, N=-1) == INVALID
+    assert _attn(lib, H=0) == INVALID
+    assert _attn(lib, rows=0) == INVALID
+    assert _attn(lib, q=FAKE + 2) == INVALID           # q not 16-byte aligned
+    assert _attn(lib, out=FAKE) == INVALID             # out overlaps q
+    assert _attn(lib, scale=float("nan")) == INVALID
+    assert _attn(lib, D=100) == UNSUPPORTED
+    assert _attn(lib, N=0) == OK                       # empty batch: nothing to do
+
+
+def test_attn_ex_workspace_checks(lib):
+    need = lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 0)
+    # 64 tokens x 1 head group x 4 partitions x 64 heads x (512 + 2) floats
+    assert need == 64 * 1 * 4 * 64 * 514 * 4
+    assert lib.sparse_decode_attn_workspace_size(1024, 128, 512, 640, 0) == 0  # large batch: no split
+    assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 64) == 64 * 10 * 64 * 514 * 4
+    st = lib.sparse_decode_attn_ex(FAKE, FAKE, 100, FAKE, FAKE, FAKE, 0.1, FAKE * 4096, 64, 64, 512,
+                                   640, 0, None, 0, None)
+    assert st == WORKSPACE
+    st = lib.sparse_decode_attn_ex(FAKE, FAKE, 100, FAKE, FAKE, FAKE, 0.1, FAKE * 4096, 64, 64, 512,
+                                   640, 0, FAKE * 8192, need - 1, None)
+    assert st == WORKSPACE
+    st = lib.sparse_decode_attn_ex(FAKE, FAKE, 100, FAKE, FAKE, FAKE, 0.1, FAKE * 4096, 64, 64, 512,
+                                   -1, 0, None, 0, None)
+    assert st == INVALID
+
+
+def _build(lib, ss=FAKE, sl=FAKE, cp=FAKE, topk=4, bt=FAKE, mb=2, N=3, win=8, k=2, swa=24,
+           ptr=FAKE, idx=FAKE, cap=None):
+    if cap is None:
+        cap = N * (win + topk)
+    return lib.build_decode_indices(ss, sl, cp, topk, bt, mb, N, win, k, swa, ptr, idx, cap, None)
+
+
+def test_builder_rejects_bad_arguments(lib):
+    assert _build(lib, win=0) == INVALID        # would divide by zero / index out of range
+    assert _build(lib, win=-3) == INVALID
+    assert _build(lib, k=0) == INVALID
+    assert _build(lib, N=-1) == INVALID
+    assert _build(lib, cap=3 * 12 - 1) == INVALID   # capacity below N*(win+topk)
+    assert _build(lib, cp=None) == INVALID          # topk > 0 without comp_pos
+    assert _build(lib, bt=None) == INVALID
+    assert _build(lib, mb=0) == INVALID
+    assert _build(lib, ptr=None) == INVALID
+    assert _build(lib, ss=None) == INVALID
+    assert _build(lib, swa=-1) == INVALID
+    assert _build(lib, N=1 << 20, win=1 << 12, topk=0, cp=None, cap=1 << 40) == INVALID  # > 2^31 entries
+
+
+def test_validate_rejects_bad_arguments(lib):
+    first = ctypes.c_int64(0)
+    assert lib.spd_validate_indices(FAKE, 10, None, 2, 100, ctypes.byref(first), None) == INVALID
+    assert lib.spd_validate_indices(None, 10, FAKE, 2, 100, ctypes.byref(first), None) == INVALID
+    assert lib.spd_validate_indices(FAKE, 10, FAKE, -1, 100, ctypes.byref(first), None) == INVALID

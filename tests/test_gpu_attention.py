@@ -1,0 +1,163 @@
+"""GPU parity of sparse decode attention (HIP path through the C ABI) against
+the fp64 oracle, at small sizes that span several tiles and ragged tails, over
+every supported head width and a range of head counts, with and without the
+split-L plan; plus the invariants the pages fix (empty slice, no sink, single
+row, permutation, determinism)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_helpers import (assert_close, bf16_to_f64, device_csr, device_inputs, log,
+                         oracle_tokens)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def spd():
+    import sparse_paged_decode_ragged_amd as m
+    return m
+
+
+def run(spd, w, idx_np, ptr_np, sink=None, **plan):
+    q, kv, s = device_inputs(w)
+    if sink is not None:
+        s = torch.from_numpy(np.asarray(sink, dtype=np.float32)).cuda()
+    idx, ptr = device_csr(idx_np, ptr_np)
+    out = spd.sparse_decode_attn(q, kv, idx, ptr, s, w.softmax_scale, **plan)
+    torch.cuda.synchronize()
+    return out
+
+
+PLANS = [dict(), dict(max_len=200, split_rows=32), dict(max_len=200, split_rows=64),
+         dict(max_len=200)]
+
+
+def test_tiny_all_tokens(spd):
+    w = W.tiny()
+    log("case tiny")
+    ref = oracle_tokens(w, w.kv_indices, w.kv_indptr)
+    for plan in [dict(), dict(max_len=64, split_rows=32)]:
+        out = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
+        assert_close(bf16_to_f64(out), ref, "tiny %s" % plan)
+        assert torch.all(out[0].view(torch.int16) == 0)  # empty slice: exactly +0.0
+
+
+LENGTHS = [0, 1, 5, 31, 32, 33, 64, 97, 200]
+
+
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
+@pytest.mark.parametrize("H", [1, 8, 16, 24, 40, 64, 128])
+def test_shapes(spd, H, D):
+    seed = 100 + H * 7 + D
+    w = W.random_csr("shapes", seed, len(LENGTHS), H, D, 700, LENGTHS)
+    log("case shapes H=%d D=%d" % (H, D))
+    ref = oracle_tokens(w, w.kv_indices, w.kv_indptr)
+    for plan in PLANS:
+        out = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
+        assert_close(bf16_to_f64(out), ref, "H=%d D=%d %s" % (H, D, plan))
+
+
+def test_many_tiles_and_long_slices(spd):
+    lengths = [640, 2048, 1, 0, 1000, 333]
+    w = W.random_csr("long", 7, len(lengths), 64, 512, 5000, lengths)
+    log("case long slices")
+    ref = oracle_tokens(w, w.kv_indices, w.kv_indptr)
+    for plan in [dict(), dict(max_len=2048), dict(max_len=2048, split_rows=96),
+                 dict(max_len=256, split_rows=128)]:   # slices longer than max_len
+        out = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
+        assert_close(bf16_to_f64(out), ref, "long %s" % plan)
+
+
+@pytest.mark.parametrize("kind", ["none", "dominant", "mixed"])
+def test_sink_variants(spd, kind):
+    lengths = [0, 3, 40, 129]
+    w = W.random_csr("sinks", 11, len(lengths), 32, 128, 300, lengths)
+    if kind == "none":
+        sink = np.full(32, -np.inf, dtype=np.float32)
+    elif kind == "dominant":
+        sink = np.full(32, 30.0, dtype=np.float32)
+    else:
+        sink = np.where(np.arange(32) % 2 == 0, -np.inf, 5.0).astype(np.float32)
+    log("case sink %s" % kind)
+    ref = oracle_tokens(w, w.kv_indices, w.kv_indptr, sink=sink)
+    for plan in PLANS:
+        out = run(spd, w, w.kv_indices, w.kv_indptr, sink=sink, **plan)
+        assert_close(bf16_to_f64(out), ref, "sink %s %s" % (kind, plan))
+        assert torch.all(out[0].view(torch.int16) == 0)
+
+
+def test_single_row_without_sink_is_bit_exact(spd):
+    """One index and attn_sink = -inf: the weight is exactly 1, so the output
+    equals the bf16 row bit for bit."""
+    w = W.random_csr("single", 12, 5, 16, 512, 50, [1, 1, 1, 1, 1])
+    sink = np.full(16, -np.inf, dtype=np.float32)
+    log("case single row")
+    for plan in [dict(), dict(max_len=32, split_rows=32)]:
+        out = run(spd, w, w.kv_indices, w.kv_indptr, sink=sink, **plan)
+        kv = W.device_bits(w.kv_bits, torch.device("cuda:0"))
+        for t in range(5):
+            row = kv[int(w.kv_indices[t])]
+            assert torch.equal(out[t].view(torch.int16), row.view(torch.int16).expand(16, -1))
+
+
+def test_all_empty_batch(spd):
+    w = W.random_csr("empty", 13, 6, 64, 512, 10, [0] * 6)
+    log("case all empty")
+    for plan in [dict(), dict(max_len=64)]:
+        out = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
+        assert torch.all(out.view(torch.int16) == 0)
+
+
+def test_permutation_and_duplicates(spd):
+    rng = np.random.default_rng(14)
+    lengths = [77, 130, 5]
+    w = W.random_csr("perm", 14, 3, 64, 256, 90, lengths)  # 90 rows: many duplicates
+    perm = w.kv_indices.copy()
+    for t in range(3):
+        a, b = w.kv_indptr[t], w.kv_indptr[t + 1]
+        perm[a:b] = rng.permutation(perm[a:b])
+    log("case permutation")
+    ref = oracle_tokens(w, w.kv_indices, w.kv_indptr)
+    o1 = bf16_to_f64(run(spd, w, w.kv_indices, w.kv_indptr))
+    o2 = bf16_to_f64(run(spd, w, perm, w.kv_indptr))
+    assert_close(o1, ref, "original order")
+    assert_close(o2, ref, "permuted order")
+
+
+def test_repeated_rows_closed_form(spd):
+    """L copies of one row: out = r * L e^s / (L e^s + e^sink)."""
+    L = 300
+    w = W.random_csr("repeat", 15, 1, 16, 512, 4, [L])
+    w.kv_indices[:] = 2
+    log("case repeated row")
+    out = bf16_to_f64(run(spd, w, w.kv_indices, w.kv_indptr, max_len=L, split_rows=64))
+    r = W.bf16_to_f32(W.host_bits(w.kv_bits)[2]).astype(np.float64)
+    q = W.bf16_to_f32(W.host_bits(w.q_bits)[0]).astype(np.float64)
+    ref = np.zeros((1, 16, 512))
+    for h in range(16):
+        s = w.softmax_scale * float(q[h] @ r)
+        ref[0, h] = r * L * math.exp(s) / (L * math.exp(s) + math.exp(float(w.attn_sink[h])))
+    assert_close(out, ref, "repeated row")
+
+
+def test_deterministic(spd):
+    w = W.random_csr("det", 16, 8, 64, 512, 3000, [640, 1, 0, 333, 1000, 64, 65, 2000])
+    log("case determinism")
+    for plan in [dict(), dict(max_len=2000)]:
+        a = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
+        b = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_validate_indices(spd):
+    d = torch.device("cuda:0")
+    ptr = torch.tensor([0, 2, 2, 5], dtype=torch.int32, device=d)
+    idx = torch.tensor([0, 9, 3, 4, 1], dtype=torch.int32, device=d)
+    assert spd.validate_indices(idx, ptr, 10) == -1
+    assert spd.validate_indices(idx, ptr, 9) == 3 + 1 + 1      # kv_indices[1] == 9 out of range
+    bad_ptr = torch.tensor([0, 3, 2, 5], dtype=torch.int32, device=d)
+    assert spd.validate_indices(idx, bad_ptr, 10) == 2        # decreasing at t = 2

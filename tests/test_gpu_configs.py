@@ -1,0 +1,163 @@
+"""GPU parity at the benchmark configurations' full sizes (decode_base fully;
+ragged, large and prefill on sampled tokens that always include the longest,
+shortest and empty slices), in the launch configuration the benchmark times,
+plus HIP-graph capture and replay of builder + attention with fixed-shape
+buffers whose contents change between replays."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import (assert_close, bf16_to_f64, dev, device_builder_inputs, device_csr,
+                         device_inputs, log, oracle_tokens)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def spd():
+    import sparse_paged_decode_ragged_amd as m
+    return m
+
+
+@pytest.fixture
+def device_data():
+    W.set_data_mode("device", dev())
+    yield
+    W.set_data_mode("host")
+
+
+def sample_tokens(indptr: np.ndarray, n: int, seed: int) -> np.ndarray:
+    L = np.diff(indptr)
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(len(L), size=min(n, len(L)), replace=False).tolist())
+    pick |= {int(np.argmax(L)), int(np.argmin(L)), 0, len(L) - 1}
+    nz = np.nonzero(L)[0]
+    if len(nz):
+        pick.add(int(nz[np.argmin(L[nz])]))
+    return np.array(sorted(pick))
+
+
+def build_on_gpu(spd, b):
+    ss, sl, cp, bt = device_builder_inputs(b)
+    ptr, idx = spd.build_decode_indices(ss, sl, cp, bt, b.win, b.k_per_block, b.swa_pages)
+    torch.cuda.synchronize()
+    optr, oidx = oracle.build_decode_indices(b.state_slot, b.swa_len, b.comp_pos, b.block_table,
+                                             b.win, b.k_per_block, b.swa_pages)
+    assert np.array_equal(ptr.cpu().numpy(), optr)
+    assert np.array_equal(idx.cpu().numpy()[:optr[-1]], oidx)
+    return ptr, idx, optr, oidx
+
+
+def test_decode_base_end_to_end(spd):
+    w = W.decode_base()
+    log("case decode_base: builder + attention, all 64 tokens")
+    ptr, idx, optr, oidx = build_on_gpu(spd, w.builder)
+    ref = oracle_tokens(w, oidx, optr)
+    q, kv, sink = device_inputs(w)
+    for plan in [dict(max_len=640), dict(), dict(max_len=640, split_rows=64),
+                 dict(max_len=640, split_rows=320)]:
+        out = spd.sparse_decode_attn(q, kv, idx, ptr, sink, w.softmax_scale, **plan)
+        torch.cuda.synchronize()
+        assert_close(bf16_to_f64(out), ref, "decode_base %s" % plan)
+
+
+def test_ragged_config(spd, device_data):
+    w = W.ragged()
+    log("case ragged: N=256, L up to 2048, 25% padded")
+    tokens = sample_tokens(w.kv_indptr, 40, 1)
+    ref = oracle_tokens(w, w.kv_indices, w.kv_indptr, tokens)
+    q, kv, sink = device_inputs(w)
+    idx, ptr = device_csr(w.kv_indices, w.kv_indptr)
+    for plan in [dict(max_len=w.max_len), dict()]:
+        out = spd.sparse_decode_attn(q, kv, idx, ptr, sink, w.softmax_scale, **plan)
+        torch.cuda.synchronize()
+        assert_close(bf16_to_f64(out[torch.from_numpy(tokens).cuda()]), ref, "ragged %s" % plan)
+        assert torch.all(out[192:].view(torch.int16) == 0)
+
+
+def test_large_config(spd, device_data):
+    w = W.large()
+    log("case large: N=1024, H=128, 4 GiB pool, K_PER_BLOCK=64")
+    ptr, idx, optr, oidx = build_on_gpu(spd, w.builder)
+    tokens = sample_tokens(optr, 20, 3)
+    ref = oracle_tokens(w, oidx, optr, tokens)
+    q, kv, sink = device_inputs(w)
+    out = spd.sparse_decode_attn(q, kv, idx, ptr, sink, w.softmax_scale, max_len=w.max_len)
+    torch.cuda.synchronize()
+    assert_close(bf16_to_f64(out[torch.from_numpy(tokens).cuda()]), ref, "large")
+
+
+def test_prefill_config(spd, device_data):
+    w = W.prefill()
+    log("case prefill: N=8192, L up to 640, sliding reuse")
+    tokens = sample_tokens(w.kv_indptr, 30, 4)
+    ref = oracle_tokens(w, w.kv_indices, w.kv_indptr, tokens)
+    q, kv, sink = device_inputs(w)
+    idx, ptr = device_csr(w.kv_indices, w.kv_indptr)
+    out = spd.sparse_decode_attn(q, kv, idx, ptr, sink, w.softmax_scale, max_len=w.max_len)
+    torch.cuda.synchronize()
+    assert_close(bf16_to_f64(out[torch.from_numpy(tokens).cuda()]), ref, "prefill")
+
+
+def test_graph_capture_and_replay(spd):
+    """Capture builder + attention once; replay with new window lengths and
+    sentinel patterns copied into the same buffers; every replay must equal the
+    eager result bit for bit and the oracle within tolerance."""
+    N, H, D, P, win, topk = 24, 64, 512, 65536, 128, 512
+    w = W.window_plus_compressed("graph", 21, N, H, D, P, win, topk, 1)
+    b = w.builder
+    ss, sl, cp, bt = device_builder_inputs(b)
+    q, kv, sink = device_inputs(w)
+    cap = N * (win + topk)
+    ptr = torch.zeros(N + 1, dtype=torch.int32, device=dev())
+    idx = torch.zeros(cap, dtype=torch.int32, device=dev())
+    out = torch.zeros((N, H, D), dtype=torch.bfloat16, device=dev())
+    ws = torch.empty(spd.sparse_decode_attn_workspace_size(N, H, D, win + topk, 0),
+                     dtype=torch.uint8, device=dev())
+    log("case graph capture")
+
+    def step():
+        spd.build_decode_indices(ss, sl, cp, bt, win, 1, b.swa_pages, kv_indptr=ptr, kv_indices=idx)
+        spd.sparse_decode_attn(q, kv, idx, ptr, sink, w.softmax_scale, out=out,
+                               max_len=win + topk, workspace=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(5)
+    for rep in range(4):
+        new_sl = rng.integers(0, win + 1, size=N).astype(np.int32)
+        new_sl[rng.random(N) < 0.2] = 0
+        new_cp = b.comp_pos.copy()
+        new_cp[rng.random((N, topk)) < rng.random()] = -1
+        new_cp[rng.random(N) < 0.2] = -1
+        sl.copy_(torch.from_numpy(new_sl))
+        cp.copy_(torch.from_numpy(new_cp))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        graph_out = out.clone()
+        graph_ptr = ptr.clone()
+        # eager, into fresh buffers, with some unrelated eager work in between
+        _ = torch.randn(1 << 20, device=dev()).sum()
+        eptr, eidx = spd.build_decode_indices(ss, sl, cp, bt, win, 1, b.swa_pages)
+        eout = spd.sparse_decode_attn(q, kv, eidx, eptr, sink, w.softmax_scale, max_len=win + topk)
+        torch.cuda.synchronize()
+        assert torch.equal(graph_ptr, eptr)
+        assert torch.equal(graph_out.view(torch.int16), eout.view(torch.int16)), "replay %d" % rep
+        optr, oidx = oracle.build_decode_indices(b.state_slot, new_sl, new_cp, b.block_table, win, 1,
+                                                 b.swa_pages)
+        assert np.array_equal(graph_ptr.cpu().numpy(), optr)
+        toks = np.array([0, 5, 11, N - 1])
+        ref = oracle_tokens(w, oidx, optr, toks)
+        assert_close(bf16_to_f64(graph_out[torch.from_numpy(toks).cuda()]), ref, "graph replay %d" % rep)

@@ -100,8 +100,8 @@ class Workload:
     H: int
     D: int
     P: int
-    q_bits: np.ndarray          # [N, H, D] uint16
-    kv_bits: np.ndarray         # [P, D] uint16
+    q_bits: object              # [N, H, D] uint16 array (host mode) or bf16 tensor (device mode)
+    kv_bits: object             # [P, D] likewise
     attn_sink: np.ndarray       # [H] float32
     softmax_scale: float        # an fp32 value
     max_len: int                # capacity bound on every token's slice length
@@ -111,12 +111,62 @@ class Workload:
     meta: Dict[str, object] = field(default_factory=dict)
 
 
+# Where q and the pool are generated: "host" (numpy, uint16 bit arrays) or
+# "device" (torch on a GPU: Philox normal draws rounded to bf16 by torch, for
+# multi-GiB pools that would take a minute on the host).  Index structure and
+# sinks always come from the numpy generator.
+_DATA_MODE = {"mode": "host", "device": None}
+
+
+def set_data_mode(mode: str, device=None) -> None:
+    assert mode in ("host", "device")
+    _DATA_MODE["mode"] = mode
+    _DATA_MODE["device"] = device
+
+
+def device_normal_bf16(shape, seed: int, device, std: float = 1.0):
+    """bf16 torch tensor of N(0, std) draws from a seeded device generator, in chunks."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    flat = out.view(-1)
+    step = 1 << 26
+    for s in range(0, flat.numel(), step):
+        e = min(flat.numel(), s + step)
+        x = torch.randn(e - s, dtype=torch.float32, device=device, generator=gen)
+        if std != 1.0:
+            x.mul_(std)
+        flat[s:e] = x.to(torch.bfloat16)
+    return out
+
+
 def _finish(name, rng, N, H, D, P, sink_std, scale, max_len, **kw) -> Workload:
     sink = (rng.standard_normal(H) * sink_std).astype(np.float32)
-    q = normal_bf16(rng, (N, H, D))
-    kv = normal_bf16(rng, (P, D))
+    if _DATA_MODE["mode"] == "device":
+        base = int(rng.integers(0, 2 ** 62))
+        q = device_normal_bf16((N, H, D), base, _DATA_MODE["device"])
+        kv = device_normal_bf16((P, D), base + 1, _DATA_MODE["device"])
+    else:
+        q = normal_bf16(rng, (N, H, D))
+        kv = normal_bf16(rng, (P, D))
     return Workload(name=name, N=N, H=H, D=D, P=P, q_bits=q, kv_bits=kv, attn_sink=sink,
                     softmax_scale=float(np.float32(scale)), max_len=max_len, **kw)
+
+
+def host_bits(x) -> np.ndarray:
+    """uint16 bf16 bit patterns on the host, from a numpy array or a bf16 torch tensor."""
+    if isinstance(x, np.ndarray):
+        return x
+    return x.contiguous().view(dtype=__import__("torch").int16).cpu().numpy().view(np.uint16)
+
+
+def device_bits(x, device):
+    """bf16 torch tensor on `device`, from uint16 bit patterns or a bf16 torch tensor."""
+    import torch
+    if isinstance(x, np.ndarray):
+        return torch.from_numpy(x.view(np.int16)).to(device).view(torch.bfloat16)
+    return x.to(device)
 
 
 def csr_from_lists(lists) -> tuple:
