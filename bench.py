@@ -1,20 +1,27 @@
-"""Benchmark: one step = the whole hot path on one batch of synthetic input --
+"""Benchmark of the hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
 build_decode_indices (window ring + compressed slots -> ragged CSR) followed by
-sparse_decode_attn -- on the decode_base configuration (N=64 tokens, H=64,
-D=512, 640 pool rows per token, 64 MiB pool), through the C ABI.
+sparse_decode_attn, through the C ABI.  The default workload is decode_base
+(N=64 tokens, H=64, D=512, 640 pool rows per token: 128 window + 512
+compressed, 64 MiB pool), the configuration the metric is quoted on.  Other
+workloads (--workload) are for exploration; those given as ready CSR indices
+(ragged, prefill) have no builder step.
 
 Inputs are resident in HBM before timing starts.  R rotating input sets
 (separate pool, queries, builder inputs, outputs) keep the touched footprint
-above twice the 256 MB Infinity Cache, so steps are fed from HBM.  Each step
-is a HIP graph (captured once per set) replayed from the host.
+above twice the 256 MB Infinity Cache, so steps are fed from HBM.  Each step is
+a HIP graph captured once per set and replayed.
 
-Prints one JSON line: tokens/s (whole job), gathered KV GB/s, the roofline
-record of the attention call, and the oracle timed on the host's cores.
+Prints one JSON line: tokens/s for the whole job, gathered KV GB/s, the
+roofline record of the attention kernel, and the oracle timed on this host's
+cores on a bounded sample.
 """
 from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -26,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "sparse decode attn tokens/s + gathered KV GB/s (% of MI355X HBM roofline)"
+MALL_BYTES = 256 << 20
 
 
 def parse():
@@ -33,20 +41,69 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=200)
-    p.add_argument("--sets", type=int, default=16)
-    p.add_argument("--eager", action="store_true", help="launch kernels directly instead of graphs")
+    p.add_argument("--workload", default="decode_base",
+                   choices=["decode_base", "tiny", "ragged", "large", "prefill"])
+    p.add_argument("--mode", default="auto", choices=["auto", "heads", "rows"])
+    p.add_argument("--split-rows", type=int, default=0)
+    p.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = automatic)")
+    p.add_argument("--eager", action="store_true", help="launch kernels directly, no graphs")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
 
 
 def algorithmic_bytes(indptr: np.ndarray, N: int, H: int, D: int) -> dict:
+    """Bytes the method must move per call: gathered KV rows, q of non-empty
+    tokens, the output, the index list, indptr and the sinks."""
     L = np.diff(indptr.astype(np.int64))
     sum_l = int(L.sum())
     nonempty = int((L > 0).sum())
     kv = sum_l * D * 2
     total = kv + nonempty * H * D * 2 + N * H * D * 2 + 4 * sum_l + 4 * (N + 1) + 4 * H
-    return {"sum_L": sum_l, "kv_bytes": kv, "B_alg": total}
+    return {"sum_L": sum_l, "kv_bytes": kv, "B_alg": total, "nonempty": nonempty}
+
+
+def cpu_baseline(w, indptr, indices, seconds):
+    """The oracle as it stands, on this host's cores, on a bounded token sample."""
+    import oracle
+    import workloads as W
+    import torch
+    oracle.set_threads(os.cpu_count() or 1)
+    N = w.N
+    L = np.diff(indptr.astype(np.int64))
+    order = np.random.default_rng(0).permutation(N)
+
+    def run(tokens):
+        tokens = np.sort(tokens)
+        sl = [indices[indptr[t]:indptr[t + 1]] for t in tokens]
+        allidx = np.concatenate(sl) if sl else np.zeros(0, dtype=np.int32)
+        uniq, inv = np.unique(allidx, return_inverse=True)
+        if isinstance(w.kv_bits, np.ndarray):
+            rows = w.kv_bits[uniq]
+            qb = w.q_bits[tokens]
+        else:
+            rows = W.host_bits(w.kv_bits[torch.from_numpy(uniq.astype(np.int64)).to(w.kv_bits.device)])
+            qb = W.host_bits(w.q_bits[torch.from_numpy(tokens).to(w.q_bits.device)])
+        sub = np.zeros(len(tokens) + 1, dtype=np.int32)
+        sub[1:] = np.cumsum([len(x) for x in sl])
+        t0 = time.perf_counter()
+        oracle.sparse_decode_attn(qb, rows, inv.astype(np.int32), sub, w.attn_sink, w.softmax_scale)
+        return time.perf_counter() - t0
+
+    # size the sample from a short probe, then time whole passes over it
+    probe = order[: min(N, 8)]
+    dt = max(run(probe), 1e-4)
+    n = int(min(N, max(len(probe), len(probe) * 0.5 * seconds / dt)))
+    sample = order[:n]
+    reps, el = 0, 0.0
+    while el < seconds:
+        el += run(sample)
+        reps += 1
+    toks = reps * n
+    return {"value": round(toks / el, 2), "unit": "tokens/s", "cores": oracle.get_threads(),
+            "kind": "oracle",
+            "sample": "%d of %d tokens (%d pool rows gathered each pass, fp64 two-pass attention "
+                      "only), %d passes, %.1f s" % (n, N, int(L[sample].sum()), reps, el)}
 
 
 def main():
@@ -61,26 +118,34 @@ def main():
     import workloads as W
 
     dev = torch.device("cuda:0")
-    w = W.decode_base()
-    b = w.builder
+    if args.workload in ("ragged", "large", "prefill"):
+        W.set_data_mode("device", dev)
+    w = W.make(args.workload)
     N, H, D = w.N, w.H, w.D
     max_len = w.max_len
-    cap = b.capacity
-    ws_bytes = spd.sparse_decode_attn_workspace_size(N, H, D, max_len, 0)
-
+    mode = {"auto": spd.MODE_AUTO, "heads": spd.MODE_HEADS, "rows": spd.MODE_ROWS}[args.mode]
+    plan = spd.sparse_decode_attn_plan_info(N, H, D, max_len, args.split_rows, mode)
+    ws_bytes = spd.sparse_decode_attn_workspace_size(N, H, D, max_len, args.split_rows, mode)
+    b = w.builder
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    pool_bytes = w.P * D * 2
+    n_sets = args.sets or max(2, min(16, math.ceil(2 * MALL_BYTES / pool_bytes)))
     q0 = W.device_bits(w.q_bits, dev)
     kv0 = W.device_bits(w.kv_bits, dev)
     sets = []
-    for r in range(args.sets):
-        s = dict(q=q0.clone(), kv=kv0.clone(), sink=torch.from_numpy(w.attn_sink).to(dev),
-                 ss=t(b.state_slot), sl=t(b.swa_len), cp=t(b.comp_pos), bt=t(b.block_table),
-                 ptr=torch.zeros(N + 1, dtype=torch.int32, device=dev),
-                 idx=torch.zeros(cap, dtype=torch.int32, device=dev),
+    for r in range(n_sets):
+        s = dict(q=q0 if r == 0 else q0.clone(), kv=kv0 if r == 0 else kv0.clone(),
+                 sink=torch.from_numpy(w.attn_sink).to(dev),
                  out=torch.empty((N, H, D), dtype=torch.bfloat16, device=dev),
                  ws=torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev))
+        if b is not None:
+            s.update(ss=t(b.state_slot), sl=t(b.swa_len), cp=t(b.comp_pos), bt=t(b.block_table),
+                     ptr=torch.zeros(N + 1, dtype=torch.int32, device=dev),
+                     idx=torch.zeros(b.capacity, dtype=torch.int32, device=dev))
+        else:
+            s.update(ptr=t(w.kv_indptr), idx=t(w.kv_indices))
         sets.append(s)
-    del q0, kv0
 
     def build(s):
         spd.build_decode_indices(s["ss"], s["sl"], s["cp"], s["bt"], b.win, b.k_per_block,
@@ -88,28 +153,26 @@ def main():
 
     def attn(s):
         spd.sparse_decode_attn(s["q"], s["kv"], s["idx"], s["ptr"], s["sink"], w.softmax_scale,
-                               out=s["out"], max_len=max_len, workspace=s["ws"])
+                               out=s["out"], max_len=max_len, split_rows=args.split_rows,
+                               mode=mode, workspace=s["ws"])
 
     def step(s):
-        build(s)
+        if b is not None:
+            build(s)
         attn(s)
 
-    # eager warm-up, then one graph per set (full step) and one per set (attention only)
-    for s in sets:
+    for s in sets:  # eager warm-up (and the indices the graphs will rebuild)
         step(s)
     torch.cuda.synchronize()
     step_graphs, attn_graphs = [], []
     if not args.eager:
         cs = torch.cuda.Stream()
         for s in sets:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cs):
-                step(s)
-            step_graphs.append(g)
-            g2 = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g2, stream=cs):
-                attn(s)
-            attn_graphs.append(g2)
+            for fn, lst in ((step, step_graphs), (attn, attn_graphs)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cs):
+                    fn(s)
+                lst.append(g)
         torch.cuda.synchronize()
 
     def run_steps(k, graphs, fn):
@@ -119,34 +182,35 @@ def main():
             else:
                 fn(sets[i % len(sets)])
 
-    run_steps(args.warmup, step_graphs, step)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    run_steps(args.steps, step_graphs, step)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    ms_per_step = ms_total / args.steps
+    def timed(k, graphs, fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        run_steps(k, graphs, fn)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
 
-    # attention call alone (the dominant kernel), same rotation, for the roofline
+    run_steps(args.warmup, step_graphs, step)
+    ms_per_step = timed(args.steps, step_graphs, step) / args.steps
+    # the attention call alone, same rotation: the roofline record's kernel
     run_steps(min(args.warmup, 64), attn_graphs, attn)
-    torch.cuda.synchronize()
-    a0 = torch.cuda.Event(enable_timing=True)
-    a1 = torch.cuda.Event(enable_timing=True)
     n_attn = max(args.steps, 100)
-    a0.record()
-    run_steps(n_attn, attn_graphs, attn)
-    a1.record()
-    torch.cuda.synchronize()
-    us_attn = a0.elapsed_time(a1) * 1e3 / n_attn
+    us_attn = timed(n_attn, attn_graphs, attn) * 1e3 / n_attn
 
     indptr = sets[0]["ptr"].cpu().numpy()
+    indices = sets[0]["idx"].cpu().numpy()[: indptr[-1]]
     ab = algorithmic_bytes(indptr, N, H, D)
     tokens_per_s = N / (ms_per_step * 1e-3)
     gathered_gbps = ab["kv_bytes"] / (ms_per_step * 1e-3) / 1e9
     achieved = ab["B_alg"] / (us_attn * 1e-6) / 1e9
+    if plan["mode"] == "rows":
+        kernel = "attn_rows_kernel<%d>" % D
+    else:
+        kernel = "attn_heads_kernel<%d,%d>" % (D, plan["heads_per_group"] // 16)
+        if plan["splits"] > 1:
+            kernel += " + attn_combine_kernel"
 
     rec = {
         "metric": METRIC,
@@ -161,35 +225,20 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "decode_base", "N": N, "H": H, "D": D, "pool_rows": w.P,
-                   "indices_per_token": max_len, "window": b.win, "compressed_per_token": b.topk,
-                   "split_plan": "auto(max_len=%d)" % max_len, "rotating_sets": args.sets,
+        "config": {"workload": args.workload, "N": N, "H": H, "D": D, "pool_rows": w.P,
+                   "max_len": max_len, "sum_L": ab["sum_L"], "nonempty_tokens": ab["nonempty"],
+                   "plan": plan, "rotating_sets": n_sets,
                    "launch": "eager" if args.eager else "hip_graph_per_step",
-                   "step": "build_decode_indices + sparse_decode_attn"},
+                   "step": ("build_decode_indices + " if b is not None else "") + "sparse_decode_attn"},
         "gathered_kv_GBps": round(gathered_gbps, 1),
         "gathered_kv_frac_of_hbm_peak": round(gathered_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "sparse_decode_attn call (attn_main + attn_combine)",
-                     "us_per_call": round(us_attn, 3), "bytes_per_call": ab["B_alg"]},
+                     "kernel": kernel, "us_per_call": round(us_attn, 3),
+                     "bytes_per_call": ab["B_alg"]},
     }
-
     if not args.no_cpu_baseline:
-        import oracle
-        oracle.set_threads(os.cpu_count() or 1)
-        optr, oidx = oracle.build_decode_indices(b.state_slot, b.swa_len, b.comp_pos,
-                                                 b.block_table, b.win, b.k_per_block, b.swa_pages)
-        reps, t0 = 0, time.perf_counter()
-        while True:
-            oracle.sparse_decode_attn(w.q_bits, w.kv_bits, oidx, optr, w.attn_sink, w.softmax_scale)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds:
-                break
-        rec["cpu_baseline"] = {"value": round(N * reps / el, 2), "unit": "tokens/s",
-                               "cores": oracle.get_threads(), "kind": "oracle",
-                               "sample": "full decode_base batch (64 tokens, attention only, fp64 "
-                                         "two-pass) repeated %d times, %.1f s" % (reps, el)}
+        rec["cpu_baseline"] = cpu_baseline(w, indptr, indices, args.cpu_seconds)
     print(json.dumps(rec))
 
 

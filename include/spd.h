@@ -95,28 +95,55 @@ SPD_API spd_status sparse_decode_attn(const void* q, const void* unified_kv, int
                                       int32_t N, int32_t H, int32_t D, void* stream);
 
 /*
- * Workspace bytes that sparse_decode_attn_ex needs for (N, H, D, max_len,
- * split_rows); 0 when the plan does not split.  Returns 0 for unsupported or
- * invalid arguments (the call itself then reports the error).
+ * Work decompositions of sparse_decode_attn_ex.  Both give the same result
+ * within the accumulation tolerance; they differ in how the work of one token
+ * is spread over workgroups:
+ *   SPD_MODE_HEADS: a workgroup takes (token, up to 64 heads, partition); its
+ *                   waves split the heads and share every gathered row.
+ *   SPD_MODE_ROWS:  a workgroup takes (token, 16 heads); its 4 waves split
+ *                   the rows and merge in LDS -- more workgroups for small
+ *                   batches without partial results in memory.  No split-L.
+ *   SPD_MODE_AUTO:  ROWS when the batch gives fewer than 256 HEADS-mode
+ *                   workgroups and split_rows == 0, else HEADS.
  */
-SPD_API size_t sparse_decode_attn_workspace_size(int32_t N, int32_t H, int32_t D, int32_t max_len,
-                                                 int32_t split_rows);
+typedef enum spd_mode { SPD_MODE_AUTO = 0, SPD_MODE_HEADS = 1, SPD_MODE_ROWS = 2 } spd_mode;
 
 /*
- * sparse_decode_attn with a split-L plan.  max_len is a capacity bound on
+ * Workspace bytes that sparse_decode_attn_ex needs for (N, H, D, max_len,
+ * split_rows, mode); 0 when the plan does not split.  Returns 0 for
+ * unsupported or invalid arguments (the call itself then reports the error).
+ */
+SPD_API size_t sparse_decode_attn_workspace_size(int32_t N, int32_t H, int32_t D, int32_t max_len,
+                                                 int32_t split_rows, int32_t mode);
+
+/*
+ * The plan sparse_decode_attn_ex would use for these arguments, for callers
+ * that size buffers or report what runs: info[0] = mode actually used
+ * (SPD_MODE_HEADS or SPD_MODE_ROWS), info[1] = heads per workgroup, info[2] =
+ * head groups, info[3] = split-L partitions (1 = none), info[4] = rows per
+ * partition.  info is a host array of 5 int32.  Returns SPD_ERR_INVALID_ARG or
+ * SPD_ERR_UNSUPPORTED exactly when sparse_decode_attn_ex would.
+ */
+SPD_API spd_status sparse_decode_attn_plan_info(int32_t N, int32_t H, int32_t D, int32_t max_len,
+                                                int32_t split_rows, int32_t mode, int32_t* info);
+
+/*
+ * sparse_decode_attn with a chosen plan.  max_len is a capacity bound on
  * every slice length, used only to size the grid and the workspace (a longer
- * slice is still computed correctly, by its last partition).  split_rows
- * fixes the partition length (rounded up to a multiple of 32); 0 chooses it
- * from N, H and max_len.  Partitions of one token are merged by a combine
- * kernel (the attention sink is counted once).  workspace/workspace_bytes: a
- * caller-owned device buffer of at least sparse_decode_attn_workspace_size
- * bytes (may be NULL when that size is 0); no state survives between calls.
+ * slice is still computed correctly, by its last partition); 0 = unknown.
+ * split_rows fixes the split-L partition length (rounded up to a multiple of
+ * 32, HEADS mode only; SPD_ERR_UNSUPPORTED with SPD_MODE_ROWS); 0 lets the
+ * plan choose from N, H and max_len.  mode is an spd_mode.  Partitions of one
+ * token are merged by a combine kernel (the attention sink is counted once).
+ * workspace/workspace_bytes: a caller-owned device buffer of at least
+ * sparse_decode_attn_workspace_size bytes, 16-byte aligned (may be NULL when
+ * that size is 0); no state survives between calls.
  */
 SPD_API spd_status sparse_decode_attn_ex(const void* q, const void* unified_kv, int64_t num_rows,
                                          const int32_t* kv_indices, const int32_t* kv_indptr,
                                          const float* attn_sink, float softmax_scale, void* out,
                                          int32_t N, int32_t H, int32_t D, int32_t max_len,
-                                         int32_t split_rows, void* workspace,
+                                         int32_t split_rows, int32_t mode, void* workspace,
                                          size_t workspace_bytes, void* stream);
 
 /*

@@ -33,7 +33,7 @@ _STATUS = {0: "SPD_OK", 1: "SPD_ERR_INVALID_ARG", 2: "SPD_ERR_UNSUPPORTED", 3: "
 EXPORTED_SYMBOLS = (
     "spd_status_string", "spd_version", "sparse_decode_attn_can_use", "sparse_decode_attn",
     "sparse_decode_attn_workspace_size", "sparse_decode_attn_ex", "build_decode_indices",
-    "spd_validate_indices",
+    "spd_validate_indices", "sparse_decode_attn_plan_info",
 )
 
 
@@ -57,15 +57,18 @@ def _load() -> ctypes.CDLL:
     lib.sparse_decode_attn_can_use.restype = ctypes.c_int
     lib.sparse_decode_attn.argtypes = [P, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32, P]
     lib.sparse_decode_attn.restype = ctypes.c_int
-    lib.sparse_decode_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.sparse_decode_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.sparse_decode_attn_workspace_size.restype = sz
     lib.sparse_decode_attn_ex.argtypes = [P, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32, i32,
-                                          i32, P, sz, P]
+                                          i32, i32, P, sz, P]
     lib.sparse_decode_attn_ex.restype = ctypes.c_int
     lib.build_decode_indices.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i32, P, P, i64, P]
     lib.build_decode_indices.restype = ctypes.c_int
     lib.spd_validate_indices.argtypes = [P, i64, P, i32, i64, ctypes.POINTER(ctypes.c_int64), P]
     lib.spd_validate_indices.restype = ctypes.c_int
+    lib.sparse_decode_attn_plan_info.argtypes = [i32, i32, i32, i32, i32, i32,
+                                                 ctypes.POINTER(ctypes.c_int32)]
+    lib.sparse_decode_attn_plan_info.restype = ctypes.c_int
     return lib
 
 
@@ -102,22 +105,39 @@ def sparse_decode_attn_can_use(H: int, D: int) -> bool:
     return bool(lib.sparse_decode_attn_can_use(int(H), int(D)))
 
 
+MODE_AUTO, MODE_HEADS, MODE_ROWS = 0, 1, 2
+
+
 def sparse_decode_attn_workspace_size(N: int, H: int, D: int, max_len: int = 0,
-                                      split_rows: int = 0) -> int:
+                                      split_rows: int = 0, mode: int = MODE_AUTO) -> int:
     return int(lib.sparse_decode_attn_workspace_size(int(N), int(H), int(D), int(max_len),
-                                                     int(split_rows)))
+                                                     int(split_rows), int(mode)))
+
+
+def sparse_decode_attn_plan_info(N: int, H: int, D: int, max_len: int = 0, split_rows: int = 0,
+                                 mode: int = MODE_AUTO) -> dict:
+    info = (ctypes.c_int32 * 5)()
+    st = lib.sparse_decode_attn_plan_info(int(N), int(H), int(D), int(max_len), int(split_rows),
+                                          int(mode), info)
+    _raise_on(st, "sparse_decode_attn_plan_info")
+    return {"mode": {1: "heads", 2: "rows"}[info[0]], "heads_per_group": info[1],
+            "head_groups": info[2], "splits": info[3],
+            "split_rows": info[4] if info[3] > 1 else None}
 
 
 def sparse_decode_attn(q: torch.Tensor, unified_kv: torch.Tensor, kv_indices: torch.Tensor,
                        kv_indptr: torch.Tensor, attn_sink: torch.Tensor, softmax_scale: float,
                        out: Optional[torch.Tensor] = None, *, max_len: int = 0,
-                       split_rows: int = 0, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                       split_rows: int = 0, mode: int = MODE_AUTO,
+                       workspace: Optional[torch.Tensor] = None,
+                       plain: bool = False) -> torch.Tensor:
     """out[N, H, D] (bf16) = sparse decode attention; see include/spd.h.
 
-    max_len == 0 and split_rows == 0 select the plain call (no split-L, no
-    workspace).  Otherwise the split-L form runs; ``workspace`` (a device
-    tensor of at least ``sparse_decode_attn_workspace_size`` bytes) is
-    allocated here when not given -- pass one in when capturing a graph.
+    plain=True calls the spec form ``sparse_decode_attn`` (automatic
+    plan, never split-L, no workspace).  Otherwise ``sparse_decode_attn_ex``
+    runs with (max_len, split_rows, mode); ``workspace`` (a device tensor of
+    at least ``sparse_decode_attn_workspace_size`` bytes) is allocated here
+    when needed and not given -- pass one in when capturing a graph.
     """
     _check(q, "q", torch.bfloat16, 3)
     _check(unified_kv, "unified_kv", torch.bfloat16, 2)
@@ -135,19 +155,19 @@ def sparse_decode_attn(q: torch.Tensor, unified_kv: torch.Tensor, kv_indices: to
             raise ValueError("out must be [N, H, D]")
     idx = kv_indices if kv_indices.numel() > 0 else kv_indptr  # any valid pointer; never read
     stream = _stream(q.device)
-    if max_len == 0 and split_rows == 0:
+    if plain:
         st = lib.sparse_decode_attn(_ptr(q), _ptr(unified_kv), unified_kv.shape[0], _ptr(idx),
                                     _ptr(kv_indptr), _ptr(attn_sink), float(softmax_scale),
                                     _ptr(out), N, H, D, stream)
         _raise_on(st, "sparse_decode_attn")
         return out
-    need = sparse_decode_attn_workspace_size(N, H, D, max_len, split_rows)
+    need = sparse_decode_attn_workspace_size(N, H, D, max_len, split_rows, mode)
     if need > 0 and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.sparse_decode_attn_ex(_ptr(q), _ptr(unified_kv), unified_kv.shape[0], _ptr(idx),
                                    _ptr(kv_indptr), _ptr(attn_sink), float(softmax_scale),
-                                   _ptr(out), N, H, D, int(max_len), int(split_rows),
+                                   _ptr(out), N, H, D, int(max_len), int(split_rows), int(mode),
                                    _ptr(workspace), ws_bytes, stream)
     _raise_on(st, "sparse_decode_attn_ex")
     return out

@@ -42,20 +42,40 @@ SPD_API int sparse_decode_attn_can_use(int32_t H, int32_t D) {
 }
 
 SPD_API size_t sparse_decode_attn_workspace_size(int32_t N, int32_t H, int32_t D, int32_t max_len,
-                                                 int32_t split_rows) {
+                                                 int32_t split_rows, int32_t mode) {
   spd::AttnPlan plan;
-  if (!spd::make_attn_plan(N, H, D, max_len, split_rows, &plan)) return 0;
+  if (!spd::make_attn_plan(N, H, D, max_len, split_rows, mode, &plan)) return 0;
   return plan.workspace_bytes;
+}
+
+SPD_API spd_status sparse_decode_attn_plan_info(int32_t N, int32_t H, int32_t D, int32_t max_len,
+                                                int32_t split_rows, int32_t mode, int32_t* info) {
+  if (!info || N < 0 || H <= 0 || D <= 0 || max_len < 0 || split_rows < 0) return SPD_ERR_INVALID_ARG;
+  if (mode != SPD_MODE_AUTO && mode != SPD_MODE_HEADS && mode != SPD_MODE_ROWS)
+    return SPD_ERR_INVALID_ARG;
+  if (!spd::attn_supported(H, D)) return SPD_ERR_UNSUPPORTED;
+  if (mode == SPD_MODE_ROWS && split_rows != 0) return SPD_ERR_UNSUPPORTED;
+  spd::AttnPlan plan;
+  if (!spd::make_attn_plan(N, H, D, max_len, split_rows, mode, &plan)) return SPD_ERR_INVALID_ARG;
+  info[0] = plan.mode;
+  info[1] = plan.heads_per_group;
+  info[2] = plan.head_groups;
+  info[3] = plan.splits;
+  info[4] = plan.split_rows;
+  return SPD_OK;
 }
 
 SPD_API spd_status sparse_decode_attn_ex(const void* q, const void* unified_kv, int64_t num_rows,
                                          const int32_t* kv_indices, const int32_t* kv_indptr,
                                          const float* attn_sink, float softmax_scale, void* out,
                                          int32_t N, int32_t H, int32_t D, int32_t max_len,
-                                         int32_t split_rows, void* workspace,
+                                         int32_t split_rows, int32_t mode, void* workspace,
                                          size_t workspace_bytes, void* stream) {
   if (N < 0 || H <= 0 || D <= 0 || num_rows <= 0 || max_len < 0 || split_rows < 0)
     return SPD_ERR_INVALID_ARG;
+  if (mode != SPD_MODE_AUTO && mode != SPD_MODE_HEADS && mode != SPD_MODE_ROWS)
+    return SPD_ERR_INVALID_ARG;
+  if (mode == SPD_MODE_ROWS && split_rows != 0) return SPD_ERR_UNSUPPORTED;
   if (!isfinite(softmax_scale)) return SPD_ERR_INVALID_ARG;
   if (!spd::attn_supported(H, D)) return SPD_ERR_UNSUPPORTED;
   if (N == 0) return SPD_OK;
@@ -73,7 +93,7 @@ SPD_API spd_status sparse_decode_attn_ex(const void* q, const void* unified_kv, 
     return SPD_ERR_INVALID_ARG;
 
   spd::AttnPlan plan;
-  if (!spd::make_attn_plan(N, H, D, max_len, split_rows, &plan)) return SPD_ERR_INVALID_ARG;
+  if (!spd::make_attn_plan(N, H, D, max_len, split_rows, mode, &plan)) return SPD_ERR_INVALID_ARG;
   if (plan.workspace_bytes > 0) {
     if (!workspace || workspace_bytes < plan.workspace_bytes) return SPD_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return SPD_ERR_INVALID_ARG;
@@ -102,7 +122,8 @@ SPD_API spd_status sparse_decode_attn(const void* q, const void* unified_kv, int
                                       const float* attn_sink, float softmax_scale, void* out,
                                       int32_t N, int32_t H, int32_t D, void* stream) {
   return sparse_decode_attn_ex(q, unified_kv, num_rows, kv_indices, kv_indptr, attn_sink,
-                               softmax_scale, out, N, H, D, 0, 0, nullptr, 0, stream);
+                               softmax_scale, out, N, H, D, 0, 0, SPD_MODE_AUTO, nullptr, 0,
+                               stream);
 }
 
 SPD_API spd_status build_decode_indices(const int32_t* state_slot, const int32_t* swa_len,

@@ -8,24 +8,31 @@
 // qk_scale = softmax_scale * log2(e); an empty slice gives zeros.
 //
 // Kernel design (MI355X-first, not a translation of the page's kernel):
-//   * one workgroup = (token, group of 16*W heads, partition of the slice);
-//     wave w owns heads [16w, 16w+16) of the group, so every gathered row is
-//     loaded once per workgroup and shared by all of its heads;
-//   * rows are gathered 32 at a time straight into LDS with
-//     global_load_lds_dwordx4 (one 1 KiB row per wave instruction at D=512),
-//     three stages in flight, XOR-swizzled by row so that both LDS read
-//     patterns below are bank-conflict free;
-//   * S^T = K Q^T on MFMA 16x16x32 bf16: A = K rows read from LDS, B = Q^T
-//     held in VGPRs for the whole slice;
-//   * the S^T accumulator layout (lane = head, 4 rows per lane) is exactly the
-//     B operand layout of O^T += V^T P^T, so P never leaves registers; V^T is
-//     read from the same LDS rows with ds_read_b64_tr_b16 (the 16-lane
-//     transpose read of gfx950);
-//   * the online softmax statistics live per lane (lane = head), so the
-//     rescale of the accumulator needs no cross-lane traffic; only the tile
-//     maximum is reduced across the four 16-lane groups;
-//   * long slices are split into partitions (split-L); partials (m, l, O) go
-//     to a workspace and a combine kernel merges them, counting the sink once.
+//   * rows are gathered straight into LDS with LDS-DMA loads
+//     (global_load_lds_dwordx4: one 1 KiB row per wave instruction at D=512),
+//     XOR-swizzled by row so that both LDS read patterns below are
+//     bank-conflict free; the row indices of a partition are staged into LDS
+//     first (global_load_lds_dword, 64 per instruction), so issuing a row load
+//     never waits on memory;
+//   * S^T = K Q^T on MFMA bf16 with A = K rows from LDS and B = Q^T held in
+//     VGPRs for the whole slice; the S^T accumulator layout (lane = head, four
+//     rows per lane) is exactly the B operand layout of O^T += V^T P^T, so P
+//     never leaves registers; V^T is read from the same LDS rows with
+//     ds_read_b64_tr_b16 (the 16-lane transpose read of gfx950);
+//   * the online-softmax state lives per lane (lane = head), so rescaling the
+//     accumulator needs no cross-lane traffic; the reference maximum is only
+//     raised when a score exceeds it by more than 2^8, so rescales are rare;
+//   * two decompositions of the work of one token:
+//       heads  -- workgroup = (token, 16*W heads, partition); wave w owns 16
+//                 heads and all waves share each 32-row tile (for batches
+//                 that already provide hundreds of workgroups);
+//       rows   -- workgroup = (token, 16 heads); its 4 waves take every 4th
+//                 16-row tile into private LDS stages (no barriers in the
+//                 loop) and merge their (m, l, O) in LDS at the end (for
+//                 small batches: 4x the workgroups, no partials in memory);
+//   * long slices may also be split across workgroups (split-L); partials
+//     (m, l, O) go to a workspace and a combine kernel merges them, counting
+//     the sink once.
 #include <math.h>
 
 #include "spd_internal.h"
@@ -35,12 +42,15 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(4))) int32_t* ScalarI32Ptr;
 typedef __attribute__((address_space(3))) bf16x4 LdsBf16x4;
 
-constexpr int kStages = 3;
+constexpr int kStages = 3;                 // heads mode: 32-row tiles in flight
+constexpr int kIdxCap = 2048;              // row indices staged in LDS at a time
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;              // log2 headroom before the reference max moves
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] in bits
 // 3:0, vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt left at their maxima).
@@ -51,26 +61,34 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Workgroup barrier without a memory fence: the LDS data it publishes was
-// written by this workgroup's own LDS-DMA loads, which each wave has already
-// waited for with wait_vmcnt.  The empty asm keeps the compiler from moving
-// memory accesses across it.
-__device__ __forceinline__ void barrier_no_fence() {
+// written by LDS-DMA loads that each wave has already waited for with
+// wait_vmcnt, or by ordinary LDS stores, which lgkmcnt(0) completes before
+// the barrier.  The empty asm keeps the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// XOR swizzle of the 16-byte chunks of LDS row r.  Rows 0..15 map to 16
-// distinct chunk positions (QK reads: 16 rows, same logical chunk) and any 4
-// consecutive rows map to distinct chunk pairs (transpose reads: 4 rows x 32 B).
-__device__ __forceinline__ int row_swizzle(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// XOR swizzle of the 16-byte chunks of LDS row r: chunk c is stored at
+// c ^ (r & 15).  Rows 0..15 then put any one logical chunk in 16 different
+// bank positions; among the layouts measured on gfx950 for the K reads (16
+// rows, one 16-byte chunk each) and the transpose reads (4 rows x 32 bytes),
+// this one gives the highest K-read rate at a near-equal transpose rate.
+__device__ __forceinline__ int row_swizzle(int r) { return r & 15; }
 
-// One 64-lane LDS-DMA load: lane i copies 16 bytes from its global address to
-// LDS bytes [lds + 16 i, lds + 16 i + 16).  Issued through asm so that the
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// LDS-DMA loads: lane i copies 4 or 16 bytes from its global address to LDS
+// bytes [lds + size*i, lds + size*(i+1)).  Issued through asm so that the
 // compiler's wait-count pass does not treat every later LDS read as depending
-// on it (it would otherwise drain all prefetched tiles before the transpose
-// reads); the kernel waits for these loads itself with wait_vmcnt.
-// m0 (which the instruction takes the LDS address from) is saved and restored
-// inside the asm, since the compiler treats it as a reserved register.
+// on them (it would otherwise drain all prefetched tiles before the transpose
+// reads); the kernels wait for these loads themselves with wait_vmcnt.  m0,
+// which holds the LDS address, is saved and restored inside the asm since the
+// compiler treats it as a reserved register.
 __device__ __forceinline__ void dma_16B(const void* gaddr, uint32_t lds_byte_addr) {
   uint32_t saved;
   asm volatile(
@@ -83,12 +101,40 @@ __device__ __forceinline__ void dma_16B(const void* gaddr, uint32_t lds_byte_add
       : "memory");
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+// Same as dma_16B with the address split into a wave-uniform base (SGPRs)
+// and a per-lane 32-bit offset.
+__device__ __forceinline__ void dma_16B_s(uint32_t lane_off, const void* sbase,
+                                          uint32_t lds_byte_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(lane_off), "s"(sbase), "s"(lds_byte_addr)
+      : "memory");
 }
 
-__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+__device__ __forceinline__ void dma_4B(const void* gaddr, uint32_t lds_byte_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gaddr), "s"(lds_byte_addr)
+      : "memory");
+}
+
+__device__ __forceinline__ f32x4 mfma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_k16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
 // Map the linear workgroup id to a work item so that consecutive work items
@@ -106,8 +152,104 @@ __device__ __forceinline__ int partitions_of(int L, int splits, int split_rows) 
   return n < splits ? n : splits;
 }
 
+// Stage the row indices [base, base + n) of a partition (n <= kIdxCap) into
+// sidx[0, n): wave w of nw issues the 64-entry groups w, w + nw, ...; each lane
+// clamps its position to the last row, so no load leaves the partition.
+__device__ __forceinline__ void stage_indices(const int32_t* part, int base, int n, int* sidx,
+                                              int wave, int nw, int lane) {
+  for (int g0 = wave * 64; g0 < n; g0 += nw * 64) {
+    const int p = g0 + lane < n ? g0 + lane : n - 1;
+    dma_4B(part + base + p, __builtin_amdgcn_readfirstlane(lds_addr(sidx + g0)));
+  }
+}
+
+// Stage attn_sink[h0 .. h0 + nh) into ssink[0, nh) (nh <= 64) with one LDS-DMA
+// load issued by wave 0, so that it completes with the index staging instead
+// of adding a dependent memory round trip before it.
+__device__ __forceinline__ void stage_sinks(const float* sink, int H, int h0, float* ssink,
+                                            int wave, int lane) {
+  if (wave == 0) {
+    const int h = h0 + lane < H ? h0 + lane : H - 1;
+    dma_4B(sink + h, __builtin_amdgcn_readfirstlane(lds_addr(ssink)));
+  }
+}
+
+// Issue the LDS-DMA loads of kRows consecutive rows of a tile: tile rows
+// [r0, r0 + kRows) whose staged indices start at sidx[p0] (positions past the
+// partition's n rows repeat its last row, so a ragged tail never reads stale
+// LDS), into LDS at dst (kLoads * 1024 bytes).  rbase is the first row's index
+// within its tile (it selects the XOR swizzle).  At D = 512 a load is one row:
+// the wave reads all its indices with one LDS read and broadcasts them with
+// v_readlane, instead of one dependent LDS round trip per load.
+template <int kRowBytes, int kLoads>
+__device__ __forceinline__ void issue_rows(const uint16_t* kv, const int* sidx, int n, int p0,
+                                           int rbase, unsigned char* dst, int lane) {
+  constexpr int kChunks = kRowBytes / 16;
+  constexpr int kRowsPerLoad = 1024 / kRowBytes;
+  static_assert(kLoads <= 64, "one lane per row index");
+  const unsigned char* base = reinterpret_cast<const unsigned char*>(kv);
+  if constexpr (kRowsPerLoad == 1) {
+    int p = p0 + (lane < kLoads ? lane : 0);
+    const int mine = sidx[p < n ? p : n - 1];
+    const uint32_t dst0 = __builtin_amdgcn_readfirstlane(lds_addr(dst));
+#pragma unroll
+    for (int ld = 0; ld < kLoads; ++ld) {
+      const int grow = __builtin_amdgcn_readlane(mine, ld);  // row index, wave-uniform
+      const unsigned char* rowp = base + (int64_t)grow * kRowBytes;
+      const uint32_t lane_off = (uint32_t)((lane ^ (row_swizzle(rbase + ld) & (kChunks - 1))) << 4);
+      dma_16B_s(lane_off, rowp, dst0 + ld * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int ld = 0; ld < kLoads; ++ld) {
+      const int rr = ld * kRowsPerLoad + lane / kChunks;
+      const int p = p0 + rr;
+      const int grow = sidx[p < n ? p : n - 1];
+      const int lchunk = (lane % kChunks) ^ (row_swizzle(rbase + rr) & (kChunks - 1));
+      dma_16B(base + (int64_t)grow * kRowBytes + lchunk * 16,
+              __builtin_amdgcn_readfirstlane(lds_addr(dst + ld * 1024)));
+    }
+  }
+}
+
+// Q^T operand of S^T = K Q^T: lane (n16, g) holds q[t, h, 32s + 8g .. +7].
+// Lanes of padding heads (h >= H) load a valid row instead; their results are
+// never stored, and nothing consumes the values here, so the compiler does not
+// wait for these loads before the index staging that follows.
 template <int D>
-__device__ __forceinline__ void store_bf16_row4(uint16_t* dst, f32x4 v, float inv) {
+__device__ __forceinline__ void load_q(const uint16_t* q, int64_t row, int g,
+                                       bf16x8 (&qreg)[D / 32]) {
+  const uint16_t* qp = q + row * D + 8 * g;
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
+}
+
+// Initial online-softmax state of a lane: the sink (log2 logit sink*log2(e))
+// as a virtual key with weight 1, in exactly one state per head (`owner`), and
+// in lane group 0 only since the per-lane denominators are summed over the
+// four 16-lane groups at the end.
+__device__ __forceinline__ void init_state(float sink_raw, bool owner, int g, float& m,
+                                           float& lpart) {
+  m = -INFINITY;
+  lpart = 0.f;
+  if (owner) {
+    const float sk = sink_raw * kLog2e;
+    m = sk;
+    if (g == 0 && sk > -INFINITY) lpart = 1.f;
+  }
+}
+
+// Write zeros for heads [h0, h0 + nh) of token t (empty slice).
+template <int D>
+__device__ __forceinline__ void zero_heads(uint16_t* out, int H, int t, int h0, int nh, int tid,
+                                           int nthreads) {
+  if (nh <= 0) return;
+  uint4* dst = reinterpret_cast<uint4*>(out + ((int64_t)t * H + h0) * D);
+  const int n = nh * D / 8;
+  for (int i = tid; i < n; i += nthreads) dst[i] = make_uint4(0, 0, 0, 0);
+}
+
+__device__ __forceinline__ void store_bf16x4(uint16_t* dst, f32x4 v, float inv) {
   bf16x4 o;
   o[0] = (__bf16)(v[0] * inv);
   o[1] = (__bf16)(v[1] * inv);
@@ -116,21 +258,77 @@ __device__ __forceinline__ void store_bf16_row4(uint16_t* dst, f32x4 v, float in
   *reinterpret_cast<bf16x4*>(dst) = o;
 }
 
+// Maximum / sum over the four 16-lane groups (lanes n16, n16+16, n16+32,
+// n16+48) with v_permlane32_swap / v_permlane16_swap: pure VALU, so it does not
+// wait behind LDS reads still in flight (ds_bpermute would).  Each swap returns
+// this lane's value and its partner's (lane ^ 32, then lane ^ 16).
+__device__ __forceinline__ float group_max4(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = fmaxf(__builtin_bit_cast(float, (unsigned)a[0]), __builtin_bit_cast(float, (unsigned)a[1]));
+  const unsigned w = __builtin_bit_cast(unsigned, v);
+  auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)b[0]), __builtin_bit_cast(float, (unsigned)b[1]));
+}
+
+__device__ __forceinline__ float group_sum4(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = __builtin_bit_cast(float, (unsigned)a[0]) + __builtin_bit_cast(float, (unsigned)a[1]);
+  const unsigned w = __builtin_bit_cast(unsigned, v);
+  auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return __builtin_bit_cast(float, (unsigned)b[0]) + __builtin_bit_cast(float, (unsigned)b[1]);
+}
+
+// Reference-max update and weights for one tile.  x[] are log2-domain scores
+// of this lane's rows (-inf for rows past the end), all of head n16.  Raises m
+// only when a score exceeds it by more than kLazy (wave-uniform decision; the
+// accumulator is rescaled then), and returns the weights 2^(x - m) as bf16.
+template <int R, int NACC>
+__device__ __forceinline__ void softmax_step(const float (&x)[R], float& m, float& lpart,
+                                             f32x4 (&acc)[NACC], __bf16 (&p)[R]) {
+  float mx = x[0];
+#pragma unroll
+  for (int j = 1; j < R; ++j) mx = fmaxf(mx, x[j]);
+  mx = group_max4(mx);
+  const bool raise = mx > m + kLazy;
+  if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+    const float mnew = raise ? mx : m;
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // 0 when m was -inf
+    lpart *= alpha;
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) acc[i] *= alpha;
+    m = mnew;
+  }
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    p[j] = (__bf16)__builtin_amdgcn_exp2f(x[j] - m);
+    psum += (float)p[j];  // the denominator sums the same rounded weights as PV
+  }
+  lpart += psum;
+}
+
+// ---------------------------------------------------------------------------
+// heads mode: workgroup = (token, 16*W heads, partition); 32-row shared tiles.
 template <int D, int W>
-__global__ void __launch_bounds__(64 * W) attn_main_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(64 * W) attn_heads_kernel(AttnArgs a) {
+  constexpr int kTile = 32;
   constexpr int kRowBytes = 2 * D;
   constexpr int kChunks = D / 8;  // 16-byte chunks per row
-  constexpr int kStageBytes = kTileRows * kRowBytes;
+  constexpr int kStageBytes = kTile * kRowBytes;
   constexpr int kKSteps = D / 32;
   constexpr int kDTiles = D / 16;
   constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows filled by one 64-lane x 16 B load
-  constexpr int kLoadsPerTile = kTileRows / kRowsPerLoad;
+  constexpr int kLoadsPerTile = kTile / kRowsPerLoad;
   constexpr int kLoadsPerWave = kLoadsPerTile / W;
   constexpr int kHeads = 16 * W;
   static_assert(D % 64 == 0 && D <= 512, "unsupported D");
   static_assert(kLoadsPerTile % W == 0, "loads must divide among waves");
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(256))) int sidx[kIdxCap];
+  __shared__ __attribute__((aligned(256))) float ssink[64];
 
   const int item = xcd_item(blockIdx.x, gridDim.x);
   const int c = item % a.splits;
@@ -154,86 +352,20 @@ __global__ void __launch_bounds__(64 * W) attn_main_kernel(AttnArgs a) {
   const bool hvalid = h < a.H;
 
   if (L <= 0) {
-    // Empty slice: the output is exactly zero.
-    const int nh = a.H - h0 < 16 ? a.H - h0 : 16;
-    if (nh > 0) {
-      uint4* dst = reinterpret_cast<uint4*>(a.out + ((int64_t)t * a.H + h0) * D);
-      const int n16b = nh * D / 8;
-      for (int i = lane; i < n16b; i += 64) dst[i] = make_uint4(0, 0, 0, 0);
-    }
+    zero_heads<D>(a.out, a.H, t, h0, a.H - h0 < 16 ? a.H - h0 : 16, lane, 64);
     return;
   }
 
   const int cb = c * a.split_rows;
   const int nrows = (c == nparts - 1) ? L - cb : a.split_rows;
-  const ScalarI32Ptr cidx = (ScalarI32Ptr)(a.kv_indices + row0 + cb);
-  const int ntiles = (nrows + kTileRows - 1) / kTileRows;
+  const int32_t* part = a.kv_indices + row0 + cb;
 
-  // Issue the LDS-DMA loads of tile `tile` (rows clamped to the last row of the
-  // partition, so a ragged tail re-reads a valid row instead of stale LDS).
-  auto issue_tile = [&](int tile) {
-    unsigned char* st = smem + (tile % kStages) * kStageBytes;
-    const int rbase = tile * kTileRows;
-#pragma unroll
-    for (int j = 0; j < kLoadsPerWave; ++j) {
-      const int ld = wave * kLoadsPerWave + j;
-      const int rfirst = ld * kRowsPerLoad;
-      int grow;
-      int rr;
-      if constexpr (kRowsPerLoad == 1) {
-        const int p = rbase + rfirst;
-        grow = cidx[p < nrows ? p : nrows - 1];
-        rr = rfirst;
-      } else {
-        const int sub = lane / kChunks;
-        rr = rfirst + sub;
-        grow = 0;
-#pragma unroll
-        for (int u = 0; u < kRowsPerLoad; ++u) {
-          const int p = rbase + rfirst + u;
-          const int v = cidx[p < nrows ? p : nrows - 1];
-          if (sub == u) grow = v;
-        }
-      }
-      const int pchunk = lane % kChunks;
-      const int lchunk = pchunk ^ (row_swizzle(rr) & (kChunks - 1));
-      const unsigned char* src =
-          reinterpret_cast<const unsigned char*>(a.kv) + (int64_t)grow * kRowBytes + lchunk * 16;
-      dma_16B(src, __builtin_amdgcn_readfirstlane(lds_addr(st + ld * 1024)));
-    }
-  };
-
-  // Prologue: the first two tiles go out before the query loads, so that the
-  // compiler's waits for the queries (it cannot see the asm DMA loads) cost no
-  // more than waiting for tile 0, which the first step needs anyway.
-  issue_tile(0);
-  if (ntiles > 1) issue_tile(1);
-
-  // Q^T operand: lane (n16, g) holds q[t, h, 32s + 8g .. +7] for k-step s.
   bf16x8 qreg[kKSteps];
-  {
-    const uint16_t* qp = a.q + ((int64_t)t * a.H + (hvalid ? h : 0)) * D + 8 * g;
-#pragma unroll
-    for (int s = 0; s < kKSteps; ++s) {
-      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
-      if (!hvalid) v = bf16x8{};
-      qreg[s] = v;
-    }
-  }
+  load_q<D>(a.q, (int64_t)t * a.H + (hvalid ? h : 0), g, qreg);
+  stage_sinks(a.sink, a.H, hg * kHeads, ssink, wave, lane);
 
-  // Online-softmax state.  The sink enters once, in partition 0, as a virtual
-  // key whose log2 logit is sink*log2(e): m starts there with weight 1.
-  // m is the reference maximum the weights are taken against; it is only
-  // raised when a score exceeds it by more than kLazy (log2 units), which
-  // bounds every weight by 2^kLazy and leaves the result unchanged.
-  constexpr float kLazy = 8.0f;
   float m = -INFINITY;
   float lpart = 0.f;  // this lane's share of the denominator
-  if (c == 0 && hvalid) {
-    const float sk = a.sink[h] * kLog2e;
-    m = sk;
-    if (g == 0 && sk > -INFINITY) lpart = 1.f;
-  }
   f32x4 acc[kDTiles];
 #pragma unroll
   for (int i = 0; i < kDTiles; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -242,84 +374,111 @@ __global__ void __launch_bounds__(64 * W) attn_main_kernel(AttnArgs a) {
   const int rtr = 4 * g + (n16 >> 2);                    // transpose-read row (and +16)
   const int sw_tr = row_swizzle(rtr) & (kChunks - 1);
 
-  for (int i = 0; i < ntiles; ++i) {
-    if (i + 1 < ntiles)
-      wait_vmcnt<kLoadsPerWave>();
-    else
-      wait_vmcnt<0>();
-    barrier_no_fence();
-    if (i + 2 < ntiles) issue_tile(i + 2);
+  for (int sc = 0; sc < nrows; sc += kIdxCap) {
+    const int n = nrows - sc < kIdxCap ? nrows - sc : kIdxCap;
+    if (sc > 0) barrier_lds();  // every wave is done with the previous stages and indices
+    stage_indices(part, sc, n, sidx, wave, W, lane);
+    wait_vmcnt<0>();
+    barrier_lds();
+    if (sc == 0) init_state(ssink[wave * 16 + n16], c == 0 && hvalid, g, m, lpart);  // partition 0
+    const int ntiles = (n + kTile - 1) / kTile;
 
-    const unsigned char* st = smem + (i % kStages) * kStageBytes;
-    const int nvalid = nrows - i * kTileRows;  // rows of this tile that exist (>= 1)
+    auto issue_tile = [&](int tile) {
+      issue_rows<kRowBytes, kLoadsPerWave>(a.kv, sidx, n, tile * kTile + wave * (kTile / W),
+                                           wave * (kTile / W),
+                                           smem + (tile % kStages) * kStageBytes +
+                                               wave * kLoadsPerWave * 1024,
+                                           lane);
+    };
 
-    // S^T[32 rows x 16 heads] = K Q^T
-    f32x4 sa = {0.f, 0.f, 0.f, 0.f};
-    f32x4 sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < kKSteps; ++s) {
-      const int pc = ((4 * s + g) ^ sw_qk) << 4;
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(st + n16 * kRowBytes + pc);
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(st + (16 + n16) * kRowBytes + pc);
-      sa = mfma_bf16(ka, qreg[s], sa);
-      sb = mfma_bf16(kb, qreg[s], sb);
-    }
+    issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
 
-    // Online softmax, log2 domain.  Lane holds rows 4g+i (sa) and 16+4g+i (sb)
-    // of head n16.
-    float x[8];
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      x[i4] = (4 * g + i4 < nvalid) ? sa[i4] * a.qk_scale : -INFINITY;
-      x[4 + i4] = (16 + 4 * g + i4 < nvalid) ? sb[i4] * a.qk_scale : -INFINITY;
-    }
-    float mx = x[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool raise = mx > m + kLazy;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // some head needs a new reference
-      const float mnew = raise ? mx : m;
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // 0 when m was -inf
-      lpart *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < kDTiles; ++dt) acc[dt] *= alpha;
-      m = mnew;
-    }
-    bf16x8 pt;
-    float psum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const __bf16 pb = (__bf16)__builtin_amdgcn_exp2f(x[j] - m);
-      pt[j] = pb;
-      psum += (float)pb;  // the denominator sums the same rounded weights as PV
-    }
-    lpart += psum;
+    for (int i = 0; i < ntiles; ++i) {
+      if (i + 1 < ntiles)
+        wait_vmcnt<kLoadsPerWave>();
+      else
+        wait_vmcnt<0>();
+      barrier_lds();
+      if (i + 2 < ntiles) issue_tile(i + 2);
 
-    // O^T[d x 16 heads] += V^T P^T; V^T via 16-lane transpose reads.
+      const unsigned char* st = smem + (i % kStages) * kStageBytes;
+      const int nvalid = n - i * kTile;  // rows of this tile that exist (>= 1)
+
+      // S^T = K Q^T.  The K operands are read in batches of kB k-steps, all
+      // reads of a batch issued before its MFMAs (sched_barrier keeps the
+      // compiler from interleaving each read with its use).
+      constexpr int kB = kKSteps < 8 ? kKSteps : 8;
+      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sa2 = sa;  // two chains per 16-row half
+      f32x4 sb = {0.f, 0.f, 0.f, 0.f}, sb2 = sb;
 #pragma unroll
-    for (int dt = 0; dt < kDTiles; ++dt) {
-      const int d = 16 * dt + 4 * (n16 & 3);
-      const int off = (((d >> 3) ^ sw_tr) << 4) + (d & 7) * 2;
-      const bf16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (LdsBf16x4*)(st + rtr * kRowBytes + off));
-      const bf16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (LdsBf16x4*)(st + (16 + rtr) * kRowBytes + off));
-      const bf16x8 vt = __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[dt] = mfma_bf16(vt, pt, acc[dt]);
+      for (int s0 = 0; s0 < kKSteps; s0 += kB) {
+        bf16x8 ka[kB], kb[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+          const int pc = ((4 * (s0 + u) + g) ^ sw_qk) << 4;
+          ka[u] = *reinterpret_cast<const bf16x8*>(st + n16 * kRowBytes + pc);
+          kb[u] = *reinterpret_cast<const bf16x8*>(st + (16 + n16) * kRowBytes + pc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+          if (u & 1) {
+            sa2 = mfma_k32(ka[u], qreg[s0 + u], sa2);
+            sb2 = mfma_k32(kb[u], qreg[s0 + u], sb2);
+          } else {
+            sa = mfma_k32(ka[u], qreg[s0 + u], sa);
+            sb = mfma_k32(kb[u], qreg[s0 + u], sb);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sa += sa2;
+      sb += sb2;
+
+      float x[8];
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        x[i4] = (4 * g + i4 < nvalid) ? sa[i4] * a.qk_scale : -INFINITY;
+        x[4 + i4] = (16 + 4 * g + i4 < nvalid) ? sb[i4] * a.qk_scale : -INFINITY;
+      }
+      __bf16 p[8];
+      softmax_step<8, kDTiles>(x, m, lpart, acc, p);
+      bf16x8 pt;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pt[j] = p[j];
+
+      // O^T += V^T P^T, V^T operands read in batches of kVB d-tiles.
+      constexpr int kVB = kDTiles < 8 ? kDTiles : 8;
+#pragma unroll
+      for (int d0 = 0; d0 < kDTiles; d0 += kVB) {
+        bf16x8 vt[kVB];
+#pragma unroll
+        for (int u = 0; u < kVB; ++u) {
+          const int d = 16 * (d0 + u) + 4 * (n16 & 3);
+          const int off = (((d >> 3) ^ sw_tr) << 4) + (d & 7) * 2;
+          const bf16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (LdsBf16x4*)(st + rtr * kRowBytes + off));
+          const bf16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (LdsBf16x4*)(st + (16 + rtr) * kRowBytes + off));
+          vt[u] = __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kVB; ++u) acc[d0 + u] = mfma_k32(vt[u], pt, acc[d0 + u]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
-  float l = lpart + __shfl_xor(lpart, 16);
-  l += __shfl_xor(l, 32);
+  const float l = group_sum4(lpart);
 
   if (nparts == 1) {
     if (hvalid) {
       const float inv = 1.0f / l;
       uint16_t* op = a.out + ((int64_t)t * a.H + h) * D + 4 * g;
 #pragma unroll
-      for (int dt = 0; dt < kDTiles; ++dt) store_bf16_row4<D>(op + 16 * dt, acc[dt], inv);
+      for (int dt = 0; dt < kDTiles; ++dt) store_bf16x4(op + 16 * dt, acc[dt], inv);
     }
   } else {
     float* base = a.ws + (int64_t)item * (kHeads * (D + 2));
@@ -333,14 +492,17 @@ __global__ void __launch_bounds__(64 * W) attn_main_kernel(AttnArgs a) {
   }
 }
 
-// Merge the partitions of each token with more than one:
+// Merge the partitions of each token with more than one (heads mode):
 //   M = max_c m_c,  l = sum_c l_c 2^(m_c - M),  O = sum_c O_c 2^(m_c - M),
-//   out = O / l.  Partition 0 already carries the sink.
+//   out = O / l.  Partition 0 already carries the sink.  Workgroup = (token,
+// head group, quarter of D), so the grid is four times the token count.
 template <int D, int W>
 __global__ void __launch_bounds__(64 * W) attn_combine_kernel(AttnArgs a) {
   constexpr int kDTiles = D / 16;
+  constexpr int kQ = kDTiles / 4;  // d-tiles per quarter
   constexpr int kHeads = 16 * W;
-  const int th = blockIdx.x;
+  const int quarter = blockIdx.x & 3;
+  const int th = blockIdx.x >> 2;
   const int hg = th % a.head_groups;
   const int t = th / a.head_groups;
   const ScalarI32Ptr indptr = (ScalarI32Ptr)a.kv_indptr;
@@ -362,40 +524,239 @@ __global__ void __launch_bounds__(64 * W) attn_combine_kernel(AttnArgs a) {
   float M = -INFINITY;
   for (int c = 0; c < nparts; ++c) M = fmaxf(M, base0[c * stride + kHeads * D + hi]);
   float lsum = 0.f;
-  f32x4 acc[kDTiles];
+  f32x4 acc[kQ];
 #pragma unroll
-  for (int i = 0; i < kDTiles; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kQ; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int c = 0; c < nparts; ++c) {
     const float* base = base0 + c * stride;
     const float w = __builtin_amdgcn_exp2f(base[kHeads * D + hi] - M);
     lsum += w * base[kHeads * D + kHeads + hi];
-    const f32x4* po = reinterpret_cast<const f32x4*>(base) + wave * kDTiles * 64 + lane;
+    const f32x4* po =
+        reinterpret_cast<const f32x4*>(base) + (wave * kDTiles + quarter * kQ) * 64 + lane;
+    f32x4 v[kQ];
 #pragma unroll
-    for (int dt = 0; dt < kDTiles; ++dt) acc[dt] += w * po[dt * 64];
+    for (int i = 0; i < kQ; ++i) v[i] = po[i * 64];
+#pragma unroll
+    for (int i = 0; i < kQ; ++i) acc[i] += w * v[i];
   }
   const float inv = 1.0f / lsum;
-  uint16_t* op = a.out + ((int64_t)t * a.H + h) * D + 4 * g;
+  uint16_t* op = a.out + ((int64_t)t * a.H + h) * D + 4 * g + 16 * quarter * kQ;
 #pragma unroll
-  for (int dt = 0; dt < kDTiles; ++dt) store_bf16_row4<D>(op + 16 * dt, acc[dt], inv);
+  for (int i = 0; i < kQ; ++i) store_bf16x4(op + 16 * i, acc[i], inv);
+}
+
+// ---------------------------------------------------------------------------
+// rows mode: workgroup = (token, 16 heads); 4 waves split the slice into
+// 16-row tiles (wave w takes tiles w, w+4, ...) staged in private LDS, then
+// merge their softmax states in LDS.
+template <int D>
+__global__ void __launch_bounds__(256) attn_rows_kernel(AttnArgs a) {
+  constexpr int kWaves = 4;
+  constexpr int kTile = 16;
+  constexpr int kRowBytes = 2 * D;
+  constexpr int kChunks = D / 8;
+  constexpr int kKSteps = D / 32;
+  constexpr int kDTiles = D / 16;
+  constexpr int kRowsPerLoad = 1024 / kRowBytes;
+  constexpr int kLoads = kTile / kRowsPerLoad;  // DMA ops per wave tile
+  constexpr int kStageBytes = kTile * kRowBytes;
+  constexpr int kWaveBytes = 2 * kStageBytes;   // == 16 heads * D * 4: room for the partial O
+  static_assert(kWaveBytes == 16 * D * 4, "partial O must fit the wave's stages");
+  static_assert(kLoads >= 1 && kLoads < 64, "bad load count");
+
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kWaves * kWaveBytes];
+  __shared__ __attribute__((aligned(256))) int sidx[kIdxCap];
+  __shared__ __attribute__((aligned(256))) float ssink[64];
+  __shared__ float sml[kWaves][2][16];
+
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const int hg = item % a.head_groups;
+  const int t = item / a.head_groups;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n16 = lane & 15;
+  const int g = lane >> 4;
+
+  const ScalarI32Ptr indptr = (ScalarI32Ptr)a.kv_indptr;
+  const int row0 = indptr[t];
+  const int L = indptr[t + 1] - row0;
+  const int h0 = hg * 16;
+  const int h = h0 + n16;
+  const bool hvalid = h < a.H;
+  const int nh = a.H - h0 < 16 ? a.H - h0 : 16;
+
+  if (L <= 0) {
+    zero_heads<D>(a.out, a.H, t, h0, nh, threadIdx.x, 64 * kWaves);
+    return;
+  }
+  const int32_t* part = a.kv_indices + row0;
+
+  bf16x8 qreg[kKSteps];
+  load_q<D>(a.q, (int64_t)t * a.H + (hvalid ? h : 0), g, qreg);
+  stage_sinks(a.sink, a.H, h0, ssink, wave, lane);
+
+  float m = -INFINITY;
+  float lpart = 0.f;
+  f32x4 acc[kDTiles];
+#pragma unroll
+  for (int i = 0; i < kDTiles; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  unsigned char* mine = smem + wave * kWaveBytes;
+  const int sw_qk = row_swizzle(n16) & (kChunks - 1);
+  const int rtr = 4 * g + (n16 >> 2);
+  const int sw_tr = row_swizzle(rtr) & (kChunks - 1);
+
+  for (int sc = 0; sc < L; sc += kIdxCap) {
+    const int n = L - sc < kIdxCap ? L - sc : kIdxCap;
+    if (sc > 0) barrier_lds();
+    stage_indices(part, sc, n, sidx, wave, kWaves, lane);
+    wait_vmcnt<0>();
+    barrier_lds();
+    if (sc == 0) init_state(ssink[n16], wave == 0 && hvalid, g, m, lpart);  // sink in wave 0
+    const int ntiles = (n + kTile - 1) / kTile;
+    const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+
+    auto issue = [&](int j) {  // this wave's j-th tile = global tile wave + 4j
+      issue_rows<kRowBytes, kLoads>(a.kv, sidx, n, (wave + kWaves * j) * kTile, 0,
+                                    mine + (j & 1) * kStageBytes, lane);
+    };
+
+    // Two tiles stay in flight: tile j's LDS stage is released as soon as its
+    // operands are in registers, and the load of tile j+2 goes into it while
+    // tile j's MFMAs run.
+    if (my_tiles > 0) issue(0);
+    if (my_tiles > 1) issue(1);
+    for (int j = 0; j < my_tiles; ++j) {
+      if (j + 1 < my_tiles)
+        wait_vmcnt<kLoads>();
+      else
+        wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      const unsigned char* st = mine + (j & 1) * kStageBytes;
+      const int nvalid = n - (wave + kWaves * j) * kTile;
+
+      // S^T = K Q^T: all K operands of the tile read first, then the MFMAs.
+      f32x4 sa = {0.f, 0.f, 0.f, 0.f};
+      {
+        bf16x8 ka[kKSteps];
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) {
+          const int pc = ((4 * s + g) ^ sw_qk) << 4;
+          ka[s] = *reinterpret_cast<const bf16x8*>(st + n16 * kRowBytes + pc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // four independent accumulation chains, so consecutive MFMAs do not
+        // wait on each other's results
+        constexpr int kCh = kKSteps < 4 ? kKSteps : 4;
+        f32x4 part[kCh];
+#pragma unroll
+        for (int c = 0; c < kCh; ++c) part[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) part[s % kCh] = mfma_k32(ka[s], qreg[s], part[s % kCh]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < kCh; ++c) sa += part[c];
+      }
+      // V^T operands: issued now, so they are in flight during the softmax.
+      bf16x4 vt[kDTiles];
+#pragma unroll
+      for (int dt = 0; dt < kDTiles; ++dt) {
+        const int d = 16 * dt + 4 * (n16 & 3);
+        const int off = (((d >> 3) ^ sw_tr) << 4) + (d & 7) * 2;
+        vt[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + rtr * kRowBytes + off));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      float x[4];
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        x[i4] = (4 * g + i4 < nvalid) ? sa[i4] * a.qk_scale : -INFINITY;
+      __bf16 p[4];
+      softmax_step<4, kDTiles>(x, m, lpart, acc, p);
+      bf16x4 pt;
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) pt[j4] = p[j4];
+      // The stage's data is now in registers: release it to the load of tile j+2.
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      asm volatile("" ::: "memory");
+      if (j + 2 < my_tiles) issue(j + 2);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dt = 0; dt < kDTiles; ++dt) acc[dt] = mfma_k16(vt[dt], pt, acc[dt]);
+    }
+  }
+
+  // Merge the four waves' states.  Wave w's partial O goes to its own stage
+  // area as [head][d] fp32 with the 16-byte column index XOR-ed by the head.
+  const float l = group_sum4(lpart);
+  {
+    f32x4* po = reinterpret_cast<f32x4*>(mine);
+#pragma unroll
+    for (int dt = 0; dt < kDTiles; ++dt) {
+      const int col = (4 * dt + g) ^ n16;  // d/4 of this lane's four values, swizzled
+      po[n16 * (D / 4) + col] = acc[dt];
+    }
+    if (g == 0) {
+      sml[wave][0][n16] = m;
+      sml[wave][1][n16] = l;
+    }
+  }
+  barrier_lds();
+
+  // Wave w produces d in [w*D/4, (w+1)*D/4) for all 16 heads: lane -> (head
+  // hh = lane % 16, sub-range of D/16 values).
+  const int hh = lane & 15;
+  const int sub = lane >> 4;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sml[w][0][hh]);
+  float wgt[kWaves];
+  float lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    wgt[w] = __builtin_amdgcn_exp2f(sml[w][0][hh] - M);  // 0 for a wave with no rows
+    lsum += wgt[w] * sml[w][1][hh];
+  }
+  const float inv = 1.0f / lsum;
+  constexpr int kPer = D / 64;  // float4 columns per lane
+  const int col0 = wave * (D / 16) + sub * kPer;
+  if (hh < nh) {
+    uint16_t* op = a.out + ((int64_t)t * a.H + h0 + hh) * D + 4 * col0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const f32x4* po = reinterpret_cast<const f32x4*>(smem + w * kWaveBytes);
+        s += wgt[w] * po[hh * (D / 4) + ((col0 + k) ^ hh)];
+      }
+      store_bf16x4(op + 4 * k, s, inv);
+    }
+  }
 }
 
 template <int D, int W>
-hipError_t launch_dw(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_heads(const AttnArgs& a, hipStream_t stream) {
   const long long items = (long long)a.N * a.head_groups * a.splits;
-  hipLaunchKernelGGL((attn_main_kernel<D, W>), dim3((unsigned)items), dim3(64 * W), 0, stream, a);
+  hipLaunchKernelGGL((attn_heads_kernel<D, W>), dim3((unsigned)items), dim3(64 * W), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL((attn_combine_kernel<D, W>), dim3((unsigned)(a.N * a.head_groups)),
+  hipLaunchKernelGGL((attn_combine_kernel<D, W>), dim3((unsigned)(a.N * a.head_groups * 4)),
                      dim3(64 * W), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const AttnArgs& a, int waves, hipStream_t stream) {
-  switch (waves) {
-    case 1: return launch_dw<D, 1>(a, stream);
-    case 2: return launch_dw<D, 2>(a, stream);
-    case 4: return launch_dw<D, 4>(a, stream);
+hipError_t launch_d(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream) {
+  if (plan.mode == kModeRows) {
+    hipLaunchKernelGGL((attn_rows_kernel<D>), dim3((unsigned)(a.N * a.head_groups)), dim3(256), 0,
+                       stream, a);
+    return hipGetLastError();
+  }
+  switch (plan.waves) {
+    case 1: return launch_heads<D, 1>(a, stream);
+    case 2: return launch_heads<D, 2>(a, stream);
+    case 4: return launch_heads<D, 4>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -407,28 +768,46 @@ bool attn_supported(int32_t H, int32_t D) {
 }
 
 bool make_attn_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t split_rows,
-                    AttnPlan* p) {
+                    int32_t mode, AttnPlan* p) {
   if (!attn_supported(H, D) || N < 0 || max_len < 0 || split_rows < 0) return false;
-  p->waves = H <= 16 ? 1 : (H <= 32 ? 2 : 4);
-  p->heads_per_group = 16 * p->waves;
-  p->head_groups = (H + p->heads_per_group - 1) / p->heads_per_group;
+  if (mode != kModeAuto && mode != kModeHeads && mode != kModeRows) return false;
+  const int heads_waves = H <= 16 ? 1 : (H <= 32 ? 2 : 4);
+  const long long heads_groups = (H + 16 * heads_waves - 1) / (16 * heads_waves);
+  // Work items the heads mode provides without split-L; the chip has 256 CUs.
+  const long long target = 256;
+  if (mode == kModeAuto)
+    mode = (split_rows == 0 && (long long)N * heads_groups < target) ? kModeRows : kModeHeads;
+  if (mode == kModeRows) {
+    if (split_rows != 0) return false;  // the rows mode does not split across workgroups
+    p->mode = kModeRows;
+    p->waves = 4;
+    p->heads_per_group = 16;
+    p->head_groups = (H + 15) / 16;
+    p->splits = 1;
+    p->split_rows = 1 << 30;
+    p->workspace_bytes = 0;
+    return (long long)N * p->head_groups <= 0x7fffffffLL;
+  }
+  p->mode = kModeHeads;
+  p->waves = heads_waves;
+  p->heads_per_group = 16 * heads_waves;
+  p->head_groups = (int)heads_groups;
   long long splits = 1, rows = 0;
   if (split_rows > 0) {
-    rows = ((long long)split_rows + kTileRows - 1) / kTileRows * kTileRows;
+    rows = ((long long)split_rows + 31) / 32 * 32;
     splits = max_len > rows ? (max_len + rows - 1) / rows : 1;
   } else if (max_len > 0 && N > 0) {
-    // Aim at about one workgroup per compute unit (256 on MI355X) when the
-    // batch alone does not provide that many; keep partitions >= 128 rows.
+    // Aim at about one workgroup per compute unit when the batch alone does
+    // not provide that many; keep partitions >= 128 rows.
     const long long base = (long long)N * p->head_groups;
-    const long long target = 256;
     if (base < target) {
-      long long want = (target + base - 1) / base;
+      const long long want = (target + base - 1) / base;
       const long long cap = (max_len + 127) / 128;
       splits = want < cap ? want : cap;
       if (splits > 64) splits = 64;
       if (splits > 1) {
         rows = (max_len + splits - 1) / splits;
-        rows = (rows + kTileRows - 1) / kTileRows * kTileRows;
+        rows = (rows + 31) / 32 * 32;
         splits = (max_len + rows - 1) / rows;
       }
     }
@@ -438,7 +817,7 @@ bool make_attn_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t sp
     rows = 1 << 30;
   }
   if (splits > 4096) return false;
-  if ((long long)N * p->head_groups * splits > 0x7fffffffLL) return false;
+  if ((long long)N * p->head_groups * splits * 4 > 0x7fffffffLL) return false;
   p->splits = (int)splits;
   p->split_rows = (int)rows;
   p->workspace_bytes = splits > 1 ? (size_t)N * p->head_groups * splits * p->heads_per_group *
@@ -449,10 +828,10 @@ bool make_attn_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t sp
 
 hipError_t launch_attention(const AttnArgs& a, int D, const AttnPlan& plan, hipStream_t stream) {
   switch (D) {
-    case 64: return launch_d<64>(a, plan.waves, stream);
-    case 128: return launch_d<128>(a, plan.waves, stream);
-    case 256: return launch_d<256>(a, plan.waves, stream);
-    case 512: return launch_d<512>(a, plan.waves, stream);
+    case 64: return launch_d<64>(a, plan, stream);
+    case 128: return launch_d<128>(a, plan, stream);
+    case 256: return launch_d<256>(a, plan, stream);
+    case 512: return launch_d<512>(a, plan, stream);
     default: return hipErrorInvalidValue;
   }
 }

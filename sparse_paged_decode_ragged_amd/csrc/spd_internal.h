@@ -8,25 +8,27 @@
 
 namespace spd {
 
-// Rows of a token's slice that one workgroup stages per step (MFMA K of the
-// PV product is 32 rows).
-constexpr int kTileRows = 32;
+// Work decompositions (values match spd_mode in include/spd.h).
+constexpr int kModeAuto = 0;
+constexpr int kModeHeads = 1;  // waves of a workgroup split the heads, share the rows
+constexpr int kModeRows = 2;   // waves of a workgroup split the rows, share 16 heads
 
 // Work decomposition of one attention call, fixed by scalar arguments only so
 // that the grid never depends on device data.
 struct AttnPlan {
-  int waves;           // waves per workgroup; each wave owns 16 heads
-  int heads_per_group; // 16 * waves
+  int mode;            // kModeHeads or kModeRows
+  int waves;           // waves per workgroup
+  int heads_per_group; // heads per workgroup
   int head_groups;     // ceil(H / heads_per_group)
   int splits;          // partitions of a slice (1 = no split-L)
-  int split_rows;      // rows per partition (multiple of kTileRows); huge when splits == 1
+  int split_rows;      // rows per partition (multiple of 32); huge when splits == 1
   size_t workspace_bytes;
 };
 
 bool attn_supported(int32_t H, int32_t D);
 // Returns false when the arguments cannot form a plan.
 bool make_attn_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t split_rows,
-                    AttnPlan* plan);
+                    int32_t mode, AttnPlan* plan);
 
 struct AttnArgs {
   const uint16_t* q;         // [N][H][D] bf16 bits

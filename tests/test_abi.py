@@ -23,8 +23,8 @@ def lib():
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     L.sparse_decode_attn.argtypes = [P, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32, P]
     L.sparse_decode_attn_ex.argtypes = [P, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32, i32,
-                                        i32, P, sz, P]
-    L.sparse_decode_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+                                        i32, i32, P, sz, P]
+    L.sparse_decode_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     L.sparse_decode_attn_workspace_size.restype = sz
     L.sparse_decode_attn_can_use.argtypes = [i32, i32]
     L.build_decode_indices.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i32, P, P, i64, P]
@@ -94,20 +94,27 @@ def test_attn_rejects_bad_arguments(lib):
 
 
 def test_attn_ex_workspace_checks(lib):
-    need = lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 0)
+    AUTO, HEADS, ROWS = 0, 1, 2
+    # decode_base shape: the automatic plan uses the rows mode, which needs no workspace
+    assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 0, AUTO) == 0
+    assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 0, ROWS) == 0
+    # heads mode splits a 640-row slice into 4 partitions of 160 rows:
     # 64 tokens x 1 head group x 4 partitions x 64 heads x (512 + 2) floats
+    need = lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 0, HEADS)
     assert need == 64 * 1 * 4 * 64 * 514 * 4
-    assert lib.sparse_decode_attn_workspace_size(1024, 128, 512, 640, 0) == 0  # large batch: no split
-    assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 64) == 64 * 10 * 64 * 514 * 4
-    st = lib.sparse_decode_attn_ex(FAKE, FAKE, 100, FAKE, FAKE, FAKE, 0.1, FAKE * 4096, 64, 64, 512,
-                                   640, 0, None, 0, None)
-    assert st == WORKSPACE
-    st = lib.sparse_decode_attn_ex(FAKE, FAKE, 100, FAKE, FAKE, FAKE, 0.1, FAKE * 4096, 64, 64, 512,
-                                   640, 0, FAKE * 8192, need - 1, None)
-    assert st == WORKSPACE
-    st = lib.sparse_decode_attn_ex(FAKE, FAKE, 100, FAKE, FAKE, FAKE, 0.1, FAKE * 4096, 64, 64, 512,
-                                   -1, 0, None, 0, None)
-    assert st == INVALID
+    assert lib.sparse_decode_attn_workspace_size(1024, 128, 512, 640, 0, AUTO) == 0  # no split
+    assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 64, AUTO) == 64 * 10 * 64 * 514 * 4
+    assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 64, ROWS) == 0  # invalid plan
+    assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 0, 7) == 0      # unknown mode
+
+    def ex(max_len=640, split=0, mode=HEADS, ws=None, ws_bytes=0):
+        return lib.sparse_decode_attn_ex(FAKE, FAKE, 100, FAKE, FAKE, FAKE, 0.1, FAKE * 4096, 64, 64,
+                                         512, max_len, split, mode, ws, ws_bytes, None)
+    assert ex() == WORKSPACE
+    assert ex(ws=FAKE * 8192, ws_bytes=need - 1) == WORKSPACE
+    assert ex(max_len=-1) == INVALID
+    assert ex(mode=7) == INVALID
+    assert ex(mode=ROWS, split=64) == UNSUPPORTED
 
 
 def _build(lib, ss=FAKE, sl=FAKE, cp=FAKE, topk=4, bt=FAKE, mb=2, N=3, win=8, k=2, swa=24,

@@ -32,7 +32,9 @@ def run(spd, w, idx_np, ptr_np, sink=None, **plan):
     return out
 
 
-PLANS = [dict(), dict(max_len=200, split_rows=32), dict(max_len=200, split_rows=64),
+ROWS, HEADS = 2, 1
+PLANS = [dict(plain=True), dict(mode=ROWS), dict(mode=HEADS),
+         dict(mode=HEADS, max_len=200, split_rows=32), dict(mode=HEADS, max_len=200, split_rows=64),
          dict(max_len=200)]
 
 
@@ -40,7 +42,7 @@ def test_tiny_all_tokens(spd):
     w = W.tiny()
     log("case tiny")
     ref = oracle_tokens(w, w.kv_indices, w.kv_indptr)
-    for plan in [dict(), dict(max_len=64, split_rows=32)]:
+    for plan in PLANS:
         out = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
         assert_close(bf16_to_f64(out), ref, "tiny %s" % plan)
         assert torch.all(out[0].view(torch.int16) == 0)  # empty slice: exactly +0.0
@@ -66,7 +68,8 @@ def test_many_tiles_and_long_slices(spd):
     w = W.random_csr("long", 7, len(lengths), 64, 512, 5000, lengths)
     log("case long slices")
     ref = oracle_tokens(w, w.kv_indices, w.kv_indptr)
-    for plan in [dict(), dict(max_len=2048), dict(max_len=2048, split_rows=96),
+    for plan in [dict(plain=True), dict(mode=ROWS), dict(mode=HEADS), dict(max_len=2048),
+                 dict(max_len=2048, split_rows=96),
                  dict(max_len=256, split_rows=128)]:   # slices longer than max_len
         out = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
         assert_close(bf16_to_f64(out), ref, "long %s" % plan)
@@ -96,7 +99,7 @@ def test_single_row_without_sink_is_bit_exact(spd):
     w = W.random_csr("single", 12, 5, 16, 512, 50, [1, 1, 1, 1, 1])
     sink = np.full(16, -np.inf, dtype=np.float32)
     log("case single row")
-    for plan in [dict(), dict(max_len=32, split_rows=32)]:
+    for plan in [dict(mode=ROWS), dict(mode=HEADS), dict(max_len=32, split_rows=32)]:
         out = run(spd, w, w.kv_indices, w.kv_indptr, sink=sink, **plan)
         kv = W.device_bits(w.kv_bits, torch.device("cuda:0"))
         for t in range(5):
@@ -107,7 +110,7 @@ def test_single_row_without_sink_is_bit_exact(spd):
 def test_all_empty_batch(spd):
     w = W.random_csr("empty", 13, 6, 64, 512, 10, [0] * 6)
     log("case all empty")
-    for plan in [dict(), dict(max_len=64)]:
+    for plan in PLANS:
         out = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
         assert torch.all(out.view(torch.int16) == 0)
 
@@ -122,10 +125,11 @@ def test_permutation_and_duplicates(spd):
         perm[a:b] = rng.permutation(perm[a:b])
     log("case permutation")
     ref = oracle_tokens(w, w.kv_indices, w.kv_indptr)
-    o1 = bf16_to_f64(run(spd, w, w.kv_indices, w.kv_indptr))
-    o2 = bf16_to_f64(run(spd, w, perm, w.kv_indptr))
-    assert_close(o1, ref, "original order")
-    assert_close(o2, ref, "permuted order")
+    for plan in [dict(mode=ROWS), dict(mode=HEADS)]:
+        o1 = bf16_to_f64(run(spd, w, w.kv_indices, w.kv_indptr, **plan))
+        o2 = bf16_to_f64(run(spd, w, perm, w.kv_indptr, **plan))
+        assert_close(o1, ref, "original order %s" % plan)
+        assert_close(o2, ref, "permuted order %s" % plan)
 
 
 def test_repeated_rows_closed_form(spd):
@@ -135,19 +139,25 @@ def test_repeated_rows_closed_form(spd):
     w.kv_indices[:] = 2
     log("case repeated row")
     out = bf16_to_f64(run(spd, w, w.kv_indices, w.kv_indptr, max_len=L, split_rows=64))
+    assert_close(out, ref_closed_form(w, L), "repeated row, split")
+    out = bf16_to_f64(run(spd, w, w.kv_indices, w.kv_indptr, mode=ROWS))
+    assert_close(out, ref_closed_form(w, L), "repeated row, rows mode")
+
+
+def ref_closed_form(w, L):
     r = W.bf16_to_f32(W.host_bits(w.kv_bits)[2]).astype(np.float64)
     q = W.bf16_to_f32(W.host_bits(w.q_bits)[0]).astype(np.float64)
     ref = np.zeros((1, 16, 512))
     for h in range(16):
         s = w.softmax_scale * float(q[h] @ r)
         ref[0, h] = r * L * math.exp(s) / (L * math.exp(s) + math.exp(float(w.attn_sink[h])))
-    assert_close(out, ref, "repeated row")
+    return ref
 
 
 def test_deterministic(spd):
     w = W.random_csr("det", 16, 8, 64, 512, 3000, [640, 1, 0, 333, 1000, 64, 65, 2000])
     log("case determinism")
-    for plan in [dict(), dict(max_len=2000)]:
+    for plan in [dict(mode=ROWS), dict(mode=HEADS), dict(max_len=2000, mode=HEADS)]:
         a = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
         b = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))

@@ -56,8 +56,8 @@ def test_decode_base_end_to_end(spd):
     ptr, idx, optr, oidx = build_on_gpu(spd, w.builder)
     ref = oracle_tokens(w, oidx, optr)
     q, kv, sink = device_inputs(w)
-    for plan in [dict(max_len=640), dict(), dict(max_len=640, split_rows=64),
-                 dict(max_len=640, split_rows=320)]:
+    for plan in [dict(max_len=640), dict(plain=True), dict(mode=1, max_len=640),
+                 dict(max_len=640, split_rows=64), dict(max_len=640, split_rows=320)]:
         out = spd.sparse_decode_attn(q, kv, idx, ptr, sink, w.softmax_scale, **plan)
         torch.cuda.synchronize()
         assert_close(bf16_to_f64(out), ref, "decode_base %s" % plan)
@@ -70,7 +70,7 @@ def test_ragged_config(spd, device_data):
     ref = oracle_tokens(w, w.kv_indices, w.kv_indptr, tokens)
     q, kv, sink = device_inputs(w)
     idx, ptr = device_csr(w.kv_indices, w.kv_indptr)
-    for plan in [dict(max_len=w.max_len), dict()]:
+    for plan in [dict(max_len=w.max_len), dict(plain=True), dict(mode=2), dict(mode=1, max_len=w.max_len)]:
         out = spd.sparse_decode_attn(q, kv, idx, ptr, sink, w.softmax_scale, **plan)
         torch.cuda.synchronize()
         assert_close(bf16_to_f64(out[torch.from_numpy(tokens).cuda()]), ref, "ragged %s" % plan)
@@ -101,7 +101,8 @@ def test_prefill_config(spd, device_data):
     assert_close(bf16_to_f64(out[torch.from_numpy(tokens).cuda()]), ref, "prefill")
 
 
-def test_graph_capture_and_replay(spd):
+@pytest.mark.parametrize("mode", [1, 2])
+def test_graph_capture_and_replay(spd, mode):
     """Capture builder + attention once; replay with new window lengths and
     sentinel patterns copied into the same buffers; every replay must equal the
     eager result bit for bit and the oracle within tolerance."""
@@ -114,14 +115,14 @@ def test_graph_capture_and_replay(spd):
     ptr = torch.zeros(N + 1, dtype=torch.int32, device=dev())
     idx = torch.zeros(cap, dtype=torch.int32, device=dev())
     out = torch.zeros((N, H, D), dtype=torch.bfloat16, device=dev())
-    ws = torch.empty(spd.sparse_decode_attn_workspace_size(N, H, D, win + topk, 0),
+    ws = torch.empty(max(16, spd.sparse_decode_attn_workspace_size(N, H, D, win + topk, 0, 1)),
                      dtype=torch.uint8, device=dev())
     log("case graph capture")
 
     def step():
         spd.build_decode_indices(ss, sl, cp, bt, win, 1, b.swa_pages, kv_indptr=ptr, kv_indices=idx)
         spd.sparse_decode_attn(q, kv, idx, ptr, sink, w.softmax_scale, out=out,
-                               max_len=win + topk, workspace=ws)
+                               max_len=win + topk, workspace=ws, mode=mode)
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -151,7 +152,8 @@ def test_graph_capture_and_replay(spd):
         # eager, into fresh buffers, with some unrelated eager work in between
         _ = torch.randn(1 << 20, device=dev()).sum()
         eptr, eidx = spd.build_decode_indices(ss, sl, cp, bt, win, 1, b.swa_pages)
-        eout = spd.sparse_decode_attn(q, kv, eidx, eptr, sink, w.softmax_scale, max_len=win + topk)
+        eout = spd.sparse_decode_attn(q, kv, eidx, eptr, sink, w.softmax_scale, max_len=win + topk,
+                                      mode=mode)
         torch.cuda.synchronize()
         assert torch.equal(graph_ptr, eptr)
         assert torch.equal(graph_out.view(torch.int16), eout.view(torch.int16)), "replay %d" % rep
