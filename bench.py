@@ -49,7 +49,80 @@ def parse():
     p.add_argument("--eager", action="store_true", help="launch kernels directly, no graphs")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--calibration-copy-mib", type=int, default=0,
+                   help="also run three plain device-to-device copies of this many MiB, the "
+                        "known-size kernel that scales the HBM byte counters")
+    p.add_argument("--pmc-summary", nargs="+", metavar="DIR",
+                   help="summarise rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE "
+                        "runs of this script) instead of benchmarking")
+    p.add_argument("--pmc-copy-mib", type=int, default=0,
+                   help="size of the calibration copy in the runs given to --pmc-summary")
     return p.parse_args()
+
+
+def kernel_sources_digest() -> str:
+    """sha256 over the attention kernel's sources: a traffic figure taken from
+    counters is only reported while these are unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_paged_decode_ragged_amd", "csrc")
+    for name in ("attn.hip", "spd_internal.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_base.md")
+
+
+def recorded_traffic(kernel: str, workload: str):
+    """Per-launch HBM bytes of `kernel` from the committed counter summary, or
+    None when there is none or the kernel sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].strip().split(": ", 1)
+                fields[k.strip("`")] = v.strip().strip("`")
+    if (fields.get("kernel") != kernel or fields.get("workload") != workload
+            or fields.get("source_digest") != kernel_sources_digest()):
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def pmc_summary(dirs, copy_mib):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel from rocprofv3
+    counter CSVs, scaled by what the same counter reads for the largest plain copy
+    in the run (copy_mib MiB read and written)."""
+    import csv
+    import glob
+    import statistics
+    per = {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    key = (r["Kernel_Name"], r["Counter_Name"])
+                    per.setdefault(key, []).append((int(r["Grid_Size"]), float(r["Counter_Value"])))
+    out = {}
+    for (name, counter), vals in per.items():
+        if "copyBuffer" in name:
+            # the calibration copy is the largest copy in the run
+            top = max(v[1] for v in vals)
+            vals = [v for v in vals if v[1] >= 0.9 * top]
+            name = "__copy_calibration__"
+        out.setdefault(name, {})[counter] = (statistics.mean(v[1] for v in vals), len(vals))
+    cal = out.get("__copy_calibration__", {})
+    factors = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        if copy_mib and counter in cal:
+            factors[counter] = copy_mib * 1024.0 / cal[counter][0]
+    return out, factors
 
 
 def algorithmic_bytes(indptr: np.ndarray, N: int, H: int, D: int) -> dict:
@@ -108,6 +181,10 @@ def cpu_baseline(w, indptr, indices, seconds):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        out, factors = pmc_summary(args.pmc_summary, args.pmc_copy_mib)
+        print(json.dumps({"per_kernel_KiB_per_dispatch": out, "scale": factors}, indent=1))
+        return
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU; --gpus %d is not supported (the path would "
               "shard by tokens with no exchange step)" % args.gpus, file=sys.stderr)
@@ -192,6 +269,15 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     run_steps(args.warmup, step_graphs, step)
     ms_per_step = timed(args.steps, step_graphs, step) / args.steps
     # the attention call alone, same rotation: the roofline record's kernel
@@ -233,7 +319,8 @@ def main():
         "gathered_kv_GBps": round(gathered_gbps, 1),
         "gathered_kv_frac_of_hbm_peak": round(gathered_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": recorded_traffic(kernel, args.workload),
                      "kernel": kernel, "us_per_call": round(us_attn, 3),
                      "bytes_per_call": ab["B_alg"]},
     }

@@ -19,9 +19,11 @@
 //     rows per lane) is exactly the B operand layout of O^T += V^T P^T, so P
 //     never leaves registers; V^T is read from the same LDS rows with
 //     ds_read_b64_tr_b16 (the 16-lane transpose read of gfx950);
-//   * the online-softmax state lives per lane (lane = head), so rescaling the
-//     accumulator needs no cross-lane traffic; the reference maximum is only
-//     raised when a score exceeds it by more than 2^8, so rescales are rare;
+//   * the online-softmax state lives per lane (lane = head); its reference
+//     maximum is fixed at the state's first tile, so the accumulator (held in
+//     AGPRs by the MFMAs) is never rescaled inside the loop; a score more than
+//     2^64 above that reference sends the workgroup through a second pass with
+//     the true maximum, which the first pass tracked;
 //   * two decompositions of the work of one token:
 //       heads  -- workgroup = (token, 16*W heads, partition); wave w owns 16
 //                 heads and all waves share each 32-row tile (for batches
@@ -47,10 +49,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(4))) int32_t* ScalarI32Ptr;
 typedef __attribute__((address_space(3))) bf16x4 LdsBf16x4;
 
-constexpr int kStages = 3;                 // heads mode: 32-row tiles in flight
 constexpr int kIdxCap = 2048;              // row indices staged in LDS at a time
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazy = 8.0f;              // log2 headroom before the reference max moves
+constexpr float kRaise = 64.0f;            // log2 headroom of the fixed reference max
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] in bits
 // 3:0, vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt left at their maxima).
@@ -77,6 +78,38 @@ __device__ __forceinline__ void barrier_lds() {
 // rows, one 16-byte chunk each) and the transpose reads (4 rows x 32 bytes),
 // this one gives the highest K-read rate at a near-equal transpose rate.
 __device__ __forceinline__ int row_swizzle(int r) { return r & 15; }
+
+// Per-lane byte offsets, within a tile's LDS stage, of the two read patterns,
+// split so that the tile-dependent part is an instruction immediate.
+//  * K read (S^T = K Q^T): lane (n16, g) reads logical 16-byte chunk 4s + g
+//    of row n16; with sw = swizzle(n16) = 4a + b that chunk is stored at
+//    4 (s ^ a) + (g ^ b) = 4 (s & ~3) + 4 ((s & 3) ^ a) + (g ^ b), i.e. at
+//    koff[s & 3] + 256 (s >> 2) bytes.
+//  * transpose read (V^T operand): lane (n16, g) reads d = 16 dt + 4 (n16 & 3)
+//    .. +3 of row rtr = 4g + n16/4; with sw = swizzle(rtr) = 2c + e, the chunk
+//    (2 dt + b1) ^ sw (b1 = bit 1 of n16) is 2 (dt ^ c) + (b1 ^ e), i.e. the
+//    read is at voff[dt & 7] + 256 (dt >> 3) bytes.
+template <int D>
+struct TileOffsets {
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kChunks = D / 8;
+  int k[4];
+  int v[8];
+  __device__ __forceinline__ TileOffsets(int n16, int g) {
+    const int rtr = 4 * g + (n16 >> 2);
+    const int sk = row_swizzle(n16) & (kChunks - 1);
+    const int sv = row_swizzle(rtr) & (kChunks - 1);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) k[u] = n16 * kRowBytes + 64 * (u ^ (sk >> 2)) + 16 * (g ^ (sk & 3));
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = rtr * kRowBytes + 32 * (u ^ (sv >> 1)) + 16 * (((n16 >> 1) & 1) ^ (sv & 1)) +
+             8 * (n16 & 1);
+  }
+  // byte offset of k-step s of the K read, and of d-tile dt of the transpose read
+  __device__ __forceinline__ int kq(int s) const { return k[s & 3] + 256 * (s >> 2); }
+  __device__ __forceinline__ int vt(int dt) const { return v[dt & 7] + 256 * (dt >> 3); }
+};
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -224,21 +257,6 @@ __device__ __forceinline__ void load_q(const uint16_t* q, int64_t row, int g,
   for (int s = 0; s < D / 32; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
 }
 
-// Initial online-softmax state of a lane: the sink (log2 logit sink*log2(e))
-// as a virtual key with weight 1, in exactly one state per head (`owner`), and
-// in lane group 0 only since the per-lane denominators are summed over the
-// four 16-lane groups at the end.
-__device__ __forceinline__ void init_state(float sink_raw, bool owner, int g, float& m,
-                                           float& lpart) {
-  m = -INFINITY;
-  lpart = 0.f;
-  if (owner) {
-    const float sk = sink_raw * kLog2e;
-    m = sk;
-    if (g == 0 && sk > -INFINITY) lpart = 1.f;
-  }
-}
-
 // Write zeros for heads [h0, h0 + nh) of token t (empty slice).
 template <int D>
 __device__ __forceinline__ void zero_heads(uint16_t* out, int H, int t, int h0, int nh, int tid,
@@ -280,33 +298,58 @@ __device__ __forceinline__ float group_sum4(float v) {
   return __builtin_bit_cast(float, (unsigned)b[0]) + __builtin_bit_cast(float, (unsigned)b[1]);
 }
 
-// Reference-max update and weights for one tile.  x[] are log2-domain scores
-// of this lane's rows (-inf for rows past the end), all of head n16.  Raises m
-// only when a score exceeds it by more than kLazy (wave-uniform decision; the
-// accumulator is rescaled then), and returns the weights 2^(x - m) as bf16.
-template <int R, int NACC>
-__device__ __forceinline__ void softmax_step(const float (&x)[R], float& m, float& lpart,
-                                             f32x4 (&acc)[NACC], __bf16 (&p)[R]) {
+// Weights of one tile.  x[] are the log2-domain scores of this lane's rows
+// (-inf for rows past the end), all of head n16.  The reference maximum m of a
+// state is fixed at its first tile (max of that tile and the sink) and never
+// moves afterwards, so the accumulator is never rescaled inside the loop: a
+// later score may exceed m, giving a weight above 1, which bf16 and fp32
+// represent exactly as long as it stays below 2^kRaise.  A tile with a score
+// beyond m + kRaise sets the returned flag (wave-uniform); the caller then
+// recomputes the whole state with m = mtrue, the running maximum tracked
+// here, which no score can exceed.  lpart is this lane's share of the
+// denominator: it sums the same bf16-rounded weights the PV product uses.
+template <int R>
+__device__ __forceinline__ bool softmax_tile(const float (&x)[R], float sink_l2, int g,
+                                             bool& first, float& m, float& mtrue, float& lpart,
+                                             __bf16 (&p)[R]) {
   float mx = x[0];
 #pragma unroll
   for (int j = 1; j < R; ++j) mx = fmaxf(mx, x[j]);
   mx = group_max4(mx);
-  const bool raise = mx > m + kLazy;
-  if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-    const float mnew = raise ? mx : m;
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // 0 when m was -inf
-    lpart *= alpha;
-#pragma unroll
-    for (int i = 0; i < NACC; ++i) acc[i] *= alpha;
-    m = mnew;
+  mtrue = fmaxf(mtrue, mx);
+  if (first) {
+    m = fmaxf(sink_l2, mx);
+    lpart = (g == 0 && sink_l2 > -INFINITY) ? __builtin_amdgcn_exp2f(sink_l2 - m) : 0.f;
+    first = false;
   }
+  const bool over = __builtin_amdgcn_ballot_w64(mx > m + kRaise) != 0;
   float psum = 0.f;
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     p[j] = (__bf16)__builtin_amdgcn_exp2f(x[j] - m);
-    psum += (float)p[j];  // the denominator sums the same rounded weights as PV
+    psum += (float)p[j];
   }
   lpart += psum;
+  return over;
+}
+
+// State of the second pass: reference max = the true maximum of the first
+// pass (and the sink), so every weight is at most 1.
+__device__ __forceinline__ void second_pass_state(float sink_l2, float mtrue, int g, float& m,
+                                                  float& lpart) {
+  m = fmaxf(sink_l2, mtrue);
+  lpart = (g == 0 && sink_l2 > -INFINITY) ? __builtin_amdgcn_exp2f(sink_l2 - m) : 0.f;
+}
+
+// OR of a wave-uniform flag over the waves of the workgroup (all waves must
+// call it; it ends with a barrier).
+__device__ __forceinline__ bool workgroup_any(bool flag, int* sflag, int wave, int nw) {
+  sflag[wave] = flag ? 1 : 0;
+  barrier_lds();
+  int any = 0;
+  for (int w = 0; w < nw; ++w) any |= sflag[w];
+  barrier_lds();  // the flags may be rewritten by a later call
+  return any != 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -315,7 +358,6 @@ template <int D, int W>
 __global__ void __launch_bounds__(64 * W) attn_heads_kernel(AttnArgs a) {
   constexpr int kTile = 32;
   constexpr int kRowBytes = 2 * D;
-  constexpr int kChunks = D / 8;  // 16-byte chunks per row
   constexpr int kStageBytes = kTile * kRowBytes;
   constexpr int kKSteps = D / 32;
   constexpr int kDTiles = D / 16;
@@ -325,10 +367,15 @@ __global__ void __launch_bounds__(64 * W) attn_heads_kernel(AttnArgs a) {
   constexpr int kHeads = 16 * W;
   static_assert(D % 64 == 0 && D <= 512, "unsupported D");
   static_assert(kLoadsPerTile % W == 0, "loads must divide among waves");
+  // 32-row tiles in flight; a wave's outstanding loads must fit the 6-bit vmcnt
+  constexpr int kAhead = 2 * kLoadsPerWave <= 63 ? 3 : 2;
+  constexpr int kStages = kAhead + 1;
+  static_assert((kStages & (kStages - 1)) == 0 || kStages == 3, "stage count");
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
   __shared__ __attribute__((aligned(256))) int sidx[kIdxCap];
   __shared__ __attribute__((aligned(256))) float ssink[64];
+  __shared__ int sflag[W];
 
   const int item = xcd_item(blockIdx.x, gridDim.x);
   const int c = item % a.splits;
@@ -364,23 +411,25 @@ __global__ void __launch_bounds__(64 * W) attn_heads_kernel(AttnArgs a) {
   load_q<D>(a.q, (int64_t)t * a.H + (hvalid ? h : 0), g, qreg);
   stage_sinks(a.sink, a.H, hg * kHeads, ssink, wave, lane);
 
-  float m = -INFINITY;
-  float lpart = 0.f;  // this lane's share of the denominator
+  const TileOffsets<D> off(n16, g);  // rows n16 / rtr, and 16 rows further
+
+  float m = -INFINITY, lpart = 0.f, mtrue = -INFINITY, sink_l2 = -INFINITY;
   f32x4 acc[kDTiles];
+  for (int pass = 0; pass < 2; ++pass) {
+  bool first = pass == 0;
+  if (pass == 1) second_pass_state(sink_l2, mtrue, g, m, lpart);
 #pragma unroll
   for (int i = 0; i < kDTiles; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int sw_qk = row_swizzle(n16) & (kChunks - 1);  // rows n16 and 16+n16
-  const int rtr = 4 * g + (n16 >> 2);                    // transpose-read row (and +16)
-  const int sw_tr = row_swizzle(rtr) & (kChunks - 1);
+  bool over = false;
 
   for (int sc = 0; sc < nrows; sc += kIdxCap) {
     const int n = nrows - sc < kIdxCap ? nrows - sc : kIdxCap;
-    if (sc > 0) barrier_lds();  // every wave is done with the previous stages and indices
+    if (sc > 0 || pass > 0) barrier_lds();  // every wave is done with the stages and indices
     stage_indices(part, sc, n, sidx, wave, W, lane);
     wait_vmcnt<0>();
     barrier_lds();
-    if (sc == 0) init_state(ssink[wave * 16 + n16], c == 0 && hvalid, g, m, lpart);  // partition 0
+    if (pass == 0 && sc == 0)  // the sink belongs to partition 0's state
+      sink_l2 = (c == 0 && hvalid) ? ssink[wave * 16 + n16] * kLog2e : -INFINITY;
     const int ntiles = (n + kTile - 1) / kTile;
 
     auto issue_tile = [&](int tile) {
@@ -391,16 +440,22 @@ __global__ void __launch_bounds__(64 * W) attn_heads_kernel(AttnArgs a) {
                                            lane);
     };
 
-    issue_tile(0);
-    if (ntiles > 1) issue_tile(1);
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k)
+      if (k < ntiles) issue_tile(k);
 
     for (int i = 0; i < ntiles; ++i) {
-      if (i + 1 < ntiles)
+      // tile i has landed once at most min(kAhead - 1, ntiles - 1 - i) later
+      // tiles of this wave are still outstanding
+      const int later = ntiles - 1 - i;
+      if (later >= kAhead - 1)
+        wait_vmcnt<(kAhead - 1) * kLoadsPerWave>();
+      else if (kAhead == 3 && later == 1)
         wait_vmcnt<kLoadsPerWave>();
       else
         wait_vmcnt<0>();
-      barrier_lds();
-      if (i + 2 < ntiles) issue_tile(i + 2);
+      barrier_lds();  // every wave's part of tile i is in LDS; tile i-1's stage is free
+      if (i + kAhead < ntiles) issue_tile(i + kAhead);
 
       const unsigned char* st = smem + (i % kStages) * kStageBytes;
       const int nvalid = n - i * kTile;  // rows of this tile that exist (>= 1)
@@ -416,9 +471,9 @@ __global__ void __launch_bounds__(64 * W) attn_heads_kernel(AttnArgs a) {
         bf16x8 ka[kB], kb[kB];
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
-          const int pc = ((4 * (s0 + u) + g) ^ sw_qk) << 4;
-          ka[u] = *reinterpret_cast<const bf16x8*>(st + n16 * kRowBytes + pc);
-          kb[u] = *reinterpret_cast<const bf16x8*>(st + (16 + n16) * kRowBytes + pc);
+          const int o = off.kq(s0 + u);
+          ka[u] = *reinterpret_cast<const bf16x8*>(st + o);
+          kb[u] = *reinterpret_cast<const bf16x8*>(st + o + 16 * kRowBytes);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -443,7 +498,7 @@ __global__ void __launch_bounds__(64 * W) attn_heads_kernel(AttnArgs a) {
         x[4 + i4] = (16 + 4 * g + i4 < nvalid) ? sb[i4] * a.qk_scale : -INFINITY;
       }
       __bf16 p[8];
-      softmax_step<8, kDTiles>(x, m, lpart, acc, p);
+      over |= softmax_tile<8>(x, sink_l2, g, first, m, mtrue, lpart, p);
       bf16x8 pt;
 #pragma unroll
       for (int j = 0; j < 8; ++j) pt[j] = p[j];
@@ -455,12 +510,10 @@ __global__ void __launch_bounds__(64 * W) attn_heads_kernel(AttnArgs a) {
         bf16x8 vt[kVB];
 #pragma unroll
         for (int u = 0; u < kVB; ++u) {
-          const int d = 16 * (d0 + u) + 4 * (n16 & 3);
-          const int off = (((d >> 3) ^ sw_tr) << 4) + (d & 7) * 2;
-          const bf16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (LdsBf16x4*)(st + rtr * kRowBytes + off));
-          const bf16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (LdsBf16x4*)(st + (16 + rtr) * kRowBytes + off));
+          const int o = off.vt(d0 + u);
+          const bf16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + o));
+          const bf16x4 vhi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + o + 16 * kRowBytes));
           vt[u] = __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -469,6 +522,8 @@ __global__ void __launch_bounds__(64 * W) attn_heads_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  }
+  if (!workgroup_any(over, sflag, wave, W)) break;
   }
 
   const float l = group_sum4(lpart);
@@ -554,7 +609,6 @@ __global__ void __launch_bounds__(256) attn_rows_kernel(AttnArgs a) {
   constexpr int kWaves = 4;
   constexpr int kTile = 16;
   constexpr int kRowBytes = 2 * D;
-  constexpr int kChunks = D / 8;
   constexpr int kKSteps = D / 32;
   constexpr int kDTiles = D / 16;
   constexpr int kRowsPerLoad = 1024 / kRowBytes;
@@ -568,6 +622,7 @@ __global__ void __launch_bounds__(256) attn_rows_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(256))) int sidx[kIdxCap];
   __shared__ __attribute__((aligned(256))) float ssink[64];
   __shared__ float sml[kWaves][2][16];
+  __shared__ int sflag[kWaves];
 
   const int item = xcd_item(blockIdx.x, gridDim.x);
   const int hg = item % a.head_groups;
@@ -596,94 +651,100 @@ __global__ void __launch_bounds__(256) attn_rows_kernel(AttnArgs a) {
   load_q<D>(a.q, (int64_t)t * a.H + (hvalid ? h : 0), g, qreg);
   stage_sinks(a.sink, a.H, h0, ssink, wave, lane);
 
-  float m = -INFINITY;
-  float lpart = 0.f;
-  f32x4 acc[kDTiles];
-#pragma unroll
-  for (int i = 0; i < kDTiles; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   unsigned char* mine = smem + wave * kWaveBytes;
-  const int sw_qk = row_swizzle(n16) & (kChunks - 1);
-  const int rtr = 4 * g + (n16 >> 2);
-  const int sw_tr = row_swizzle(rtr) & (kChunks - 1);
+  const TileOffsets<D> off(n16, g);
 
-  for (int sc = 0; sc < L; sc += kIdxCap) {
-    const int n = L - sc < kIdxCap ? L - sc : kIdxCap;
-    if (sc > 0) barrier_lds();
-    stage_indices(part, sc, n, sidx, wave, kWaves, lane);
-    wait_vmcnt<0>();
-    barrier_lds();
-    if (sc == 0) init_state(ssink[n16], wave == 0 && hvalid, g, m, lpart);  // sink in wave 0
-    const int ntiles = (n + kTile - 1) / kTile;
-    const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
-
-    auto issue = [&](int j) {  // this wave's j-th tile = global tile wave + 4j
-      issue_rows<kRowBytes, kLoads>(a.kv, sidx, n, (wave + kWaves * j) * kTile, 0,
-                                    mine + (j & 1) * kStageBytes, lane);
-    };
-
-    // Two tiles stay in flight: tile j's LDS stage is released as soon as its
-    // operands are in registers, and the load of tile j+2 goes into it while
-    // tile j's MFMAs run.
-    if (my_tiles > 0) issue(0);
-    if (my_tiles > 1) issue(1);
-    for (int j = 0; j < my_tiles; ++j) {
-      if (j + 1 < my_tiles)
-        wait_vmcnt<kLoads>();
-      else
-        wait_vmcnt<0>();
-      asm volatile("" ::: "memory");
-      const unsigned char* st = mine + (j & 1) * kStageBytes;
-      const int nvalid = n - (wave + kWaves * j) * kTile;
-
-      // S^T = K Q^T: all K operands of the tile read first, then the MFMAs.
-      f32x4 sa = {0.f, 0.f, 0.f, 0.f};
-      {
-        bf16x8 ka[kKSteps];
+  float m = -INFINITY, lpart = 0.f, mtrue = -INFINITY, sink_l2 = -INFINITY;
+  f32x4 acc[kDTiles];
+  for (int pass = 0; pass < 2; ++pass) {
+    bool first = pass == 0;
+    if (pass == 1) second_pass_state(sink_l2, mtrue, g, m, lpart);
 #pragma unroll
-        for (int s = 0; s < kKSteps; ++s) {
-          const int pc = ((4 * s + g) ^ sw_qk) << 4;
-          ka[s] = *reinterpret_cast<const bf16x8*>(st + n16 * kRowBytes + pc);
+    for (int i = 0; i < kDTiles; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bool over = false;
+
+    for (int sc = 0; sc < L; sc += kIdxCap) {
+      const int n = L - sc < kIdxCap ? L - sc : kIdxCap;
+      const bool restage = sc > 0 || (pass == 1 && L > kIdxCap);
+      if (restage) {
+        barrier_lds();  // every wave is done with the indices and its stages
+        stage_indices(part, sc, n, sidx, wave, kWaves, lane);
+        wait_vmcnt<0>();
+        barrier_lds();
+      } else if (pass == 0) {
+        stage_indices(part, sc, n, sidx, wave, kWaves, lane);
+        wait_vmcnt<0>();
+        barrier_lds();
+        sink_l2 = (wave == 0 && hvalid) ? ssink[n16] * kLog2e : -INFINITY;  // sink in wave 0
+      }
+      const int ntiles = (n + kTile - 1) / kTile;
+      const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+
+      auto issue = [&](int j) {  // this wave's j-th tile = global tile wave + 4j
+        issue_rows<kRowBytes, kLoads>(a.kv, sidx, n, (wave + kWaves * j) * kTile, 0,
+                                      mine + (j & 1) * kStageBytes, lane);
+      };
+
+      // Two tiles stay in flight: tile j's LDS stage is released as soon as
+      // its operands are in registers, and the load of tile j+2 goes into it
+      // while tile j's MFMAs run.
+      if (my_tiles > 0) issue(0);
+      if (my_tiles > 1) issue(1);
+      for (int j = 0; j < my_tiles; ++j) {
+        if (j + 1 < my_tiles)
+          wait_vmcnt<kLoads>();
+        else
+          wait_vmcnt<0>();
+        asm volatile("" ::: "memory");
+        const unsigned char* st = mine + (j & 1) * kStageBytes;
+        const int nvalid = n - (wave + kWaves * j) * kTile;
+
+        // S^T = K Q^T: all K operands of the tile read first, then the MFMAs
+        // in four independent accumulation chains.
+        f32x4 sa = {0.f, 0.f, 0.f, 0.f};
+        {
+          bf16x8 ka[kKSteps];
+#pragma unroll
+          for (int s = 0; s < kKSteps; ++s) {
+            ka[s] = *reinterpret_cast<const bf16x8*>(st + off.kq(s));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          constexpr int kCh = kKSteps < 4 ? kKSteps : 4;
+          f32x4 part[kCh];
+#pragma unroll
+          for (int c = 0; c < kCh; ++c) part[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < kKSteps; ++s) part[s % kCh] = mfma_k32(ka[s], qreg[s], part[s % kCh]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int c = 0; c < kCh; ++c) sa += part[c];
+        }
+        // V^T operands: issued now, so they are in flight during the softmax.
+        bf16x4 vt[kDTiles];
+#pragma unroll
+        for (int dt = 0; dt < kDTiles; ++dt) {
+          vt[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + off.vt(dt)));
         }
         __builtin_amdgcn_sched_barrier(0);
-        // four independent accumulation chains, so consecutive MFMAs do not
-        // wait on each other's results
-        constexpr int kCh = kKSteps < 4 ? kKSteps : 4;
-        f32x4 part[kCh];
+        float x[4];
 #pragma unroll
-        for (int c = 0; c < kCh; ++c) part[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i4 = 0; i4 < 4; ++i4)
+          x[i4] = (4 * g + i4 < nvalid) ? sa[i4] * a.qk_scale : -INFINITY;
+        __bf16 p[4];
+        over |= softmax_tile<4>(x, sink_l2, g, first, m, mtrue, lpart, p);
+        bf16x4 pt;
 #pragma unroll
-        for (int s = 0; s < kKSteps; ++s) part[s % kCh] = mfma_k32(ka[s], qreg[s], part[s % kCh]);
+        for (int j4 = 0; j4 < 4; ++j4) pt[j4] = p[j4];
+        // The stage's data is now in registers: release it to the load of tile j+2.
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+        if (j + 2 < my_tiles) issue(j + 2);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < kCh; ++c) sa += part[c];
+        for (int dt = 0; dt < kDTiles; ++dt) acc[dt] = mfma_k16(vt[dt], pt, acc[dt]);
       }
-      // V^T operands: issued now, so they are in flight during the softmax.
-      bf16x4 vt[kDTiles];
-#pragma unroll
-      for (int dt = 0; dt < kDTiles; ++dt) {
-        const int d = 16 * dt + 4 * (n16 & 3);
-        const int off = (((d >> 3) ^ sw_tr) << 4) + (d & 7) * 2;
-        vt[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + rtr * kRowBytes + off));
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      float x[4];
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4)
-        x[i4] = (4 * g + i4 < nvalid) ? sa[i4] * a.qk_scale : -INFINITY;
-      __bf16 p[4];
-      softmax_step<4, kDTiles>(x, m, lpart, acc, p);
-      bf16x4 pt;
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) pt[j4] = p[j4];
-      // The stage's data is now in registers: release it to the load of tile j+2.
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      asm volatile("" ::: "memory");
-      if (j + 2 < my_tiles) issue(j + 2);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int dt = 0; dt < kDTiles; ++dt) acc[dt] = mfma_k16(vt[dt], pt, acc[dt]);
     }
+    if (!workgroup_any(over, sflag, wave, kWaves)) break;
   }
 
   // Merge the four waves' states.  Wave w's partial O goes to its own stage
