@@ -10,8 +10,9 @@ workloads (--workload) are for exploration; those given as ready CSR indices
 
 Inputs are resident in HBM before timing starts.  R rotating input sets
 (separate pool, queries, builder inputs, outputs) keep the touched footprint
-above twice the 256 MB Infinity Cache, so steps are fed from HBM.  Each step is
-a HIP graph captured once per set and replayed.
+above twice the 256 MB Infinity Cache, so steps are fed from HBM.  The timed
+loops replay one HIP graph that holds one step per set back to back (single-step
+graphs cover a remainder), timed with HIP events on the replay stream.
 
 Prints one JSON line: tokens/s for the whole job, gathered KV GB/s, the
 roofline record of the attention kernel, and the oracle timed on this host's
@@ -241,30 +242,44 @@ def main():
     for s in sets:  # eager warm-up (and the indices the graphs will rebuild)
         step(s)
     torch.cuda.synchronize()
-    step_graphs, attn_graphs = [], []
+    # One graph per set for each of (step, attention call), plus one graph that
+    # holds every set's call back to back: the timed loops replay the latter,
+    # so consecutive calls are not separated by per-graph launch gaps.
+    single = {"step": [], "attn": []}
+    chain = {}
+    cs = torch.cuda.Stream()
     if not args.eager:
-        cs = torch.cuda.Stream()
-        for s in sets:
-            for fn, lst in ((step, step_graphs), (attn, attn_graphs)):
+        for name, fn in (("step", step), ("attn", attn)):
+            for s in sets:
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=cs):
                     fn(s)
-                lst.append(g)
+                single[name].append(g)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cs):
+                for s in sets:
+                    fn(s)
+            chain[name] = g
         torch.cuda.synchronize()
 
-    def run_steps(k, graphs, fn):
-        for i in range(k):
-            if graphs:
-                graphs[i % len(graphs)].replay()
-            else:
+    def run_calls(k, name, fn):
+        """Exactly k calls, rotating over the sets."""
+        if args.eager:
+            for i in range(k):
                 fn(sets[i % len(sets)])
+            return
+        for _ in range(k // len(sets)):
+            chain[name].replay()
+        for i in range(k % len(sets)):
+            single[name][i].replay()
 
-    def timed(k, graphs, fn):
+    def timed(k, name, fn):
+        # events on the stream the calls run on (graphs replay on the current stream)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
-        run_steps(k, graphs, fn)
+        run_calls(k, name, fn)
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
@@ -278,12 +293,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    run_steps(args.warmup, step_graphs, step)
-    ms_per_step = timed(args.steps, step_graphs, step) / args.steps
+    run_calls(args.warmup, "step", step)
+    ms_per_step = timed(args.steps, "step", step) / args.steps
     # the attention call alone, same rotation: the roofline record's kernel
-    run_steps(min(args.warmup, 64), attn_graphs, attn)
+    run_calls(min(args.warmup, 64), "attn", attn)
     n_attn = max(args.steps, 100)
-    us_attn = timed(n_attn, attn_graphs, attn) * 1e3 / n_attn
+    us_attn = timed(n_attn, "attn", attn) * 1e3 / n_attn
 
     indptr = sets[0]["ptr"].cpu().numpy()
     indices = sets[0]["idx"].cpu().numpy()[: indptr[-1]]
@@ -314,7 +329,7 @@ def main():
         "config": {"workload": args.workload, "N": N, "H": H, "D": D, "pool_rows": w.P,
                    "max_len": max_len, "sum_L": ab["sum_L"], "nonempty_tokens": ab["nonempty"],
                    "plan": plan, "rotating_sets": n_sets,
-                   "launch": "eager" if args.eager else "hip_graph_per_step",
+                   "launch": "eager" if args.eager else "hip_graph_of_%d_steps" % n_sets,
                    "step": ("build_decode_indices + " if b is not None else "") + "sparse_decode_attn"},
         "gathered_kv_GBps": round(gathered_gbps, 1),
         "gathered_kv_frac_of_hbm_peak": round(gathered_gbps / HBM_PEAK_GBPS, 4),

@@ -171,3 +171,51 @@ def test_validate_indices(spd):
     assert spd.validate_indices(idx, ptr, 9) == 3 + 1 + 1      # kv_indices[1] == 9 out of range
     bad_ptr = torch.tensor([0, 3, 2, 5], dtype=torch.int32, device=d)
     assert spd.validate_indices(idx, bad_ptr, 10) == 2        # decreasing at t = 2
+
+
+def test_late_large_scores_take_the_second_pass(spd):
+    """Rows planted in later tiles whose score for head 0 lies far (> 64 in
+    log2 units) above everything in the first tile of the state that reads
+    them: the reference maximum fixed at that first tile is left behind, so the
+    kernel must redo the state with the true maximum.  Two planted rows of
+    nearby scores keep the expected output a genuine mix of rows.  The 2100-row
+    token also crosses the 2048-index staging chunk."""
+    lengths = [300, 700, 40, 2100, 0]
+    w = W.random_csr("late", 17, len(lengths), 64, 512, 6000, lengths, replace=False)
+    kv = w.kv_bits.copy()
+    q = W.bf16_to_f32(w.q_bits).astype(np.float32)
+    plants = {0: (100, 290), 1: (150, 650), 3: (1000, 2090)}
+    for t, (p2, p1) in plants.items():
+        a = int(w.kv_indptr[t])
+        kv[int(w.kv_indices[a + p1])] = W.bf16_bits(4.0 * q[t, 0])   # score ~ 90
+        kv[int(w.kv_indices[a + p2])] = W.bf16_bits(3.9 * q[t, 0])   # ~ 2 lower
+    w.kv_bits = kv
+    log("case late large scores")
+    ref = oracle_tokens(w, w.kv_indices, w.kv_indptr)
+    for plan in PLANS + [dict(mode=HEADS, max_len=2100, split_rows=256)]:
+        out = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
+        assert_close(bf16_to_f64(out), ref, "late large %s" % plan)
+
+
+@pytest.mark.parametrize("case", __import__("golden_cases").attention_cases(), ids=lambda c: c["name"])
+def test_worked_examples_padded(spd, case):
+    """The hand-worked fixtures of tests/golden/, with D zero-padded to 64 (the
+    padding adds nothing to any score and yields zero output columns)."""
+    N, H, Dg = case["q"].shape
+    D = 64
+    q = np.zeros((N, H, D), dtype=np.float32)
+    q[:, :, :Dg] = case["q"]
+    kv = np.zeros((case["kv"].shape[0], D), dtype=np.float32)
+    kv[:, :Dg] = case["kv"]
+    ref = np.zeros((N, H, D))
+    ref[:, :, :Dg] = case["out"]
+    d = torch.device("cuda:0")
+    qd = torch.from_numpy(W.bf16_bits(q).view(np.int16)).to(d).view(torch.bfloat16)
+    kvd = torch.from_numpy(W.bf16_bits(kv).view(np.int16)).to(d).view(torch.bfloat16)
+    sink = torch.from_numpy(case["attn_sink"]).to(d)
+    idx, ptr = device_csr(case["kv_indices"], case["kv_indptr"])
+    log("case golden %s" % case["name"])
+    for plan in PLANS:
+        out = spd.sparse_decode_attn(qd, kvd, idx, ptr, sink, case["softmax_scale"], **plan)
+        torch.cuda.synchronize()
+        assert_close(bf16_to_f64(out), ref, "golden %s %s" % (case["name"], plan))

@@ -74,14 +74,15 @@ def test_decode_base_config(spd):
 
 
 def test_hand_worked_example(spd):
-    """Same hand-derived case as the oracle pin: indptr [0,5,9,9],
-    indices [8,9,10,22,15,0,1,2,3]."""
-    b = W.BuilderInputs(np.array([2, 0, 1], dtype=np.int32), np.array([3, 4, 0], dtype=np.int32),
-                        np.array([[0, 3, -1], [-1, -1, -1], [-1, -1, -1]], dtype=np.int32),
-                        np.array([[5, 1], [0, 0], [0, 0]], dtype=np.int32), 4, 2, 12)
+    """The hand-derived fixture tests/golden/builder_worked_example.json."""
+    import golden_cases
+    c = golden_cases.builder_case()
+    b = W.BuilderInputs(c["state_slot"], c["swa_len"], c["comp_pos"], c["block_table"], c["win"],
+                        c["k_per_block"], c["swa_pages"])
     log("case builder hand example")
     ss, sl, cp, bt = device_builder_inputs(b)
-    ptr, idx = spd.build_decode_indices(ss, sl, cp, bt, 4, 2, 12)
+    ptr, idx = spd.build_decode_indices(ss, sl, cp, bt, b.win, b.k_per_block, b.swa_pages)
     torch.cuda.synchronize()
-    assert ptr.cpu().tolist() == [0, 5, 9, 9]
-    assert idx.cpu().tolist()[:9] == [8, 9, 10, 22, 15, 0, 1, 2, 3]
+    n = int(c["kv_indptr"][-1])
+    assert ptr.cpu().tolist() == c["kv_indptr"].tolist()
+    assert idx.cpu().tolist()[:n] == c["kv_indices"].tolist()

@@ -16,6 +16,7 @@ import pytest
 import torch
 
 import brute
+import golden_cases
 import workloads as W
 
 LN2 = math.log(2.0)
@@ -49,18 +50,18 @@ def test_matches_brute_force_softmax(oracle_mod, seed):
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
 
 
-def test_worked_example_closed_form(oracle_mod):
-    """Hand-derived case: q=[1,0], rows r0=[1,0], r1=[0,1], slice [r0, r1, r1],
-    scale=ln 4, sink=0.  Scores are ln 4, 0, 0; with the sink's exp(0)=1 the
-    weights are 4, 1, 1 over a denominator 4+1+1+1 = 7, so out = [4/7, 2/7]."""
-    q = W.bf16_bits(np.array([[[1.0, 0.0]]], dtype=np.float32))
-    kv = W.bf16_bits(np.array([[1.0, 0.0], [0.0, 1.0]], dtype=np.float32))
-    idx = np.array([0, 1, 1], dtype=np.int32)
-    indptr = np.array([0, 3], dtype=np.int32)
-    sink = np.zeros(1, dtype=np.float32)
-    out = oracle_mod.sparse_decode_attn(q, kv, idx, indptr, sink, math.log(4.0))
-    # softmax_scale is an fp32 value, so exp(scale) is 4 only to fp32 precision
-    np.testing.assert_allclose(out[0, 0], [4.0 / 7.0, 2.0 / 7.0], rtol=2e-7)
+@pytest.mark.parametrize("case", golden_cases.attention_cases(), ids=lambda c: c["name"])
+def test_worked_examples(oracle_mod, case):
+    """Hand-worked fixtures (tests/golden/attention_worked_examples.json): exact
+    fractions derived from the definition, covering the sink as a virtual key
+    in natural-log units, a -inf sink and an empty slice."""
+    q = W.bf16_bits(case["q"])
+    kv = W.bf16_bits(case["kv"])
+    out = oracle_mod.sparse_decode_attn(q, kv, case["kv_indices"], case["kv_indptr"],
+                                        case["attn_sink"], case["softmax_scale"])
+    # softmax_scale and the sink are fp32 values, so the weights match the
+    # stated integers only to fp32 precision
+    np.testing.assert_allclose(out, case["out"], rtol=1e-6, atol=1e-7)
 
 
 @pytest.mark.parametrize("seed", range(6))

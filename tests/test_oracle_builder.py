@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import brute
+import golden_cases
 import workloads as W
 
 
@@ -43,18 +44,13 @@ def test_matches_membership_brute_force(oracle_mod, seed):
 
 
 def test_hand_worked_example(oracle_mod):
-    """Hand-derived from the slot formulas: win=4, K_PER_BLOCK=2, swa_pages=12.
-    Token 0: state 2, ring length 3 -> 8, 9, 10; comp_pos [0, 3, -1] with
-    block_table [5, 1] -> 12+5*2+0 = 22, then 12+1*2+1 = 15.
-    Token 1: state 0, ring length 4 -> 0..3; comp_pos all -1 -> nothing.
-    Token 2: padding: empty ring, no compressed entries -> zero length."""
-    ss = np.array([2, 0, 1], dtype=np.int32)
-    sl = np.array([3, 4, 0], dtype=np.int32)
-    cp = np.array([[0, 3, -1], [-1, -1, -1], [-1, -1, -1]], dtype=np.int32)
-    bt = np.array([[5, 1], [0, 0], [0, 0]], dtype=np.int32)
-    indptr, indices = oracle_mod.build_decode_indices(ss, sl, cp, bt, 4, 2, 12)
-    assert indptr.tolist() == [0, 5, 9, 9]
-    assert indices.tolist() == [8, 9, 10, 22, 15, 0, 1, 2, 3]
+    """The hand-derived fixture tests/golden/builder_worked_example.json."""
+    c = golden_cases.builder_case()
+    indptr, indices = oracle_mod.build_decode_indices(c["state_slot"], c["swa_len"], c["comp_pos"],
+                                                      c["block_table"], c["win"], c["k_per_block"],
+                                                      c["swa_pages"])
+    assert indptr.tolist() == c["kv_indptr"].tolist()
+    assert indices.tolist() == c["kv_indices"].tolist()
 
 
 def test_order_window_then_compressed(oracle_mod):
