@@ -157,6 +157,10 @@ SPD_API spd_status build_decode_indices(const int32_t* state_slot, const int32_t
   a.win = win;
   a.k_per_block = k_per_block;
   a.swa_pages = swa_pages;
+  a.comp_vec4 = a.comp_pos != nullptr && topk % 4 == 0 &&
+                (reinterpret_cast<uintptr_t>(comp_pos) & 15) == 0;
+  const int64_t lim = (int64_t)max_blocks * k_per_block;
+  a.comp_limit = (uint32_t)(lim < (int64_t(1) << 31) ? lim : (int64_t(1) << 31));
   const hipError_t e = spd::launch_build_indices(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPD_OK : SPD_ERR_HIP;
 }

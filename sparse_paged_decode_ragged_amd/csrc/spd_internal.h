@@ -52,6 +52,8 @@ struct BuildArgs {
   int32_t* kv_indptr;
   int32_t* kv_indices;
   int32_t topk, max_blocks, N, win, k_per_block, swa_pages;
+  int32_t comp_vec4;    // comp_pos rows are 16-byte aligned (aligned base, topk % 4 == 0)
+  uint32_t comp_limit;  // min(max_blocks * k_per_block, 2^31): entry p is valid iff 0 <= p < it
 };
 
 hipError_t launch_build_indices(const BuildArgs& args, hipStream_t stream);

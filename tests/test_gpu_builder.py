@@ -53,6 +53,7 @@ def check(spd, b: W.BuilderInputs, what: str):
     (3, 300, 32, 100, 8, 13, 50),
     (4, 3000, 8, 70, 16, 5, 40),      # several 1024-token scan chunks
     (5, 1025, 128, 64, 64, 1, 100),
+    (6, 200, 64, 512, 8, 64, 100),    # N * topk above the one-launch limit, N <= 1024
 ])
 def test_random_bit_exact(spd, seed, N, win, topk, k, mb, nb):
     check(spd, _random_inputs(seed, N, win, topk, k, mb, nb), "random N=%d" % N)
@@ -86,3 +87,37 @@ def test_hand_worked_example(spd):
     n = int(c["kv_indptr"][-1])
     assert ptr.cpu().tolist() == c["kv_indptr"].tolist()
     assert idx.cpu().tolist()[:n] == c["kv_indices"].tolist()
+
+
+def test_defensive_rules_and_unaligned_rows(spd):
+    """Out-of-contract metadata takes the documented device rule: swa_len is
+    clamped to [0, win] and a comp_pos entry whose block lookup falls outside
+    [0, max_blocks) (or any negative entry) is dropped.  Expected output: the
+    oracle on the sanitised input.  The comp_pos rows are passed as a view one
+    int32 past a 16-byte boundary with topk % 4 == 0, so the 4-entries-per-load
+    path must not be taken."""
+    rng = np.random.default_rng(77)
+    N, win, topk, k, mb, nb = 40, 16, 64, 4, 6, 30
+    b = _random_inputs(78, N, win, topk, k, mb, nb)
+    cp = b.comp_pos.copy()
+    cp[rng.random(cp.shape) < 0.1] = mb * k + rng.integers(0, 50)      # beyond the table
+    cp[rng.random(cp.shape) < 0.05] = -7
+    sl = b.swa_len.copy()
+    sl[:3] = [-2, win + 5, win]
+    clean_cp = np.where((cp >= 0) & (cp < mb * k), cp, -1).astype(np.int32)
+    clean_sl = np.clip(sl, 0, win).astype(np.int32)
+    optr, oidx = oracle.build_decode_indices(b.state_slot, clean_sl, clean_cp, b.block_table,
+                                             win, k, b.swa_pages)
+    log("case builder defensive rules")
+    d = torch.device("cuda:0")
+    flat = torch.zeros(cp.size + 1, dtype=torch.int32, device=d)
+    flat[1:] = torch.from_numpy(cp.reshape(-1)).to(d)
+    cp_view = flat[1:].view(N, topk)                 # data pointer 4 bytes past the allocation
+    assert cp_view.data_ptr() % 16 != 0
+    ss = torch.from_numpy(b.state_slot).to(d)
+    sld = torch.from_numpy(sl.astype(np.int32)).to(d)
+    bt = torch.from_numpy(b.block_table).to(d)
+    ptr, idx = spd.build_decode_indices(ss, sld, cp_view, bt, win, k, b.swa_pages)
+    torch.cuda.synchronize()
+    assert np.array_equal(ptr.cpu().numpy(), optr)
+    assert np.array_equal(idx.cpu().numpy()[:optr[-1]], oidx)
