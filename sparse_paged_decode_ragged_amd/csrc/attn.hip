@@ -685,47 +685,51 @@ __global__ void __launch_bounds__(256) attn_rows_kernel(AttnArgs a) {
                                       mine + (j & 1) * kStageBytes, lane);
       };
 
-      // Two tiles stay in flight: tile j's LDS stage is released as soon as
-      // its operands are in registers, and the load of tile j+2 goes into it
-      // while tile j's MFMAs run.
+      // Software pipeline over this wave's tiles, two LDS stages: the V^T
+      // reads of tile j run under tile j's QK MFMAs, the K reads of tile j+1
+      // run under tile j's PV MFMAs, and the load of tile j+2 goes into tile
+      // j's stage as soon as its reads are done.  (sched_group_barrier fixes
+      // the interleave: one MFMA per two LDS reads, then two per one.)
+      constexpr int kCh = kKSteps < 4 ? kKSteps : 4;  // independent QK chains
+      bf16x8 ka[kKSteps];
       if (my_tiles > 0) issue(0);
       if (my_tiles > 1) issue(1);
-      for (int j = 0; j < my_tiles; ++j) {
-        if (j + 1 < my_tiles)
+      if (my_tiles > 0) {
+        if (my_tiles > 1)
           wait_vmcnt<kLoads>();
         else
           wait_vmcnt<0>();
         asm volatile("" ::: "memory");
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) ka[s] = *reinterpret_cast<const bf16x8*>(mine + off.kq(s));
+      }
+      for (int j = 0; j < my_tiles; ++j) {
         const unsigned char* st = mine + (j & 1) * kStageBytes;
+        const unsigned char* stn = mine + ((j + 1) & 1) * kStageBytes;
         const int nvalid = n - (wave + kWaves * j) * kTile;
 
-        // S^T = K Q^T: all K operands of the tile read first, then the MFMAs
-        // in four independent accumulation chains.
-        f32x4 sa = {0.f, 0.f, 0.f, 0.f};
-        {
-          bf16x8 ka[kKSteps];
+        // S^T = K Q^T (four chains) with the V^T reads of the same tile.
+        f32x4 part[kCh];
 #pragma unroll
-          for (int s = 0; s < kKSteps; ++s) {
-            ka[s] = *reinterpret_cast<const bf16x8*>(st + off.kq(s));
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          constexpr int kCh = kKSteps < 4 ? kKSteps : 4;
-          f32x4 part[kCh];
-#pragma unroll
-          for (int c = 0; c < kCh; ++c) part[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < kKSteps; ++s) part[s % kCh] = mfma_k32(ka[s], qreg[s], part[s % kCh]);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int c = 0; c < kCh; ++c) sa += part[c];
-        }
-        // V^T operands: issued now, so they are in flight during the softmax.
+        for (int c = 0; c < kCh; ++c) part[c] = f32x4{0.f, 0.f, 0.f, 0.f};
         bf16x4 vt[kDTiles];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int dt = 0; dt < kDTiles; ++dt) {
-          vt[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + off.vt(dt)));
+        for (int s = 0; s < kKSteps; ++s) {
+          part[s % kCh] = mfma_k32(ka[s], qreg[s], part[s % kCh]);
+          vt[2 * s] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + off.vt(2 * s)));
+          vt[2 * s + 1] =
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + off.vt(2 * s + 1)));
+        }
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
         }
         __builtin_amdgcn_sched_barrier(0);
+        f32x4 sa = part[0];
+#pragma unroll
+        for (int c = 1; c < kCh; ++c) sa += part[c];
         float x[4];
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4)
@@ -735,13 +739,31 @@ __global__ void __launch_bounds__(256) attn_rows_kernel(AttnArgs a) {
         bf16x4 pt;
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4) pt[j4] = p[j4];
-        // The stage's data is now in registers: release it to the load of tile j+2.
+        // Every read of tile j's stage is complete: it takes the load of tile j+2.
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         asm volatile("" ::: "memory");
         if (j + 2 < my_tiles) issue(j + 2);
+        if (j + 1 < my_tiles) {  // tile j+1 has landed once only tile j+2 may be outstanding
+          if (j + 2 < my_tiles)
+            wait_vmcnt<kLoads>();
+          else
+            wait_vmcnt<0>();
+        }
+        asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
+        // O^T += V^T P^T, with the K reads of tile j+1 (harmless stale reads
+        // after the last tile: the stage is in bounds and the values unused).
 #pragma unroll
-        for (int dt = 0; dt < kDTiles; ++dt) acc[dt] = mfma_k16(vt[dt], pt, acc[dt]);
+        for (int dt = 0; dt < kDTiles; ++dt) {
+          acc[dt] = mfma_k16(vt[dt], pt, acc[dt]);
+          if (dt & 1) ka[dt >> 1] = *reinterpret_cast<const bf16x8*>(stn + off.kq(dt >> 1));
+        }
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (!workgroup_any(over, sflag, wave, kWaves)) break;
@@ -832,8 +854,10 @@ bool make_attn_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t sp
                     int32_t mode, AttnPlan* p) {
   if (!attn_supported(H, D) || N < 0 || max_len < 0 || split_rows < 0) return false;
   if (mode != kModeAuto && mode != kModeHeads && mode != kModeRows) return false;
+  // heads mode: 16 heads per wave, 16*W heads per workgroup
   const int heads_waves = H <= 16 ? 1 : (H <= 32 ? 2 : 4);
-  const long long heads_groups = (H + 16 * heads_waves - 1) / (16 * heads_waves);
+  const int heads_per = 16 * heads_waves;
+  const long long heads_groups = (H + heads_per - 1) / heads_per;
   // Work items the heads mode provides without split-L; the chip has 256 CUs.
   const long long target = 256;
   if (mode == kModeAuto)
@@ -851,7 +875,7 @@ bool make_attn_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t sp
   }
   p->mode = kModeHeads;
   p->waves = heads_waves;
-  p->heads_per_group = 16 * heads_waves;
+  p->heads_per_group = heads_per;
   p->head_groups = (int)heads_groups;
   long long splits = 1, rows = 0;
   if (split_rows > 0) {

@@ -15,9 +15,9 @@
 //     every token up to its own sixteen (so it needs no other workgroup's
 //     result), writes their kv_indptr entries and scatters them;
 //   otherwise:
-//     1. count+scan (N <= 1024): one 1024-thread workgroup counts every
-//        token's entries (window length + valid comp_pos entries) and writes
-//        kv_indptr; or, for larger N, 1a. count (one wave per token) and
+//     1. count+scan (N <= 1024, N * topk <= 2^18): one 1024-thread workgroup
+//        counts every token's entries (window length + valid comp_pos entries)
+//        and writes kv_indptr; otherwise 1a. count (one wave per token) and
 //        1b. scan (one workgroup, in place);
 //     2. scatter: one wave per token writes the window slots, then the valid
 //        compressed slots compacted in comp_pos order (ballot + mbcnt).
@@ -397,7 +397,7 @@ hipError_t launch_build_indices(const BuildArgs& a, hipStream_t stream) {
                        stream, a);
     return hipGetLastError();
   }
-  if (a.N <= kSmallN) {
+  if (a.N <= kSmallN && (int64_t)a.N * (a.comp_pos ? a.topk : 0) <= 4 * kFusedEntries) {
     hipLaunchKernelGGL(build_count_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
   } else {
     hipLaunchKernelGGL(build_count_kernel, dim3(blocks), dim3(256), 0, stream, a);
