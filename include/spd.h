@@ -179,6 +179,38 @@ SPD_API spd_status build_decode_indices(const int32_t* state_slot, const int32_t
                                         int64_t indices_capacity, void* stream);
 
 /*
+ * sparse_decode_attn with the page transform fused into the attention kernel:
+ * each workgroup derives its token's row list from the builder's inputs, by
+ * exactly the rule of build_decode_indices above (window slots, then the
+ * valid compressed slots in comp_pos order), and gathers those rows; the
+ * ragged kv_indices / kv_indptr are never materialised.  The result equals
+ * build_decode_indices followed by sparse_decode_attn on its output, bit for
+ * bit: the rows are the same and are visited in the same order.  (The page
+ * transform as a structure of its own that several kernels share: prhub
+ * sglang attention-tag page, entry of 2026-09-16 on the DSV4.1 indexer
+ * kernels; the slot formulas: sglang PR #28392 summary page, "key source
+ * snippet".)
+ *
+ *   q, unified_kv, attn_sink, softmax_scale, out, N, H, D: as sparse_decode_attn
+ *   state_slot, swa_len, comp_pos, topk, block_table, max_blocks, win,
+ *   k_per_block, swa_pages: as build_decode_indices (same host checks, same
+ *                device-side clamping of swa_len and dropping of comp_pos
+ *                entries outside [0, max_blocks * k_per_block))
+ *   mode         an spd_mode; never splits a token across workgroups, so no
+ *                workspace
+ *
+ * win + topk must not exceed 2048 (a token's whole list is built in LDS before
+ * its first row is loaded): SPD_ERR_UNSUPPORTED otherwise.  Caller
+ * precondition (not checked): the produced slots lie in [0, num_rows).
+ */
+SPD_API spd_status sparse_decode_attn_paged(
+    const void* q, const void* unified_kv, int64_t num_rows, const int32_t* state_slot,
+    const int32_t* swa_len, const int32_t* comp_pos, int32_t topk, const int32_t* block_table,
+    int32_t max_blocks, int32_t win, int32_t k_per_block, int32_t swa_pages,
+    const float* attn_sink, float softmax_scale, void* out, int32_t N, int32_t H, int32_t D,
+    int32_t mode, void* stream);
+
+/*
  * Debug check of the attention call's index preconditions: kv_indptr[0] == 0,
  * kv_indptr non-decreasing, kv_indptr[N] <= num_indices (the length of the
  * kv_indices buffer), and every kv_indices[j], j < kv_indptr[N], in

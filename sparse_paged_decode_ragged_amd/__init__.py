@@ -12,6 +12,10 @@ Call names follow the C ABI:
   softmax_scale, out=None, *, max_len=0, split_rows=0, workspace=None)``
 * ``build_decode_indices(state_slot, swa_len, comp_pos, block_table, win,
   k_per_block, swa_pages, kv_indptr=None, kv_indices=None)``
+* ``sparse_decode_attn_paged(q, unified_kv, state_slot, swa_len, comp_pos,
+  block_table, win, k_per_block, swa_pages, attn_sink, softmax_scale,
+  out=None)`` -- the two above in one kernel (the page transform fused into
+  the attention call; no kv_indices in memory)
 * ``sparse_decode_attn_workspace_size``, ``sparse_decode_attn_can_use``,
   ``validate_indices``
 """
@@ -33,7 +37,7 @@ _STATUS = {0: "SPD_OK", 1: "SPD_ERR_INVALID_ARG", 2: "SPD_ERR_UNSUPPORTED", 3: "
 EXPORTED_SYMBOLS = (
     "spd_status_string", "spd_version", "sparse_decode_attn_can_use", "sparse_decode_attn",
     "sparse_decode_attn_workspace_size", "sparse_decode_attn_ex", "build_decode_indices",
-    "spd_validate_indices", "sparse_decode_attn_plan_info",
+    "spd_validate_indices", "sparse_decode_attn_plan_info", "sparse_decode_attn_paged",
 )
 
 
@@ -62,6 +66,9 @@ def _load() -> ctypes.CDLL:
     lib.sparse_decode_attn_ex.argtypes = [P, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32, i32,
                                           i32, i32, P, sz, P]
     lib.sparse_decode_attn_ex.restype = ctypes.c_int
+    lib.sparse_decode_attn_paged.argtypes = [P, P, i64, P, P, P, i32, P, i32, i32, i32, i32, P,
+                                             ctypes.c_float, P, i32, i32, i32, i32, P]
+    lib.sparse_decode_attn_paged.restype = ctypes.c_int
     lib.build_decode_indices.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i32, P, P, i64, P]
     lib.build_decode_indices.restype = ctypes.c_int
     lib.spd_validate_indices.argtypes = [P, i64, P, i32, i64, ctypes.POINTER(ctypes.c_int64), P]
@@ -207,6 +214,46 @@ def build_decode_indices(state_slot: torch.Tensor, swa_len: torch.Tensor,
                                   kv_indices.numel(), _stream(dev))
     _raise_on(st, "build_decode_indices")
     return kv_indptr, kv_indices
+
+
+def sparse_decode_attn_paged(q: torch.Tensor, unified_kv: torch.Tensor, state_slot: torch.Tensor,
+                             swa_len: torch.Tensor, comp_pos: Optional[torch.Tensor],
+                             block_table: Optional[torch.Tensor], win: int, k_per_block: int,
+                             swa_pages: int, attn_sink: torch.Tensor, softmax_scale: float,
+                             out: Optional[torch.Tensor] = None, *,
+                             mode: int = MODE_AUTO) -> torch.Tensor:
+    """out[N, H, D] (bf16): build_decode_indices + sparse_decode_attn in one
+    kernel, with each token's rows derived on the device (see include/spd.h).
+    Needs win + topk <= 2048; never splits, so it takes no workspace."""
+    _check(q, "q", torch.bfloat16, 3)
+    _check(unified_kv, "unified_kv", torch.bfloat16, 2)
+    _check(state_slot, "state_slot", torch.int32, 1)
+    _check(swa_len, "swa_len", torch.int32, 1)
+    _check(attn_sink, "attn_sink", torch.float32, 1)
+    N, H, D = q.shape
+    if unified_kv.shape[1] != D or attn_sink.shape[0] != H or state_slot.shape[0] != N or \
+            swa_len.shape[0] != N:
+        raise ValueError("shape mismatch between q, unified_kv, state_slot, swa_len and attn_sink")
+    topk, max_blocks = 0, 0
+    if comp_pos is not None:
+        _check(comp_pos, "comp_pos", torch.int32, 2)
+        _check(block_table, "block_table", torch.int32, 2)
+        topk, max_blocks = comp_pos.shape[1], block_table.shape[1]
+        if comp_pos.shape[0] != N or block_table.shape[0] != N:
+            raise ValueError("comp_pos and block_table must have N rows")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16, 3)
+        if tuple(out.shape) != (N, H, D):
+            raise ValueError("out must be [N, H, D]")
+    st = lib.sparse_decode_attn_paged(_ptr(q), _ptr(unified_kv), unified_kv.shape[0],
+                                      _ptr(state_slot), _ptr(swa_len), _ptr(comp_pos), topk,
+                                      _ptr(block_table), max_blocks, int(win), int(k_per_block),
+                                      int(swa_pages), _ptr(attn_sink), float(softmax_scale),
+                                      _ptr(out), N, H, D, int(mode), _stream(q.device))
+    _raise_on(st, "sparse_decode_attn_paged")
+    return out
 
 
 def validate_indices(kv_indices: torch.Tensor, kv_indptr: torch.Tensor, num_rows: int) -> int:

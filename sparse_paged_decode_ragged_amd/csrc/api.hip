@@ -99,7 +99,7 @@ SPD_API spd_status sparse_decode_attn_ex(const void* q, const void* unified_kv, 
     if (!aligned(workspace, 16)) return SPD_ERR_INVALID_ARG;
   }
 
-  spd::AttnArgs a;
+  spd::AttnArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.kv = static_cast<const uint16_t*>(unified_kv);
   a.kv_indices = kv_indices;
@@ -126,6 +126,69 @@ SPD_API spd_status sparse_decode_attn(const void* q, const void* unified_kv, int
                                stream);
 }
 
+SPD_API spd_status sparse_decode_attn_paged(
+    const void* q, const void* unified_kv, int64_t num_rows, const int32_t* state_slot,
+    const int32_t* swa_len, const int32_t* comp_pos, int32_t topk, const int32_t* block_table,
+    int32_t max_blocks, int32_t win, int32_t k_per_block, int32_t swa_pages,
+    const float* attn_sink, float softmax_scale, void* out, int32_t N, int32_t H, int32_t D,
+    int32_t mode, void* stream) {
+  if (N < 0 || H <= 0 || D <= 0 || num_rows <= 0) return SPD_ERR_INVALID_ARG;
+  if (topk < 0 || win <= 0 || k_per_block <= 0 || swa_pages < 0 || max_blocks < 0)
+    return SPD_ERR_INVALID_ARG;
+  if (comp_pos == nullptr && topk > 0) return SPD_ERR_INVALID_ARG;
+  if (comp_pos != nullptr && topk > 0 && (block_table == nullptr || max_blocks <= 0))
+    return SPD_ERR_INVALID_ARG;
+  if (mode != SPD_MODE_AUTO && mode != SPD_MODE_HEADS && mode != SPD_MODE_ROWS)
+    return SPD_ERR_INVALID_ARG;
+  if (!isfinite(softmax_scale)) return SPD_ERR_INVALID_ARG;
+  if (!spd::attn_supported(H, D)) return SPD_ERR_UNSUPPORTED;
+  if ((int64_t)win + topk > spd::kPagedMaxLen) return SPD_ERR_UNSUPPORTED;
+  if (N == 0) return SPD_OK;
+  if (!q || !unified_kv || !state_slot || !swa_len || !attn_sink || !out) return SPD_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(unified_kv, 16) || !aligned(out, 16) || !aligned(state_slot, 4) ||
+      !aligned(swa_len, 4) || !aligned(attn_sink, 4) ||
+      (topk > 0 && (!aligned(comp_pos, 4) || !aligned(block_table, 4))))
+    return SPD_ERR_INVALID_ARG;
+  if (num_rows > (int64_t)1 << 40) return SPD_ERR_INVALID_ARG;
+  const size_t qo_bytes = (size_t)N * H * D * 2;
+  if (overlap(out, qo_bytes, q, qo_bytes) ||
+      overlap(out, qo_bytes, unified_kv, (size_t)num_rows * D * 2) ||
+      overlap(out, qo_bytes, attn_sink, (size_t)H * 4))
+    return SPD_ERR_INVALID_ARG;
+
+  // Each token's list is built whole in LDS, so no split-L (max_len 0 asks
+  // the planner for none).
+  spd::AttnPlan plan;
+  if (!spd::make_attn_plan(N, H, D, 0, 0, mode, &plan) || plan.splits != 1)
+    return SPD_ERR_INVALID_ARG;
+
+  spd::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint16_t*>(unified_kv);
+  a.sink = attn_sink;
+  a.out = static_cast<uint16_t*>(out);
+  a.qk_scale = (float)((double)softmax_scale * kLog2eD);
+  a.N = N;
+  a.H = H;
+  a.head_groups = plan.head_groups;
+  a.splits = 1;
+  a.split_rows = plan.split_rows;
+  a.paged = 1;
+  a.state_slot = state_slot;
+  a.swa_len = swa_len;
+  a.comp_pos = topk > 0 ? comp_pos : nullptr;
+  a.block_table = block_table;
+  a.topk = topk;
+  a.max_blocks = max_blocks;
+  a.win = win;
+  a.k_per_block = k_per_block;
+  a.swa_pages = swa_pages;
+  const int64_t lim = (int64_t)max_blocks * k_per_block;
+  a.comp_limit = (uint32_t)(lim < (int64_t(1) << 31) ? lim : (int64_t(1) << 31));
+  const hipError_t e = spd::launch_attention(a, D, plan, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPD_OK : SPD_ERR_HIP;
+}
+
 SPD_API spd_status build_decode_indices(const int32_t* state_slot, const int32_t* swa_len,
                                         const int32_t* comp_pos, int32_t topk,
                                         const int32_t* block_table, int32_t max_blocks, int32_t N,
@@ -144,7 +207,7 @@ SPD_API spd_status build_decode_indices(const int32_t* state_slot, const int32_t
   if (N > 0 && (state_slot == nullptr || swa_len == nullptr || kv_indices == nullptr))
     return SPD_ERR_INVALID_ARG;
 
-  spd::BuildArgs a;
+  spd::BuildArgs a{};
   a.state_slot = state_slot;
   a.swa_len = swa_len;
   a.comp_pos = topk > 0 ? comp_pos : nullptr;

@@ -50,6 +50,7 @@ typedef const __attribute__((address_space(4))) int32_t* ScalarI32Ptr;
 typedef __attribute__((address_space(3))) bf16x4 LdsBf16x4;
 
 constexpr int kIdxCap = 2048;              // row indices staged in LDS at a time
+static_assert(kPagedMaxLen <= kIdxCap, "a paged list is built in LDS at once");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRaise = 64.0f;            // log2 headroom of the fixed reference max
 
@@ -194,6 +195,73 @@ __device__ __forceinline__ void stage_indices(const int32_t* part, int base, int
     const int p = g0 + lane < n ? g0 + lane : n - 1;
     dma_4B(part + base + p, __builtin_amdgcn_readfirstlane(lds_addr(sidx + g0)));
   }
+}
+
+// The page transform of token t, in the index builder's order: the window
+// slots state_slot*win + r for r < clamp(swa_len, 0, win), then each valid
+// entry p of the token's comp_pos row (0 <= p < max_blocks*K), in row order,
+// as swa_pages + block_table[t][p / K]*K + p mod K (sglang PR #28392 summary
+// page, "key source snippet").  All NT threads of the workgroup call it; it
+// writes the list into sidx[0, L), returns L and ends with a barrier.  Each
+// group of 8*NT comp_pos entries costs two memory round trips (the entries,
+// then their block-table lookups); the valid ones are compacted with per-wave
+// ballots and a prefix over the per-wave counts in scount[8 * NT / 64].
+template <int NT>
+__device__ int stage_paged_list(const AttnArgs& a, int t, int* sidx, int* scount) {
+  constexpr int kW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t s0 = (int64_t)((ScalarI32Ptr)a.state_slot)[t] * a.win;
+  int sl = ((ScalarI32Ptr)a.swa_len)[t];
+  sl = sl < 0 ? 0 : (sl > a.win ? a.win : sl);
+  const int ntop = a.comp_pos != nullptr ? a.topk : 0;
+  const int32_t* row = a.comp_pos + (int64_t)t * a.topk;
+  const int32_t* bt = a.block_table + (int64_t)t * a.max_blocks;
+  for (int r = tid; r < sl; r += NT) sidx[r] = (int32_t)(s0 + r);
+  int total = sl;
+  for (int c0 = 0; c0 < ntop; c0 += 8 * NT) {
+    int p[8], blk[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = c0 + u * NT + tid;
+      const int x = row[c < ntop ? c : ntop - 1];
+      p[u] = c < ntop ? x : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool ok = (unsigned)p[u] < a.comp_limit;  // a negative p compares as >= 2^31
+      const int x = bt[ok ? p[u] / a.k_per_block : 0];
+      blk[u] = ok ? x : 0;
+    }
+    unsigned long long mask[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      mask[u] = __ballot((unsigned)p[u] < a.comp_limit);
+      if (lane == 0) scount[u * kW + wave] = __popcll(mask[u]);
+    }
+    barrier_lds();
+    int run = total;  // valid entries before group slot (u, wave), in (u, wave) order
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      int before = run;
+#pragma unroll
+      for (int w = 0; w < kW; ++w) {
+        const int v = scount[u * kW + w];
+        before += w < wave ? v : 0;
+        run += v;
+      }
+      if ((unsigned)p[u] < a.comp_limit) {
+        const int below = __builtin_amdgcn_mbcnt_hi((unsigned)(mask[u] >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((unsigned)mask[u], 0));
+        sidx[before + below] = (int32_t)((int64_t)a.swa_pages + (int64_t)blk[u] * a.k_per_block +
+                                         p[u] % a.k_per_block);
+      }
+    }
+    total = run;
+    barrier_lds();  // scount is reused by the next group
+  }
+  barrier_lds();
+  return total;
 }
 
 // Stage attn_sink[h0 .. h0 + nh) into ssink[0, nh) (nh <= 64) with one LDS-DMA
@@ -354,7 +422,7 @@ __device__ __forceinline__ bool workgroup_any(bool flag, int* sflag, int wave, i
 
 // ---------------------------------------------------------------------------
 // heads mode: workgroup = (token, 16*W heads, partition); 32-row shared tiles.
-template <int D, int W>
+template <int D, int W, bool kPaged>
 __global__ void __launch_bounds__(64 * W) attn_heads_kernel(AttnArgs a) {
   constexpr int kTile = 32;
   constexpr int kRowBytes = 2 * D;
@@ -376,6 +444,7 @@ __global__ void __launch_bounds__(64 * W) attn_heads_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(256))) int sidx[kIdxCap];
   __shared__ __attribute__((aligned(256))) float ssink[64];
   __shared__ int sflag[W];
+  __shared__ int scount[8 * W];  // page transform: valid entries per (group slot, wave)
 
   const int item = xcd_item(blockIdx.x, gridDim.x);
   const int c = item % a.splits;
@@ -388,9 +457,16 @@ __global__ void __launch_bounds__(64 * W) attn_heads_kernel(AttnArgs a) {
   const int n16 = lane & 15;
   const int g = lane >> 4;
 
-  const ScalarI32Ptr indptr = (ScalarI32Ptr)a.kv_indptr;
-  const int row0 = indptr[t];
-  const int L = indptr[t + 1] - row0;
+  int L;
+  const int32_t* part = nullptr;
+  if constexpr (kPaged) {  // no split: c == 0
+    L = stage_paged_list<64 * W>(a, t, sidx, scount);
+  } else {
+    const ScalarI32Ptr indptr = (ScalarI32Ptr)a.kv_indptr;
+    const int row0 = indptr[t];
+    L = indptr[t + 1] - row0;
+    part = a.kv_indices + row0;
+  }
   const int nparts = partitions_of(L, a.splits, a.split_rows);
   if (c >= nparts) return;  // nothing for this partition
 
@@ -405,7 +481,7 @@ __global__ void __launch_bounds__(64 * W) attn_heads_kernel(AttnArgs a) {
 
   const int cb = c * a.split_rows;
   const int nrows = (c == nparts - 1) ? L - cb : a.split_rows;
-  const int32_t* part = a.kv_indices + row0 + cb;
+  if constexpr (!kPaged) part += cb;
 
   bf16x8 qreg[kKSteps];
   load_q<D>(a.q, (int64_t)t * a.H + (hvalid ? h : 0), g, qreg);
@@ -425,7 +501,7 @@ __global__ void __launch_bounds__(64 * W) attn_heads_kernel(AttnArgs a) {
   for (int sc = 0; sc < nrows; sc += kIdxCap) {
     const int n = nrows - sc < kIdxCap ? nrows - sc : kIdxCap;
     if (sc > 0 || pass > 0) barrier_lds();  // every wave is done with the stages and indices
-    stage_indices(part, sc, n, sidx, wave, W, lane);
+    if constexpr (!kPaged) stage_indices(part, sc, n, sidx, wave, W, lane);  // paged: built once
     wait_vmcnt<0>();
     barrier_lds();
     if (pass == 0 && sc == 0)  // the sink belongs to partition 0's state
@@ -604,7 +680,7 @@ __global__ void __launch_bounds__(64 * W) attn_combine_kernel(AttnArgs a) {
 // rows mode: workgroup = (token, 16 heads); 4 waves split the slice into
 // 16-row tiles (wave w takes tiles w, w+4, ...) staged in private LDS, then
 // merge their softmax states in LDS.
-template <int D>
+template <int D, bool kPaged>
 __global__ void __launch_bounds__(256) attn_rows_kernel(AttnArgs a) {
   constexpr int kWaves = 4;
   constexpr int kTile = 16;
@@ -623,6 +699,7 @@ __global__ void __launch_bounds__(256) attn_rows_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(256))) float ssink[64];
   __shared__ float sml[kWaves][2][16];
   __shared__ int sflag[kWaves];
+  __shared__ int scount[8 * kWaves];  // page transform: valid entries per (group slot, wave)
 
   const int item = xcd_item(blockIdx.x, gridDim.x);
   const int hg = item % a.head_groups;
@@ -633,9 +710,16 @@ __global__ void __launch_bounds__(256) attn_rows_kernel(AttnArgs a) {
   const int n16 = lane & 15;
   const int g = lane >> 4;
 
-  const ScalarI32Ptr indptr = (ScalarI32Ptr)a.kv_indptr;
-  const int row0 = indptr[t];
-  const int L = indptr[t + 1] - row0;
+  int L;
+  const int32_t* part = nullptr;
+  if constexpr (kPaged) {
+    L = stage_paged_list<64 * kWaves>(a, t, sidx, scount);
+  } else {
+    const ScalarI32Ptr indptr = (ScalarI32Ptr)a.kv_indptr;
+    const int row0 = indptr[t];
+    L = indptr[t + 1] - row0;
+    part = a.kv_indices + row0;
+  }
   const int h0 = hg * 16;
   const int h = h0 + n16;
   const bool hvalid = h < a.H;
@@ -645,7 +729,6 @@ __global__ void __launch_bounds__(256) attn_rows_kernel(AttnArgs a) {
     zero_heads<D>(a.out, a.H, t, h0, nh, threadIdx.x, 64 * kWaves);
     return;
   }
-  const int32_t* part = a.kv_indices + row0;
 
   bf16x8 qreg[kKSteps];
   load_q<D>(a.q, (int64_t)t * a.H + (hvalid ? h : 0), g, qreg);
@@ -666,13 +749,13 @@ __global__ void __launch_bounds__(256) attn_rows_kernel(AttnArgs a) {
     for (int sc = 0; sc < L; sc += kIdxCap) {
       const int n = L - sc < kIdxCap ? L - sc : kIdxCap;
       const bool restage = sc > 0 || (pass == 1 && L > kIdxCap);
-      if (restage) {
+      if (restage) {  // (never with the page transform: its lists fit kIdxCap)
         barrier_lds();  // every wave is done with the indices and its stages
-        stage_indices(part, sc, n, sidx, wave, kWaves, lane);
+        if constexpr (!kPaged) stage_indices(part, sc, n, sidx, wave, kWaves, lane);
         wait_vmcnt<0>();
         barrier_lds();
       } else if (pass == 0) {
-        stage_indices(part, sc, n, sidx, wave, kWaves, lane);
+        if constexpr (!kPaged) stage_indices(part, sc, n, sidx, wave, kWaves, lane);
         wait_vmcnt<0>();
         barrier_lds();
         sink_l2 = (wave == 0 && hvalid) ? ssink[n16] * kLog2e : -INFINITY;  // sink in wave 0
@@ -821,7 +904,12 @@ __global__ void __launch_bounds__(256) attn_rows_kernel(AttnArgs a) {
 template <int D, int W>
 hipError_t launch_heads(const AttnArgs& a, hipStream_t stream) {
   const long long items = (long long)a.N * a.head_groups * a.splits;
-  hipLaunchKernelGGL((attn_heads_kernel<D, W>), dim3((unsigned)items), dim3(64 * W), 0, stream, a);
+  if (a.paged)
+    hipLaunchKernelGGL((attn_heads_kernel<D, W, true>), dim3((unsigned)items), dim3(64 * W), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((attn_heads_kernel<D, W, false>), dim3((unsigned)items), dim3(64 * W), 0,
+                       stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   hipLaunchKernelGGL((attn_combine_kernel<D, W>), dim3((unsigned)(a.N * a.head_groups * 4)),
@@ -832,8 +920,12 @@ hipError_t launch_heads(const AttnArgs& a, hipStream_t stream) {
 template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream) {
   if (plan.mode == kModeRows) {
-    hipLaunchKernelGGL((attn_rows_kernel<D>), dim3((unsigned)(a.N * a.head_groups)), dim3(256), 0,
-                       stream, a);
+    if (a.paged)
+      hipLaunchKernelGGL((attn_rows_kernel<D, true>), dim3((unsigned)(a.N * a.head_groups)),
+                         dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_rows_kernel<D, false>), dim3((unsigned)(a.N * a.head_groups)),
+                         dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   switch (plan.waves) {

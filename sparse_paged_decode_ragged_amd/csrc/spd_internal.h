@@ -40,7 +40,21 @@ struct AttnArgs {
   float* ws;                 // split partials (splits > 1)
   float qk_scale;            // softmax_scale * log2(e)
   int32_t N, H, head_groups, splits, split_rows;
+  // Page transform (sparse_decode_attn_paged): when paged != 0 each token's
+  // rows are derived from these, as build_decode_indices derives them, and
+  // kv_indices / kv_indptr are not read.  win + topk <= kPagedMaxLen, no split.
+  int32_t paged;
+  const int32_t* state_slot;   // [N]
+  const int32_t* swa_len;      // [N]
+  const int32_t* comp_pos;     // [N][topk] or null
+  const int32_t* block_table;  // [N][max_blocks]
+  int32_t topk, max_blocks, win, k_per_block, swa_pages;
+  uint32_t comp_limit;         // min(max_blocks * k_per_block, 2^31)
 };
+
+// Longest per-token list the paged entry point accepts (win + topk): the
+// whole list is built in LDS before the first row is loaded.
+constexpr int kPagedMaxLen = 2048;
 
 hipError_t launch_attention(const AttnArgs& args, int D, const AttnPlan& plan, hipStream_t stream);
 

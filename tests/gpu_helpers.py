@@ -86,3 +86,22 @@ def assert_close(gpu: np.ndarray, ref: np.ndarray, what: str = ""):
                              % (what, int(bad.sum()), bad.size, i, gpu[i], ref[i]))
     log("  %s: max|err| %.3g, max err/bound %.3f" % (what, err.max() if err.size else 0.0,
                                                      (err / bound).max() if err.size else 0.0))
+
+
+def random_builder_inputs(seed, N, win, topk, k, max_blocks, n_blocks) -> W.BuilderInputs:
+    """Builder inputs with every kind of token: random window lengths (some 0,
+    some full), sentinel entries, all-sentinel rows and padded tokens; valid
+    comp_pos entries lie in [0, max_blocks * k), block ids in [0, n_blocks)."""
+    rng = np.random.default_rng(seed)
+    state_slot = rng.permutation(N + 5)[:N].astype(np.int32)
+    swa_len = rng.integers(0, win + 1, size=N).astype(np.int32)
+    swa_len[rng.random(N) < 0.15] = 0
+    swa_len[rng.random(N) < 0.15] = win
+    comp_pos = rng.integers(0, max_blocks * k, size=(N, topk)).astype(np.int32)
+    comp_pos[rng.random((N, topk)) < 0.3] = -1
+    comp_pos[rng.random(N) < 0.1] = -1                  # all-sentinel rows
+    block_table = rng.integers(0, n_blocks, size=(N, max_blocks)).astype(np.int32)
+    pad = rng.random(N) < 0.1                          # padded tokens: nothing at all
+    swa_len[pad] = 0
+    comp_pos[pad] = -1
+    return W.BuilderInputs(state_slot, swa_len, comp_pos, block_table, win, k, (N + 5) * win)

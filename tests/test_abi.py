@@ -29,6 +29,8 @@ def lib():
     L.sparse_decode_attn_can_use.argtypes = [i32, i32]
     L.build_decode_indices.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i32, P, P, i64, P]
     L.spd_validate_indices.argtypes = [P, i64, P, i32, i64, ctypes.POINTER(ctypes.c_int64), P]
+    L.sparse_decode_attn_paged.argtypes = [P, P, i64, P, P, P, i32, P, i32, i32, i32, i32, P,
+                                           ctypes.c_float, P, i32, i32, i32, i32, P]
     L.spd_status_string.argtypes = [ctypes.c_int]
     L.spd_status_string.restype = ctypes.c_char_p
     return L
@@ -144,3 +146,37 @@ def test_validate_rejects_bad_arguments(lib):
     assert lib.spd_validate_indices(FAKE, 10, None, 2, 100, ctypes.byref(first), None) == INVALID
     assert lib.spd_validate_indices(None, 10, FAKE, 2, 100, ctypes.byref(first), None) == INVALID
     assert lib.spd_validate_indices(FAKE, 10, FAKE, -1, 100, ctypes.byref(first), None) == INVALID
+
+
+def _paged(lib, q=FAKE, kv=FAKE, rows=100, ss=FAKE, sl=FAKE, cp=FAKE, topk=4, bt=FAKE, mb=2, win=8,
+           k=2, swa=24, sink=FAKE, scale=0.1, out=FAKE * 4096, N=2, H=8, D=64, mode=0):
+    return lib.sparse_decode_attn_paged(q, kv, rows, ss, sl, cp, topk, bt, mb, win, k, swa, sink,
+                                        scale, out, N, H, D, mode, None)
+
+
+def test_paged_attn_rejects_bad_arguments(lib):
+    # the builder's argument rules
+    assert _paged(lib, win=0) == INVALID
+    assert _paged(lib, k=0) == INVALID
+    assert _paged(lib, swa=-1) == INVALID
+    assert _paged(lib, topk=-1) == INVALID
+    assert _paged(lib, cp=None) == INVALID          # topk > 0 without comp_pos
+    assert _paged(lib, bt=None) == INVALID
+    assert _paged(lib, mb=0) == INVALID
+    assert _paged(lib, ss=None) == INVALID
+    assert _paged(lib, sl=None) == INVALID
+    # the attention call's rules
+    assert _paged(lib, q=None) == INVALID
+    assert _paged(lib, kv=None) == INVALID
+    assert _paged(lib, sink=None) == INVALID
+    assert _paged(lib, out=None) == INVALID
+    assert _paged(lib, rows=0) == INVALID
+    assert _paged(lib, q=FAKE + 2) == INVALID       # q not 16-byte aligned
+    assert _paged(lib, out=FAKE) == INVALID         # out overlaps q
+    assert _paged(lib, scale=float("inf")) == INVALID
+    assert _paged(lib, mode=5) == INVALID
+    assert _paged(lib, D=100) == UNSUPPORTED
+    # a token's list is built whole in LDS: win + topk <= 2048
+    assert _paged(lib, win=1024, topk=1025) == UNSUPPORTED
+    assert _paged(lib, N=0) == OK                   # empty batch: nothing to do
+    assert _paged(lib, N=0, topk=0, cp=None, bt=None, mb=0) == OK

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_helpers import device_builder_inputs, log
+from gpu_helpers import device_builder_inputs, log, random_builder_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -16,22 +16,6 @@ pytestmark = pytest.mark.gpu
 def spd():
     import sparse_paged_decode_ragged_amd as m
     return m
-
-
-def _random_inputs(seed, N, win, topk, k, max_blocks, n_blocks):
-    rng = np.random.default_rng(seed)
-    state_slot = rng.permutation(N + 5)[:N].astype(np.int32)
-    swa_len = rng.integers(0, win + 1, size=N).astype(np.int32)
-    swa_len[rng.random(N) < 0.15] = 0
-    swa_len[rng.random(N) < 0.15] = win
-    comp_pos = rng.integers(0, max_blocks * k, size=(N, topk)).astype(np.int32)
-    comp_pos[rng.random((N, topk)) < 0.3] = -1
-    comp_pos[rng.random(N) < 0.1] = -1                  # all-sentinel rows
-    block_table = rng.integers(0, n_blocks, size=(N, max_blocks)).astype(np.int32)
-    pad = rng.random(N) < 0.1                          # padded tokens: nothing at all
-    swa_len[pad] = 0
-    comp_pos[pad] = -1
-    return W.BuilderInputs(state_slot, swa_len, comp_pos, block_table, win, k, (N + 5) * win)
 
 
 def check(spd, b: W.BuilderInputs, what: str):
@@ -56,7 +40,7 @@ def check(spd, b: W.BuilderInputs, what: str):
     (6, 200, 64, 512, 8, 64, 100),    # N * topk above the one-launch limit, N <= 1024
 ])
 def test_random_bit_exact(spd, seed, N, win, topk, k, mb, nb):
-    check(spd, _random_inputs(seed, N, win, topk, k, mb, nb), "random N=%d" % N)
+    check(spd, random_builder_inputs(seed, N, win, topk, k, mb, nb), "random N=%d" % N)
 
 
 def test_window_only(spd):
@@ -98,7 +82,7 @@ def test_defensive_rules_and_unaligned_rows(spd):
     path must not be taken."""
     rng = np.random.default_rng(77)
     N, win, topk, k, mb, nb = 40, 16, 64, 4, 6, 30
-    b = _random_inputs(78, N, win, topk, k, mb, nb)
+    b = random_builder_inputs(78, N, win, topk, k, mb, nb)
     cp = b.comp_pos.copy()
     cp[rng.random(cp.shape) < 0.1] = mb * k + rng.integers(0, 50)      # beyond the table
     cp[rng.random(cp.shape) < 0.05] = -7
