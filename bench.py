@@ -133,8 +133,9 @@ def algorithmic_bytes(indptr: np.ndarray, N: int, H: int, D: int) -> dict:
     sum_l = int(L.sum())
     nonempty = int((L > 0).sum())
     kv = sum_l * D * 2
-    total = kv + nonempty * H * D * 2 + N * H * D * 2 + 4 * sum_l + 4 * (N + 1) + 4 * H
-    return {"sum_L": sum_l, "kv_bytes": kv, "B_alg": total, "nonempty": nonempty}
+    qo = nonempty * H * D * 2 + N * H * D * 2
+    total = kv + qo + 4 * sum_l + 4 * (N + 1) + 4 * H
+    return {"sum_L": sum_l, "kv_bytes": kv, "qo_bytes": qo, "B_alg": total, "nonempty": nonempty}
 
 
 def cpu_baseline(w, indptr, indices, seconds):
@@ -239,17 +240,27 @@ def main():
             build(s)
         attn(s)
 
+    # The same step with the page transform fused into the attention kernel
+    # (builder-shaped workloads whose lists fit the paged call).
+    has_paged = b is not None and b.win + b.topk <= 2048
+
+    def paged(s):
+        spd.sparse_decode_attn_paged(s["q"], s["kv"], s["ss"], s["sl"], s["cp"], s["bt"], b.win,
+                                     b.k_per_block, b.swa_pages, s["sink"], w.softmax_scale,
+                                     out=s["out"], mode=mode)
+
     for s in sets:  # eager warm-up (and the indices the graphs will rebuild)
         step(s)
     torch.cuda.synchronize()
     # One graph per set for each of (step, attention call), plus one graph that
     # holds every set's call back to back: the timed loops replay the latter,
     # so consecutive calls are not separated by per-graph launch gaps.
-    single = {"step": [], "attn": []}
+    single = {"step": [], "attn": [], "paged": []}
     chain = {}
     cs = torch.cuda.Stream()
     if not args.eager:
-        for name, fn in (("step", step), ("attn", attn)):
+        kinds = (("step", step), ("attn", attn)) + ((("paged", paged),) if has_paged else ())
+        for name, fn in kinds:
             for s in sets:
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=cs):
@@ -300,6 +311,11 @@ def main():
     n_attn = max(args.steps, 100)
     us_attn = timed(n_attn, "attn", attn) * 1e3 / n_attn
 
+    us_paged = None
+    if has_paged:
+        run_calls(min(args.warmup, 64), "paged", paged)
+        us_paged = timed(n_attn, "paged", paged) * 1e3 / n_attn
+
     indptr = sets[0]["ptr"].cpu().numpy()
     indices = sets[0]["idx"].cpu().numpy()[: indptr[-1]]
     ab = algorithmic_bytes(indptr, N, H, D)
@@ -339,6 +355,23 @@ def main():
                      "kernel": kernel, "us_per_call": round(us_attn, 3),
                      "bytes_per_call": ab["B_alg"]},
     }
+    if us_paged is not None:
+        pp = spd.sparse_decode_attn_plan_info(N, H, D, 0, 0, mode)  # the paged call never splits
+        kernel_paged = ("attn_rows_kernel<%d, paged>" % D if pp["mode"] == "rows" else
+                        "attn_heads_kernel<%d,%d, paged>" % (D, pp["heads_per_group"] // 16))
+        # what the fused kernel must move: the rows, q, out, the sinks and the
+        # builder inputs it reads (state_slot, swa_len, comp_pos, one block-table
+        # entry per valid compressed entry) instead of kv_indptr / kv_indices
+        n_win = int(np.clip(b.swa_len, 0, b.win).sum())
+        b_paged = (ab["kv_bytes"] + ab["qo_bytes"] + 4 * H + 8 * N + 4 * N * b.topk +
+                   4 * (ab["sum_L"] - n_win))
+        ach_p = b_paged / (us_paged * 1e-6) / 1e9
+        rec["fused_page_transform"] = {
+            "step": "sparse_decode_attn_paged", "ms_per_step": round(us_paged * 1e-3, 6),
+            "tokens_per_s": round(N / (us_paged * 1e-6), 1),
+            "kernel": kernel_paged,
+            "us_per_call": round(us_paged, 3), "bytes_per_call": int(b_paged),
+            "achieved_GBps": round(ach_p, 1), "frac": round(ach_p / HBM_PEAK_GBPS, 4)}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, indptr, indices, args.cpu_seconds)
     print(json.dumps(rec))
