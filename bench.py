@@ -324,6 +324,8 @@ def main():
     achieved = ab["B_alg"] / (us_attn * 1e-6) / 1e9
     if plan["mode"] == "rows":
         kernel = "attn_rows_kernel<%d>" % D
+    elif plan.get("wide"):
+        kernel = "attn_wide_kernel<%d,%d>" % (D, plan["heads_per_group"] // 32)
     else:
         kernel = "attn_heads_kernel<%d,%d>" % (D, plan["heads_per_group"] // 16)
         if plan["splits"] > 1:
@@ -358,6 +360,8 @@ def main():
     if us_paged is not None:
         pp = spd.sparse_decode_attn_plan_info(N, H, D, 0, 0, mode)  # the paged call never splits
         kernel_paged = ("attn_rows_kernel<%d, paged>" % D if pp["mode"] == "rows" else
+                        "attn_wide_kernel<%d,%d, paged>" % (D, pp["heads_per_group"] // 32)
+                        if pp.get("wide") else
                         "attn_heads_kernel<%d,%d, paged>" % (D, pp["heads_per_group"] // 16))
         # what the fused kernel must move: the rows, q, out, the sinks and the
         # builder inputs it reads (state_slot, swa_len, comp_pos, one block-table

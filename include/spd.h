@@ -98,15 +98,26 @@ SPD_API spd_status sparse_decode_attn(const void* q, const void* unified_kv, int
  * Work decompositions of sparse_decode_attn_ex.  Both give the same result
  * within the accumulation tolerance; they differ in how the work of one token
  * is spread over workgroups:
- *   SPD_MODE_HEADS: a workgroup takes (token, up to 64 heads, partition); its
- *                   waves split the heads and share every gathered row.
+ *   SPD_MODE_HEADS: a workgroup takes (token, up to 128 heads, partition);
+ *                   its waves split the heads and share every gathered row.
+ *                   Waves take 16 heads, or 32 (64 or 128 heads per
+ *                   workgroup) when H % 64 == 0, nothing is split and the
+ *                   batch gives enough workgroups to fill the chip.
  *   SPD_MODE_ROWS:  a workgroup takes (token, 16 heads); its 4 waves split
  *                   the rows and merge in LDS -- more workgroups for small
  *                   batches without partial results in memory.  No split-L.
+ *   SPD_MODE_WIDE:  SPD_MODE_HEADS on 32-head waves whatever the batch size:
+ *                   needs H % 64 == 0 and no split-L (SPD_ERR_UNSUPPORTED
+ *                   otherwise).
  *   SPD_MODE_AUTO:  ROWS when the batch gives fewer than 256 HEADS-mode
  *                   workgroups and split_rows == 0, else HEADS.
  */
-typedef enum spd_mode { SPD_MODE_AUTO = 0, SPD_MODE_HEADS = 1, SPD_MODE_ROWS = 2 } spd_mode;
+typedef enum spd_mode {
+  SPD_MODE_AUTO = 0,
+  SPD_MODE_HEADS = 1,
+  SPD_MODE_ROWS = 2,
+  SPD_MODE_WIDE = 3
+} spd_mode;
 
 /*
  * Workspace bytes that sparse_decode_attn_ex needs for (N, H, D, max_len,
@@ -121,8 +132,10 @@ SPD_API size_t sparse_decode_attn_workspace_size(int32_t N, int32_t H, int32_t D
  * that size buffers or report what runs: info[0] = mode actually used
  * (SPD_MODE_HEADS or SPD_MODE_ROWS), info[1] = heads per workgroup, info[2] =
  * head groups, info[3] = split-L partitions (1 = none), info[4] = rows per
- * partition.  info is a host array of 5 int32.  Returns SPD_ERR_INVALID_ARG or
- * SPD_ERR_UNSUPPORTED exactly when sparse_decode_attn_ex would.
+ * partition, info[5] = 1 when the heads mode runs on 32-head waves (64 or 128
+ * heads per workgroup) else 0.  info is a host array of 6 int32.  Returns
+ * SPD_ERR_INVALID_ARG or SPD_ERR_UNSUPPORTED exactly when
+ * sparse_decode_attn_ex would.
  */
 SPD_API spd_status sparse_decode_attn_plan_info(int32_t N, int32_t H, int32_t D, int32_t max_len,
                                                 int32_t split_rows, int32_t mode, int32_t* info);

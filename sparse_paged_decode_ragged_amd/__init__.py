@@ -112,7 +112,7 @@ def sparse_decode_attn_can_use(H: int, D: int) -> bool:
     return bool(lib.sparse_decode_attn_can_use(int(H), int(D)))
 
 
-MODE_AUTO, MODE_HEADS, MODE_ROWS = 0, 1, 2
+MODE_AUTO, MODE_HEADS, MODE_ROWS, MODE_WIDE = 0, 1, 2, 3
 
 
 def sparse_decode_attn_workspace_size(N: int, H: int, D: int, max_len: int = 0,
@@ -123,13 +123,13 @@ def sparse_decode_attn_workspace_size(N: int, H: int, D: int, max_len: int = 0,
 
 def sparse_decode_attn_plan_info(N: int, H: int, D: int, max_len: int = 0, split_rows: int = 0,
                                  mode: int = MODE_AUTO) -> dict:
-    info = (ctypes.c_int32 * 5)()
+    info = (ctypes.c_int32 * 6)()
     st = lib.sparse_decode_attn_plan_info(int(N), int(H), int(D), int(max_len), int(split_rows),
                                           int(mode), info)
     _raise_on(st, "sparse_decode_attn_plan_info")
     return {"mode": {1: "heads", 2: "rows"}[info[0]], "heads_per_group": info[1],
             "head_groups": info[2], "splits": info[3],
-            "split_rows": info[4] if info[3] > 1 else None}
+            "split_rows": info[4] if info[3] > 1 else None, "wide": bool(info[5])}
 
 
 def sparse_decode_attn(q: torch.Tensor, unified_kv: torch.Tensor, kv_indices: torch.Tensor,

@@ -51,10 +51,12 @@ SPD_API size_t sparse_decode_attn_workspace_size(int32_t N, int32_t H, int32_t D
 SPD_API spd_status sparse_decode_attn_plan_info(int32_t N, int32_t H, int32_t D, int32_t max_len,
                                                 int32_t split_rows, int32_t mode, int32_t* info) {
   if (!info || N < 0 || H <= 0 || D <= 0 || max_len < 0 || split_rows < 0) return SPD_ERR_INVALID_ARG;
-  if (mode != SPD_MODE_AUTO && mode != SPD_MODE_HEADS && mode != SPD_MODE_ROWS)
+  if (mode != SPD_MODE_AUTO && mode != SPD_MODE_HEADS && mode != SPD_MODE_ROWS &&
+      mode != SPD_MODE_WIDE)
     return SPD_ERR_INVALID_ARG;
   if (!spd::attn_supported(H, D)) return SPD_ERR_UNSUPPORTED;
   if (mode == SPD_MODE_ROWS && split_rows != 0) return SPD_ERR_UNSUPPORTED;
+  if (mode == SPD_MODE_WIDE && (split_rows != 0 || H % 64 != 0)) return SPD_ERR_UNSUPPORTED;
   spd::AttnPlan plan;
   if (!spd::make_attn_plan(N, H, D, max_len, split_rows, mode, &plan)) return SPD_ERR_INVALID_ARG;
   info[0] = plan.mode;
@@ -62,6 +64,7 @@ SPD_API spd_status sparse_decode_attn_plan_info(int32_t N, int32_t H, int32_t D,
   info[2] = plan.head_groups;
   info[3] = plan.splits;
   info[4] = plan.split_rows;
+  info[5] = plan.wide;
   return SPD_OK;
 }
 
@@ -73,11 +76,13 @@ SPD_API spd_status sparse_decode_attn_ex(const void* q, const void* unified_kv, 
                                          size_t workspace_bytes, void* stream) {
   if (N < 0 || H <= 0 || D <= 0 || num_rows <= 0 || max_len < 0 || split_rows < 0)
     return SPD_ERR_INVALID_ARG;
-  if (mode != SPD_MODE_AUTO && mode != SPD_MODE_HEADS && mode != SPD_MODE_ROWS)
+  if (mode != SPD_MODE_AUTO && mode != SPD_MODE_HEADS && mode != SPD_MODE_ROWS &&
+      mode != SPD_MODE_WIDE)
     return SPD_ERR_INVALID_ARG;
   if (mode == SPD_MODE_ROWS && split_rows != 0) return SPD_ERR_UNSUPPORTED;
   if (!isfinite(softmax_scale)) return SPD_ERR_INVALID_ARG;
   if (!spd::attn_supported(H, D)) return SPD_ERR_UNSUPPORTED;
+  if (mode == SPD_MODE_WIDE && (split_rows != 0 || H % 64 != 0)) return SPD_ERR_UNSUPPORTED;
   if (N == 0) return SPD_OK;
   if (!q || !unified_kv || !kv_indices || !kv_indptr || !attn_sink || !out)
     return SPD_ERR_INVALID_ARG;
@@ -138,10 +143,12 @@ SPD_API spd_status sparse_decode_attn_paged(
   if (comp_pos == nullptr && topk > 0) return SPD_ERR_INVALID_ARG;
   if (comp_pos != nullptr && topk > 0 && (block_table == nullptr || max_blocks <= 0))
     return SPD_ERR_INVALID_ARG;
-  if (mode != SPD_MODE_AUTO && mode != SPD_MODE_HEADS && mode != SPD_MODE_ROWS)
+  if (mode != SPD_MODE_AUTO && mode != SPD_MODE_HEADS && mode != SPD_MODE_ROWS &&
+      mode != SPD_MODE_WIDE)
     return SPD_ERR_INVALID_ARG;
   if (!isfinite(softmax_scale)) return SPD_ERR_INVALID_ARG;
   if (!spd::attn_supported(H, D)) return SPD_ERR_UNSUPPORTED;
+  if (mode == SPD_MODE_WIDE && H % 64 != 0) return SPD_ERR_UNSUPPORTED;
   if ((int64_t)win + topk > spd::kPagedMaxLen) return SPD_ERR_UNSUPPORTED;
   if (N == 0) return SPD_OK;
   if (!q || !unified_kv || !state_slot || !swa_len || !attn_sink || !out) return SPD_ERR_INVALID_ARG;

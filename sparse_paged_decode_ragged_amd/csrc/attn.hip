@@ -53,6 +53,7 @@ constexpr int kIdxCap = 2048;              // row indices staged in LDS at a tim
 static_assert(kPagedMaxLen <= kIdxCap, "a paged list is built in LDS at once");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRaise = 64.0f;            // log2 headroom of the fixed reference max
+constexpr bool kUseWide = true;            // heads mode on 32-head waves where it applies
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] in bits
 // 3:0, vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt left at their maxima).
@@ -164,6 +165,12 @@ __device__ __forceinline__ void dma_4B(const void* gaddr, uint32_t lds_byte_addr
 
 __device__ __forceinline__ f32x4 mfma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 mfma_k16(bf16x4 a, bf16x4 b, f32x4 c) {
@@ -677,6 +684,268 @@ __global__ void __launch_bounds__(64 * W) attn_combine_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// wide heads mode: workgroup = (token, 32*W heads), W waves of 32 heads each,
+// sharing every 32-row tile staged in LDS (no split-L).  A 32-head wave reads
+// each K and V^T operand from LDS once for two 16-head MFMA blocks, half the
+// LDS bytes per flop of a 16-head wave:
+//  * S^T = K Q^T on 16x16x32 MFMAs: the K operand of rows r0..r0+15 (one b128
+//    read per k-step) meets the Q^T operands of both head blocks;
+//  * O^T += V^T P^T on 32x32x16 MFMAs (M = 32 values of d, N = the 32 heads,
+//    K = 16 rows): lane (n, kg) of the B operand must hold P of rows
+//    8kg..8kg+7 for head n.  The 16x16 score layout gives lane (h, g) rows
+//    4g..4g+3 of head h of each block, so the B operand is the two blocks' P
+//    after one v_permlane16_swap per dword (lanes 16..31 of block 0's value
+//    trade with lanes 0..15 of block 1's, in each half-wave): the K index of
+//    the product is then exactly the row.  The A operand (V^T, lane (d, kg)
+//    holding rows 8kg..8kg+7 of column d) is two transposing reads.
+// The accumulator of a wave is 32 heads x D fp32 (256 AGPRs at D = 512).
+
+// Per-lane byte offsets of the 32x32x16 V^T operand reads within a stage:
+// lane (G = lane / 16, j = lane % 16) reads row 8 (G / 2) + 4 half + j / 4,
+// d = 32 dt + 16 (G % 2) + 4 (j % 4) .. +3, i.e. logical 16-byte chunk
+// 4 dt + b (b = 2 (G % 2) + (j / 2) % 2) at byte 8 (j % 2); stored at chunk
+// (4 dt + b) ^ sw with sw = swizzle(row) < 16, that is
+// 4 ((dt % 4) ^ (sw / 4)) + 16 (dt / 4) ... split as v[half][dt % 4] + 256 (dt / 4).
+template <int D>
+struct WideVtOffsets {
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kChunks = D / 8;
+  int v[2][4];
+  __device__ __forceinline__ explicit WideVtOffsets(int lane) {
+    const int G = lane >> 4, j = lane & 15;
+    const int b = 2 * (G & 1) + ((j >> 1) & 1);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = 8 * (G >> 1) + 4 * half + (j >> 2);
+      const int sw = row_swizzle(row) & (kChunks - 1);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        v[half][u] = row * kRowBytes + 64 * (u ^ (sw >> 2)) + 16 * (b ^ (sw & 3)) + 8 * (j & 1);
+    }
+  }
+  __device__ __forceinline__ int at(int dt, int half) const { return v[half][dt & 3] + 256 * (dt >> 2); }
+};
+
+// B operand of the 32x32x16 PV product from the two head blocks' weights of
+// 16 rows (p0: block 0, p1: block 1, each this lane's 4 rows): see above.
+__device__ __forceinline__ bf16x8 wide_p_operand(bf16x4 p0, bf16x4 p1) {
+  const auto x = __builtin_bit_cast(HIP_vector_base<unsigned, 2>::Native_vec_, p0);
+  const auto y = __builtin_bit_cast(HIP_vector_base<unsigned, 2>::Native_vec_, p1);
+  const auto s0 = __builtin_amdgcn_permlane16_swap(x[0], y[0], false, false);
+  const auto s1 = __builtin_amdgcn_permlane16_swap(x[1], y[1], false, false);
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 r = {(unsigned)s0[0], (unsigned)s1[0], (unsigned)s0[1], (unsigned)s1[1]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+template <int D, int W, bool kPaged>
+__global__ void __launch_bounds__(64 * W) attn_wide_kernel(AttnArgs a) {
+  constexpr int kTile = 32;
+  constexpr int kRowBytes = 2 * D;
+  constexpr int kStageBytes = kTile * kRowBytes;
+  constexpr int kKSteps = D / 32;
+  constexpr int kDT = D / 32;  // 32-wide d-tiles of the PV product
+  constexpr int kRowsPerLoad = 1024 / kRowBytes;
+  constexpr int kLoadsPerTile = kTile / kRowsPerLoad;
+  constexpr int kLoadsPerWave = kLoadsPerTile / W;
+  constexpr int kHeads = 32 * W;
+  static_assert(D % 64 == 0 && D <= 512, "unsupported D");
+  static_assert(kLoadsPerTile % W == 0, "loads must divide among waves");
+  // W = 4: one workgroup per CU, two tiles in flight; W = 2: two workgroups
+  // per CU (LDS <= 80 KiB each), one tile in flight per workgroup
+  constexpr int kAhead = W >= 4 ? 2 : 1;
+  constexpr int kStages = kAhead + 1;
+
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(256))) int sidx[kIdxCap];
+  __shared__ __attribute__((aligned(256))) float ssink[kHeads];
+  __shared__ int sflag[W];
+  __shared__ int scount[8 * W];
+
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const int hg = item % a.head_groups;
+  const int t = item / a.head_groups;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n16 = lane & 15;
+  const int g = lane >> 4;
+
+  int L;
+  const int32_t* part = nullptr;
+  if constexpr (kPaged) {
+    L = stage_paged_list<64 * W>(a, t, sidx, scount);
+  } else {
+    const ScalarI32Ptr indptr = (ScalarI32Ptr)a.kv_indptr;
+    const int row0 = indptr[t];
+    L = indptr[t + 1] - row0;
+    part = a.kv_indices + row0;
+  }
+  const int h0 = hg * kHeads + wave * 32;  // first head of this wave (H % kHeads == 0)
+  if (L <= 0) {
+    zero_heads<D>(a.out, a.H, t, h0, 32, lane, 64);
+    return;
+  }
+
+  bf16x8 q0[kKSteps], q1[kKSteps];  // Q^T operands of head blocks 0 and 1
+  load_q<D>(a.q, (int64_t)t * a.H + h0 + n16, g, q0);
+  load_q<D>(a.q, (int64_t)t * a.H + h0 + 16 + n16, g, q1);
+  if (wave == 0) {  // the workgroup's kHeads sinks (kHeads <= 128), one LDS-DMA per 64
+#pragma unroll
+    for (int c = 0; c < kHeads; c += 64)
+      dma_4B(a.sink + hg * kHeads + c + lane, __builtin_amdgcn_readfirstlane(lds_addr(ssink + c)));
+  }
+
+  const TileOffsets<D> off(n16, g);
+  const WideVtOffsets<D> voff(lane);
+
+  float m0 = -INFINITY, l0 = 0.f, mt0 = -INFINITY, sk0 = -INFINITY;
+  float m1 = -INFINITY, l1 = 0.f, mt1 = -INFINITY, sk1 = -INFINITY;
+  f32x16 acc[kDT];
+  for (int pass = 0; pass < 2; ++pass) {
+    bool first0 = pass == 0, first1 = pass == 0;
+    if (pass == 1) {
+      second_pass_state(sk0, mt0, g, m0, l0);
+      second_pass_state(sk1, mt1, g, m1, l1);
+    }
+#pragma unroll
+    for (int i = 0; i < kDT; ++i) acc[i] = f32x16{};
+    bool over = false;
+
+    for (int sc = 0; sc < L; sc += kIdxCap) {
+      const int n = L - sc < kIdxCap ? L - sc : kIdxCap;
+      if (sc > 0 || pass > 0) barrier_lds();  // every wave is done with the stages and indices
+      if constexpr (!kPaged) stage_indices(part, sc, n, sidx, wave, W, lane);
+      wait_vmcnt<0>();
+      barrier_lds();
+      if (pass == 0 && sc == 0) {
+        sk0 = ssink[wave * 32 + n16] * kLog2e;
+        sk1 = ssink[wave * 32 + 16 + n16] * kLog2e;
+      }
+      const int ntiles = (n + kTile - 1) / kTile;
+
+      auto issue_tile = [&](int tile) {
+        issue_rows<kRowBytes, kLoadsPerWave>(a.kv, sidx, n, tile * kTile + wave * (kTile / W),
+                                             wave * (kTile / W),
+                                             smem + (tile % kStages) * kStageBytes +
+                                                 wave * kLoadsPerWave * 1024,
+                                             lane);
+      };
+#pragma unroll
+      for (int k = 0; k < kAhead; ++k)
+        if (k < ntiles) issue_tile(k);
+
+      for (int i = 0; i < ntiles; ++i) {
+        // tile i has landed once at most min(kAhead - 1, ntiles - 1 - i)
+        // later tiles of this wave are still outstanding
+        if (kAhead == 2 && i + 1 < ntiles)
+          wait_vmcnt<kLoadsPerWave>();
+        else
+          wait_vmcnt<0>();
+        barrier_lds();  // every wave's part of tile i is in LDS; tile i-1's stage is free
+        if (i + kAhead < ntiles) issue_tile(i + kAhead);
+
+        // The stage's offset is opaque to the compiler: it would otherwise keep
+        // every lane offset precomputed for each stage (registers it lacks).
+        int stoff = (i % kStages) * kStageBytes;
+        asm volatile("" : "+v"(stoff));
+        const unsigned char* st = smem + stoff;
+        const int nvalid = n - i * kTile;
+
+        // S^T = K Q^T: rows 0-15 and 16-31 of the tile, head blocks 0 and 1
+        constexpr int kB = kKSteps < 4 ? kKSteps : 4;
+        f32x4 s00 = {0.f, 0.f, 0.f, 0.f}, s01 = s00, s10 = s00, s11 = s00;
+#pragma unroll
+        for (int s0 = 0; s0 < kKSteps; s0 += kB) {
+          bf16x8 ka[kB], kb[kB];
+#pragma unroll
+          for (int u = 0; u < kB; ++u) {
+            const int o = off.kq(s0 + u);
+            ka[u] = *reinterpret_cast<const bf16x8*>(st + o);
+            kb[u] = *reinterpret_cast<const bf16x8*>(st + o + 16 * kRowBytes);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < kB; ++u) {
+            s00 = mfma_k32(ka[u], q0[s0 + u], s00);
+            s01 = mfma_k32(ka[u], q1[s0 + u], s01);
+            s10 = mfma_k32(kb[u], q0[s0 + u], s10);
+            s11 = mfma_k32(kb[u], q1[s0 + u], s11);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+
+        float x0[8], x1[8];
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const bool v0 = 4 * g + i4 < nvalid, v1 = 16 + 4 * g + i4 < nvalid;
+          x0[i4] = v0 ? s00[i4] * a.qk_scale : -INFINITY;
+          x0[4 + i4] = v1 ? s10[i4] * a.qk_scale : -INFINITY;
+          x1[i4] = v0 ? s01[i4] * a.qk_scale : -INFINITY;
+          x1[4 + i4] = v1 ? s11[i4] * a.qk_scale : -INFINITY;
+        }
+        __bf16 p0[8], p1[8];
+        over |= softmax_tile<8>(x0, sk0, g, first0, m0, mt0, l0, p0);
+        over |= softmax_tile<8>(x1, sk1, g, first1, m1, mt1, l1, p1);
+        bf16x8 pb[2];  // B operands for rows 0-15 and 16-31
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          bf16x4 a0, a1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a0[e] = p0[4 * rb + e];
+            a1[e] = p1[4 * rb + e];
+          }
+          pb[rb] = wide_p_operand(a0, a1);
+        }
+
+        // O^T += V^T P^T, V^T operands read in batches of kVB d-tiles
+        constexpr int kVB = kDT < 4 ? kDT : 4;
+#pragma unroll
+        for (int d0 = 0; d0 < kDT; d0 += kVB) {
+          bf16x8 va[kVB], vb[kVB];
+#pragma unroll
+          for (int u = 0; u < kVB; ++u) {
+            const int o0 = voff.at(d0 + u, 0), o1 = voff.at(d0 + u, 1);
+            const bf16x4 a_lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + o0));
+            const bf16x4 a_hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + o1));
+            const bf16x4 b_lo =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + o0 + 16 * kRowBytes));
+            const bf16x4 b_hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + o1 + 16 * kRowBytes));
+            va[u] = __builtin_shufflevector(a_lo, a_hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            vb[u] = __builtin_shufflevector(b_lo, b_hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < kVB; ++u) {
+            acc[d0 + u] = mfma32(va[u], pb[0], acc[d0 + u]);
+            acc[d0 + u] = mfma32(vb[u], pb[1], acc[d0 + u]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    if (!workgroup_any(over, sflag, wave, W)) break;
+  }
+
+  // lane (n, hf) = lane n + 32 hf holds, for head h0 + n, d = 32 dt + 8 e4 +
+  // 4 hf + e as element 4 e4 + e of acc[dt]; its denominator is block n / 16's
+  // l of head n % 16, which every lane with lane % 16 == n % 16 holds.
+  const float lb0 = group_sum4(l0), lb1 = group_sum4(l1);
+  const int n = lane & 31, hf = lane >> 5;
+  const float inv = 1.0f / (n < 16 ? lb0 : lb1);
+  uint16_t* op = a.out + ((int64_t)t * a.H + h0 + n) * D + 4 * hf;
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const f32x4 v = {acc[dt][4 * e4], acc[dt][4 * e4 + 1], acc[dt][4 * e4 + 2], acc[dt][4 * e4 + 3]};
+      store_bf16x4(op + 32 * dt + 8 * e4, v, inv);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // rows mode: workgroup = (token, 16 heads); 4 waves split the slice into
 // 16-row tiles (wave w takes tiles w, w+4, ...) staged in private LDS, then
 // merge their softmax states in LDS.
@@ -917,6 +1186,16 @@ hipError_t launch_heads(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, int W>
+hipError_t launch_wide(const AttnArgs& a, hipStream_t stream) {
+  const unsigned items = (unsigned)((long long)a.N * a.head_groups);
+  if (a.paged)
+    hipLaunchKernelGGL((attn_wide_kernel<D, W, true>), dim3(items), dim3(64 * W), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_wide_kernel<D, W, false>), dim3(items), dim3(64 * W), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream) {
   if (plan.mode == kModeRows) {
@@ -927,6 +1206,12 @@ hipError_t launch_d(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream)
       hipLaunchKernelGGL((attn_rows_kernel<D, false>), dim3((unsigned)(a.N * a.head_groups)),
                          dim3(256), 0, stream, a);
     return hipGetLastError();
+  }
+  if (plan.wide) {
+    if (a.splits != 1) return hipErrorInvalidValue;
+    if (plan.waves == 4) return launch_wide<D, 4>(a, stream);
+    if (plan.waves == 2) return launch_wide<D, 2>(a, stream);
+    return hipErrorInvalidValue;
   }
   switch (plan.waves) {
     case 1: return launch_heads<D, 1>(a, stream);
@@ -945,7 +1230,20 @@ bool attn_supported(int32_t H, int32_t D) {
 bool make_attn_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t split_rows,
                     int32_t mode, AttnPlan* p) {
   if (!attn_supported(H, D) || N < 0 || max_len < 0 || split_rows < 0) return false;
-  if (mode != kModeAuto && mode != kModeHeads && mode != kModeRows) return false;
+  if (mode != kModeAuto && mode != kModeHeads && mode != kModeRows && mode != kModeWide)
+    return false;
+  if (mode == kModeWide) {  // 32-head waves, no split-L
+    if (H % 64 != 0 || split_rows != 0) return false;
+    p->mode = kModeHeads;
+    p->wide = 1;
+    p->waves = H % 128 == 0 ? 4 : 2;
+    p->heads_per_group = 32 * p->waves;
+    p->head_groups = H / p->heads_per_group;
+    p->splits = 1;
+    p->split_rows = 1 << 30;
+    p->workspace_bytes = 0;
+    return (long long)N * p->head_groups <= 0x7fffffffLL;
+  }
   // heads mode: 16 heads per wave, 16*W heads per workgroup
   const int heads_waves = H <= 16 ? 1 : (H <= 32 ? 2 : 4);
   const int heads_per = 16 * heads_waves;
@@ -957,6 +1255,7 @@ bool make_attn_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t sp
   if (mode == kModeRows) {
     if (split_rows != 0) return false;  // the rows mode does not split across workgroups
     p->mode = kModeRows;
+    p->wide = 0;
     p->waves = 4;
     p->heads_per_group = 16;
     p->head_groups = (H + 15) / 16;
@@ -992,6 +1291,21 @@ bool make_attn_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t sp
   if (splits <= 1) {
     splits = 1;
     rows = 1 << 30;
+  }
+  // Without split-L, head counts that are multiples of 64 run on 32-head
+  // waves: 128 heads per workgroup (4 waves, one workgroup per CU) when
+  // H % 128 == 0, else 64 (2 waves: two workgroups share a CU, so the batch
+  // must give at least two per CU to keep every SIMD busy).
+  p->wide = 0;
+  if (kUseWide && splits == 1 && H % 64 == 0) {
+    const int w = H % 128 == 0 ? 4 : 2;
+    const long long items = (long long)N * (H / (32 * w));
+    if (items >= (w == 4 ? target : 2 * target)) {
+      p->wide = 1;
+      p->waves = w;
+      p->heads_per_group = 32 * w;
+      p->head_groups = H / p->heads_per_group;
+    }
   }
   if (splits > 4096) return false;
   if ((long long)N * p->head_groups * splits * 4 > 0x7fffffffLL) return false;

@@ -12,6 +12,7 @@ namespace spd {
 constexpr int kModeAuto = 0;
 constexpr int kModeHeads = 1;  // waves of a workgroup split the heads, share the rows
 constexpr int kModeRows = 2;   // waves of a workgroup split the rows, share 16 heads
+constexpr int kModeWide = 3;   // heads mode on 32-head waves, asked for explicitly
 
 // Work decomposition of one attention call, fixed by scalar arguments only so
 // that the grid never depends on device data.
@@ -20,6 +21,7 @@ struct AttnPlan {
   int waves;           // waves per workgroup
   int heads_per_group; // heads per workgroup
   int head_groups;     // ceil(H / heads_per_group)
+  int wide;            // heads mode with 32-head waves (attn_wide_kernel)
   int splits;          // partitions of a slice (1 = no split-L)
   int split_rows;      // rows per partition (multiple of 32); huge when splits == 1
   size_t workspace_bytes;

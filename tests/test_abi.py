@@ -117,6 +117,11 @@ def test_attn_ex_workspace_checks(lib):
     assert ex(max_len=-1) == INVALID
     assert ex(mode=7) == INVALID
     assert ex(mode=ROWS, split=64) == UNSUPPORTED
+    WIDE = 3
+    assert ex(mode=WIDE, split=64) == UNSUPPORTED    # 32-head waves never split
+    assert lib.sparse_decode_attn_ex(FAKE, FAKE, 100, FAKE, FAKE, FAKE, 0.1, FAKE * 4096, 64, 40,
+                                     512, 640, 0, WIDE, None, 0, None) == UNSUPPORTED  # H % 64
+    assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 0, WIDE) == 0
 
 
 def _build(lib, ss=FAKE, sl=FAKE, cp=FAKE, topk=4, bt=FAKE, mb=2, N=3, win=8, k=2, swa=24,

@@ -32,10 +32,15 @@ def run(spd, w, idx_np, ptr_np, sink=None, **plan):
     return out
 
 
-ROWS, HEADS = 2, 1
+ROWS, HEADS, WIDE = 2, 1, 3
 PLANS = [dict(plain=True), dict(mode=ROWS), dict(mode=HEADS),
          dict(mode=HEADS, max_len=200, split_rows=32), dict(mode=HEADS, max_len=200, split_rows=64),
          dict(max_len=200)]
+
+
+def plans(H):
+    """PLANS, plus the 32-head-wave heads mode where it applies (H % 64 == 0)."""
+    return PLANS + ([dict(mode=WIDE)] if H % 64 == 0 else [])
 
 
 def test_tiny_all_tokens(spd):
@@ -58,7 +63,7 @@ def test_shapes(spd, H, D):
     w = W.random_csr("shapes", seed, len(LENGTHS), H, D, 700, LENGTHS)
     log("case shapes H=%d D=%d" % (H, D))
     ref = oracle_tokens(w, w.kv_indices, w.kv_indptr)
-    for plan in PLANS:
+    for plan in plans(H):
         out = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
         assert_close(bf16_to_f64(out), ref, "H=%d D=%d %s" % (H, D, plan))
 
@@ -68,49 +73,52 @@ def test_many_tiles_and_long_slices(spd):
     w = W.random_csr("long", 7, len(lengths), 64, 512, 5000, lengths)
     log("case long slices")
     ref = oracle_tokens(w, w.kv_indices, w.kv_indptr)
-    for plan in [dict(plain=True), dict(mode=ROWS), dict(mode=HEADS), dict(max_len=2048),
+    for plan in [dict(plain=True), dict(mode=ROWS), dict(mode=HEADS), dict(mode=WIDE), dict(max_len=2048),
                  dict(max_len=2048, split_rows=96),
                  dict(max_len=256, split_rows=128)]:   # slices longer than max_len
         out = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
         assert_close(bf16_to_f64(out), ref, "long %s" % plan)
 
 
+@pytest.mark.parametrize("H", [32, 64])
 @pytest.mark.parametrize("kind", ["none", "dominant", "mixed"])
-def test_sink_variants(spd, kind):
+def test_sink_variants(spd, kind, H):
     lengths = [0, 3, 40, 129]
-    w = W.random_csr("sinks", 11, len(lengths), 32, 128, 300, lengths)
+    w = W.random_csr("sinks", 11, len(lengths), H, 128, 300, lengths)
     if kind == "none":
-        sink = np.full(32, -np.inf, dtype=np.float32)
+        sink = np.full(H, -np.inf, dtype=np.float32)
     elif kind == "dominant":
-        sink = np.full(32, 30.0, dtype=np.float32)
+        sink = np.full(H, 30.0, dtype=np.float32)
     else:
-        sink = np.where(np.arange(32) % 2 == 0, -np.inf, 5.0).astype(np.float32)
-    log("case sink %s" % kind)
+        sink = np.where(np.arange(H) % 2 == 0, -np.inf, 5.0).astype(np.float32)
+    log("case sink %s H=%d" % (kind, H))
     ref = oracle_tokens(w, w.kv_indices, w.kv_indptr, sink=sink)
-    for plan in PLANS:
+    for plan in plans(w.H):
         out = run(spd, w, w.kv_indices, w.kv_indptr, sink=sink, **plan)
         assert_close(bf16_to_f64(out), ref, "sink %s %s" % (kind, plan))
         assert torch.all(out[0].view(torch.int16) == 0)
 
 
-def test_single_row_without_sink_is_bit_exact(spd):
+@pytest.mark.parametrize("H", [16, 64])
+def test_single_row_without_sink_is_bit_exact(spd, H):
     """One index and attn_sink = -inf: the weight is exactly 1, so the output
     equals the bf16 row bit for bit."""
-    w = W.random_csr("single", 12, 5, 16, 512, 50, [1, 1, 1, 1, 1])
-    sink = np.full(16, -np.inf, dtype=np.float32)
-    log("case single row")
-    for plan in [dict(mode=ROWS), dict(mode=HEADS), dict(max_len=32, split_rows=32)]:
+    w = W.random_csr("single", 12, 5, H, 512, 50, [1, 1, 1, 1, 1])
+    sink = np.full(H, -np.inf, dtype=np.float32)
+    log("case single row H=%d" % H)
+    extra = [dict(mode=WIDE)] if H % 64 == 0 else []
+    for plan in [dict(mode=ROWS), dict(mode=HEADS), dict(max_len=32, split_rows=32)] + extra:
         out = run(spd, w, w.kv_indices, w.kv_indptr, sink=sink, **plan)
         kv = W.device_bits(w.kv_bits, torch.device("cuda:0"))
         for t in range(5):
             row = kv[int(w.kv_indices[t])]
-            assert torch.equal(out[t].view(torch.int16), row.view(torch.int16).expand(16, -1))
+            assert torch.equal(out[t].view(torch.int16), row.view(torch.int16).expand(H, -1))
 
 
 def test_all_empty_batch(spd):
     w = W.random_csr("empty", 13, 6, 64, 512, 10, [0] * 6)
     log("case all empty")
-    for plan in PLANS:
+    for plan in plans(w.H):
         out = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
         assert torch.all(out.view(torch.int16) == 0)
 
@@ -125,7 +133,7 @@ def test_permutation_and_duplicates(spd):
         perm[a:b] = rng.permutation(perm[a:b])
     log("case permutation")
     ref = oracle_tokens(w, w.kv_indices, w.kv_indptr)
-    for plan in [dict(mode=ROWS), dict(mode=HEADS)]:
+    for plan in [dict(mode=ROWS), dict(mode=HEADS), dict(mode=WIDE)]:
         o1 = bf16_to_f64(run(spd, w, w.kv_indices, w.kv_indptr, **plan))
         o2 = bf16_to_f64(run(spd, w, perm, w.kv_indptr, **plan))
         assert_close(o1, ref, "original order %s" % plan)
@@ -157,7 +165,7 @@ def ref_closed_form(w, L):
 def test_deterministic(spd):
     w = W.random_csr("det", 16, 8, 64, 512, 3000, [640, 1, 0, 333, 1000, 64, 65, 2000])
     log("case determinism")
-    for plan in [dict(mode=ROWS), dict(mode=HEADS), dict(max_len=2000, mode=HEADS)]:
+    for plan in [dict(mode=ROWS), dict(mode=HEADS), dict(mode=WIDE), dict(max_len=2000, mode=HEADS)]:
         a = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
         b = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
@@ -192,7 +200,7 @@ def test_late_large_scores_take_the_second_pass(spd):
     w.kv_bits = kv
     log("case late large scores")
     ref = oracle_tokens(w, w.kv_indices, w.kv_indptr)
-    for plan in PLANS + [dict(mode=HEADS, max_len=2100, split_rows=256)]:
+    for plan in plans(w.H) + [dict(mode=HEADS, max_len=2100, split_rows=256)]:
         out = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
         assert_close(bf16_to_f64(out), ref, "late large %s" % plan)
 

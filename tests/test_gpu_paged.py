@@ -82,16 +82,18 @@ def check(spd, w: W.Workload, mode: int, what: str, tokens=None):
     assert_close(bf16_to_f64(got), ref, "%s mode=%d" % (what, mode))
 
 
-@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("mode", [1, 2, 3])
 @pytest.mark.parametrize("seed,N,H,D,win,topk,k,mb,nb", [
     (11, 9, 8, 64, 16, 24, 4, 3, 9),
     (12, 20, 64, 512, 128, 512, 1, 512, 3000),
     (13, 33, 16, 128, 32, 100, 8, 13, 50),
     (14, 6, 128, 256, 64, 300, 64, 5, 40),
-    (15, 5, 40, 512, 128, 1920, 16, 120, 200),   # the longest list: win + topk = 2048
+    (15, 5, 64, 512, 128, 1920, 16, 120, 200),   # the longest list: win + topk = 2048
     (16, 12, 24, 64, 8, 70, 2, 40, 90),
 ])
 def test_random_inputs(spd, mode, seed, N, H, D, win, topk, k, mb, nb):
+    if mode == 3 and H % 64:
+        pytest.skip("the 32-head-wave mode needs H % 64 == 0")
     b = random_builder_inputs(seed, N, win, topk, k, mb, nb)
     # a few entries past the block table: the builder drops them, so must the paged call
     b.comp_pos[0, : min(3, topk)] = mb * k + np.arange(min(3, topk), dtype=np.int32)
@@ -122,7 +124,7 @@ def test_compressed_only_and_all_padded(spd, mode):
 
 def test_decode_base_config(spd):
     w = W.decode_base()
-    for mode in (0, 1, 2):
+    for mode in (0, 1, 2, 3):
         check(spd, w, mode, "decode_base")
 
 
