@@ -37,6 +37,8 @@
 //     the sink once.
 #include <math.h>
 
+#include <type_traits>
+
 #include "spd_internal.h"
 
 namespace spd {
@@ -81,6 +83,16 @@ __device__ __forceinline__ void barrier_lds() {
 // this one gives the highest K-read rate at a near-equal transpose rate.
 __device__ __forceinline__ int row_swizzle(int r) { return r & 15; }
 
+// The swizzle of the 32-head-wave (wide) tiles: chunk c of row r is stored at
+// c ^ (4 (r mod 4) + (r / 4) mod 4).  Its transposing reads (four consecutive
+// rows per 16-lane group) then spread over every bank, as do the K reads.
+__device__ __forceinline__ int wide_swizzle(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+template <int kSwz>
+__device__ __forceinline__ int tile_swizzle(int r) {
+  return kSwz == 0 ? row_swizzle(r) : wide_swizzle(r & 15);
+}
+
 // Per-lane byte offsets, within a tile's LDS stage, of the two read patterns,
 // split so that the tile-dependent part is an instruction immediate.
 //  * K read (S^T = K Q^T): lane (n16, g) reads logical 16-byte chunk 4s + g
@@ -91,7 +103,7 @@ __device__ __forceinline__ int row_swizzle(int r) { return r & 15; }
 //    .. +3 of row rtr = 4g + n16/4; with sw = swizzle(rtr) = 2c + e, the chunk
 //    (2 dt + b1) ^ sw (b1 = bit 1 of n16) is 2 (dt ^ c) + (b1 ^ e), i.e. the
 //    read is at voff[dt & 7] + 256 (dt >> 3) bytes.
-template <int D>
+template <int D, int kSwz = 0>
 struct TileOffsets {
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kChunks = D / 8;
@@ -99,8 +111,8 @@ struct TileOffsets {
   int v[8];
   __device__ __forceinline__ TileOffsets(int n16, int g) {
     const int rtr = 4 * g + (n16 >> 2);
-    const int sk = row_swizzle(n16) & (kChunks - 1);
-    const int sv = row_swizzle(rtr) & (kChunks - 1);
+    const int sk = tile_swizzle<kSwz>(n16) & (kChunks - 1);
+    const int sv = tile_swizzle<kSwz>(rtr) & (kChunks - 1);
 #pragma unroll
     for (int u = 0; u < 4; ++u) k[u] = n16 * kRowBytes + 64 * (u ^ (sk >> 2)) + 16 * (g ^ (sk & 3));
 #pragma unroll
@@ -289,9 +301,10 @@ __device__ __forceinline__ void stage_sinks(const float* sink, int H, int h0, fl
 // within its tile (it selects the XOR swizzle).  At D = 512 a load is one row:
 // the wave reads all its indices with one LDS read and broadcasts them with
 // v_readlane, instead of one dependent LDS round trip per load.
-template <int kRowBytes, int kLoads>
+template <int kRowBytes, int kLoads, int kSwz = 0>
 __device__ __forceinline__ void issue_rows(const uint16_t* kv, const int* sidx, int n, int p0,
                                            int rbase, unsigned char* dst, int lane) {
+  auto row_swizzle = [](int r) { return tile_swizzle<kSwz>(r); };
   constexpr int kChunks = kRowBytes / 16;
   constexpr int kRowsPerLoad = 1024 / kRowBytes;
   static_assert(kLoads <= 64, "one lane per row index");
@@ -704,7 +717,7 @@ __global__ void __launch_bounds__(64 * W) attn_combine_kernel(AttnArgs a) {
 // lane (G = lane / 16, j = lane % 16) reads row 8 (G / 2) + 4 half + j / 4,
 // d = 32 dt + 16 (G % 2) + 4 (j % 4) .. +3, i.e. logical 16-byte chunk
 // 4 dt + b (b = 2 (G % 2) + (j / 2) % 2) at byte 8 (j % 2); stored at chunk
-// (4 dt + b) ^ sw with sw = swizzle(row) < 16, that is
+// (4 dt + b) ^ sw with sw = wide_swizzle(row) < 16, that is
 // 4 ((dt % 4) ^ (sw / 4)) + 16 (dt / 4) ... split as v[half][dt % 4] + 256 (dt / 4).
 template <int D>
 struct WideVtOffsets {
@@ -717,7 +730,7 @@ struct WideVtOffsets {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int row = 8 * (G >> 1) + 4 * half + (j >> 2);
-      const int sw = row_swizzle(row) & (kChunks - 1);
+      const int sw = wide_swizzle(row) & (kChunks - 1);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         v[half][u] = row * kRowBytes + 64 * (u ^ (sw >> 2)) + 16 * (b ^ (sw & 3)) + 8 * (j & 1);
@@ -796,7 +809,7 @@ __global__ void __launch_bounds__(64 * W) attn_wide_kernel(AttnArgs a) {
       dma_4B(a.sink + hg * kHeads + c + lane, __builtin_amdgcn_readfirstlane(lds_addr(ssink + c)));
   }
 
-  const TileOffsets<D> off(n16, g);
+  const TileOffsets<D, 1> off(n16, g);
   const WideVtOffsets<D> voff(lane);
 
   float m0 = -INFINITY, l0 = 0.f, mt0 = -INFINITY, sk0 = -INFINITY;
@@ -825,7 +838,7 @@ __global__ void __launch_bounds__(64 * W) attn_wide_kernel(AttnArgs a) {
       const int ntiles = (n + kTile - 1) / kTile;
 
       auto issue_tile = [&](int tile) {
-        issue_rows<kRowBytes, kLoadsPerWave>(a.kv, sidx, n, tile * kTile + wave * (kTile / W),
+        issue_rows<kRowBytes, kLoadsPerWave, 1>(a.kv, sidx, n, tile * kTile + wave * (kTile / W),
                                              wave * (kTile / W),
                                              smem + (tile % kStages) * kStageBytes +
                                                  wave * kLoadsPerWave * 1024,
@@ -852,25 +865,34 @@ __global__ void __launch_bounds__(64 * W) attn_wide_kernel(AttnArgs a) {
         const unsigned char* st = smem + stoff;
         const int nvalid = n - i * kTile;
 
-        // S^T = K Q^T: rows 0-15 and 16-31 of the tile, head blocks 0 and 1
-        constexpr int kB = kKSteps < 4 ? kKSteps : 4;
+        // S^T = K Q^T: rows 0-15 and 16-31 of the tile, head blocks 0 and 1.
+        // The K reads run two k-steps ahead of the MFMAs that consume them
+        // (sched_group_barrier pins the interleave: four MFMAs per k-step,
+        // each pair followed by one of the two reads of k-step s + 2).
         f32x4 s00 = {0.f, 0.f, 0.f, 0.f}, s01 = s00, s10 = s00, s11 = s00;
+        {
+          bf16x8 ka[kKSteps], kb[kKSteps];
 #pragma unroll
-        for (int s0 = 0; s0 < kKSteps; s0 += kB) {
-          bf16x8 ka[kB], kb[kB];
-#pragma unroll
-          for (int u = 0; u < kB; ++u) {
-            const int o = off.kq(s0 + u);
+          for (int u = 0; u < kKSteps; ++u) {
+            const int o = off.kq(u);
             ka[u] = *reinterpret_cast<const bf16x8*>(st + o);
             kb[u] = *reinterpret_cast<const bf16x8*>(st + o + 16 * kRowBytes);
           }
-          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int u = 0; u < kB; ++u) {
-            s00 = mfma_k32(ka[u], q0[s0 + u], s00);
-            s01 = mfma_k32(ka[u], q1[s0 + u], s01);
-            s10 = mfma_k32(kb[u], q0[s0 + u], s10);
-            s11 = mfma_k32(kb[u], q1[s0 + u], s11);
+          for (int u = 0; u < kKSteps; ++u) {
+            s00 = mfma_k32(ka[u], q0[u], s00);
+            s01 = mfma_k32(ka[u], q1[u], s01);
+            s10 = mfma_k32(kb[u], q0[u], s10);
+            s11 = mfma_k32(kb[u], q1[u], s11);
+          }
+          constexpr int kPre = kKSteps < 2 ? kKSteps : 2;
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre, 0);  // reads of k-steps 0, 1
+#pragma unroll
+          for (int u = 0; u < kKSteps; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if (u + kPre < kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if (u + kPre < kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -899,14 +921,13 @@ __global__ void __launch_bounds__(64 * W) attn_wide_kernel(AttnArgs a) {
           pb[rb] = wide_p_operand(a0, a1);
         }
 
-        // O^T += V^T P^T, V^T operands read in batches of kVB d-tiles
-        constexpr int kVB = kDT < 4 ? kDT : 4;
+        // O^T += V^T P^T: the four transposing reads of d-tile dt + 2 run
+        // under the two MFMAs of d-tile dt (pinned as for S^T above).
+        {
+          bf16x8 va[kDT], vb[kDT];
 #pragma unroll
-        for (int d0 = 0; d0 < kDT; d0 += kVB) {
-          bf16x8 va[kVB], vb[kVB];
-#pragma unroll
-          for (int u = 0; u < kVB; ++u) {
-            const int o0 = voff.at(d0 + u, 0), o1 = voff.at(d0 + u, 1);
+          for (int u = 0; u < kDT; ++u) {
+            const int o0 = voff.at(u, 0), o1 = voff.at(u, 1);
             const bf16x4 a_lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + o0));
             const bf16x4 a_hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + o1));
             const bf16x4 b_lo =
@@ -916,11 +937,19 @@ __global__ void __launch_bounds__(64 * W) attn_wide_kernel(AttnArgs a) {
             va[u] = __builtin_shufflevector(a_lo, a_hi, 0, 1, 2, 3, 4, 5, 6, 7);
             vb[u] = __builtin_shufflevector(b_lo, b_hi, 0, 1, 2, 3, 4, 5, 6, 7);
           }
-          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int u = 0; u < kVB; ++u) {
-            acc[d0 + u] = mfma32(va[u], pb[0], acc[d0 + u]);
-            acc[d0 + u] = mfma32(vb[u], pb[1], acc[d0 + u]);
+          for (int u = 0; u < kDT; ++u) {
+            acc[u] = mfma32(va[u], pb[0], acc[u]);
+            acc[u] = mfma32(vb[u], pb[1], acc[u]);
+          }
+          constexpr int kPre = kDT < 2 ? kDT : 2;
+          __builtin_amdgcn_sched_group_barrier(0x100, 4 * kPre, 0);  // reads of d-tiles 0, 1
+#pragma unroll
+          for (int u = 0; u < kDT; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (u + kPre < kDT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (u + kPre < kDT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
