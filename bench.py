@@ -51,8 +51,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calibration-copy-mib", type=int, default=0,
-                   help="also run three plain device-to-device copies of this many MiB, the "
-                        "known-size kernel that scales the HBM byte counters")
+                   help="also run a kernel of known traffic three times (bitwise_not over this "
+                        "many MiB of int32: reads and writes exactly that much), which scales "
+                        "the HBM byte counters")
     p.add_argument("--pmc-summary", nargs="+", metavar="DIR",
                    help="summarise rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE "
                         "runs of this script) instead of benchmarking")
@@ -73,16 +74,16 @@ def kernel_sources_digest() -> str:
     return h.hexdigest()[:16]
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_base.md")
 
 
 def recorded_traffic(kernel: str, workload: str):
     """Per-launch HBM bytes of `kernel` from the committed counter summary, or
     None when there is none or the kernel sources changed since it was taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.md" % workload)
+    if not os.path.exists(path):
         return None
     fields = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if line.startswith("- ") and ": " in line:
                 k, v = line[2:].strip().split(": ", 1)
@@ -98,8 +99,8 @@ def recorded_traffic(kernel: str, workload: str):
 
 def pmc_summary(dirs, copy_mib):
     """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel from rocprofv3
-    counter CSVs, scaled by what the same counter reads for the largest plain copy
-    in the run (copy_mib MiB read and written)."""
+    counter CSVs, and the factors that scale each counter to bytes: what it reads
+    for the calibration kernel of the same run (copy_mib MiB read and written)."""
     import csv
     import glob
     import statistics
@@ -112,10 +113,7 @@ def pmc_summary(dirs, copy_mib):
                     per.setdefault(key, []).append((int(r["Grid_Size"]), float(r["Counter_Value"])))
     out = {}
     for (name, counter), vals in per.items():
-        if "copyBuffer" in name:
-            # the calibration copy is the largest copy in the run
-            top = max(v[1] for v in vals)
-            vals = [v for v in vals if v[1] >= 0.9 * top]
+        if "bitwise_not" in name:  # the calibration kernel (see --calibration-copy-mib)
             name = "__copy_calibration__"
         out.setdefault(name, {})[counter] = (statistics.mean(v[1] for v in vals), len(vals))
     cal = out.get("__copy_calibration__", {})
@@ -296,11 +294,13 @@ def main():
         return e0.elapsed_time(e1)
 
     if args.calibration_copy_mib:
-        n = args.calibration_copy_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        # a kernel of known traffic and a name of its own: bitwise_not over
+        # calibration_copy_mib MiB of int32 reads and writes exactly that much
+        n = (args.calibration_copy_mib << 20) // 4
+        src = torch.ones(n, dtype=torch.int32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
