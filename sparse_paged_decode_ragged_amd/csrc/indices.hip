@@ -342,7 +342,7 @@ __global__ void __launch_bounds__(1024) build_fused_small_kernel(BuildArgs a) {
 #pragma unroll
   for (int j = 0; j < kSmallN / 64; ++j) {
     const int s = lane + 64 * j;
-    wx[j] = a.swa_len[s < t ? s : 0];
+    wx[j] = a.swa_len[s < t && s < a.N ? s : 0];  // (waves past the batch: in bounds, unused)
   }
   int wl = 0;
 #pragma unroll
