@@ -51,6 +51,13 @@ def _load() -> ctypes.CDLL:
         lib.spd_oracle_build_decode_indices.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i32, P,
                                                         P, i64]
         lib.spd_oracle_build_decode_indices.restype = ctypes.c_int
+        lib.spd_oracle_sparse_decode_attn_fp8.argtypes = [P, P, P, i64, P, P, P, ctypes.c_float,
+                                                          i32, i32, i32, P, i32, P]
+        lib.spd_oracle_sparse_decode_attn_fp8.restype = ctypes.c_int
+        lib.spd_oracle_quantize_fp8.argtypes = [P, i32, i32, P, P]
+        lib.spd_oracle_quantize_fp8.restype = ctypes.c_int
+        lib.spd_oracle_e4m3_value.argtypes = [ctypes.c_int]
+        lib.spd_oracle_e4m3_value.restype = ctypes.c_double
         lib.spd_oracle_set_threads.argtypes = [ctypes.c_int]
         lib.spd_oracle_set_threads.restype = None
         lib.spd_oracle_get_threads.argtypes = []
@@ -96,6 +103,53 @@ def sparse_decode_attn(q_bits: np.ndarray, kv_bits: np.ndarray, kv_indices: np.n
     rc = _load().spd_oracle_sparse_decode_attn(
         _ptr(q_bits), _ptr(kv_bits), kv_bits.shape[0], _ptr(kv_indices), _ptr(kv_indptr),
         _ptr(attn_sink), float(np.float32(softmax_scale)), N, H, D, _ptr(tokens),
+        0 if tokens is None else len(tokens), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected its input (code %d)" % rc)
+    return out
+
+
+def e4m3_value(code: int) -> float:
+    """The OCP e4m3 value of an 8-bit code (NaN for 0x7f / 0xff)."""
+    return float(_load().spd_oracle_e4m3_value(int(code)))
+
+
+def quantize_fp8(src_bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """FP8 store of bf16 rows ``[n, D]`` (uint16 bit patterns): returns the e4m3
+    codes ``[n, D]`` uint8 and the per-row fp32 scales ``[n]`` (the steps are in
+    the C source)."""
+    src_bits = np.ascontiguousarray(src_bits, dtype=np.uint16)
+    n, D = src_bits.shape
+    codes = np.zeros((n, D), dtype=np.uint8)
+    scales = np.zeros(n, dtype=np.float32)
+    rc = _load().spd_oracle_quantize_fp8(_ptr(src_bits), n, D, _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError("oracle quantiser rejected its input (code %d)" % rc)
+    return codes, scales
+
+
+def sparse_decode_attn_fp8(q_bits: np.ndarray, kv_codes: np.ndarray, kv_scale: np.ndarray,
+                           kv_indices: np.ndarray, kv_indptr: np.ndarray, attn_sink: np.ndarray,
+                           softmax_scale: float, tokens: Optional[np.ndarray] = None) -> np.ndarray:
+    """sparse_decode_attn over an FP8 pool: row r is kv_scale[r] * e4m3(kv_codes[r])."""
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    kv_codes = np.ascontiguousarray(kv_codes, dtype=np.uint8)
+    kv_scale = np.ascontiguousarray(kv_scale, dtype=np.float32)
+    kv_indices = np.ascontiguousarray(kv_indices, dtype=np.int32)
+    kv_indptr = np.ascontiguousarray(kv_indptr, dtype=np.int32)
+    attn_sink = np.ascontiguousarray(attn_sink, dtype=np.float32)
+    N, H, D = q_bits.shape
+    assert kv_codes.ndim == 2 and kv_codes.shape[1] == D and kv_scale.shape == (kv_codes.shape[0],)
+    assert kv_indptr.shape == (N + 1,) and attn_sink.shape == (H,)
+    if tokens is not None:
+        tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    n_out = N if tokens is None else len(tokens)
+    out = np.zeros((n_out, H, D), dtype=np.float64)
+    if kv_indices.size == 0:
+        kv_indices = np.zeros(1, dtype=np.int32)
+    rc = _load().spd_oracle_sparse_decode_attn_fp8(
+        _ptr(q_bits), _ptr(kv_codes), _ptr(kv_scale), kv_codes.shape[0], _ptr(kv_indices),
+        _ptr(kv_indptr), _ptr(attn_sink), float(np.float32(softmax_scale)), N, H, D, _ptr(tokens),
         0 if tokens is None else len(tokens), _ptr(out))
     if rc != 0:
         raise ValueError("oracle rejected its input (code %d)" % rc)

@@ -25,6 +25,13 @@
  *   - the production index builder emits ragged-packed indices with no
  *     sentinel values.
  *
+ * FP8 pool (the pages' caches have FP8 variants; on the sglang PR #25898
+ * summary page, sections "comment highlights" and "risks and impact", a
+ * review flags the ROCm software FP8 conversion rounding half up where
+ * round-to-nearest-even is wanted): a row is stored as D OCP e4m3 codes plus
+ * one fp32 scale, and its value is scale * e4m3(code); the quantiser rounds
+ * to nearest even.
+ *
  * Readings where the page is silent (each is listed in the design notes):
  *   - the sink is a natural-log logit in the units of the scaled score
  *     softmax_scale * q.k (it is not multiplied by softmax_scale);
@@ -49,6 +56,34 @@ static double bf16_bits_to_double(uint16_t b) {
   float f;
   memcpy(&f, &u, sizeof f);
   return (double)f;
+}
+
+/* OCP e4m3 (the "fn" variant: no infinities) -> double, from its definition:
+ * sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 is
+ * subnormal (m * 2^-9); S.1111.111 is NaN. */
+static double e4m3_to_double(uint8_t c) {
+  const int s = (c >> 7) & 1, e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+double spd_oracle_e4m3_value(int code) { return e4m3_to_double((uint8_t)code); }
+
+/* A pool row decoded to fp64: bf16 bits, or (when kv8 is given) fp8 codes
+ * times the row's scale. */
+static void decode_row(const uint16_t* kv, const uint8_t* kv8, const float* kv_scale, int64_t r,
+                       int32_t D, double* dst) {
+  if (kv8) {
+    const double sc = (double)kv_scale[r];
+    for (int32_t d = 0; d < D; ++d) dst[d] = sc * e4m3_to_double(kv8[r * (int64_t)D + d]);
+  } else {
+    for (int32_t d = 0; d < D; ++d) dst[d] = bf16_bits_to_double(kv[r * (int64_t)D + d]);
+  }
 }
 
 void spd_oracle_set_threads(int n) {
@@ -80,7 +115,8 @@ int spd_oracle_get_threads(void) {
  * weighted sum.  All arithmetic in fp64.  Returns 0, or -1 when an index is
  * outside [0, num_rows) (a caller precondition on the page).
  */
-static int attend_one_token(const uint16_t* q, const uint16_t* kv, int64_t num_rows,
+static int attend_one_token(const uint16_t* q, const uint16_t* kv, const uint8_t* kv8,
+                            const float* kv_scale, int64_t num_rows,
                             const int32_t* kv_indices, const int32_t* kv_indptr,
                             const float* attn_sink, double sigma, int32_t t, int32_t H,
                             int32_t D, double* out_t /* [H][D] */) {
@@ -104,8 +140,7 @@ static int attend_one_token(const uint16_t* q, const uint16_t* kv, int64_t num_r
       free(rows); free(qd); free(s);
       return -1;
     }
-    for (int32_t d = 0; d < D; ++d)
-      rows[j * D + d] = bf16_bits_to_double(kv[r * (int64_t)D + d]);
+    decode_row(kv, kv8, kv_scale, r, D, rows + j * D);
   }
 
   for (int32_t h = 0; h < H; ++h) {
@@ -143,11 +178,11 @@ static int attend_one_token(const uint16_t* q, const uint16_t* kv, int64_t num_r
  * Returns 0 on success, -1 on an out-of-range index or a decreasing indptr,
  * -2 on allocation failure, -3 on bad sizes.
  */
-int spd_oracle_sparse_decode_attn(const uint16_t* q, const uint16_t* kv, int64_t num_rows,
-                                  const int32_t* kv_indices, const int32_t* kv_indptr,
-                                  const float* attn_sink, float softmax_scale, int32_t N,
-                                  int32_t H, int32_t D, const int32_t* tokens,
-                                  int32_t n_tokens, double* out) {
+static int attend_all(const uint16_t* q, const uint16_t* kv, const uint8_t* kv8,
+                      const float* kv_scale, int64_t num_rows, const int32_t* kv_indices,
+                      const int32_t* kv_indptr, const float* attn_sink, float softmax_scale,
+                      int32_t N, int32_t H, int32_t D, const int32_t* tokens, int32_t n_tokens,
+                      double* out) {
   if (N < 0 || H <= 0 || D <= 0 || num_rows < 0) return -3;
   const int32_t n_out = tokens ? n_tokens : N;
   const double sigma = (double)softmax_scale;
@@ -161,8 +196,8 @@ int spd_oracle_sparse_decode_attn(const uint16_t* q, const uint16_t* kv, int64_t
     if (t < 0 || t >= N)
       rc = -3;
     else
-      rc = attend_one_token(q, kv, num_rows, kv_indices, kv_indptr, attn_sink, sigma, t, H, D,
-                            out + (int64_t)i * H * D);
+      rc = attend_one_token(q, kv, kv8, kv_scale, num_rows, kv_indices, kv_indptr, attn_sink,
+                            sigma, t, H, D, out + (int64_t)i * H * D);
     if (rc != 0) {
 #ifdef _OPENMP
 #pragma omp critical
@@ -171,6 +206,93 @@ int spd_oracle_sparse_decode_attn(const uint16_t* q, const uint16_t* kv, int64_t
     }
   }
   return status;
+}
+
+int spd_oracle_sparse_decode_attn(const uint16_t* q, const uint16_t* kv, int64_t num_rows,
+                                  const int32_t* kv_indices, const int32_t* kv_indptr,
+                                  const float* attn_sink, float softmax_scale, int32_t N,
+                                  int32_t H, int32_t D, const int32_t* tokens,
+                                  int32_t n_tokens, double* out) {
+  return attend_all(q, kv, NULL, NULL, num_rows, kv_indices, kv_indptr, attn_sink, softmax_scale,
+                    N, H, D, tokens, n_tokens, out);
+}
+
+/* The same definition over an FP8 pool: row r is kv_scale[r] * e4m3(kv8[r][:]). */
+int spd_oracle_sparse_decode_attn_fp8(const uint16_t* q, const uint8_t* kv8,
+                                      const float* kv_scale, int64_t num_rows,
+                                      const int32_t* kv_indices, const int32_t* kv_indptr,
+                                      const float* attn_sink, float softmax_scale, int32_t N,
+                                      int32_t H, int32_t D, const int32_t* tokens,
+                                      int32_t n_tokens, double* out) {
+  if (!kv8 || !kv_scale) return -3;
+  return attend_all(q, NULL, kv8, kv_scale, num_rows, kv_indices, kv_indptr, attn_sink,
+                    softmax_scale, N, H, D, tokens, n_tokens, out);
+}
+
+/*
+ * FP8 quantisation of bf16 rows (the store into an FP8 pool), in fp32
+ * arithmetic step by step, so that a device implementation doing the same
+ * IEEE operations gives the same codes:
+ *   amax  = max_d |x_d|                       (exact)
+ *   amax < 2^-64:  scale = 0, every code 0    (a zero row)
+ *   else:  scale = amax / 448, inv = 448 / amax   (fp32, correctly rounded)
+ *          y_d = x_d * inv (fp32), clamped to [-448, 448]
+ *          code_d = |y_d| rounded to the nearest e4m3 value, ties to the even
+ *                   mantissa, with the sign bit of x_d
+ * 448 is the largest finite e4m3 value.  Rounding, for a = |y_d|:
+ *   a < 2^-6 (subnormal range):  m = rint(a * 2^9), code = m  (m = 8 is 2^-6)
+ *   else: e = floor(log2 a), q = rint(a * 2^(3-e)) in [8, 16] (16: e + 1, q = 8),
+ *         code = (e + 7) << 3 | (q - 8)
+ * rint rounds half to even in the default rounding mode.
+ */
+static uint8_t e4m3_rne(float y, int negative) {
+  float a = fabsf(y);
+  uint8_t code;
+  if (a < 0.015625f) { /* 2^-6 */
+    code = (uint8_t)rintf(a * 512.0f);
+  } else {
+    uint32_t bits;
+    memcpy(&bits, &a, sizeof bits);
+    int e = (int)((bits >> 23) & 0xff) - 127;
+    float q = rintf(ldexpf(a, 3 - e));
+    if (q >= 16.0f) {
+      e += 1;
+      q = 8.0f;
+    }
+    code = (uint8_t)(((e + 7) << 3) | ((int)q - 8));
+  }
+  return negative ? (uint8_t)(code | 0x80) : code;
+}
+
+int spd_oracle_quantize_fp8(const uint16_t* src, int32_t n, int32_t D, uint8_t* codes,
+                            float* scales) {
+  if (n < 0 || D <= 0) return -3;
+  for (int32_t i = 0; i < n; ++i) {
+    const uint16_t* x = src + (int64_t)i * D;
+    float amax = 0.0f;
+    for (int32_t d = 0; d < D; ++d) {
+      const float v = fabsf((float)bf16_bits_to_double(x[d]));
+      if (v > amax) amax = v;
+    }
+    uint8_t* c = codes + (int64_t)i * D;
+    if (!(amax >= 5.421010862427522e-20f)) { /* 2^-64, also catches NaN */
+      scales[i] = 0.0f;
+      memset(c, 0, (size_t)D);
+      continue;
+    }
+    const volatile float amax_v = amax;  /* keep each fp32 operation as written */
+    const float scale = amax_v / 448.0f;
+    const float inv = 448.0f / amax_v;
+    scales[i] = scale;
+    for (int32_t d = 0; d < D; ++d) {
+      const float xv = (float)bf16_bits_to_double(x[d]);
+      float y = xv * inv;
+      if (y > 448.0f) y = 448.0f;
+      if (y < -448.0f) y = -448.0f;
+      c[d] = e4m3_rne(y, (x[d] >> 15) & 1);
+    }
+  }
+  return 0;
 }
 
 /*
