@@ -224,6 +224,64 @@ SPD_API spd_status sparse_decode_attn_paged(
     int32_t mode, void* stream);
 
 /*
+ * FP8 pool.  The page's caches have FP8 variants, filled by stores that
+ * quantise rows as they scatter them into the pool (sglang PR #25898 summary
+ * page, "key files": the fused norm/RoPE/store kernel and the store-cache
+ * kernels); a review on that page ("comment highlights", "risks and impact")
+ * asks for round-to-nearest-even in the conversion, not round-half-up.
+ * Format: row r of the pool is D OCP e4m3 codes (1 sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits; no infinities; 0x7f / 0xff are NaN) in
+ * kv_fp8[r][0 .. D) plus one fp32 scale kv_scale[r]; its value is
+ * kv_scale[r] * e4m3(code).
+ */
+
+/*
+ * sparse_decode_attn over an FP8 pool: the same operation (same index
+ * contract, sink and numerics) with the row value kv_scale[r] * e4m3(code),
+ * used as both key and value.  fp32 accumulation; the codes are converted to
+ * bf16 exactly, the scale multiplies the row's scores and its softmax weight.
+ * Work decomposition: the rows mode of sparse_decode_attn_ex (workgroup =
+ * token x 16 heads, no split, no workspace).
+ *
+ *   q, kv_indices, kv_indptr, attn_sink, softmax_scale, out, N, H, D:
+ *                as sparse_decode_attn (same alignment and preconditions:
+ *                every index in [0, num_rows))
+ *   kv_fp8       [num_rows, D] uint8 e4m3 codes, 16-byte aligned
+ *   kv_scale     [num_rows] fp32, 4-byte aligned
+ *
+ * Returns SPD_ERR_UNSUPPORTED where sparse_decode_attn_can_use(H, D) is 0.
+ */
+SPD_API spd_status sparse_decode_attn_fp8(const void* q, const void* kv_fp8,
+                                          const float* kv_scale, int64_t num_rows,
+                                          const int32_t* kv_indices, const int32_t* kv_indptr,
+                                          const float* attn_sink, float softmax_scale, void* out,
+                                          int32_t N, int32_t H, int32_t D, void* stream);
+
+/*
+ * Quantising store into an FP8 pool: bf16 row i of src goes to pool row
+ * slots[i] (row i when slots is NULL) as codes plus a scale:
+ *   amax = max_d |x_d|;  amax < 2^-64 (a zero row): scale 0, every code 0;
+ *   else scale = amax / 448 and inv = 448 / amax (fp32, correctly rounded),
+ *        y_d = clamp(x_d * inv, -448, 448) (fp32),
+ *        code_d = y_d rounded to the nearest e4m3 value, ties to even
+ *        (448 is the largest finite e4m3 value, so |x| = amax stores +-448).
+ * The inputs must be finite (a row holding an infinity or a NaN stores
+ * unspecified codes).
+ *
+ *   src       [n, D] bf16, 16-byte aligned;  D in {64, 128, 256, 512}
+ *   slots     [n] int32 destination rows, or NULL; a slot outside
+ *             [0, num_rows) skips its row (nothing is written for it).  Two
+ *             rows with the same slot race.
+ *   kv_fp8    [num_rows, D] uint8 (out), 16-byte aligned
+ *   kv_scale  [num_rows] fp32 (out)
+ *
+ * Host checks: n >= 0, num_rows > 0, n <= num_rows when slots is NULL, no
+ * overlap between the source and the pool.  n == 0 returns SPD_OK.
+ */
+SPD_API spd_status quantize_kv_fp8(const void* src, const int32_t* slots, int32_t n, int32_t D,
+                                   void* kv_fp8, float* kv_scale, int64_t num_rows, void* stream);
+
+/*
  * Debug check of the attention call's index preconditions: kv_indptr[0] == 0,
  * kv_indptr non-decreasing, kv_indptr[N] <= num_indices (the length of the
  * kv_indices buffer), and every kv_indices[j], j < kv_indptr[N], in

@@ -16,6 +16,11 @@ Call names follow the C ABI:
   block_table, win, k_per_block, swa_pages, attn_sink, softmax_scale,
   out=None)`` -- the two above in one kernel (the page transform fused into
   the attention call; no kv_indices in memory)
+* ``sparse_decode_attn_fp8(q, kv_fp8, kv_scale, kv_indices, kv_indptr,
+  attn_sink, softmax_scale, out=None)`` -- the same attention over an FP8 pool
+  (e4m3 codes times a per-row fp32 scale)
+* ``quantize_kv_fp8(src, kv_fp8, kv_scale, slots=None)`` -- the quantising
+  store that fills such a pool
 * ``sparse_decode_attn_workspace_size``, ``sparse_decode_attn_can_use``,
   ``validate_indices``
 """
@@ -38,6 +43,7 @@ EXPORTED_SYMBOLS = (
     "spd_status_string", "spd_version", "sparse_decode_attn_can_use", "sparse_decode_attn",
     "sparse_decode_attn_workspace_size", "sparse_decode_attn_ex", "build_decode_indices",
     "spd_validate_indices", "sparse_decode_attn_plan_info", "sparse_decode_attn_paged",
+    "sparse_decode_attn_fp8", "quantize_kv_fp8",
 )
 
 
@@ -69,6 +75,11 @@ def _load() -> ctypes.CDLL:
     lib.sparse_decode_attn_paged.argtypes = [P, P, i64, P, P, P, i32, P, i32, i32, i32, i32, P,
                                              ctypes.c_float, P, i32, i32, i32, i32, P]
     lib.sparse_decode_attn_paged.restype = ctypes.c_int
+    lib.sparse_decode_attn_fp8.argtypes = [P, P, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32,
+                                           P]
+    lib.sparse_decode_attn_fp8.restype = ctypes.c_int
+    lib.quantize_kv_fp8.argtypes = [P, P, i32, i32, P, P, i64, P]
+    lib.quantize_kv_fp8.restype = ctypes.c_int
     lib.build_decode_indices.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i32, P, P, i64, P]
     lib.build_decode_indices.restype = ctypes.c_int
     lib.spd_validate_indices.argtypes = [P, i64, P, i32, i64, ctypes.POINTER(ctypes.c_int64), P]
@@ -254,6 +265,64 @@ def sparse_decode_attn_paged(q: torch.Tensor, unified_kv: torch.Tensor, state_sl
                                       _ptr(out), N, H, D, int(mode), _stream(q.device))
     _raise_on(st, "sparse_decode_attn_paged")
     return out
+
+
+def _fp8_codes(t: torch.Tensor, name: str) -> torch.Tensor:
+    """An FP8 pool tensor as its uint8 codes (float8_e4m3fn is viewed, not converted)."""
+    if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    _check(t, name, torch.uint8, 2)
+    return t
+
+
+def sparse_decode_attn_fp8(q: torch.Tensor, kv_fp8: torch.Tensor, kv_scale: torch.Tensor,
+                           kv_indices: torch.Tensor, kv_indptr: torch.Tensor,
+                           attn_sink: torch.Tensor, softmax_scale: float,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[N, H, D] (bf16): sparse decode attention over an FP8 pool whose row r
+    is kv_scale[r] * e4m3(kv_fp8[r]) (uint8 codes or a float8_e4m3fn tensor);
+    see include/spd.h."""
+    _check(q, "q", torch.bfloat16, 3)
+    codes = _fp8_codes(kv_fp8, "kv_fp8")
+    _check(kv_scale, "kv_scale", torch.float32, 1)
+    _check(kv_indices, "kv_indices", torch.int32, 1)
+    _check(kv_indptr, "kv_indptr", torch.int32, 1)
+    _check(attn_sink, "attn_sink", torch.float32, 1)
+    N, H, D = q.shape
+    if codes.shape[1] != D or kv_scale.shape[0] != codes.shape[0] or \
+            kv_indptr.shape[0] != N + 1 or attn_sink.shape[0] != H:
+        raise ValueError("shape mismatch between q, kv_fp8, kv_scale, kv_indptr and attn_sink")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16, 3)
+        if tuple(out.shape) != (N, H, D):
+            raise ValueError("out must be [N, H, D]")
+    idx = kv_indices if kv_indices.numel() > 0 else kv_indptr  # any valid pointer; never read
+    st = lib.sparse_decode_attn_fp8(_ptr(q), _ptr(codes), _ptr(kv_scale), codes.shape[0],
+                                    _ptr(idx), _ptr(kv_indptr), _ptr(attn_sink),
+                                    float(softmax_scale), _ptr(out), N, H, D, _stream(q.device))
+    _raise_on(st, "sparse_decode_attn_fp8")
+    return out
+
+
+def quantize_kv_fp8(src: torch.Tensor, kv_fp8: torch.Tensor, kv_scale: torch.Tensor,
+                    slots: Optional[torch.Tensor] = None) -> None:
+    """Store bf16 rows src[n, D] into the FP8 pool (kv_fp8 [num_rows, D] codes,
+    kv_scale [num_rows]) at rows slots[n] (0 .. n-1 when None), in place."""
+    _check(src, "src", torch.bfloat16, 2)
+    codes = _fp8_codes(kv_fp8, "kv_fp8")
+    _check(kv_scale, "kv_scale", torch.float32, 1)
+    n, D = src.shape
+    if codes.shape[1] != D or kv_scale.shape[0] != codes.shape[0]:
+        raise ValueError("shape mismatch between src, kv_fp8 and kv_scale")
+    if slots is not None:
+        _check(slots, "slots", torch.int32, 1)
+        if slots.shape[0] != n:
+            raise ValueError("slots must have one entry per source row")
+    st = lib.quantize_kv_fp8(_ptr(src), _ptr(slots), n, D, _ptr(codes), _ptr(kv_scale),
+                             codes.shape[0], _stream(src.device))
+    _raise_on(st, "quantize_kv_fp8")
 
 
 def validate_indices(kv_indices: torch.Tensor, kv_indptr: torch.Tensor, num_rows: int) -> int:

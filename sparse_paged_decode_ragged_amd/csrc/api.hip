@@ -196,6 +196,79 @@ SPD_API spd_status sparse_decode_attn_paged(
   return e == hipSuccess ? SPD_OK : SPD_ERR_HIP;
 }
 
+SPD_API spd_status sparse_decode_attn_fp8(const void* q, const void* kv_fp8,
+                                          const float* kv_scale, int64_t num_rows,
+                                          const int32_t* kv_indices, const int32_t* kv_indptr,
+                                          const float* attn_sink, float softmax_scale, void* out,
+                                          int32_t N, int32_t H, int32_t D, void* stream) {
+  if (N < 0 || H <= 0 || D <= 0 || num_rows <= 0) return SPD_ERR_INVALID_ARG;
+  if (!isfinite(softmax_scale)) return SPD_ERR_INVALID_ARG;
+  if (!spd::attn_supported(H, D)) return SPD_ERR_UNSUPPORTED;
+  if (N == 0) return SPD_OK;
+  if (!q || !kv_fp8 || !kv_scale || !kv_indices || !kv_indptr || !attn_sink || !out)
+    return SPD_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(kv_fp8, 16) || !aligned(out, 16) || !aligned(kv_scale, 4) ||
+      !aligned(kv_indices, 4) || !aligned(kv_indptr, 4) || !aligned(attn_sink, 4))
+    return SPD_ERR_INVALID_ARG;
+  if (num_rows > (int64_t)1 << 40) return SPD_ERR_INVALID_ARG;
+  const size_t qo_bytes = (size_t)N * H * D * 2;
+  if (overlap(out, qo_bytes, q, qo_bytes) ||
+      overlap(out, qo_bytes, kv_fp8, (size_t)num_rows * D) ||
+      overlap(out, qo_bytes, kv_scale, (size_t)num_rows * 4) ||
+      overlap(out, qo_bytes, attn_sink, (size_t)H * 4) ||
+      overlap(out, qo_bytes, kv_indptr, (size_t)(N + 1) * 4))
+    return SPD_ERR_INVALID_ARG;
+  const long long groups = (H + 15) / 16;
+  if ((long long)N * groups > 0x7fffffffLL) return SPD_ERR_INVALID_ARG;
+
+  spd::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv8 = static_cast<const uint8_t*>(kv_fp8);
+  a.kv_scale = kv_scale;
+  a.kv_indices = kv_indices;
+  a.kv_indptr = kv_indptr;
+  a.sink = attn_sink;
+  a.out = static_cast<uint16_t*>(out);
+  a.qk_scale = (float)((double)softmax_scale * kLog2eD);
+  a.N = N;
+  a.H = H;
+  a.head_groups = (int32_t)groups;
+  a.splits = 1;
+  a.split_rows = 1 << 30;
+  const hipError_t e = spd::launch_attention_fp8(a, D, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPD_OK : SPD_ERR_HIP;
+}
+
+SPD_API spd_status quantize_kv_fp8(const void* src, const int32_t* slots, int32_t n, int32_t D,
+                                   void* kv_fp8, float* kv_scale, int64_t num_rows, void* stream) {
+  if (n < 0 || D <= 0 || num_rows <= 0) return SPD_ERR_INVALID_ARG;
+  if (D != 64 && D != 128 && D != 256 && D != 512) return SPD_ERR_UNSUPPORTED;
+  if (n == 0) return SPD_OK;
+  if (!src || !kv_fp8 || !kv_scale) return SPD_ERR_INVALID_ARG;
+  if (!aligned(src, 16) || !aligned(kv_fp8, 16) || !aligned(kv_scale, 4) ||
+      (slots && !aligned(slots, 4)))
+    return SPD_ERR_INVALID_ARG;
+  if (!slots && n > num_rows) return SPD_ERR_INVALID_ARG;
+  if (num_rows > (int64_t)1 << 40) return SPD_ERR_INVALID_ARG;
+  const size_t src_bytes = (size_t)n * D * 2;
+  if (overlap(src, src_bytes, kv_fp8, (size_t)num_rows * D) ||
+      overlap(src, src_bytes, kv_scale, (size_t)num_rows * 4) ||
+      overlap(kv_fp8, (size_t)num_rows * D, kv_scale, (size_t)num_rows * 4) ||
+      (slots && (overlap(slots, (size_t)n * 4, kv_fp8, (size_t)num_rows * D) ||
+                 overlap(slots, (size_t)n * 4, kv_scale, (size_t)num_rows * 4))))
+    return SPD_ERR_INVALID_ARG;
+
+  spd::QuantArgs a{};
+  a.src = static_cast<const uint16_t*>(src);
+  a.slots = slots;
+  a.kv8 = static_cast<uint8_t*>(kv_fp8);
+  a.kv_scale = kv_scale;
+  a.n = n;
+  a.num_rows = num_rows;
+  const hipError_t e = spd::launch_quantize_fp8(a, D, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPD_OK : SPD_ERR_HIP;
+}
+
 SPD_API spd_status build_decode_indices(const int32_t* state_slot, const int32_t* swa_len,
                                         const int32_t* comp_pos, int32_t topk,
                                         const int32_t* block_table, int32_t max_blocks, int32_t N,

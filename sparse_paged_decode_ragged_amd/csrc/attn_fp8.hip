@@ -1,0 +1,482 @@
+// attn_fp8.hip -- sparse decode attention over an FP8 pool, and the
+// quantising store that fills such a pool, gfx950.
+//
+// Pool format (sglang PR #25898 summary page, "key files": its fused
+// norm/RoPE/store kernel and its store-cache kernels quantise rows to FP8 as
+// they scatter them into the paged caches; "comment highlights" and "risks
+// and impact": the conversion is to round to nearest even, not half up): row
+// r holds D OCP e4m3 codes (sign, 4 exponent bits with bias 7, 3 mantissa
+// bits; no infinities; 0x7f and 0xff are NaN) and one fp32 scale, and its
+// value is kv_scale[r] * e4m3(code).  The attention is the one of attn.hip
+// (sglang PR #28392 summary page, "key source snippet") with that row as both
+// key and value.
+//
+// Quantiser, per row x[0, D): amax = max |x|; a row with amax < 2^-64 stores
+// scale 0 and zero codes; otherwise scale = amax / 448 and inv = 448 / amax
+// (fp32, correctly rounded), y = clamp(x * inv, -448, 448) in fp32, and the
+// code is y rounded to the nearest e4m3 value, ties to even (v_cvt_pk_fp8_f32).
+// 448 is the largest finite e4m3 value, so the largest |x| maps to +-448.
+//
+// Attention kernel (rows decomposition, as attn_rows_kernel: workgroup =
+// token x 16 heads, its 4 waves take every 4th 16-row tile and merge their
+// states in LDS at the end):
+//   * a tile's rows are gathered as codes (D bytes a row, half a bf16 row) by
+//     LDS-DMA loads into one of two FP8 slots of the wave, together with the
+//     16 row scales;
+//   * the wave reads each tile once, in the K-operand pattern of
+//     S^T = K Q^T, and converts the codes to bf16 exactly (every e4m3 value is
+//     a bf16 value) with v_cvt_pk_f32_fp8; the converted values are the MFMA
+//     operand and are also written to a bf16 stage laid out as in attn.hip,
+//     from which the V^T operand is read with ds_read_b64_tr_b16.  This
+//     conversion of tile j+1 runs under the PV MFMAs of tile j;
+//   * the scale multiplies its row's scores and its softmax weight, which
+//     becomes P' = bf16(p * scale); the denominator sums the unscaled p.
+#include "attn_device.h"
+
+namespace spd {
+namespace {
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Eight e4m3 codes (bytes of raw, in order) -> eight bf16 values, exactly:
+// v_cvt_pk_f32_fp8 decodes two codes to fp32, and the top half of each such
+// fp32 is its bf16 value (an e4m3 value has at most 4 significant bits and an
+// exponent well inside the bf16 range).  (The vector elements are copied to
+// scalars before __builtin_bit_cast: applied to a subscripted vector element
+// directly, this clang reads element 0 whatever the subscript.)
+__device__ __forceinline__ unsigned bf16_pair_of(float lo, float hi) {
+  return __builtin_amdgcn_perm(__builtin_bit_cast(unsigned, hi), __builtin_bit_cast(unsigned, lo),
+                               0x07060302u);  // top halves of lo (bits 0-15) and hi
+}
+
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 raw) {
+  u32x4 w;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[h], false);  // bytes 0, 1
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[h], true);   // bytes 2, 3
+    const float b0 = lo[0], b1 = lo[1], b2 = hi[0], b3 = hi[1];
+    w[2 * h] = bf16_pair_of(b0, b1);
+    w[2 * h + 1] = bf16_pair_of(b2, b3);
+  }
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Byte offsets of the K-operand read of an FP8 tile (16 rows of D codes; the
+// 16-byte chunk c of row r is stored at c ^ (r & 15), within the row's D / 16
+// chunks, by issue_rows).  Lane (n16, g) reads codes 32 s + 8 g .. + 7 of row
+// n16 for k-step s: half g & 1 of logical chunk 2 s + (g >> 1).  With
+// w = swizzle(n16) ^ (g >> 1) that chunk is stored at 2 (s ^ (w >> 1)) + (w & 1),
+// i.e. the read is at k[s & 7] + 256 (s >> 3) bytes.  In the first 32 lanes
+// the 16 rows then hit 16 different 4-bank groups, at D >= 256.
+template <int D>
+struct Fp8Offsets {
+  static constexpr int kN = D / 32 < 8 ? D / 32 : 8;
+  int k[kN];
+  __device__ __forceinline__ Fp8Offsets(int n16, int g) {
+    constexpr int kChunks = D / 16;
+    const int w = (row_swizzle(n16) & (kChunks - 1)) ^ (g >> 1);
+#pragma unroll
+    for (int u = 0; u < kN; ++u) k[u] = n16 * D + 32 * (u ^ (w >> 1)) + 16 * (w & 1) + 8 * (g & 1);
+  }
+  __device__ __forceinline__ int kq(int s) const { return k[s & 7] + 256 * (s >> 3); }
+};
+
+// The scales of the 16 rows of a tile (staged indices from sidx[p0]; positions
+// past n repeat the last row) into sc[0, 64): lane l loads the scale of tile
+// row l & 15, so lanes 16 .. 63 repeat the first 16.
+__device__ __forceinline__ void issue_scales(const float* kv_scale, const int* sidx, int n, int p0,
+                                             float* sc, int lane) {
+  const int p = p0 + (lane & 15);
+  const int grow = sidx[p < n ? p : n - 1];
+  dma_4B(kv_scale + grow, __builtin_amdgcn_readfirstlane(lds_addr(sc)));
+}
+
+// softmax_tile with fp32 weights: pf[j] = 2^(x[j] - m), unrounded, for the
+// caller to scale by its row's FP8 scale before rounding to bf16; lpart sums
+// them.  Reference maximum, its headroom and the second-pass flag as in
+// softmax_tile.
+template <int R>
+__device__ __forceinline__ bool softmax_tile_f32(const float (&x)[R], float sink_l2, int g,
+                                                 bool& first, float& m, float& mtrue,
+                                                 float& lpart, float (&pf)[R]) {
+  float mx = x[0];
+#pragma unroll
+  for (int j = 1; j < R; ++j) mx = fmaxf(mx, x[j]);
+  mx = group_max4(mx);
+  mtrue = fmaxf(mtrue, mx);
+  if (first) {
+    m = fmaxf(sink_l2, mx);
+    lpart = (g == 0 && sink_l2 > -INFINITY) ? __builtin_amdgcn_exp2f(sink_l2 - m) : 0.f;
+    first = false;
+  }
+  const bool over = __builtin_amdgcn_ballot_w64(mx > m + kRaise) != 0;
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    pf[j] = __builtin_amdgcn_exp2f(x[j] - m);
+    psum += pf[j];
+  }
+  lpart += psum;
+  return over;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) attn_rows_fp8_kernel(AttnArgs a) {
+  constexpr int kWaves = 4;
+  constexpr int kTile = 16;
+  constexpr int kKSteps = D / 32;
+  constexpr int kDTiles = D / 16;
+  constexpr int kLoads = kTile * D / 1024;    // LDS-DMA ops per FP8 tile
+  constexpr int kPerTile = kLoads + 1;        // and the scale load
+  constexpr int kStageBytes = kTile * 2 * D;  // bf16 stage
+  constexpr int kSlotBytes = kTile * D;       // FP8 slot
+  constexpr int kWaveBytes = kStageBytes + 2 * kSlotBytes;
+  constexpr int kAhead = kKSteps < 4 ? kKSteps : 4;  // FP8 reads issued ahead of use
+  static_assert(kWaveBytes == 16 * D * 4, "partial O must fit the wave's LDS");
+  static_assert(kLoads >= 1 && 2 * kPerTile < 64, "bad load count");
+
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kWaves * kWaveBytes];
+  __shared__ __attribute__((aligned(256))) int sidx[kIdxCap];
+  __shared__ __attribute__((aligned(256))) float ssink[64];
+  __shared__ __attribute__((aligned(256))) float sscale[kWaves][2][64];
+  __shared__ float sml[kWaves][2][16];
+  __shared__ int sflag[kWaves];
+
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const int hg = item % a.head_groups;
+  const int t = item / a.head_groups;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n16 = lane & 15;
+  const int g = lane >> 4;
+
+  const ScalarI32Ptr indptr = (ScalarI32Ptr)a.kv_indptr;
+  const int row0 = indptr[t];
+  const int L = indptr[t + 1] - row0;
+  const int32_t* part = a.kv_indices + row0;
+  const int h0 = hg * 16;
+  const int h = h0 + n16;
+  const bool hvalid = h < a.H;
+  const int nh = a.H - h0 < 16 ? a.H - h0 : 16;
+
+  if (L <= 0) {
+    zero_heads<D>(a.out, a.H, t, h0, nh, threadIdx.x, 64 * kWaves);
+    return;
+  }
+
+  bf16x8 qreg[kKSteps];
+  load_q<D>(a.q, (int64_t)t * a.H + (hvalid ? h : 0), g, qreg);
+  stage_sinks(a.sink, a.H, h0, ssink, wave, lane);
+
+  unsigned char* mine = smem + wave * kWaveBytes;  // bf16 stage, then the two FP8 slots
+  unsigned char* slots = mine + kStageBytes;
+  const uint16_t* kv8 = reinterpret_cast<const uint16_t*>(a.kv8);  // rows of D bytes
+  const TileOffsets<D> off(n16, g);
+  const Fp8Offsets<D> off8(n16, g);
+
+  float m = -INFINITY, lpart = 0.f, mtrue = -INFINITY, sink_l2 = -INFINITY;
+  f32x4 acc[kDTiles];
+  for (int pass = 0; pass < 2; ++pass) {
+    bool first = pass == 0;
+    if (pass == 1) second_pass_state(sink_l2, mtrue, g, m, lpart);
+#pragma unroll
+    for (int i = 0; i < kDTiles; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bool over = false;
+
+    for (int sc = 0; sc < L; sc += kIdxCap) {
+      const int n = L - sc < kIdxCap ? L - sc : kIdxCap;
+      const bool restage = sc > 0 || (pass == 1 && L > kIdxCap);
+      if (restage) {
+        barrier_lds();  // every wave is done with the indices and its slots
+        stage_indices(part, sc, n, sidx, wave, kWaves, lane);
+        wait_vmcnt<0>();
+        barrier_lds();
+      } else if (pass == 0) {
+        stage_indices(part, sc, n, sidx, wave, kWaves, lane);
+        wait_vmcnt<0>();
+        barrier_lds();
+        sink_l2 = (wave == 0 && hvalid) ? ssink[n16] * kLog2e : -INFINITY;  // sink in wave 0
+      }
+      const int ntiles = (n + kTile - 1) / kTile;
+      const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+
+      auto issue = [&](int j) {  // this wave's j-th tile = global tile wave + 4j
+        const int p0 = (wave + kWaves * j) * kTile;
+        issue_rows<D, kLoads>(kv8, sidx, n, p0, 0, slots + (j & 1) * kSlotBytes, lane);
+        issue_scales(a.kv_scale, sidx, n, p0, sscale[wave][j & 1], lane);
+      };
+
+      // Pipeline over this wave's tiles: one bf16 stage, two FP8 slots.  In
+      // iteration j: S^T of tile j (K operand in registers) with the V^T reads
+      // of tile j from the stage; softmax; then the PV MFMAs of tile j with the
+      // conversion of tile j+1 (FP8 slot -> K operand registers + stage), after
+      // which that slot takes the loads of tile j+3.
+      bf16x8 ka[kKSteps];
+      f32x4 scl = {0.f, 0.f, 0.f, 0.f};  // scales of rows 4g .. 4g+3 of the current tile
+      if (my_tiles > 0) issue(0);
+      if (my_tiles > 1) issue(1);
+      if (my_tiles > 0) {
+        if (my_tiles > 1)
+          wait_vmcnt<kPerTile>();
+        else
+          wait_vmcnt<0>();
+        asm volatile("" ::: "memory");
+        u32x2 raw[kKSteps];
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) raw[s] = *reinterpret_cast<const u32x2*>(slots + off8.kq(s));
+        scl = *reinterpret_cast<const f32x4*>(&sscale[wave][0][4 * g]);
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) {
+          ka[s] = e4m3x8_to_bf16(raw[s]);
+          *reinterpret_cast<bf16x8*>(mine + off.kq(s)) = ka[s];
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): slot 0 is read
+        asm volatile("" ::: "memory");
+        if (my_tiles > 2) issue(2);
+      }
+      for (int j = 0; j < my_tiles; ++j) {
+        const int nvalid = n - (wave + kWaves * j) * kTile;
+        constexpr int kCh = kKSteps < 4 ? kKSteps : 4;  // independent QK chains
+        f32x4 part_s[kCh];
+#pragma unroll
+        for (int c = 0; c < kCh; ++c) part_s[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x4 vt[kDTiles];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) {
+          part_s[s % kCh] = mfma_k32(ka[s], qreg[s], part_s[s % kCh]);
+          vt[2 * s] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(mine + off.vt(2 * s)));
+          vt[2 * s + 1] =
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(mine + off.vt(2 * s + 1)));
+        }
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 sa = part_s[0];
+#pragma unroll
+        for (int c = 1; c < kCh; ++c) sa += part_s[c];
+        float x[4];
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          x[i4] = (4 * g + i4 < nvalid) ? sa[i4] * (a.qk_scale * scl[i4]) : -INFINITY;
+        float pf[4];
+        over |= softmax_tile_f32<4>(x, sink_l2, g, first, m, mtrue, lpart, pf);
+        bf16x4 pt;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) pt[i4] = (__bf16)(pf[i4] * scl[i4]);
+        // The stage's transposing reads are complete: it may take tile j+1.
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+        if (j + 1 < my_tiles) {  // tile j+1 has landed once only tile j+2 may be outstanding
+          if (j + 2 < my_tiles)
+            wait_vmcnt<kPerTile>();
+          else
+            wait_vmcnt<0>();
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        // O^T += V^T P^T, with the conversion of tile j+1 (after the last tile
+        // it converts a stale slot: in bounds, and the values are unused).
+        const unsigned char* s8 = slots + ((j + 1) & 1) * kSlotBytes;
+        u32x2 raw[kKSteps];
+#pragma unroll
+        for (int s = 0; s < kAhead; ++s) raw[s] = *reinterpret_cast<const u32x2*>(s8 + off8.kq(s));
+        const f32x4 scn = *reinterpret_cast<const f32x4*>(&sscale[wave][(j + 1) & 1][4 * g]);
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) {
+          if (s + kAhead < kKSteps)
+            raw[s + kAhead] = *reinterpret_cast<const u32x2*>(s8 + off8.kq(s + kAhead));
+          acc[2 * s] = mfma_k16(vt[2 * s], pt, acc[2 * s]);
+          acc[2 * s + 1] = mfma_k16(vt[2 * s + 1], pt, acc[2 * s + 1]);
+          ka[s] = e4m3x8_to_bf16(raw[s]);
+          *reinterpret_cast<bf16x8*>(mine + off.kq(s)) = ka[s];
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead + 1, 0);  // LDS reads
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) {
+          if (s + kAhead < kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU: conversion
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        scl = scn;
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): slot (j+1) & 1 is read
+        asm volatile("" ::: "memory");
+        if (j + 3 < my_tiles) issue(j + 3);
+      }
+    }
+    if (!workgroup_any(over, sflag, wave, kWaves)) break;
+  }
+
+  // Merge the four waves' states (as attn_rows_kernel): wave w's partial O
+  // goes to its own LDS area as [head][d] fp32, 16-byte columns XOR-ed by head.
+  const float l = group_sum4(lpart);
+  {
+    f32x4* po = reinterpret_cast<f32x4*>(mine);
+#pragma unroll
+    for (int dt = 0; dt < kDTiles; ++dt) {
+      const int col = (4 * dt + g) ^ n16;
+      po[n16 * (D / 4) + col] = acc[dt];
+    }
+    if (g == 0) {
+      sml[wave][0][n16] = m;
+      sml[wave][1][n16] = l;
+    }
+  }
+  barrier_lds();
+
+  const int hh = lane & 15;
+  const int sub = lane >> 4;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sml[w][0][hh]);
+  float wgt[kWaves];
+  float lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    wgt[w] = __builtin_amdgcn_exp2f(sml[w][0][hh] - M);  // 0 for a wave with no rows
+    lsum += wgt[w] * sml[w][1][hh];
+  }
+  const float inv = 1.0f / lsum;
+  constexpr int kPer = D / 64;
+  const int col0 = wave * (D / 16) + sub * kPer;
+  if (hh < nh) {
+    uint16_t* op = a.out + ((int64_t)t * a.H + h0 + hh) * D + 4 * col0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const f32x4* po = reinterpret_cast<const f32x4*>(smem + w * kWaveBytes);
+        s += wgt[w] * po[hh * (D / 4) + ((col0 + k) ^ hh)];
+      }
+      store_bf16x4(op + 4 * k, s, inv);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Quantising store: one wave per source row, D / 64 values per lane; row i
+// goes to pool row slots[i] (i when slots is null); a slot outside
+// [0, num_rows) skips the row.
+template <int D>
+__global__ void __launch_bounds__(256) quantize_fp8_kernel(QuantArgs a) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= a.n) return;  // wave-uniform
+  const int64_t slot = a.slots != nullptr ? (int64_t)a.slots[i] : i;
+  if (slot < 0 || slot >= a.num_rows) return;
+
+  const uint16_t* src = a.src + i * D + lane * E;
+  uint16_t xb[E];
+  if constexpr (E == 8) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xb[2 * e] = (uint16_t)(v[e] & 0xffff);
+      xb[2 * e + 1] = (uint16_t)(v[e] >> 16);
+    }
+  } else if constexpr (E == 4) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      xb[2 * e] = (uint16_t)(v[e] & 0xffff);
+      xb[2 * e + 1] = (uint16_t)(v[e] >> 16);
+    }
+  } else if constexpr (E == 2) {
+    const unsigned v = *reinterpret_cast<const unsigned*>(src);
+    xb[0] = (uint16_t)(v & 0xffff);
+    xb[1] = (uint16_t)(v >> 16);
+  } else {
+    xb[0] = src[0];
+  }
+  float x[E];
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    x[e] = __builtin_bit_cast(float, (unsigned)xb[e] << 16);
+    amax = fmaxf(amax, fabsf(x[e]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+
+  unsigned code[(E + 3) / 4];
+  float scale = 0.f;
+#pragma unroll
+  for (int c = 0; c < (E + 3) / 4; ++c) code[c] = 0;
+  if (amax >= 0x1p-64f) {  // else a zero row: scale 0, codes 0
+    scale = amax / 448.0f;
+    const float inv = 448.0f / amax;
+    float y[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) y[e] = fminf(fmaxf(x[e] * inv, -448.0f), 448.0f);
+#pragma unroll
+    for (int c = 0; c < (E + 3) / 4; ++c) {
+      const float y0 = y[4 * c];
+      const float y1 = 4 * c + 1 < E ? y[4 * c + 1] : 0.f;
+      unsigned w = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+      if (4 * c + 2 < E) {
+        const float y3 = 4 * c + 3 < E ? y[4 * c + 3] : 0.f;
+        w = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(y[4 * c + 2], y3, (int)w, true);
+      }
+      code[c] = w;
+    }
+  }
+  uint8_t* dst = a.kv8 + slot * D + lane * E;
+  if constexpr (E == 8) {
+    *reinterpret_cast<u32x2*>(dst) = u32x2{code[0], code[1]};
+  } else if constexpr (E == 4) {
+    *reinterpret_cast<unsigned*>(dst) = code[0];
+  } else if constexpr (E == 2) {
+    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(code[0] & 0xffff);
+  } else {
+    dst[0] = (uint8_t)(code[0] & 0xff);
+  }
+  if (lane == 0) a.kv_scale[slot] = scale;
+}
+
+template <int D>
+hipError_t launch_fp8_d(const AttnArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_rows_fp8_kernel<D>), dim3((unsigned)(a.N * a.head_groups)), dim3(256),
+                     0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_quant_d(const QuantArgs& a, hipStream_t stream) {
+  const long long blocks = ((long long)a.n + 3) / 4;
+  hipLaunchKernelGGL((quantize_fp8_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention_fp8(const AttnArgs& a, int D, hipStream_t stream) {
+  switch (D) {
+    case 64: return launch_fp8_d<64>(a, stream);
+    case 128: return launch_fp8_d<128>(a, stream);
+    case 256: return launch_fp8_d<256>(a, stream);
+    case 512: return launch_fp8_d<512>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_quantize_fp8(const QuantArgs& a, int D, hipStream_t stream) {
+  switch (D) {
+    case 64: return launch_quant_d<64>(a, stream);
+    case 128: return launch_quant_d<128>(a, stream);
+    case 256: return launch_quant_d<256>(a, stream);
+    case 512: return launch_quant_d<512>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace spd

@@ -52,6 +52,10 @@ struct AttnArgs {
   const int32_t* block_table;  // [N][max_blocks]
   int32_t topk, max_blocks, win, k_per_block, swa_pages;
   uint32_t comp_limit;         // min(max_blocks * k_per_block, 2^31)
+  // FP8 pool (sparse_decode_attn_fp8): row r is kv_scale[r] * e4m3(kv8[r][:]);
+  // kv is not read.
+  const uint8_t* kv8;          // [num_rows][D] OCP e4m3 codes
+  const float* kv_scale;       // [num_rows]
 };
 
 // Longest per-token list the paged entry point accepts (win + topk): the
@@ -59,6 +63,21 @@ struct AttnArgs {
 constexpr int kPagedMaxLen = 2048;
 
 hipError_t launch_attention(const AttnArgs& args, int D, const AttnPlan& plan, hipStream_t stream);
+
+// Attention over an FP8 pool: rows mode (workgroup = token x 16 heads), no
+// split; args.kv8 / args.kv_scale replace args.kv.
+hipError_t launch_attention_fp8(const AttnArgs& args, int D, hipStream_t stream);
+
+struct QuantArgs {
+  const uint16_t* src;   // [n][D] bf16 rows
+  const int32_t* slots;  // [n] destination rows, or null for 0 .. n-1
+  uint8_t* kv8;          // [num_rows][D] e4m3 codes (out)
+  float* kv_scale;       // [num_rows] (out)
+  int32_t n;
+  int64_t num_rows;
+};
+
+hipError_t launch_quantize_fp8(const QuantArgs& args, int D, hipStream_t stream);
 
 struct BuildArgs {
   const int32_t* state_slot;

@@ -31,6 +31,8 @@ def lib():
     L.spd_validate_indices.argtypes = [P, i64, P, i32, i64, ctypes.POINTER(ctypes.c_int64), P]
     L.sparse_decode_attn_paged.argtypes = [P, P, i64, P, P, P, i32, P, i32, i32, i32, i32, P,
                                            ctypes.c_float, P, i32, i32, i32, i32, P]
+    L.sparse_decode_attn_fp8.argtypes = [P, P, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32, P]
+    L.quantize_kv_fp8.argtypes = [P, P, i32, i32, P, P, i64, P]
     L.spd_status_string.argtypes = [ctypes.c_int]
     L.spd_status_string.restype = ctypes.c_char_p
     return L
@@ -185,3 +187,51 @@ def test_paged_attn_rejects_bad_arguments(lib):
     assert _paged(lib, win=1024, topk=1025) == UNSUPPORTED
     assert _paged(lib, N=0) == OK                   # empty batch: nothing to do
     assert _paged(lib, N=0, topk=0, cp=None, bt=None, mb=0) == OK
+
+
+def _fp8(lib, q=FAKE, kv=FAKE, sc=FAKE * 8192, rows=100, idx=FAKE, ptr=FAKE, sink=FAKE, scale=0.1,
+         out=FAKE * 4096, N=2, H=8, D=64):
+    return lib.sparse_decode_attn_fp8(q, kv, sc, rows, idx, ptr, sink, scale, out, N, H, D, None)
+
+
+def test_fp8_attn_rejects_bad_arguments(lib):
+    assert _fp8(lib, N=0) == OK                          # nothing to do
+    assert _fp8(lib, N=-1) == INVALID
+    assert _fp8(lib, rows=0) == INVALID
+    assert _fp8(lib, H=0) == INVALID
+    assert _fp8(lib, D=100) == UNSUPPORTED
+    assert _fp8(lib, H=2048) == UNSUPPORTED
+    assert _fp8(lib, scale=float("nan")) == INVALID
+    assert _fp8(lib, kv=None) == INVALID
+    assert _fp8(lib, sc=None) == INVALID
+    assert _fp8(lib, idx=None) == INVALID
+    assert _fp8(lib, kv=FAKE + 8) == INVALID           # codes must be 16-byte aligned
+    assert _fp8(lib, sc=FAKE * 8192 + 2) == INVALID    # scales 4-byte aligned
+    assert _fp8(lib, q=FAKE + 4) == INVALID
+    assert _fp8(lib, out=FAKE) == INVALID               # out overlaps q (both at FAKE)
+    assert _fp8(lib, out=FAKE * 8192) == INVALID        # out overlaps the scales
+    assert _fp8(lib, rows=1 << 41) == INVALID
+
+
+def _quant(lib, src=FAKE, slots=None, n=4, D=64, kv=FAKE * 4096, sc=FAKE * 8192, rows=100):
+    return lib.quantize_kv_fp8(src, slots, n, D, kv, sc, rows, None)
+
+
+def test_quantize_rejects_bad_arguments(lib):
+    assert _quant(lib, n=0) == OK
+    assert _quant(lib, n=-1) == INVALID
+    assert _quant(lib, rows=0) == INVALID
+    assert _quant(lib, D=0) == INVALID
+    assert _quant(lib, D=96) == UNSUPPORTED
+    assert _quant(lib, D=576) == UNSUPPORTED
+    assert _quant(lib, src=None) == INVALID
+    assert _quant(lib, kv=None) == INVALID
+    assert _quant(lib, sc=None) == INVALID
+    assert _quant(lib, src=FAKE + 8) == INVALID         # 16-byte alignment
+    assert _quant(lib, kv=FAKE * 4096 + 4) == INVALID
+    assert _quant(lib, sc=FAKE * 8192 + 1) == INVALID
+    assert _quant(lib, slots=FAKE * 16 + 2) == INVALID
+    assert _quant(lib, n=200, rows=100) == INVALID      # without slots, row i goes to row i
+    assert _quant(lib, kv=FAKE) == INVALID              # pool overlaps the source
+    assert _quant(lib, sc=FAKE * 4096 + 64 * 50) == INVALID   # scales inside the codes
+    assert _quant(lib, slots=FAKE * 8192, n=4) == INVALID     # slots overlap the scales

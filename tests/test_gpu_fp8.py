@@ -1,0 +1,179 @@
+"""GPU parity of the FP8 pool calls (through the C ABI):
+
+* quantize_kv_fp8 against the oracle's quantiser, bit for bit (codes and
+  scales): both take every rounding decision in fp32 with the same IEEE
+  operations;
+* sparse_decode_attn_fp8 against the oracle's attention over the same FP8 pool
+  (made by the oracle's quantiser from seeded bf16 rows), within
+  |d| <= 1e-2 + 1e-2 |ref|.
+
+Cases: every supported D, head counts that are not a multiple of 16, empty and
+ragged slices, a slice longer than the 2048 indices staged at a time, zero
+rows (scale 0), a -inf sink, rows planted late in a slice whose scores lie
+far above the first tile (the fixed reference maximum then takes the second
+pass), slots that scatter, skip and leave rows untouched, and the decode-base
+configuration at full size on sampled tokens."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import assert_close, bf16_to_f64, dev, device_csr, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def spd():
+    import sparse_paged_decode_ragged_amd as m
+    return m
+
+
+def to_dev_bits(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev()).view(torch.bfloat16)
+
+
+def rows_with_magnitudes(rng, n, D):
+    """bf16 rows of mixed scale: N(0, 1) times a per-row factor in [2^-30, 2^30],
+    plus zero rows, rows below the 2^-64 zero-row threshold, rows with
+    negative zeros and rows holding exact e4m3 ties."""
+    x = rng.standard_normal((n, D)).astype(np.float32)
+    x *= (2.0 ** rng.uniform(-30, 30, size=(n, 1))).astype(np.float32)
+    bits = W.bf16_bits(x)
+    bits[1] = 0                                   # a zero row
+    bits[2] = W.bf16_bits(x[2] * np.float32(2.0 ** -70) / np.abs(x[2]).max())  # amax < 2^-64
+    bits[3, ::2] = 0x8000                         # negative zeros in a nonzero row
+    # row 4: amax 448 (scale 1) and midpoints between consecutive e4m3 values
+    grid = np.array([oracle.e4m3_value(c) for c in range(0x7F)])
+    mids = ((grid[:-1] + grid[1:]) / 2).astype(np.float32)
+    row = rng.choice(mids, size=D).astype(np.float32) * np.where(rng.random(D) < 0.5, -1, 1)
+    row[0] = 448.0
+    bits[4] = W.bf16_bits(row)
+    return bits
+
+
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
+def test_quantize_matches_oracle_bit_for_bit(spd, D):
+    log("case fp8 quantize D=%d" % D)
+    rng = np.random.default_rng(100 + D)
+    n, P = 300, 420
+    bits = rows_with_magnitudes(rng, n, D)
+    slots = rng.permutation(P)[:n].astype(np.int32)
+    slots[7] = -1                                  # skipped
+    slots[8] = P + 3                               # skipped
+    codes_ref, scales_ref = oracle.quantize_fp8(bits)
+    kv8 = torch.full((P, D), 0x5A, dtype=torch.uint8, device=dev())
+    ksc = torch.full((P,), -1.0, dtype=torch.float32, device=dev())
+    spd.quantize_kv_fp8(to_dev_bits(bits), kv8, ksc, torch.from_numpy(slots).to(dev()))
+    torch.cuda.synchronize()
+    got_codes, got_scales = kv8.cpu().numpy(), ksc.cpu().numpy()
+    ok = (slots >= 0) & (slots < P)
+    assert np.array_equal(got_codes[slots[ok]], codes_ref[ok])
+    assert np.array_equal(got_scales[slots[ok]].view(np.uint32), scales_ref[ok].view(np.uint32))
+    untouched = np.setdiff1d(np.arange(P), slots[ok])
+    assert np.all(got_codes[untouched] == 0x5A) and np.all(got_scales[untouched] == -1.0)
+
+
+def test_quantize_without_slots(spd):
+    log("case fp8 quantize no slots")
+    rng = np.random.default_rng(7)
+    bits = rows_with_magnitudes(rng, 37, 512)
+    kv8 = torch.zeros((40, 512), dtype=torch.uint8, device=dev())
+    ksc = torch.zeros(40, dtype=torch.float32, device=dev())
+    spd.quantize_kv_fp8(to_dev_bits(bits), kv8.view(torch.float8_e4m3fn), ksc)
+    torch.cuda.synchronize()
+    codes_ref, scales_ref = oracle.quantize_fp8(bits)
+    assert np.array_equal(kv8.cpu().numpy()[:37], codes_ref)
+    assert np.array_equal(ksc.cpu().numpy()[:37], scales_ref)
+
+
+def fp8_pool(rng, P, D, zero_rows=None):
+    """(bf16 bits, codes, scales): seeded N(0, 1) rows quantised by the oracle;
+    zero_rows are zero."""
+    x = rng.standard_normal((P, D)).astype(np.float32)
+    if zero_rows is not None:
+        x[zero_rows] = 0.0
+    bits = W.bf16_bits(x)
+    codes, scales = oracle.quantize_fp8(bits)
+    return bits, codes, scales
+
+
+def run_fp8(spd, q_bits, codes, scales, idx, ptr, sink, scale):
+    q = to_dev_bits(q_bits)
+    kv8 = torch.from_numpy(codes).to(dev())
+    ksc = torch.from_numpy(scales).to(dev())
+    di, dp = device_csr(idx, ptr)
+    out = spd.sparse_decode_attn_fp8(q, kv8, ksc, di, dp, torch.from_numpy(sink).to(dev()), scale)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("seed,H,D,lengths", [
+    (1, 8, 64, [0, 1, 17, 64, 3]),
+    (2, 24, 128, [5, 0, 130, 16, 33]),
+    (3, 64, 256, [200, 1, 0, 64]),
+    (4, 64, 512, [640, 0, 15, 16, 17, 300]),
+    (5, 16, 512, [2500, 7]),                 # more than 2048 indices: staged twice
+    (6, 128, 512, [48, 96]),
+])
+def test_attention_matches_oracle(spd, seed, H, D, lengths):
+    log("case fp8 attention seed=%d H=%d D=%d L=%s" % (seed, H, D, lengths))
+    rng = np.random.default_rng(seed)
+    N, P = len(lengths), 3000
+    _, codes, scales = fp8_pool(rng, P, D, zero_rows=rng.choice(P, size=20, replace=False))
+    idx, ptr = W.csr_from_lists([rng.integers(0, P, size=L) for L in lengths])
+    q_bits = W.normal_bf16(rng, (N, H, D))
+    sink = rng.standard_normal(H).astype(np.float32)
+    sink[0] = -np.inf
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    out = run_fp8(spd, q_bits, codes, scales, idx, ptr, sink, scale)
+    ref = oracle.sparse_decode_attn_fp8(q_bits, codes, scales, idx, ptr, sink, scale)
+    assert_close(bf16_to_f64(out), ref, "fp8 H=%d D=%d" % (H, D))
+    empty = np.nonzero(np.diff(ptr) == 0)[0]
+    if len(empty):
+        assert torch.all(out[torch.from_numpy(empty).to(dev())].view(torch.int16) == 0)
+
+
+def test_attention_second_pass(spd):
+    """Rows planted late in a slice, parallel to q[t, 0], score far (> 64 in
+    log2 units) above the first tile, so the reference maximum fixed there is
+    left behind and the kernel redoes the state with the true maximum.  Two
+    planted rows of nearby scores keep the output a genuine mix of rows."""
+    log("case fp8 attention second pass")
+    rng = np.random.default_rng(11)
+    H, D, P = 32, 512, 4000
+    lengths = [300, 700, 40, 2100]
+    lists = [rng.choice(P, size=L, replace=False) for L in lengths]
+    idx, ptr = W.csr_from_lists(lists)
+    q_bits = W.normal_bf16(rng, (len(lengths), H, D))
+    q = W.bf16_to_f32(q_bits)
+    x = rng.standard_normal((P, D)).astype(np.float32)
+    plants = {0: (100, 290), 1: (150, 650), 3: (1000, 2090)}
+    for t, (p2, p1) in plants.items():
+        x[lists[t][p1]] = 4.0 * q[t, 0]            # score ~ 90 in log2 units
+        x[lists[t][p2]] = 3.9 * q[t, 0]            # about 2 lower
+    codes, scales = oracle.quantize_fp8(W.bf16_bits(x))
+    sink = rng.standard_normal(H).astype(np.float32)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    out = run_fp8(spd, q_bits, codes, scales, idx, ptr, sink, scale)
+    ref = oracle.sparse_decode_attn_fp8(q_bits, codes, scales, idx, ptr, sink, scale)
+    assert_close(bf16_to_f64(out), ref, "fp8 second pass")
+
+
+def test_decode_base_config(spd):
+    """decode_base (N=64, H=64, D=512, 640 rows a token) with its pool
+    quantised by the oracle; sampled tokens against the oracle."""
+    log("case fp8 decode_base")
+    w = W.decode_base()
+    b = w.builder
+    ptr, idx = oracle.build_decode_indices(b.state_slot, b.swa_len, b.comp_pos, b.block_table,
+                                           b.win, b.k_per_block, b.swa_pages)
+    codes, scales = oracle.quantize_fp8(w.kv_bits)
+    out = run_fp8(spd, w.q_bits, codes, scales, idx, ptr, w.attn_sink, w.softmax_scale)
+    tokens = np.array([0, 13, 40, 63])
+    sub = [idx[ptr[t]:ptr[t + 1]] for t in tokens]
+    sidx, sptr = W.csr_from_lists(sub)
+    ref = oracle.sparse_decode_attn_fp8(w.q_bits[tokens], codes, scales, sidx, sptr, w.attn_sink,
+                                        w.softmax_scale)
+    assert_close(bf16_to_f64(out[torch.from_numpy(tokens).to(dev())]), ref, "fp8 decode_base")
