@@ -16,7 +16,10 @@ graphs cover a remainder), timed with HIP events on the replay stream.
 
 Prints one JSON line: tokens/s for the whole job, gathered KV GB/s, the
 roofline record of the attention kernel, and the oracle timed on this host's
-cores on a bounded sample.
+cores on a bounded sample.  Two variants of the attention call are timed the
+same way and reported beside it: the page transform fused into the kernel
+(sparse_decode_attn_paged) and the call over an FP8 pool filled from the same
+bf16 rows by the quantising store (sparse_decode_attn_fp8).
 """
 from __future__ import annotations
 
@@ -49,6 +52,7 @@ def parse():
     p.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = automatic)")
     p.add_argument("--eager", action="store_true", help="launch kernels directly, no graphs")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-fp8", action="store_true", help="skip the FP8-pool measurement")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calibration-copy-mib", type=int, default=0,
                    help="also run a kernel of known traffic three times (bitwise_not over this "
@@ -247,8 +251,30 @@ def main():
                                      b.k_per_block, b.swa_pages, s["sink"], w.softmax_scale,
                                      out=s["out"], mode=mode)
 
+    # The attention call over an FP8 pool (e4m3 codes + one fp32 scale per row),
+    # each set's pool filled from its bf16 pool by the quantising store before
+    # timing; an FP8 pool is half the bytes, so twice the sets keep the touched
+    # footprint out of the Infinity Cache.
+    has_fp8 = not args.no_fp8 and args.split_rows == 0
+    fp8_sets = []
+    if has_fp8:
+        n8 = max(2, min(32, math.ceil(2 * MALL_BYTES / (w.P * D))))
+        for r in range(n8):
+            base = sets[r % n_sets]
+            kv8 = torch.empty((w.P, D), dtype=torch.uint8, device=dev)
+            ksc = torch.empty(w.P, dtype=torch.float32, device=dev)
+            spd.quantize_kv_fp8(base["kv"], kv8, ksc)
+            fp8_sets.append(dict(base, q=base["q"].clone(), kv8=kv8, ksc=ksc,
+                                 out=torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)))
+
+    def attn_fp8(s):
+        spd.sparse_decode_attn_fp8(s["q"], s["kv8"], s["ksc"], s["idx"], s["ptr"], s["sink"],
+                                   w.softmax_scale, out=s["out"])
+
     for s in sets:  # eager warm-up (and the indices the graphs will rebuild)
         step(s)
+    for s in fp8_sets:
+        attn_fp8(s)
     torch.cuda.synchronize()
     # One graph per set for each of (step, attention call), plus one graph that
     # holds every set's call back to back: the timed loops replay the latter,
@@ -269,17 +295,30 @@ def main():
                 for s in sets:
                     fn(s)
             chain[name] = g
+        if has_fp8:
+            single["fp8"] = []
+            for s in fp8_sets:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cs):
+                    attn_fp8(s)
+                single["fp8"].append(g)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cs):
+                for s in fp8_sets:
+                    attn_fp8(s)
+            chain["fp8"] = g
         torch.cuda.synchronize()
 
     def run_calls(k, name, fn):
         """Exactly k calls, rotating over the sets."""
+        group = fp8_sets if name == "fp8" else sets
         if args.eager:
             for i in range(k):
-                fn(sets[i % len(sets)])
+                fn(group[i % len(group)])
             return
-        for _ in range(k // len(sets)):
+        for _ in range(k // len(group)):
             chain[name].replay()
-        for i in range(k % len(sets)):
+        for i in range(k % len(group)):
             single[name][i].replay()
 
     def timed(k, name, fn):
@@ -315,6 +354,11 @@ def main():
     if has_paged:
         run_calls(min(args.warmup, 64), "paged", paged)
         us_paged = timed(n_attn, "paged", paged) * 1e3 / n_attn
+
+    us_fp8 = None
+    if has_fp8:
+        run_calls(min(args.warmup, 64), "fp8", attn_fp8)
+        us_fp8 = timed(n_attn, "fp8", attn_fp8) * 1e3 / n_attn
 
     indptr = sets[0]["ptr"].cpu().numpy()
     indices = sets[0]["idx"].cpu().numpy()[: indptr[-1]]
@@ -376,6 +420,16 @@ def main():
             "kernel": kernel_paged,
             "us_per_call": round(us_paged, 3), "bytes_per_call": int(b_paged),
             "achieved_GBps": round(ach_p, 1), "frac": round(ach_p / HBM_PEAK_GBPS, 4)}
+    if us_fp8 is not None:
+        # what the FP8 call must move: D code bytes and a 4-byte scale per
+        # gathered row, q, out, the indices, kv_indptr and the sinks
+        b_fp8 = ab["sum_L"] * (D + 4) + ab["qo_bytes"] + 4 * ab["sum_L"] + 4 * (N + 1) + 4 * H
+        ach8 = b_fp8 / (us_fp8 * 1e-6) / 1e9
+        rec["fp8_pool"] = {
+            "call": "sparse_decode_attn_fp8", "kernel": "attn_rows_fp8_kernel<%d>" % D,
+            "rotating_sets": len(fp8_sets), "us_per_call": round(us_fp8, 3),
+            "tokens_per_s": round(N / (us_fp8 * 1e-6), 1), "bytes_per_call": int(b_fp8),
+            "achieved_GBps": round(ach8, 1), "frac": round(ach8 / HBM_PEAK_GBPS, 4)}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, indptr, indices, args.cpu_seconds)
     print(json.dumps(rec))

@@ -21,14 +21,14 @@
 // token x 16 heads, its 4 waves take every 4th 16-row tile and merge their
 // states in LDS at the end):
 //   * a tile's rows are gathered as codes (D bytes a row, half a bf16 row) by
-//     LDS-DMA loads into one of two FP8 slots of the wave, together with the
-//     16 row scales;
-//   * the wave reads each tile once, in the K-operand pattern of
-//     S^T = K Q^T, and converts the codes to bf16 exactly (every e4m3 value is
-//     a bf16 value) with v_cvt_pk_f32_fp8; the converted values are the MFMA
-//     operand and are also written to a bf16 stage laid out as in attn.hip,
-//     from which the V^T operand is read with ds_read_b64_tr_b16.  This
-//     conversion of tile j+1 runs under the PV MFMAs of tile j;
+//     LDS-DMA loads into one of four FP8 slots of the wave, with the 16 row
+//     scales beside them, so three tiles are in flight while one is used;
+//   * the MFMAs stay bf16: the K operand of S^T = K Q^T is read from the slot
+//     in the MFMA's lane order (ds_read_b64) and the V^T operand of
+//     O^T += V^T P^T with the 8-bit transposing read ds_read_b64_tr_b8; both
+//     are converted to bf16 in registers by v_cvt_scalef32_pk_bf16_fp8 with
+//     scale 1, which is exact (every e4m3 value is a bf16 value).  Each tile
+//     costs 16 bytes of LDS reads per code and no LDS writes;
 //   * the scale multiplies its row's scores and its softmax weight, which
 //     becomes P' = bf16(p * scale); the denominator sums the unscaled p.
 #include "attn_device.h"
@@ -38,29 +38,24 @@ namespace {
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 LdsV2i32;
 
-// Eight e4m3 codes (bytes of raw, in order) -> eight bf16 values, exactly:
-// v_cvt_pk_f32_fp8 decodes two codes to fp32, and the top half of each such
-// fp32 is its bf16 value (an e4m3 value has at most 4 significant bits and an
-// exponent well inside the bf16 range).  (The vector elements are copied to
-// scalars before __builtin_bit_cast: applied to a subscripted vector element
-// directly, this clang reads element 0 whatever the subscript.)
-__device__ __forceinline__ unsigned bf16_pair_of(float lo, float hi) {
-  return __builtin_amdgcn_perm(__builtin_bit_cast(unsigned, hi), __builtin_bit_cast(unsigned, lo),
-                               0x07060302u);  // top halves of lo (bits 0-15) and hi
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Four e4m3 codes (bytes of raw, in order) -> four bf16 values, exactly
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1 decodes two codes per instruction;
+// an e4m3 value has at most 4 significant bits and an exponent well inside
+// the bf16 range).
+__device__ __forceinline__ bf16x4 e4m3x4_to_bf16(unsigned raw) {
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw, 1.0f, false);  // bytes 0, 1
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw, 1.0f, true);   // bytes 2, 3
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
 }
 
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 raw) {
-  u32x4 w;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[h], false);  // bytes 0, 1
-    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[h], true);   // bytes 2, 3
-    const float b0 = lo[0], b1 = lo[1], b2 = hi[0], b3 = hi[1];
-    w[2 * h] = bf16_pair_of(b0, b1);
-    w[2 * h + 1] = bf16_pair_of(b2, b3);
-  }
-  return __builtin_bit_cast(bf16x8, w);
+  return __builtin_shufflevector(e4m3x4_to_bf16(raw[0]), e4m3x4_to_bf16(raw[1]), 0, 1, 2, 3, 4,
+                                 5, 6, 7);
 }
 
 // Byte offsets of the K-operand read of an FP8 tile (16 rows of D codes; the
@@ -81,6 +76,36 @@ struct Fp8Offsets {
     for (int u = 0; u < kN; ++u) k[u] = n16 * D + 32 * (u ^ (w >> 1)) + 16 * (w & 1) + 8 * (g & 1);
   }
   __device__ __forceinline__ int kq(int s) const { return k[s & 7] + 256 * (s >> 3); }
+};
+
+// Byte offsets of the V^T reads (ds_read_b64_tr_b8) of an FP8 tile.  Within
+// each 16-lane group the read gives destination lane i byte e from source
+// lane 2e + i/8, byte i % 8.  Source lane (n16, g), with e = n16 / 2 and
+// b = n16 % 2, points at row 4g + e % 4, columns 16 c + 8b .. + 7 of logical
+// chunk c = dt + kPair * (e / 4): destination lane (i, g) then holds rows
+// 4g .. 4g+3 of column 16 dt + i in bytes 0-3 and of column 16 (dt + kPair) + i
+// in bytes 4-7, the V^T operands of two 16x16x16 MFMAs (d-tiles dt and
+// dt + kPair).  Pair pp covers dt = 2 kPair (pp / kPair) + pp % kPair.  With
+// kPair = 8 (D >= 256) the 16 (row, chunk) reads of each half-wave fall on
+// distinct 4-bank groups.  With sw = the row's swizzle (< 2 kPair), the read of
+// pair pp is at v[pp % kPair] + 32 kPair (pp / kPair) bytes.
+template <int D>
+struct Fp8VtOffsets {
+  static constexpr int kDTiles = D / 16;
+  static constexpr int kPair = kDTiles / 2 < 8 ? kDTiles / 2 : 8;
+  int v[kPair];
+  __device__ __forceinline__ Fp8VtOffsets(int n16, int g) {
+    const int e = n16 >> 1, b = n16 & 1;
+    const int r = 4 * g + (e & 3), h = e >> 2;
+    const int sw = row_swizzle(r) & (kDTiles - 1);
+#pragma unroll
+    for (int u = 0; u < kPair; ++u)
+      v[u] = r * D + 16 * (kPair * (h ^ (sw / kPair)) + (u ^ (sw % kPair))) + 8 * b;
+  }
+  __device__ __forceinline__ int pair(int pp) const {
+    return v[pp % kPair] + 32 * kPair * (pp / kPair);
+  }
+  static constexpr int first_dtile(int pp) { return 2 * kPair * (pp / kPair) + pp % kPair; }
 };
 
 // The scales of the 16 rows of a tile (staged indices from sidx[p0]; positions
@@ -126,21 +151,22 @@ template <int D>
 __global__ void __launch_bounds__(256) attn_rows_fp8_kernel(AttnArgs a) {
   constexpr int kWaves = 4;
   constexpr int kTile = 16;
-  constexpr int kKSteps = D / 32;
+  constexpr int kKSteps = D / 32;             // also the V^T read pairs of a tile
   constexpr int kDTiles = D / 16;
+  constexpr int kSlots = 4;                   // FP8 tile slots per wave
   constexpr int kLoads = kTile * D / 1024;    // LDS-DMA ops per FP8 tile
   constexpr int kPerTile = kLoads + 1;        // and the scale load
-  constexpr int kStageBytes = kTile * 2 * D;  // bf16 stage
-  constexpr int kSlotBytes = kTile * D;       // FP8 slot
-  constexpr int kWaveBytes = kStageBytes + 2 * kSlotBytes;
-  constexpr int kAhead = kKSteps < 4 ? kKSteps : 4;  // FP8 reads issued ahead of use
+  constexpr int kSlotBytes = kTile * D;
+  constexpr int kWaveBytes = kSlots * kSlotBytes;
+  constexpr int kAhead = kKSteps < 4 ? kKSteps : 4;  // LDS reads issued ahead of use
   static_assert(kWaveBytes == 16 * D * 4, "partial O must fit the wave's LDS");
-  static_assert(kLoads >= 1 && 2 * kPerTile < 64, "bad load count");
+  static_assert(kLoads >= 1 && (kSlots - 1) * kPerTile < 64, "bad load count");
+  using Vt = Fp8VtOffsets<D>;
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kWaves * kWaveBytes];
   __shared__ __attribute__((aligned(256))) int sidx[kIdxCap];
   __shared__ __attribute__((aligned(256))) float ssink[64];
-  __shared__ __attribute__((aligned(256))) float sscale[kWaves][2][64];
+  __shared__ __attribute__((aligned(256))) float sscale[kWaves][kSlots][64];
   __shared__ float sml[kWaves][2][16];
   __shared__ int sflag[kWaves];
 
@@ -171,11 +197,10 @@ __global__ void __launch_bounds__(256) attn_rows_fp8_kernel(AttnArgs a) {
   load_q<D>(a.q, (int64_t)t * a.H + (hvalid ? h : 0), g, qreg);
   stage_sinks(a.sink, a.H, h0, ssink, wave, lane);
 
-  unsigned char* mine = smem + wave * kWaveBytes;  // bf16 stage, then the two FP8 slots
-  unsigned char* slots = mine + kStageBytes;
+  unsigned char* mine = smem + wave * kWaveBytes;  // the wave's FP8 slots
   const uint16_t* kv8 = reinterpret_cast<const uint16_t*>(a.kv8);  // rows of D bytes
-  const TileOffsets<D> off(n16, g);
   const Fp8Offsets<D> off8(n16, g);
+  const Vt offv(n16, g);
 
   float m = -INFINITY, lpart = 0.f, mtrue = -INFINITY, sink_l2 = -INFINITY;
   f32x4 acc[kDTiles];
@@ -203,59 +228,66 @@ __global__ void __launch_bounds__(256) attn_rows_fp8_kernel(AttnArgs a) {
       const int ntiles = (n + kTile - 1) / kTile;
       const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
 
-      auto issue = [&](int j) {  // this wave's j-th tile = global tile wave + 4j
+      auto issue = [&](int j) {  // this wave's j-th tile = global tile wave + 4j, slot j % 4
         const int p0 = (wave + kWaves * j) * kTile;
-        issue_rows<D, kLoads>(kv8, sidx, n, p0, 0, slots + (j & 1) * kSlotBytes, lane);
-        issue_scales(a.kv_scale, sidx, n, p0, sscale[wave][j & 1], lane);
+        issue_rows<D, kLoads>(kv8, sidx, n, p0, 0, mine + (j % kSlots) * kSlotBytes, lane);
+        issue_scales(a.kv_scale, sidx, n, p0, sscale[wave][j % kSlots], lane);
       };
-
-      // Pipeline over this wave's tiles: one bf16 stage, two FP8 slots.  In
-      // iteration j: S^T of tile j (K operand in registers) with the V^T reads
-      // of tile j from the stage; softmax; then the PV MFMAs of tile j with the
-      // conversion of tile j+1 (FP8 slot -> K operand registers + stage), after
-      // which that slot takes the loads of tile j+3.
-      bf16x8 ka[kKSteps];
-      f32x4 scl = {0.f, 0.f, 0.f, 0.f};  // scales of rows 4g .. 4g+3 of the current tile
-      if (my_tiles > 0) issue(0);
-      if (my_tiles > 1) issue(1);
-      if (my_tiles > 0) {
-        if (my_tiles > 1)
+      // Wait until tile j has landed.  Every tile up to j + 3 (below my_tiles)
+      // has been issued by then, in order, so exactly those after j may stay
+      // in flight.
+      auto wait_tile = [&](int j) {
+        const int later = my_tiles - 1 - j;
+        if (later >= 3)
+          wait_vmcnt<3 * kPerTile>();
+        else if (later == 2)
+          wait_vmcnt<2 * kPerTile>();
+        else if (later == 1)
           wait_vmcnt<kPerTile>();
         else
           wait_vmcnt<0>();
+      };
+
+      // Pipeline over this wave's tiles, four slots: in iteration j, S^T of
+      // tile j (K operand in registers) with the V^T reads of tile j; once
+      // those reads are done the slot takes the loads of tile j+4; then the PV
+      // MFMAs of tile j with the K-operand reads of tile j+1.
+      bf16x8 ka[kKSteps];
+      f32x4 scl = {0.f, 0.f, 0.f, 0.f};  // scales of rows 4g .. 4g+3 of the current tile
+#pragma unroll
+      for (int j = 0; j < kSlots; ++j)  // tiles 0 .. 3 fill the four slots
+        if (j < my_tiles) issue(j);
+      if (my_tiles > 0) {
+        wait_tile(0);
         asm volatile("" ::: "memory");
         u32x2 raw[kKSteps];
 #pragma unroll
-        for (int s = 0; s < kKSteps; ++s) raw[s] = *reinterpret_cast<const u32x2*>(slots + off8.kq(s));
+        for (int s = 0; s < kKSteps; ++s) raw[s] = *reinterpret_cast<const u32x2*>(mine + off8.kq(s));
         scl = *reinterpret_cast<const f32x4*>(&sscale[wave][0][4 * g]);
 #pragma unroll
-        for (int s = 0; s < kKSteps; ++s) {
-          ka[s] = e4m3x8_to_bf16(raw[s]);
-          *reinterpret_cast<bf16x8*>(mine + off.kq(s)) = ka[s];
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): slot 0 is read
-        asm volatile("" ::: "memory");
-        if (my_tiles > 2) issue(2);
+        for (int s = 0; s < kKSteps; ++s) ka[s] = e4m3x8_to_bf16(raw[s]);
       }
       for (int j = 0; j < my_tiles; ++j) {
+        const unsigned char* st = mine + (j % kSlots) * kSlotBytes;
         const int nvalid = n - (wave + kWaves * j) * kTile;
         constexpr int kCh = kKSteps < 4 ? kKSteps : 4;  // independent QK chains
         f32x4 part_s[kCh];
 #pragma unroll
         for (int c = 0; c < kCh; ++c) part_s[c] = f32x4{0.f, 0.f, 0.f, 0.f};
         bf16x4 vt[kDTiles];
+        u32x2 vraw[kKSteps];
         __builtin_amdgcn_sched_barrier(0);
+        // S^T = K Q^T (four chains) with the V^T reads of the same tile
 #pragma unroll
         for (int s = 0; s < kKSteps; ++s) {
           part_s[s % kCh] = mfma_k32(ka[s], qreg[s], part_s[s % kCh]);
-          vt[2 * s] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(mine + off.vt(2 * s)));
-          vt[2 * s + 1] =
-              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(mine + off.vt(2 * s + 1)));
+          vraw[s] = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((LdsV2i32*)(st + offv.pair(s))));
         }
 #pragma unroll
         for (int s = 0; s < kKSteps; ++s) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
         }
         __builtin_amdgcn_sched_barrier(0);
         f32x4 sa = part_s[0];
@@ -270,46 +302,43 @@ __global__ void __launch_bounds__(256) attn_rows_fp8_kernel(AttnArgs a) {
         bf16x4 pt;
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) pt[i4] = (__bf16)(pf[i4] * scl[i4]);
-        // The stage's transposing reads are complete: it may take tile j+1.
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) {
+          vt[Vt::first_dtile(s)] = e4m3x4_to_bf16(vraw[s][0]);
+          vt[Vt::first_dtile(s) + Vt::kPair] = e4m3x4_to_bf16(vraw[s][1]);
+        }
+        // Every read of tile j's slot is complete: it takes the loads of tile j+4.
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         asm volatile("" ::: "memory");
-        if (j + 1 < my_tiles) {  // tile j+1 has landed once only tile j+2 may be outstanding
-          if (j + 2 < my_tiles)
-            wait_vmcnt<kPerTile>();
-          else
-            wait_vmcnt<0>();
-        }
+        if (j + kSlots < my_tiles) issue(j + kSlots);
+        if (j + 1 < my_tiles) wait_tile(j + 1);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        // O^T += V^T P^T, with the conversion of tile j+1 (after the last tile
-        // it converts a stale slot: in bounds, and the values are unused).
-        const unsigned char* s8 = slots + ((j + 1) & 1) * kSlotBytes;
-        u32x2 raw[kKSteps];
+        // O^T += V^T P^T with the K-operand reads of tile j+1 (after the last
+        // tile they read a slot with no load in flight: in bounds, unused).
+        const unsigned char* sn = mine + ((j + 1) % kSlots) * kSlotBytes;
+        u32x2 kraw[kKSteps];
 #pragma unroll
-        for (int s = 0; s < kAhead; ++s) raw[s] = *reinterpret_cast<const u32x2*>(s8 + off8.kq(s));
-        const f32x4 scn = *reinterpret_cast<const f32x4*>(&sscale[wave][(j + 1) & 1][4 * g]);
+        for (int s = 0; s < kAhead; ++s) kraw[s] = *reinterpret_cast<const u32x2*>(sn + off8.kq(s));
+        const f32x4 scn = *reinterpret_cast<const f32x4*>(&sscale[wave][(j + 1) % kSlots][4 * g]);
 #pragma unroll
         for (int s = 0; s < kKSteps; ++s) {
           if (s + kAhead < kKSteps)
-            raw[s + kAhead] = *reinterpret_cast<const u32x2*>(s8 + off8.kq(s + kAhead));
-          acc[2 * s] = mfma_k16(vt[2 * s], pt, acc[2 * s]);
-          acc[2 * s + 1] = mfma_k16(vt[2 * s + 1], pt, acc[2 * s + 1]);
-          ka[s] = e4m3x8_to_bf16(raw[s]);
-          *reinterpret_cast<bf16x8*>(mine + off.kq(s)) = ka[s];
+            kraw[s + kAhead] = *reinterpret_cast<const u32x2*>(sn + off8.kq(s + kAhead));
+          const int d0 = Vt::first_dtile(s);
+          acc[d0] = mfma_k16(vt[d0], pt, acc[d0]);
+          acc[d0 + Vt::kPair] = mfma_k16(vt[d0 + Vt::kPair], pt, acc[d0 + Vt::kPair]);
+          ka[s] = e4m3x8_to_bf16(kraw[s]);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, kAhead + 1, 0);  // LDS reads
 #pragma unroll
         for (int s = 0; s < kKSteps; ++s) {
           if (s + kAhead < kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU: conversion
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU: conversion
         }
         __builtin_amdgcn_sched_barrier(0);
         scl = scn;
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): slot (j+1) & 1 is read
-        asm volatile("" ::: "memory");
-        if (j + 3 < my_tiles) issue(j + 3);
       }
     }
     if (!workgroup_any(over, sflag, wave, kWaves)) break;

@@ -135,6 +135,24 @@ def test_attention_matches_oracle(spd, seed, H, D, lengths):
         assert torch.all(out[torch.from_numpy(empty).to(dev())].view(torch.int16) == 0)
 
 
+def test_every_code_decodes_exactly(spd):
+    """Single-row slices and no sink: the output is the row itself,
+    scale * e4m3(code), which bf16 holds exactly for a power-of-two scale.  The
+    rows hold every finite code (subnormals and both zeros included), each code
+    in several column positions, so every conversion path must be exact."""
+    log("case fp8 every code")
+    H, D, P = 16, 512, 8
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    codes = np.stack([np.resize(np.roll(finite, 37 * r), D) for r in range(P)]).astype(np.uint8)
+    scales = (2.0 ** np.arange(-4, 4)).astype(np.float32)
+    idx, ptr = W.csr_from_lists([[r] for r in range(P)])
+    q_bits = W.normal_bf16(np.random.default_rng(5), (P, H, D))
+    sink = np.full(H, -np.inf, dtype=np.float32)
+    out = run_fp8(spd, q_bits, codes, scales, idx, ptr, sink, 0.05)
+    ref = oracle.sparse_decode_attn_fp8(q_bits, codes, scales, idx, ptr, sink, 0.05)
+    assert np.array_equal(bf16_to_f64(out), ref)
+
+
 def test_attention_second_pass(spd):
     """Rows planted late in a slice, parallel to q[t, 0], score far (> 64 in
     log2 units) above the first tile, so the reference maximum fixed there is
