@@ -11,9 +11,8 @@
 // loads before it consumes any of them, so each costs one or two memory round
 // trips however long comp_pos is (a kernel boundary costs a few microseconds,
 // so small batches get one launch):
-//   small batches (N <= 1024, N * topk <= 2^16): one launch; workgroup b counts
-//     every token up to its own sixteen (so it needs no other workgroup's
-//     result), writes their kv_indptr entries and scatters them;
+//   batches of one workgroup (N <= 16, N * topk <= 2^16): one launch that
+//     counts every token, writes kv_indptr and scatters them;
 //   otherwise:
 //     1. count+scan (N <= 1024, N * topk <= 2^18): one 1024-thread workgroup
 //        counts every token's entries (window length + valid comp_pos entries)
@@ -29,6 +28,11 @@ namespace {
 constexpr int kBatch = 8;           // comp_pos entries per lane in flight (512 per wave)
 constexpr int kSmallN = 1024;       // largest batch counted by the single-workgroup kernel
 constexpr int kFusedEntries = 1 << 16;  // largest N * topk built by the one-launch kernel
+// Largest batch built by the one-launch kernel: one workgroup.  Beyond it each
+// workgroup recounts every earlier token and the launch saved no longer pays
+// (64 tokens x 512 entries: 10.1 us in one launch, 8.4 us as count+scan and
+// scatter).
+constexpr int kFusedMaxN = 16;
 
 __device__ __forceinline__ int clamp_swa(int v, int win) { return v < 0 ? 0 : (v > win ? win : v); }
 
@@ -322,8 +326,9 @@ __device__ __forceinline__ void count_flat(const BuildArgs& a, int last, int* cn
   }
 }
 
-// Small batches (N <= 1024, N * topk <= kFusedEntries): the whole builder in
-// one launch.  Workgroup b (16 waves) owns tokens 16b .. 16b+15, one per wave,
+// Batches of one workgroup (N <= kFusedMaxN, N * topk <= kFusedEntries; the
+// kernel itself is correct for any N <= kSmallN): the whole builder in one
+// launch.  Workgroup b (16 waves) owns tokens 16b .. 16b+15, one per wave,
 // and counts every token up to its last one itself, so it knows its prefix
 // without waiting for any other workgroup; then each wave writes its token's
 // kv_indptr entry and scatters the token.
@@ -392,7 +397,7 @@ hipError_t launch_build_indices(const BuildArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(build_count_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
     return hipGetLastError();
   }
-  if (a.N <= kSmallN && (int64_t)a.N * (a.comp_pos ? a.topk : 0) <= kFusedEntries) {
+  if (a.N <= kFusedMaxN && (int64_t)a.N * (a.comp_pos ? a.topk : 0) <= kFusedEntries) {
     hipLaunchKernelGGL(build_fused_small_kernel, dim3((unsigned)((a.N + 15) / 16)), dim3(1024), 0,
                        stream, a);
     return hipGetLastError();

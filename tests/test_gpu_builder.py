@@ -38,6 +38,8 @@ def check(spd, b: W.BuilderInputs, what: str):
     (4, 3000, 8, 70, 16, 5, 40),      # several 1024-token scan chunks
     (5, 1025, 128, 64, 64, 1, 100),
     (6, 200, 64, 512, 8, 64, 100),    # N * topk above the one-launch limit, N <= 1024
+    (7, 2, 8, 5000, 4, 1300, 500),    # one-launch kernel: a wave's part spans 3 batches
+    (8, 3, 8, 2047, 2, 1100, 300),    # the same with rows of one entry per load
 ])
 def test_random_bit_exact(spd, seed, N, win, topk, k, mb, nb):
     check(spd, random_builder_inputs(seed, N, win, topk, k, mb, nb), "random N=%d" % N)
