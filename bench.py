@@ -66,13 +66,19 @@ def parse():
     return p.parse_args()
 
 
-def kernel_sources_digest() -> str:
-    """sha256 over the attention kernel's sources: a traffic figure taken from
-    counters is only reported while these are unchanged."""
+def kernel_sources(kernel: str) -> tuple:
+    """The source files an attention kernel is built from."""
+    main = "attn_fp8.hip" if "fp8" in kernel else "attn.hip"
+    return (main, "attn_device.h", "spd_internal.h")
+
+
+def kernel_sources_digest(kernel: str) -> str:
+    """sha256 over the kernel's sources: a traffic figure taken from counters is
+    only reported while these are unchanged."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_paged_decode_ragged_amd", "csrc")
-    for name in ("attn.hip", "spd_internal.h"):
+    for name in kernel_sources(kernel):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -81,8 +87,9 @@ def kernel_sources_digest() -> str:
 
 
 def recorded_traffic(kernel: str, workload: str):
-    """Per-launch HBM bytes of `kernel` from the committed counter summary, or
-    None when there is none or the kernel sources changed since it was taken."""
+    """Per-launch HBM bytes of `kernel` from the committed counter summary
+    profiles/hbm_traffic_<workload>.md, or None when there is none or the
+    kernel sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.md" % workload)
     if not os.path.exists(path):
         return None
@@ -93,7 +100,7 @@ def recorded_traffic(kernel: str, workload: str):
                 k, v = line[2:].strip().split(": ", 1)
                 fields[k.strip("`")] = v.strip().strip("`")
     if (fields.get("kernel") != kernel or fields.get("workload") != workload
-            or fields.get("source_digest") != kernel_sources_digest()):
+            or fields.get("source_digest") != kernel_sources_digest(kernel)):
         return None
     try:
         return float(fields["traffic_bytes_per_launch"])
@@ -428,6 +435,7 @@ def main():
         rec["fp8_pool"] = {
             "call": "sparse_decode_attn_fp8", "kernel": "attn_rows_fp8_kernel<%d>" % D,
             "rotating_sets": len(fp8_sets), "us_per_call": round(us_fp8, 3),
+            "traffic": recorded_traffic("attn_rows_fp8_kernel<%d>" % D, args.workload + "_fp8"),
             "tokens_per_s": round(N / (us_fp8 * 1e-6), 1), "bytes_per_call": int(b_fp8),
             "achieved_GBps": round(ach8, 1), "frac": round(ach8 / HBM_PEAK_GBPS, 4)}
     if not args.no_cpu_baseline:
