@@ -56,6 +56,9 @@ def _load() -> ctypes.CDLL:
         lib.spd_oracle_sparse_decode_attn_fp8.restype = ctypes.c_int
         lib.spd_oracle_quantize_fp8.argtypes = [P, i32, i32, P, P]
         lib.spd_oracle_quantize_fp8.restype = ctypes.c_int
+        lib.spd_oracle_qk_norm_rope.argtypes = [P, P, P, P, ctypes.c_float, P, P, i32, i32, P, i32,
+                                                i32, i32, i32, P, P, P]
+        lib.spd_oracle_qk_norm_rope.restype = ctypes.c_int
         lib.spd_oracle_e4m3_value.argtypes = [ctypes.c_int]
         lib.spd_oracle_e4m3_value.restype = ctypes.c_double
         lib.spd_oracle_set_threads.argtypes = [ctypes.c_int]
@@ -154,6 +157,38 @@ def sparse_decode_attn_fp8(q_bits: np.ndarray, kv_codes: np.ndarray, kv_scale: n
     if rc != 0:
         raise ValueError("oracle rejected its input (code %d)" % rc)
     return out
+
+
+def qk_norm_rope(q_bits: np.ndarray, kv_bits: np.ndarray, q_weight: np.ndarray,
+                 kv_weight: np.ndarray, eps: float, positions: np.ndarray, cos_sin: np.ndarray,
+                 state_slot: np.ndarray, win: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """The decode-step producer (steps in the C source): q [N, H, D] and kv [N, D] as
+    bf16 bits, fp32 weights [D], positions [N], cos_sin [max_pos, rope_dim] fp32.
+    Returns (q_out [N, H, D] fp64, kv_out [N, D] fp64, ring slot [N] int64; -1 and
+    zero rows for a position outside the table)."""
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    kv_bits = np.ascontiguousarray(kv_bits, dtype=np.uint16)
+    q_weight = np.ascontiguousarray(q_weight, dtype=np.float32)
+    kv_weight = np.ascontiguousarray(kv_weight, dtype=np.float32)
+    positions = np.ascontiguousarray(positions, dtype=np.int32)
+    cos_sin = np.ascontiguousarray(cos_sin, dtype=np.float32)
+    state_slot = np.ascontiguousarray(state_slot, dtype=np.int32)
+    N, H, D = q_bits.shape
+    max_pos, rope_dim = cos_sin.shape
+    assert kv_bits.shape == (N, D) and q_weight.shape == (D,) and kv_weight.shape == (D,)
+    assert positions.shape == (N,) and state_slot.shape == (N,)
+    q_out = np.zeros((N, H, D), dtype=np.float64)
+    kv_out = np.zeros((N, D), dtype=np.float64)
+    slot = np.zeros(N, dtype=np.int64)
+    if cos_sin.size == 0:
+        cos_sin = np.zeros(1, dtype=np.float32)
+    rc = _load().spd_oracle_qk_norm_rope(_ptr(q_bits), _ptr(kv_bits), _ptr(q_weight),
+                                         _ptr(kv_weight), float(eps), _ptr(positions),
+                                         _ptr(cos_sin), max_pos, rope_dim, _ptr(state_slot),
+                                         int(win), N, H, D, _ptr(q_out), _ptr(kv_out), _ptr(slot))
+    if rc != 0:
+        raise ValueError("oracle rejected its input (code %d)" % rc)
+    return q_out, kv_out, slot
 
 
 def build_decode_indices(state_slot: np.ndarray, swa_len: np.ndarray,

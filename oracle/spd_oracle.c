@@ -337,3 +337,67 @@ int spd_oracle_build_decode_indices(const int32_t* state_slot, const int32_t* sw
   }
   return 0;
 }
+
+/*
+ * Producer of the decode step: per-head RMSNorm of q, RMSNorm of the token's
+ * new KV row, rotary embedding of both, and the ring slot the KV row is
+ * stored in (sglang PR #25898 summary page, "key files": one kernel does the
+ * q per-head RMSNorm, the KV RMSNorm, RoPE, the FP8 quantisation and the paged
+ * sliding-window store; its helpers are a batched RMSNorm, a GPT-J rotation
+ * and a batched RoPE).  Readings (the page names the steps, not their
+ * formulas):
+ *   RMSNorm of a row x[0, D) with weight w:  x_d * w_d / sqrt(mean_d(x_d^2) + eps)
+ *   RoPE, GPT-J (interleaved) pairs on the last rope_dim entries (o = D - rope_dim):
+ *     for i < rope_dim / 2, c = cos_sin[p][i], s = cos_sin[p][rope_dim/2 + i],
+ *     (y[o+2i], y[o+2i+1]) <- (y[o+2i] c - y[o+2i+1] s, y[o+2i] s + y[o+2i+1] c)
+ *   where p = positions[t] and cos_sin is the caller's table [max_pos][rope_dim];
+ *   the KV row's ring slot: state_slot[t] * win + p mod win (the window ring
+ *   holds positions p - win + 1 .. p, slot p mod win).
+ * Outputs in fp64, unrounded: q_out [N][H][D], kv_out [N][D], slot_out [N].
+ * A token with p outside [0, max_pos) gets slot_out = -1 and zero rows.
+ */
+static void norm_rope_row(const uint16_t* x, const float* w, double eps, const float* cs,
+                          int32_t rope_dim, int32_t D, double* y) {
+  double ss = 0.0;
+  for (int32_t d = 0; d < D; ++d) {
+    const double v = bf16_bits_to_double(x[d]);
+    ss += v * v;
+  }
+  const double inv = 1.0 / sqrt(ss / D + eps);
+  for (int32_t d = 0; d < D; ++d) y[d] = bf16_bits_to_double(x[d]) * inv * (double)w[d];
+  const int32_t o = D - rope_dim, half = rope_dim / 2;
+  for (int32_t i = 0; i < half; ++i) {
+    const double c = cs[i], s = cs[half + i];
+    const double a = y[o + 2 * i], b = y[o + 2 * i + 1];
+    y[o + 2 * i] = a * c - b * s;
+    y[o + 2 * i + 1] = a * s + b * c;
+  }
+}
+
+int spd_oracle_qk_norm_rope(const uint16_t* q, const uint16_t* kv, const float* q_weight,
+                            const float* kv_weight, float eps, const int32_t* positions,
+                            const float* cos_sin, int32_t max_pos, int32_t rope_dim,
+                            const int32_t* state_slot, int32_t win, int32_t N, int32_t H,
+                            int32_t D, double* q_out, double* kv_out, int64_t* slot_out) {
+  if (N < 0 || H <= 0 || D <= 0 || rope_dim < 0 || rope_dim > D || (rope_dim & 1) || win <= 0 ||
+      max_pos < 0 || !(eps >= 0.0f))
+    return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t t = 0; t < N; ++t) {
+    const int32_t p = positions[t];
+    if (p < 0 || p >= max_pos) {
+      memset(q_out + (int64_t)t * H * D, 0, sizeof(double) * (size_t)H * D);
+      memset(kv_out + (int64_t)t * D, 0, sizeof(double) * (size_t)D);
+      slot_out[t] = -1;
+      continue;
+    }
+    const float* cs = cos_sin + (int64_t)p * rope_dim;
+    for (int32_t h = 0; h < H; ++h)
+      norm_rope_row(q + ((int64_t)t * H + h) * D, q_weight, (double)eps, cs, rope_dim, D,
+                    q_out + ((int64_t)t * H + h) * D);
+    norm_rope_row(kv + (int64_t)t * D, kv_weight, (double)eps, cs, rope_dim, D,
+                  kv_out + (int64_t)t * D);
+    slot_out[t] = (int64_t)state_slot[t] * win + p % win;
+  }
+  return 0;
+}
