@@ -282,6 +282,43 @@ SPD_API spd_status quantize_kv_fp8(const void* src, const int32_t* slots, int32_
                                    void* kv_fp8, float* kv_scale, int64_t num_rows, void* stream);
 
 /*
+ * The decode-step producer: writes the rows the attention reads.  sglang PR
+ * #25898 summary page, "key files": one fused kernel does the q per-head
+ * RMSNorm, the KV RMSNorm, RoPE, the FP8 quantisation and the paged
+ * sliding-window store.  For each token t with position p = positions[t]:
+ *
+ *   RMSNorm(x, w) = x_d * w_d / sqrt(mean_d(x_d^2) + eps)        (fp32)
+ *   RoPE: on the last rope_dim entries (o = D - rope_dim), GPT-J pairs:
+ *     for i < rope_dim/2, c = cos_sin[p][i], s = cos_sin[p][rope_dim/2 + i]:
+ *     (y[o+2i], y[o+2i+1]) <- (y[o+2i] c - y[o+2i+1] s, y[o+2i] s + y[o+2i+1] c)
+ *   q_out[t,h,:] = bf16(RoPE(RMSNorm(q[t,h,:], q_weight)))       for every head h
+ *   row          = bf16(RoPE(RMSNorm(kv[t,:], kv_weight)))
+ *   slot         = state_slot[t] * win + p mod win                (the window ring)
+ *   unified_kv[slot,:] = row;  and/or  (kv_fp8[slot,:], kv_scale[slot]) = the
+ *   quantize_kv_fp8 store of row.
+ *
+ *   q, q_out   [N, H, D] bf16, 16-byte aligned; q_out may be q (in place),
+ *              no other overlap
+ *   kv         [N, D] bf16, each token's new KV row
+ *   q_weight, kv_weight  [D] fp32;  eps >= 0
+ *   positions  [N] int32; cos_sin [max_pos, rope_dim] fp32 (cos, then sin),
+ *              may be NULL when rope_dim == 0; rope_dim even, 0 <= rope_dim <= D
+ *   state_slot [N] int32;  win > 0
+ *   unified_kv [num_rows, D] bf16 pool, or NULL;  kv_fp8 [num_rows, D] codes
+ *              with kv_scale [num_rows], or NULL; at least one pool
+ *
+ * A token whose position is negative, or (when rope_dim > 0) not below
+ * max_pos, is skipped (nothing is written for it); a KV row whose slot lies
+ * outside [0, num_rows) is not stored.  D in {64, 128, 256, 512} (SPD_ERR_UNSUPPORTED otherwise).  One
+ * launch; graph-capturable.
+ */
+SPD_API spd_status fused_qk_norm_rope_swa_store(
+    const void* q, void* q_out, const void* kv, const float* q_weight, const float* kv_weight,
+    float eps, const int32_t* positions, const float* cos_sin, int32_t max_pos, int32_t rope_dim,
+    const int32_t* state_slot, int32_t win, void* unified_kv, void* kv_fp8, float* kv_scale,
+    int64_t num_rows, int32_t N, int32_t H, int32_t D, void* stream);
+
+/*
  * Debug check of the attention call's index preconditions: kv_indptr[0] == 0,
  * kv_indptr non-decreasing, kv_indptr[N] <= num_indices (the length of the
  * kv_indices buffer), and every kv_indices[j], j < kv_indptr[N], in

@@ -165,7 +165,7 @@ def qk_norm_rope(q_bits: np.ndarray, kv_bits: np.ndarray, q_weight: np.ndarray,
     """The decode-step producer (steps in the C source): q [N, H, D] and kv [N, D] as
     bf16 bits, fp32 weights [D], positions [N], cos_sin [max_pos, rope_dim] fp32.
     Returns (q_out [N, H, D] fp64, kv_out [N, D] fp64, ring slot [N] int64; -1 and
-    zero rows for a position outside the table)."""
+    zero rows for a negative position, or one outside the table when rope_dim > 0)."""
     q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
     kv_bits = np.ascontiguousarray(kv_bits, dtype=np.uint16)
     q_weight = np.ascontiguousarray(q_weight, dtype=np.float32)

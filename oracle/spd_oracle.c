@@ -354,7 +354,8 @@ int spd_oracle_build_decode_indices(const int32_t* state_slot, const int32_t* sw
  *   the KV row's ring slot: state_slot[t] * win + p mod win (the window ring
  *   holds positions p - win + 1 .. p, slot p mod win).
  * Outputs in fp64, unrounded: q_out [N][H][D], kv_out [N][D], slot_out [N].
- * A token with p outside [0, max_pos) gets slot_out = -1 and zero rows.
+ * A token with p < 0, or p >= max_pos when rope_dim > 0 (a position the table
+ * does not hold), gets slot_out = -1 and zero rows.
  */
 static void norm_rope_row(const uint16_t* x, const float* w, double eps, const float* cs,
                           int32_t rope_dim, int32_t D, double* y) {
@@ -385,7 +386,7 @@ int spd_oracle_qk_norm_rope(const uint16_t* q, const uint16_t* kv, const float* 
 #pragma omp parallel for schedule(dynamic, 1)
   for (int32_t t = 0; t < N; ++t) {
     const int32_t p = positions[t];
-    if (p < 0 || p >= max_pos) {
+    if (p < 0 || (rope_dim > 0 && p >= max_pos)) {
       memset(q_out + (int64_t)t * H * D, 0, sizeof(double) * (size_t)H * D);
       memset(kv_out + (int64_t)t * D, 0, sizeof(double) * (size_t)D);
       slot_out[t] = -1;

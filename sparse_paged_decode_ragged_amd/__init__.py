@@ -21,6 +21,10 @@ Call names follow the C ABI:
   (e4m3 codes times a per-row fp32 scale)
 * ``quantize_kv_fp8(src, kv_fp8, kv_scale, slots=None)`` -- the quantising
   store that fills such a pool
+* ``fused_qk_norm_rope_swa_store(q, kv, q_weight, kv_weight, eps, positions,
+  cos_sin, state_slot, win, unified_kv=None, kv_fp8=None, kv_scale=None,
+  q_out=None)`` -- the decode-step producer that writes the rows the attention
+  reads (RMSNorm + RoPE of q and the KV row, KV row into its window-ring slot)
 * ``sparse_decode_attn_workspace_size``, ``sparse_decode_attn_can_use``,
   ``validate_indices``
 """
@@ -43,7 +47,7 @@ EXPORTED_SYMBOLS = (
     "spd_status_string", "spd_version", "sparse_decode_attn_can_use", "sparse_decode_attn",
     "sparse_decode_attn_workspace_size", "sparse_decode_attn_ex", "build_decode_indices",
     "spd_validate_indices", "sparse_decode_attn_plan_info", "sparse_decode_attn_paged",
-    "sparse_decode_attn_fp8", "quantize_kv_fp8",
+    "sparse_decode_attn_fp8", "quantize_kv_fp8", "fused_qk_norm_rope_swa_store",
 )
 
 
@@ -80,6 +84,9 @@ def _load() -> ctypes.CDLL:
     lib.sparse_decode_attn_fp8.restype = ctypes.c_int
     lib.quantize_kv_fp8.argtypes = [P, P, i32, i32, P, P, i64, P]
     lib.quantize_kv_fp8.restype = ctypes.c_int
+    lib.fused_qk_norm_rope_swa_store.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, i32, i32, P,
+                                                 i32, P, P, P, i64, i32, i32, i32, P]
+    lib.fused_qk_norm_rope_swa_store.restype = ctypes.c_int
     lib.build_decode_indices.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i32, P, P, i64, P]
     lib.build_decode_indices.restype = ctypes.c_int
     lib.spd_validate_indices.argtypes = [P, i64, P, i32, i64, ctypes.POINTER(ctypes.c_int64), P]
@@ -323,6 +330,63 @@ def quantize_kv_fp8(src: torch.Tensor, kv_fp8: torch.Tensor, kv_scale: torch.Ten
     st = lib.quantize_kv_fp8(_ptr(src), _ptr(slots), n, D, _ptr(codes), _ptr(kv_scale),
                              codes.shape[0], _stream(src.device))
     _raise_on(st, "quantize_kv_fp8")
+
+
+def fused_qk_norm_rope_swa_store(q: torch.Tensor, kv: torch.Tensor, q_weight: torch.Tensor,
+                                 kv_weight: torch.Tensor, eps: float, positions: torch.Tensor,
+                                 cos_sin: Optional[torch.Tensor], state_slot: torch.Tensor,
+                                 win: int, unified_kv: Optional[torch.Tensor] = None,
+                                 kv_fp8: Optional[torch.Tensor] = None,
+                                 kv_scale: Optional[torch.Tensor] = None,
+                                 q_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The decode-step producer (see include/spd.h): returns q_out [N, H, D] (bf16,
+    normed and rotated; pass q_out=q for in place) and stores each token's normed,
+    rotated KV row into its window-ring slot of unified_kv and/or the FP8 pool."""
+    _check(q, "q", torch.bfloat16, 3)
+    _check(kv, "kv", torch.bfloat16, 2)
+    _check(q_weight, "q_weight", torch.float32, 1)
+    _check(kv_weight, "kv_weight", torch.float32, 1)
+    _check(positions, "positions", torch.int32, 1)
+    _check(state_slot, "state_slot", torch.int32, 1)
+    N, H, D = q.shape
+    max_pos, rope_dim = 0, 0
+    if cos_sin is not None:
+        _check(cos_sin, "cos_sin", torch.float32, 2)
+        max_pos, rope_dim = cos_sin.shape
+    if tuple(kv.shape) != (N, D) or q_weight.shape[0] != D or kv_weight.shape[0] != D or \
+            positions.shape[0] != N or state_slot.shape[0] != N:
+        raise ValueError("shape mismatch between q, kv, the weights, positions and state_slot")
+    num_rows = None
+    codes = None
+    if unified_kv is not None:
+        _check(unified_kv, "unified_kv", torch.bfloat16, 2)
+        num_rows = unified_kv.shape[0]
+    if kv_fp8 is not None:
+        codes = _fp8_codes(kv_fp8, "kv_fp8")
+        _check(kv_scale, "kv_scale", torch.float32, 1)
+        if num_rows is not None and codes.shape[0] != num_rows:
+            raise ValueError("the bf16 and FP8 pools must have the same rows")
+        num_rows = codes.shape[0]
+        if kv_scale.shape[0] != num_rows:
+            raise ValueError("kv_scale must have one entry per pool row")
+    if num_rows is None:
+        raise ValueError("give unified_kv and/or kv_fp8 with kv_scale")
+    for pool in (unified_kv, codes):
+        if pool is not None and pool.shape[1] != D:
+            raise ValueError("pool rows must have D entries")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    else:
+        _check(q_out, "q_out", torch.bfloat16, 3)
+        if tuple(q_out.shape) != (N, H, D):
+            raise ValueError("q_out must be [N, H, D]")
+    st = lib.fused_qk_norm_rope_swa_store(
+        _ptr(q), _ptr(q_out), _ptr(kv), _ptr(q_weight), _ptr(kv_weight), float(eps),
+        _ptr(positions), _ptr(cos_sin), max_pos, rope_dim, _ptr(state_slot), int(win),
+        _ptr(unified_kv), _ptr(codes), _ptr(kv_scale) if codes is not None else None, num_rows,
+        N, H, D, _stream(q.device))
+    _raise_on(st, "fused_qk_norm_rope_swa_store")
+    return q_out
 
 
 def validate_indices(kv_indices: torch.Tensor, kv_indptr: torch.Tensor, num_rows: int) -> int:

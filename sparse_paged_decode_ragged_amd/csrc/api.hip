@@ -269,6 +269,64 @@ SPD_API spd_status quantize_kv_fp8(const void* src, const int32_t* slots, int32_
   return e == hipSuccess ? SPD_OK : SPD_ERR_HIP;
 }
 
+SPD_API spd_status fused_qk_norm_rope_swa_store(
+    const void* q, void* q_out, const void* kv, const float* q_weight, const float* kv_weight,
+    float eps, const int32_t* positions, const float* cos_sin, int32_t max_pos, int32_t rope_dim,
+    const int32_t* state_slot, int32_t win, void* unified_kv, void* kv_fp8, float* kv_scale,
+    int64_t num_rows, int32_t N, int32_t H, int32_t D, void* stream) {
+  if (N < 0 || H <= 0 || D <= 0 || win <= 0 || max_pos < 0 || num_rows <= 0)
+    return SPD_ERR_INVALID_ARG;
+  if (rope_dim < 0 || rope_dim > D || (rope_dim & 1) || !(eps >= 0.0f) || !isfinite(eps))
+    return SPD_ERR_INVALID_ARG;
+  if (D != 64 && D != 128 && D != 256 && D != 512) return SPD_ERR_UNSUPPORTED;
+  if (!unified_kv && !kv_fp8) return SPD_ERR_INVALID_ARG;  // the KV row must go somewhere
+  if (kv_fp8 && !kv_scale) return SPD_ERR_INVALID_ARG;
+  if ((int64_t)N * H > ((int64_t)1 << 40) || num_rows > ((int64_t)1 << 40)) return SPD_ERR_INVALID_ARG;
+  if (N == 0) return SPD_OK;
+  if (!q || !q_out || !kv || !q_weight || !kv_weight || !positions || !state_slot ||
+      (rope_dim > 0 && (!cos_sin || max_pos == 0)))
+    return SPD_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(q_out, 16) || !aligned(kv, 16) || !aligned(q_weight, 4) ||
+      !aligned(kv_weight, 4) || !aligned(positions, 4) || !aligned(state_slot, 4) ||
+      (cos_sin && !aligned(cos_sin, 4)) || (unified_kv && !aligned(unified_kv, 16)) ||
+      (kv_fp8 && !aligned(kv_fp8, 16)) || (kv_scale && !aligned(kv_scale, 4)))
+    return SPD_ERR_INVALID_ARG;
+  const size_t qb = (size_t)N * H * D * 2, kvb = (size_t)N * D * 2;
+  const size_t pool16 = (size_t)num_rows * D * 2, pool8 = (size_t)num_rows * D;
+  // q_out may be q itself (in place), but no other overlap
+  if ((q_out != q && overlap(q_out, qb, q, qb)) || overlap(q_out, qb, kv, kvb) ||
+      (unified_kv && (overlap(unified_kv, pool16, q_out, qb) || overlap(unified_kv, pool16, q, qb) ||
+                      overlap(unified_kv, pool16, kv, kvb))) ||
+      (kv_fp8 && (overlap(kv_fp8, pool8, q_out, qb) || overlap(kv_fp8, pool8, q, qb) ||
+                  overlap(kv_fp8, pool8, kv, kvb) || overlap(kv_scale, (size_t)num_rows * 4, kv_fp8, pool8) ||
+                  overlap(kv_scale, (size_t)num_rows * 4, q_out, qb))) ||
+      (unified_kv && kv_fp8 && (overlap(unified_kv, pool16, kv_fp8, pool8) ||
+                                overlap(unified_kv, pool16, kv_scale, (size_t)num_rows * 4))))
+    return SPD_ERR_INVALID_ARG;
+
+  spd::ProducerArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_out = static_cast<uint16_t*>(q_out);
+  a.kv = static_cast<const uint16_t*>(kv);
+  a.q_weight = q_weight;
+  a.kv_weight = kv_weight;
+  a.eps = eps;
+  a.positions = positions;
+  a.cos_sin = cos_sin;
+  a.max_pos = max_pos;
+  a.rope_dim = rope_dim;
+  a.state_slot = state_slot;
+  a.win = win;
+  a.kv_bf16 = static_cast<uint16_t*>(unified_kv);
+  a.kv8 = static_cast<uint8_t*>(kv_fp8);
+  a.kv_scale = kv_scale;
+  a.num_rows = num_rows;
+  a.N = N;
+  a.H = H;
+  const hipError_t e = spd::launch_producer(a, D, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPD_OK : SPD_ERR_HIP;
+}
+
 SPD_API spd_status build_decode_indices(const int32_t* state_slot, const int32_t* swa_len,
                                         const int32_t* comp_pos, int32_t topk,
                                         const int32_t* block_table, int32_t max_blocks, int32_t N,

@@ -32,6 +32,7 @@
 //   * the scale multiplies its row's scores and its softmax weight, which
 //     becomes P' = bf16(p * scale); the denominator sums the unscaled p.
 #include "attn_device.h"
+#include "row_device.h"
 
 namespace spd {
 namespace {
@@ -404,72 +405,9 @@ __global__ void __launch_bounds__(256) quantize_fp8_kernel(QuantArgs a) {
   const int64_t slot = a.slots != nullptr ? (int64_t)a.slots[i] : i;
   if (slot < 0 || slot >= a.num_rows) return;
 
-  const uint16_t* src = a.src + i * D + lane * E;
-  uint16_t xb[E];
-  if constexpr (E == 8) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      xb[2 * e] = (uint16_t)(v[e] & 0xffff);
-      xb[2 * e + 1] = (uint16_t)(v[e] >> 16);
-    }
-  } else if constexpr (E == 4) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(src);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      xb[2 * e] = (uint16_t)(v[e] & 0xffff);
-      xb[2 * e + 1] = (uint16_t)(v[e] >> 16);
-    }
-  } else if constexpr (E == 2) {
-    const unsigned v = *reinterpret_cast<const unsigned*>(src);
-    xb[0] = (uint16_t)(v & 0xffff);
-    xb[1] = (uint16_t)(v >> 16);
-  } else {
-    xb[0] = src[0];
-  }
   float x[E];
-  float amax = 0.f;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    x[e] = __builtin_bit_cast(float, (unsigned)xb[e] << 16);
-    amax = fmaxf(amax, fabsf(x[e]));
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-
-  unsigned code[(E + 3) / 4];
-  float scale = 0.f;
-#pragma unroll
-  for (int c = 0; c < (E + 3) / 4; ++c) code[c] = 0;
-  if (amax >= 0x1p-64f) {  // else a zero row: scale 0, codes 0
-    scale = amax / 448.0f;
-    const float inv = 448.0f / amax;
-    float y[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) y[e] = fminf(fmaxf(x[e] * inv, -448.0f), 448.0f);
-#pragma unroll
-    for (int c = 0; c < (E + 3) / 4; ++c) {
-      const float y0 = y[4 * c];
-      const float y1 = 4 * c + 1 < E ? y[4 * c + 1] : 0.f;
-      unsigned w = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-      if (4 * c + 2 < E) {
-        const float y3 = 4 * c + 3 < E ? y[4 * c + 3] : 0.f;
-        w = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(y[4 * c + 2], y3, (int)w, true);
-      }
-      code[c] = w;
-    }
-  }
-  uint8_t* dst = a.kv8 + slot * D + lane * E;
-  if constexpr (E == 8) {
-    *reinterpret_cast<u32x2*>(dst) = u32x2{code[0], code[1]};
-  } else if constexpr (E == 4) {
-    *reinterpret_cast<unsigned*>(dst) = code[0];
-  } else if constexpr (E == 2) {
-    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(code[0] & 0xffff);
-  } else {
-    dst[0] = (uint8_t)(code[0] & 0xff);
-  }
-  if (lane == 0) a.kv_scale[slot] = scale;
+  load_bf16_lane<E>(a.src + i * D + lane * E, x);
+  store_fp8_lane<E>(x, a.kv8 + slot * D + lane * E, a.kv_scale + slot, lane);
 }
 
 template <int D>

@@ -1,0 +1,119 @@
+// producer.hip -- the decode-step producer, gfx950: per-head RMSNorm of q,
+// RMSNorm of each token's new KV row, rotary embedding of both, and the store
+// of the KV row into its window-ring slot of the pool (bf16 and/or FP8).
+//
+// Source: sglang PR #25898 summary page, "key files": one fused kernel does
+// the q per-head RMSNorm, the KV RMSNorm, RoPE, the FP8 quantisation and the
+// paged sliding-window store (helpers: a batched RMSNorm, a GPT-J rotation, a
+// batched RoPE).  The page names the steps, not their formulas; the readings:
+//   * RMSNorm of a row x[0, D) with an fp32 weight w: x_d * w_d / sqrt(mean(x^2) + eps);
+//   * RoPE with GPT-J (interleaved) pairs on the last rope_dim entries
+//     (o = D - rope_dim): for i < rope_dim / 2, with c = cos_sin[p][i] and
+//     s = cos_sin[p][rope_dim/2 + i] from the caller's table,
+//     (y[o+2i], y[o+2i+1]) <- (y[o+2i] c - y[o+2i+1] s, y[o+2i] s + y[o+2i+1] c);
+//   * the KV row of token t at position p goes to pool row
+//     state_slot[t] * win + p mod win (the ring keeps positions p-win+1 .. p);
+//   * every output is rounded to bf16; the FP8 store quantises that bf16 row
+//     exactly as quantize_kv_fp8 would.
+//
+// Work: one wave per row, D / 64 entries a lane (entries 2i, 2i+1 of a pair
+// sit in one lane for D >= 128; at D = 64 the partner comes from lane ^ 1).
+// Rows [0, N*H) are q rows (token r / H), rows [N*H, N*H + N) KV rows.  The
+// kernel is bound by HBM: it reads and writes each row once.
+#include <math.h>
+
+#include "row_device.h"
+#include "spd_internal.h"
+
+namespace spd {
+namespace {
+
+template <int D>
+__global__ void __launch_bounds__(256) qk_norm_rope_store_kernel(ProducerArgs a) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t nq = (int64_t)a.N * a.H;
+  if (r >= nq + a.N) return;  // wave-uniform
+  const bool is_kv = r >= nq;
+  const int t = is_kv ? (int)(r - nq) : (int)(r / a.H);
+  const int p = a.positions[t];
+  // a position outside the table (when there is one to read): nothing is written
+  if (p < 0 || (a.rope_dim > 0 && p >= a.max_pos)) return;
+  int64_t slot = 0;
+  if (is_kv) {
+    slot = (int64_t)a.state_slot[t] * a.win + p % a.win;
+    if (slot < 0 || slot >= a.num_rows) return;  // outside the pool: nothing is written
+  }
+  const uint16_t* src = is_kv ? a.kv + (int64_t)t * D : a.q + r * D;
+  float x[E];
+  load_bf16_lane<E>(src + lane * E, x);
+
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) ss += x[e] * x[e];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+  const float* w = is_kv ? a.kv_weight : a.q_weight;
+  float y[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) y[e] = x[e] * inv * w[lane * E + e];
+
+  const int o = D - a.rope_dim, half = a.rope_dim >> 1;
+  const float* cs = a.cos_sin + (int64_t)p * a.rope_dim;
+  if constexpr (E >= 2) {
+#pragma unroll
+    for (int e = 0; e < E; e += 2) {
+      const int d = lane * E + e;
+      if (d >= o) {
+        const int i = (d - o) >> 1;
+        const float c = cs[i], s = cs[half + i];
+        const float y0 = y[e], y1 = y[e + 1];
+        y[e] = y0 * c - y1 * s;
+        y[e + 1] = y0 * s + y1 * c;
+      }
+    }
+  } else {
+    const float partner = __shfl_xor(y[0], 1);
+    if (lane >= o) {
+      const int i = (lane - o) >> 1;
+      const float c = cs[i], s = cs[half + i];
+      y[0] = (lane & 1) == 0 ? y[0] * c - partner * s : partner * s + y[0] * c;
+    }
+  }
+
+  if (!is_kv) {
+    store_bf16_lane<E>(a.q_out + r * D + lane * E, y);
+    return;
+  }
+  if (a.kv_bf16 != nullptr) store_bf16_lane<E>(a.kv_bf16 + slot * D + lane * E, y);
+  if (a.kv8 != nullptr) {
+    float yb[E];  // the bf16 row, as the FP8 store's input
+#pragma unroll
+    for (int e = 0; e < E; ++e) yb[e] = __builtin_bit_cast(float, bf16_rne_bits(y[e]) << 16);
+    store_fp8_lane<E>(yb, a.kv8 + slot * D + lane * E, a.kv_scale + slot, lane);
+  }
+}
+
+template <int D>
+hipError_t launch_producer_d(const ProducerArgs& a, hipStream_t stream) {
+  const long long rows = (long long)a.N * a.H + a.N;
+  hipLaunchKernelGGL((qk_norm_rope_store_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256),
+                     0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_producer(const ProducerArgs& a, int D, hipStream_t stream) {
+  switch (D) {
+    case 64: return launch_producer_d<64>(a, stream);
+    case 128: return launch_producer_d<128>(a, stream);
+    case 256: return launch_producer_d<256>(a, stream);
+    case 512: return launch_producer_d<512>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace spd

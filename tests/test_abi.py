@@ -33,6 +33,8 @@ def lib():
                                            ctypes.c_float, P, i32, i32, i32, i32, P]
     L.sparse_decode_attn_fp8.argtypes = [P, P, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32, P]
     L.quantize_kv_fp8.argtypes = [P, P, i32, i32, P, P, i64, P]
+    L.fused_qk_norm_rope_swa_store.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, i32, i32, P,
+                                               i32, P, P, P, i64, i32, i32, i32, P]
     L.spd_status_string.argtypes = [ctypes.c_int]
     L.spd_status_string.restype = ctypes.c_char_p
     return L
@@ -235,3 +237,40 @@ def test_quantize_rejects_bad_arguments(lib):
     assert _quant(lib, kv=FAKE) == INVALID              # pool overlaps the source
     assert _quant(lib, sc=FAKE * 4096 + 64 * 50) == INVALID   # scales inside the codes
     assert _quant(lib, slots=FAKE * 8192, n=4) == INVALID     # slots overlap the scales
+
+
+def _prod(lib, q=FAKE, q_out=FAKE * 16, kv=FAKE * 32, qw=FAKE * 48, kw=FAKE * 48 + 4096,
+          eps=1e-6, pos=FAKE * 64, cs=FAKE * 80, max_pos=16, rope_dim=64, slot=FAKE * 96, win=8,
+          pool=FAKE * 4096, fp8=None, sc=None, rows=1000, N=4, H=8, D=512):
+    return lib.fused_qk_norm_rope_swa_store(q, q_out, kv, qw, kw, eps, pos, cs, max_pos, rope_dim,
+                                            slot, win, pool, fp8, sc, rows, N, H, D, None)
+
+
+def test_producer_rejects_bad_arguments(lib):
+    assert _prod(lib, N=0) == OK
+    assert _prod(lib, N=-1) == INVALID
+    assert _prod(lib, H=0) == INVALID
+    assert _prod(lib, D=96) == UNSUPPORTED
+    assert _prod(lib, D=1024) == UNSUPPORTED
+    assert _prod(lib, win=0) == INVALID
+    assert _prod(lib, rows=0) == INVALID
+    assert _prod(lib, rope_dim=63) == INVALID            # odd
+    assert _prod(lib, rope_dim=600) == INVALID           # > D
+    assert _prod(lib, rope_dim=-2) == INVALID
+    assert _prod(lib, eps=-1.0) == INVALID
+    assert _prod(lib, eps=float("nan")) == INVALID
+    assert _prod(lib, eps=float("inf")) == INVALID
+    assert _prod(lib, pool=None) == INVALID              # no pool to store into
+    assert _prod(lib, pool=None, fp8=FAKE * 4096) == INVALID   # FP8 pool without scales
+    assert _prod(lib, cs=None) == INVALID                # rope_dim > 0 needs the table
+    assert _prod(lib, max_pos=0) == INVALID
+    assert _prod(lib, q=None) == INVALID
+    assert _prod(lib, kv=None) == INVALID
+    assert _prod(lib, pos=None) == INVALID
+    assert _prod(lib, q=FAKE + 8) == INVALID             # 16-byte alignment
+    assert _prod(lib, pool=FAKE * 4096 + 4) == INVALID
+    assert _prod(lib, qw=FAKE * 48 + 2) == INVALID
+    assert _prod(lib, q_out=FAKE + 1024) == INVALID      # partial overlap with q
+    assert _prod(lib, pool=FAKE * 16) == INVALID         # pool over q_out
+    assert _prod(lib, pool=FAKE * 32 - 4096) == INVALID  # pool over kv
+    assert _prod(lib, fp8=FAKE * 8192, sc=FAKE * 8192 + 1000) == INVALID   # scales in the codes

@@ -1,0 +1,155 @@
+"""GPU parity of fused_qk_norm_rope_swa_store (through the C ABI) against the
+oracle's producer:
+
+* q_out and the stored bf16 KV rows within |d| <= 1e-2 + 1e-2 |ref| of the
+  oracle's fp64 values (in practice within one bf16 rounding);
+* the KV rows land in exactly the oracle's ring slots, every other pool row is
+  left as it was, tokens whose position is outside the table write nothing;
+* the FP8 store: for each row whose bf16 values equal the oracle's values
+  rounded to bf16 (the FP8 store quantises the bf16 row), codes and scale equal
+  the oracle quantiser's, bit for bit; every row decodes to within half an
+  e4m3 spacing (plus the bf16 rounding) of the oracle's values.
+
+Cases: every supported D, rotary widths 0, part of the row and all of it,
+positions that wrap the ring, in-place q, both pools at once, a decode-base
+batch (N=64, H=64, D=512) and a large batch (N=1024, H=128) sampled."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import assert_close, bf16_to_f64, dev, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def spd():
+    import sparse_paged_decode_ragged_amd as m
+    return m
+
+
+def rope_table(max_pos, rope_dim, base=10000.0):
+    i = np.arange(rope_dim // 2)
+    ang = np.arange(max_pos)[:, None] * base ** (-2.0 * i / rope_dim)[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def to_dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev()).view(torch.bfloat16)
+    return torch.from_numpy(a).to(dev())
+
+
+def bf16_round(x64: np.ndarray) -> np.ndarray:
+    """fp64 -> the nearest bf16 value (via fp32, both round to nearest even;
+    double rounding is harmless at the sizes checked)."""
+    return W.bf16_to_f32(W.bf16_bits(x64.astype(np.float32))).astype(np.float64)
+
+
+def make_case(seed, N, H, D, rope_dim, win, n_slots, max_pos=4096):
+    rng = np.random.default_rng(seed)
+    q = W.normal_bf16(rng, (N, H, D), std=2.0)
+    kv = W.normal_bf16(rng, (N, D))
+    qw = (1.0 + 0.3 * rng.standard_normal(D)).astype(np.float32)
+    kw = (1.0 + 0.3 * rng.standard_normal(D)).astype(np.float32)
+    pos = rng.integers(0, max_pos, size=N).astype(np.int32)
+    slot = rng.permutation(n_slots)[:N].astype(np.int32)
+    cs = rope_table(max_pos, rope_dim)
+    return q, kv, qw, kw, pos, cs, slot
+
+
+def run_and_check(spd, case, win, num_rows, eps=1e-6, fp8=True, bf16=True, in_place=False,
+                  what=""):
+    q, kv, qw, kw, pos, cs, slot = case
+    N, H, D = q.shape
+    qo_ref, kv_ref, slot_ref = oracle.qk_norm_rope(q, kv, qw, kw, eps, pos, cs, slot, win)
+    dq = to_dev(q)
+    pool = torch.full((num_rows, D), 0.5, dtype=torch.bfloat16, device=dev()) if bf16 else None
+    kv8 = torch.full((num_rows, D), 0x5A, dtype=torch.uint8, device=dev()) if fp8 else None
+    ksc = torch.full((num_rows,), -1.0, dtype=torch.float32, device=dev()) if fp8 else None
+    q_out = dq if in_place else torch.full_like(dq, 3.0)
+    spd.fused_qk_norm_rope_swa_store(dq, to_dev(kv), to_dev(qw), to_dev(kw), eps, to_dev(pos),
+                                     to_dev(cs) if cs.shape[1] else None, to_dev(slot), win,
+                                     unified_kv=pool, kv_fp8=kv8, kv_scale=ksc, q_out=q_out)
+    torch.cuda.synchronize()
+    live = slot_ref >= 0
+    got_q = bf16_to_f64(q_out)
+    assert_close(got_q[live], qo_ref[live], "q_out " + what)
+    if not in_place and (~live).any():
+        assert np.all(got_q[~live] == 3.0), "a token outside the table wrote q_out"
+    stored = slot_ref[live]
+    untouched = np.setdiff1d(np.arange(num_rows), stored)
+    if bf16:
+        p = bf16_to_f64(pool)
+        assert_close(p[stored], kv_ref[live], "kv row " + what)
+        assert np.all(p[untouched] == 0.5), "a pool row outside the ring slots changed"
+    if fp8:
+        codes = kv8.cpu().numpy()
+        scales = ksc.cpu().numpy()
+        assert np.all(codes[untouched] == 0x5A) and np.all(scales[untouched] == -1.0)
+        ref_rows = bf16_round(kv_ref[live])
+        ref_codes, ref_scales = oracle.quantize_fp8(W.bf16_bits(ref_rows.astype(np.float32)))
+        if bf16:
+            same = np.all(bf16_to_f64(pool)[stored] == ref_rows, axis=1)
+        else:
+            same = np.ones(len(stored), dtype=bool)
+        n_same = int(same.sum())
+        log("  fp8 rows whose bf16 row equals the oracle's: %d of %d" % (n_same, len(stored)))
+        assert n_same >= 0.5 * len(stored)
+        assert np.array_equal(codes[stored][same], ref_codes[same])
+        assert np.array_equal(scales[stored][same], ref_scales[same])
+        table = np.array([oracle.e4m3_value(c) for c in range(256)])
+        dec = table[codes[stored]] * scales[stored][:, None]
+        # half a spacing of e4m3 (2^-4 of the value, or 2^-10 * scale below 2^-6 * scale)
+        # plus the bf16 rounding of the row and of the amax
+        s = scales[stored][:, None].astype(np.float64)
+        bound = 0.5 * np.maximum(np.abs(kv_ref[live]) * 2.0 ** -3, s * 2.0 ** -9) + \
+            np.abs(kv_ref[live]) * 2.0 ** -7 + 1e-6
+        assert np.all(np.abs(dec - kv_ref[live]) <= bound)
+    return q_out
+
+
+@pytest.mark.parametrize("D,rope_dim", [(64, 64), (64, 0), (128, 32), (256, 64), (512, 64),
+                                        (512, 512)])
+def test_matches_oracle(spd, D, rope_dim):
+    log("case producer D=%d rope_dim=%d" % (D, rope_dim))
+    N, H, win = 37, 12, 16
+    case = make_case(D + rope_dim, N, H, D, rope_dim, win, n_slots=60)
+    run_and_check(spd, case, win, num_rows=60 * win + 7, what="D=%d rope=%d" % (D, rope_dim))
+
+
+def test_in_place_wrapping_positions_and_skipped_tokens(spd):
+    log("case producer in place, wrap, skipped tokens")
+    N, H, D, win, max_pos = 24, 8, 512, 8, 100
+    q, kv, qw, kw, pos, cs, slot = make_case(5, N, H, D, 64, win, n_slots=30, max_pos=max_pos)
+    # tokens 0..7: one request at consecutive positions 13..20, which wrap its
+    # ring of 8 (slots 5, 6, 7, 0, 1, 2, 3, 4 of ring 2); the others have rings
+    # of their own
+    pos[:8] = np.arange(8) + 13
+    slot[:8] = 2
+    slot[8:] = np.random.default_rng(6).permutation(np.arange(3, 30))[:N - 8]
+    pos[8] = -1                          # outside the table: nothing written
+    pos[9] = max_pos                     # outside the table
+    run_and_check(spd, (q, kv, qw, kw, pos, cs, slot), win, num_rows=30 * win, in_place=True,
+                  what="in place")
+
+
+def test_fp8_pool_alone_and_bf16_pool_alone(spd):
+    log("case producer single pools")
+    case = make_case(9, 20, 4, 256, 64, 32, n_slots=25)
+    run_and_check(spd, case, 32, num_rows=25 * 32, bf16=False, what="fp8 only")
+    run_and_check(spd, case, 32, num_rows=25 * 32, fp8=False, what="bf16 only")
+
+
+@pytest.mark.parametrize("N,H", [(64, 64), (1024, 128)])
+def test_decode_batches(spd, N, H):
+    """decode_base's batch shape and the large one's (D=512, a 64-wide rotary
+    part, win=128, one ring per token as in those configurations)."""
+    log("case producer N=%d H=%d" % (N, H))
+    D, win = 512, 128
+    q, kv, qw, kw, pos, cs, slot = make_case(11 + N, N, H, D, 64, win, n_slots=N)
+    slot = np.arange(N, dtype=np.int32)
+    run_and_check(spd, (q, kv, qw, kw, pos, cs, slot), win, num_rows=N * win, what="N=%d" % N)

@@ -141,3 +141,13 @@ def test_ring_occupancy():
         assert sorted(window.tolist()) == list(range(s * win, s * win + win))
         if p + 1 < P:
             assert slot[p + 1] == slot[p - win + 1]
+
+
+def test_without_rotary_part_positions_have_no_table_bound():
+    """rope_dim = 0 reads no table, so any position >= 0 is stored (slot p mod win)
+    and only a negative one is skipped."""
+    q = bits(np.ones((3, 1, 4)))
+    kv = bits(np.ones((3, 4)))
+    _, _, slot = run(q, kv, pos=np.array([0, 1000003, -5], np.int32),
+                     cs=np.zeros((0, 0), np.float32), slot=np.array([1, 2, 3], np.int32), win=8)
+    assert slot.tolist() == [8, 2 * 8 + 1000003 % 8, -1]
