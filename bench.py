@@ -19,7 +19,9 @@ roofline record of the attention kernel, and the oracle timed on this host's
 cores on a bounded sample.  Two variants of the attention call are timed the
 same way and reported beside it: the page transform fused into the kernel
 (sparse_decode_attn_paged) and the call over an FP8 pool filled from the same
-bf16 rows by the quantising store (sparse_decode_attn_fp8).
+bf16 rows by the quantising store (sparse_decode_attn_fp8).  For builder-shaped
+workloads the decode-step producer that writes the window rows
+(fused_qk_norm_rope_swa_store) is timed too.
 """
 from __future__ import annotations
 
@@ -53,6 +55,7 @@ def parse():
     p.add_argument("--eager", action="store_true", help="launch kernels directly, no graphs")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8-pool measurement")
+    p.add_argument("--no-producer", action="store_true", help="skip the producer measurement")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calibration-copy-mib", type=int, default=0,
                    help="also run a kernel of known traffic three times (bitwise_not over this "
@@ -274,6 +277,27 @@ def main():
             fp8_sets.append(dict(base, q=base["q"].clone(), kv8=kv8, ksc=ksc,
                                  out=torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)))
 
+    # The decode-step producer (builder-shaped workloads): RMSNorm + RoPE of q
+    # and of each token's new KV row, the KV row stored into its window-ring
+    # slot of the set's bf16 pool; q_out is a buffer of its own, so the
+    # attention legs keep their inputs.  Rotary width 64, positions < 4096.
+    has_producer = not args.no_producer and b is not None
+    rope_dim, max_pos = 64, 4096
+    if has_producer:
+        prng = np.random.default_rng(12345)
+        ang = np.arange(max_pos)[:, None] * 10000.0 ** (-2.0 * np.arange(rope_dim // 2) / rope_dim)
+        cos_sin = torch.from_numpy(
+            np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)).to(dev)
+        qw = torch.from_numpy((1 + 0.1 * prng.standard_normal(D)).astype(np.float32)).to(dev)
+        kw = torch.from_numpy((1 + 0.1 * prng.standard_normal(D)).astype(np.float32)).to(dev)
+        for s in sets:
+            s.update(q_prod=torch.empty_like(s["q"]), kv_new=W.device_bits(W.normal_bf16(prng, (N, D)), dev),
+                     pos=torch.from_numpy(prng.integers(0, max_pos, size=N).astype(np.int32)).to(dev))
+
+    def producer(s):
+        spd.fused_qk_norm_rope_swa_store(s["q"], s["kv_new"], qw, kw, 1e-6, s["pos"], cos_sin,
+                                         s["ss"], b.win, unified_kv=s["kv"], q_out=s["q_prod"])
+
     def attn_fp8(s):
         spd.sparse_decode_attn_fp8(s["q"], s["kv8"], s["ksc"], s["idx"], s["ptr"], s["sink"],
                                    w.softmax_scale, out=s["out"])
@@ -286,11 +310,12 @@ def main():
     # One graph per set for each of (step, attention call), plus one graph that
     # holds every set's call back to back: the timed loops replay the latter,
     # so consecutive calls are not separated by per-graph launch gaps.
-    single = {"step": [], "attn": [], "paged": []}
+    single = {"step": [], "attn": [], "paged": [], "producer": []}
     chain = {}
     cs = torch.cuda.Stream()
     if not args.eager:
-        kinds = (("step", step), ("attn", attn)) + ((("paged", paged),) if has_paged else ())
+        kinds = ((("step", step), ("attn", attn)) + ((("paged", paged),) if has_paged else ()) +
+                 ((("producer", producer),) if has_producer else ()))
         for name, fn in kinds:
             for s in sets:
                 g = torch.cuda.CUDAGraph()
@@ -361,6 +386,11 @@ def main():
     if has_paged:
         run_calls(min(args.warmup, 64), "paged", paged)
         us_paged = timed(n_attn, "paged", paged) * 1e3 / n_attn
+
+    us_prod = None
+    if has_producer:
+        run_calls(min(args.warmup, 64), "producer", producer)
+        us_prod = timed(n_attn, "producer", producer) * 1e3 / n_attn
 
     us_fp8 = None
     if has_fp8:
@@ -438,6 +468,15 @@ def main():
             "traffic": recorded_traffic("attn_rows_fp8_kernel<%d>" % D, args.workload + "_fp8"),
             "tokens_per_s": round(N / (us_fp8 * 1e-6), 1), "bytes_per_call": int(b_fp8),
             "achieved_GBps": round(ach8, 1), "frac": round(ach8 / HBM_PEAK_GBPS, 4)}
+    if us_prod is not None:
+        # q read and written, each token's KV row read and stored, the two
+        # weights, the table rows used, positions and state slots
+        b_prod = 4 * N * H * D + 4 * N * D + 8 * D + 4 * N * rope_dim + 8 * N
+        achp = b_prod / (us_prod * 1e-6) / 1e9
+        rec["producer"] = {
+            "call": "fused_qk_norm_rope_swa_store", "kernel": "qk_norm_rope_store_kernel<%d>" % D,
+            "rope_dim": rope_dim, "us_per_call": round(us_prod, 3), "bytes_per_call": int(b_prod),
+            "achieved_GBps": round(achp, 1), "frac": round(achp / HBM_PEAK_GBPS, 4)}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, indptr, indices, args.cpu_seconds)
     print(json.dumps(rec))

@@ -8,6 +8,7 @@
 
 #include "spd.h"
 #include "spd_internal.h"
+#include "store_internal.h"
 
 namespace {
 

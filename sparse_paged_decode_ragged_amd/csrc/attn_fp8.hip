@@ -33,6 +33,7 @@
 //     becomes P' = bf16(p * scale); the denominator sums the unscaled p.
 #include "attn_device.h"
 #include "row_device.h"
+#include "store_internal.h"
 
 namespace spd {
 namespace {

@@ -23,7 +23,7 @@
 #include <math.h>
 
 #include "row_device.h"
-#include "spd_internal.h"
+#include "store_internal.h"
 
 namespace spd {
 namespace {
