@@ -56,6 +56,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8-pool measurement")
     p.add_argument("--no-producer", action="store_true", help="skip the producer measurement")
+    p.add_argument("--no-prefill", action="store_true", help="skip the shared-window measurement")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calibration-copy-mib", type=int, default=0,
                    help="also run a kernel of known traffic three times (bitwise_not over this "
@@ -294,6 +295,25 @@ def main():
             s.update(q_prod=torch.empty_like(s["q"]), kv_new=W.device_bits(W.normal_bf16(prng, (N, D)), dev),
                      pos=torch.from_numpy(prng.integers(0, max_pos, size=N).astype(np.int32)).to(dev))
 
+    # Prefill-shaped workloads whose lists are windows of one index stream: the
+    # same batch through sparse_prefill_attn (tokens that share rows share a
+    # workgroup).
+    has_prefill = not args.no_prefill and "stream" in w.meta
+    if has_prefill:
+        m = w.meta
+        pf_stream, pf_start, pf_len = t(m["stream"]), t(m["win_start"]), t(m["win_len"])
+        for s in sets:
+            s.update(out_pf=torch.empty((N, H, D), dtype=torch.bfloat16, device=dev))
+
+    def prefill(s, group=0):
+        spd.sparse_prefill_attn(s["q"], s["kv"], pf_stream, pf_start, pf_len, s["sink"],
+                                w.softmax_scale, out=s["out_pf"], tokens_per_group=group)
+
+    shared_group = 128 // H  # the grouping that fills four waves with shared tokens
+
+    def prefill_shared(s):
+        prefill(s, shared_group)
+
     def producer(s):
         spd.fused_qk_norm_rope_swa_store(s["q"], s["kv_new"], qw, kw, 1e-6, s["pos"], cos_sin,
                                          s["ss"], b.win, unified_kv=s["kv"], q_out=s["q_prod"])
@@ -310,12 +330,14 @@ def main():
     # One graph per set for each of (step, attention call), plus one graph that
     # holds every set's call back to back: the timed loops replay the latter,
     # so consecutive calls are not separated by per-graph launch gaps.
-    single = {"step": [], "attn": [], "paged": [], "producer": []}
+    single = {"step": [], "attn": [], "paged": [], "producer": [], "prefill": [],
+              "prefill_shared": []}
     chain = {}
     cs = torch.cuda.Stream()
     if not args.eager:
         kinds = ((("step", step), ("attn", attn)) + ((("paged", paged),) if has_paged else ()) +
-                 ((("producer", producer),) if has_producer else ()))
+                 ((("producer", producer),) if has_producer else ()) +
+                 ((("prefill", prefill), ("prefill_shared", prefill_shared)) if has_prefill else ()))
         for name, fn in kinds:
             for s in sets:
                 g = torch.cuda.CUDAGraph()
@@ -386,6 +408,13 @@ def main():
     if has_paged:
         run_calls(min(args.warmup, 64), "paged", paged)
         us_paged = timed(n_attn, "paged", paged) * 1e3 / n_attn
+
+    us_pf = None
+    if has_prefill:
+        run_calls(min(args.warmup, 64), "prefill", prefill)
+        us_pf = timed(n_attn, "prefill", prefill) * 1e3 / n_attn
+        run_calls(min(args.warmup, 64), "prefill_shared", prefill_shared)
+        us_pf_shared = timed(n_attn, "prefill_shared", prefill_shared) * 1e3 / n_attn
 
     us_prod = None
     if has_producer:
@@ -468,6 +497,27 @@ def main():
             "traffic": recorded_traffic("attn_rows_fp8_kernel<%d>" % D, args.workload + "_fp8"),
             "tokens_per_s": round(N / (us_fp8 * 1e-6), 1), "bytes_per_call": int(b_fp8),
             "achieved_GBps": round(ach8, 1), "frac": round(ach8 / HBM_PEAK_GBPS, 4)}
+    if us_pf is not None:
+        # what the shared-window call must move: q of non-empty tokens and out,
+        # each stream position some window covers once (its row and its index),
+        # the windows and the sinks
+        m = w.meta
+        cover = np.zeros(len(m["stream"]) + 1, dtype=np.int64)
+        ok = m["win_len"] > 0
+        np.add.at(cover, m["win_start"][ok], 1)
+        np.add.at(cover, m["win_start"][ok] + m["win_len"][ok], -1)
+        U = int((np.cumsum(cover)[:-1] > 0).sum())
+        b_pf = ab["qo_bytes"] + U * (2 * D + 4) + 8 * N + 4 * H
+        achf = b_pf / (us_pf * 1e-6) / 1e9
+        rec["prefill"] = {
+            "call": "sparse_prefill_attn", "kernel": "attn_wide_kernel<%d,%d, windows>" % (
+                D, 4 if H == 128 else 2),
+            "tokens_per_workgroup": 1 if H >= 64 else 2, "us_per_call": round(us_pf, 3),
+            "tokens_per_s": round(N / (us_pf * 1e-6), 1), "covered_stream_positions": U,
+            "bytes_per_call": int(b_pf), "achieved_GBps": round(achf, 1),
+            "frac": round(achf / HBM_PEAK_GBPS, 4),
+            "speedup_vs_decode_call": round(us_attn / us_pf, 3),
+            "tokens_per_workgroup_%d_us" % shared_group: round(us_pf_shared, 3)}
     if us_prod is not None:
         # q read and written, each token's KV row read and stored, the two
         # weights, the table rows used, positions and state slots

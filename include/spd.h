@@ -224,6 +224,45 @@ SPD_API spd_status sparse_decode_attn_paged(
     int32_t mode, void* stream);
 
 /*
+ * Sparse attention for a batch of query tokens whose row lists are windows of
+ * one shared index stream (prefill-shaped batches, where consecutive tokens
+ * share most of their rows: sglang PR #28392 summary page, "implementation
+ * breakdown" and "key files", the paged prefill module beside the decode
+ * one).  Token t attends to
+ *
+ *   J_t = kv_stream[win_start[t] : win_start[t] + win_len[t]]
+ *
+ * with exactly the operation and numerics of sparse_decode_attn (sink,
+ * log2-domain softmax, empty window -> zeros).  A CSR batch is the case of
+ * windows that do not overlap (win_start = kv_indptr[t], win_len = its
+ * length).  A workgroup serves tokens_per_group consecutive tokens (their
+ * tokens_per_group * H query rows, 64 or 128, fill two or four waves of 32
+ * heads), gathers the union of their windows once, and each token masks the
+ * rows outside its own window, so overlapping windows are read once per group;
+ * the cost grows with the union's span, so tokens of one group should overlap.
+ * tokens_per_group = 0 picks one token per workgroup at H = 64 and 128 and two
+ * at H = 32 (on the prefill batch of this library's measurements, two tokens a
+ * workgroup at H = 64 gathered fewer bytes but ran slower: the rows they share
+ * were already L2 hits, and each wave still reads every row it uses from LDS).
+ *
+ *   q, unified_kv, attn_sink, softmax_scale, out, N, D: as sparse_decode_attn
+ *   H            32, 64 or 128, and tokens_per_group * H in {64, 128}
+ *                (SPD_ERR_UNSUPPORTED otherwise)
+ *   kv_stream    [stream_len] int32 pool rows, each in [0, num_rows)
+ *                (NULL allowed when stream_len == 0); stream_len < 2^31
+ *   win_start, win_len  [N] int32; a window with win_len <= 0, win_start < 0
+ *                or win_start + win_len > stream_len counts as empty
+ *
+ * No workspace, no split; graph-capturable.
+ */
+SPD_API spd_status sparse_prefill_attn(const void* q, const void* unified_kv, int64_t num_rows,
+                                       const int32_t* kv_stream, int64_t stream_len,
+                                       const int32_t* win_start, const int32_t* win_len,
+                                       const float* attn_sink, float softmax_scale, void* out,
+                                       int32_t N, int32_t H, int32_t D, int32_t tokens_per_group,
+                                       void* stream);
+
+/*
  * FP8 pool.  The page's caches have FP8 variants, filled by stores that
  * quantise rows as they scatter them into the pool (sglang PR #25898 summary
  * page, "key files": the fused norm/RoPE/store kernel and the store-cache

@@ -16,6 +16,9 @@ Call names follow the C ABI:
   block_table, win, k_per_block, swa_pages, attn_sink, softmax_scale,
   out=None)`` -- the two above in one kernel (the page transform fused into
   the attention call; no kv_indices in memory)
+* ``sparse_prefill_attn(q, unified_kv, kv_stream, win_start, win_len, attn_sink,
+  softmax_scale, out=None)`` -- the same attention for tokens whose row lists
+  are windows of one index stream (consecutive tokens sharing rows)
 * ``sparse_decode_attn_fp8(q, kv_fp8, kv_scale, kv_indices, kv_indptr,
   attn_sink, softmax_scale, out=None)`` -- the same attention over an FP8 pool
   (e4m3 codes times a per-row fp32 scale)
@@ -48,6 +51,7 @@ EXPORTED_SYMBOLS = (
     "sparse_decode_attn_workspace_size", "sparse_decode_attn_ex", "build_decode_indices",
     "spd_validate_indices", "sparse_decode_attn_plan_info", "sparse_decode_attn_paged",
     "sparse_decode_attn_fp8", "quantize_kv_fp8", "fused_qk_norm_rope_swa_store",
+    "sparse_prefill_attn",
 )
 
 
@@ -83,6 +87,9 @@ def _load() -> ctypes.CDLL:
                                            P]
     lib.sparse_decode_attn_fp8.restype = ctypes.c_int
     lib.quantize_kv_fp8.argtypes = [P, P, i32, i32, P, P, i64, P]
+    lib.sparse_prefill_attn.argtypes = [P, P, i64, P, i64, P, P, P, ctypes.c_float, P, i32, i32,
+                                        i32, i32, P]
+    lib.sparse_prefill_attn.restype = ctypes.c_int
     lib.quantize_kv_fp8.restype = ctypes.c_int
     lib.fused_qk_norm_rope_swa_store.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, i32, i32, P,
                                                  i32, P, P, P, i64, i32, i32, i32, P]
@@ -271,6 +278,38 @@ def sparse_decode_attn_paged(q: torch.Tensor, unified_kv: torch.Tensor, state_sl
                                       int(swa_pages), _ptr(attn_sink), float(softmax_scale),
                                       _ptr(out), N, H, D, int(mode), _stream(q.device))
     _raise_on(st, "sparse_decode_attn_paged")
+    return out
+
+
+def sparse_prefill_attn(q: torch.Tensor, unified_kv: torch.Tensor, kv_stream: torch.Tensor,
+                        win_start: torch.Tensor, win_len: torch.Tensor, attn_sink: torch.Tensor,
+                        softmax_scale: float, out: Optional[torch.Tensor] = None, *,
+                        tokens_per_group: int = 0) -> torch.Tensor:
+    """out[N, H, D] (bf16): token t attends to
+    kv_stream[win_start[t] : win_start[t] + win_len[t]]; tokens_per_group
+    consecutive tokens share a workgroup (0: automatic; see include/spd.h)."""
+    _check(q, "q", torch.bfloat16, 3)
+    _check(unified_kv, "unified_kv", torch.bfloat16, 2)
+    _check(kv_stream, "kv_stream", torch.int32, 1)
+    _check(win_start, "win_start", torch.int32, 1)
+    _check(win_len, "win_len", torch.int32, 1)
+    _check(attn_sink, "attn_sink", torch.float32, 1)
+    N, H, D = q.shape
+    if unified_kv.shape[1] != D or win_start.shape[0] != N or win_len.shape[0] != N or \
+            attn_sink.shape[0] != H:
+        raise ValueError("shape mismatch between q, unified_kv, the windows and attn_sink")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16, 3)
+        if tuple(out.shape) != (N, H, D):
+            raise ValueError("out must be [N, H, D]")
+    st = lib.sparse_prefill_attn(_ptr(q), _ptr(unified_kv), unified_kv.shape[0],
+                                 _ptr(kv_stream) if kv_stream.numel() > 0 else None,
+                                 kv_stream.numel(), _ptr(win_start), _ptr(win_len),
+                                 _ptr(attn_sink), float(softmax_scale), _ptr(out), N, H, D,
+                                 int(tokens_per_group), _stream(q.device))
+    _raise_on(st, "sparse_prefill_attn")
     return out
 
 

@@ -197,6 +197,58 @@ SPD_API spd_status sparse_decode_attn_paged(
   return e == hipSuccess ? SPD_OK : SPD_ERR_HIP;
 }
 
+SPD_API spd_status sparse_prefill_attn(const void* q, const void* unified_kv, int64_t num_rows,
+                                       const int32_t* kv_stream, int64_t stream_len,
+                                       const int32_t* win_start, const int32_t* win_len,
+                                       const float* attn_sink, float softmax_scale, void* out,
+                                       int32_t N, int32_t H, int32_t D, int32_t tokens_per_group,
+                                       void* stream) {
+  if (N < 0 || H <= 0 || D <= 0 || num_rows <= 0 || stream_len < 0 || tokens_per_group < 0)
+    return SPD_ERR_INVALID_ARG;
+  if (!isfinite(softmax_scale)) return SPD_ERR_INVALID_ARG;
+  if ((D != 64 && D != 128 && D != 256 && D != 512) || (H != 32 && H != 64 && H != 128))
+    return SPD_ERR_UNSUPPORTED;
+  // automatic: 64 query rows (two 32-head waves) per workgroup, one token at
+  // H = 64; H = 128 needs four waves for one token
+  const int T = tokens_per_group > 0 ? tokens_per_group : (H == 128 ? 1 : 64 / H);
+  if ((long long)T * H != 64 && (long long)T * H != 128) return SPD_ERR_UNSUPPORTED;
+  if (stream_len > 0x7fffffffLL || num_rows > (int64_t)1 << 40) return SPD_ERR_INVALID_ARG;
+  if (N == 0) return SPD_OK;
+  if (!q || !unified_kv || !win_start || !win_len || !attn_sink || !out ||
+      (stream_len > 0 && !kv_stream))
+    return SPD_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(unified_kv, 16) || !aligned(out, 16) || !aligned(win_start, 4) ||
+      !aligned(win_len, 4) || !aligned(attn_sink, 4) || (kv_stream && !aligned(kv_stream, 4)))
+    return SPD_ERR_INVALID_ARG;
+  const size_t qo_bytes = (size_t)N * H * D * 2;
+  if (overlap(out, qo_bytes, q, qo_bytes) ||
+      overlap(out, qo_bytes, unified_kv, (size_t)num_rows * D * 2) ||
+      overlap(out, qo_bytes, attn_sink, (size_t)H * 4) ||
+      overlap(out, qo_bytes, win_start, (size_t)N * 4) ||
+      overlap(out, qo_bytes, win_len, (size_t)N * 4) ||
+      (kv_stream && overlap(out, qo_bytes, kv_stream, (size_t)stream_len * 4)))
+    return SPD_ERR_INVALID_ARG;
+
+  spd::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint16_t*>(unified_kv);
+  a.kv_indices = kv_stream;
+  a.sink = attn_sink;
+  a.out = static_cast<uint16_t*>(out);
+  a.qk_scale = (float)((double)softmax_scale * kLog2eD);
+  a.N = N;
+  a.H = H;
+  a.head_groups = 1;
+  a.splits = 1;
+  a.split_rows = 1 << 30;
+  a.win_start = win_start;
+  a.win_len = win_len;
+  a.stream_len = stream_len;
+  a.tokens_per_group = T;
+  const hipError_t e = spd::launch_prefill(a, D, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPD_OK : SPD_ERR_HIP;
+}
+
 SPD_API spd_status sparse_decode_attn_fp8(const void* q, const void* kv_fp8,
                                           const float* kv_scale, int64_t num_rows,
                                           const int32_t* kv_indices, const int32_t* kv_indptr,

@@ -351,7 +351,10 @@ __device__ __forceinline__ bf16x8 wide_p_operand(bf16x4 p0, bf16x4 p1) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-template <int D, int W, bool kPaged>
+// kWin: 0 = CSR slices; 1 = one token a workgroup whose slice is its window of
+// the index stream (no masks); 2 = tokens_per_group tokens share the union of
+// their windows, each wave masking the rows outside its token's window.
+template <int D, int W, bool kPaged, int kWin = 0>
 __global__ void __launch_bounds__(64 * W) attn_wide_kernel(AttnArgs a) {
   constexpr int kTile = 32;
   constexpr int kRowBytes = 2 * D;
@@ -386,27 +389,75 @@ __global__ void __launch_bounds__(64 * W) attn_wide_kernel(AttnArgs a) {
 
   int L;
   const int32_t* part = nullptr;
-  if constexpr (kPaged) {
-    L = stage_paged_list<64 * W>(a, t, sidx, scount);
+  int tok = t;                       // this wave's token
+  int h0 = hg * kHeads + wave * 32;  // first head of this wave (H % kHeads == 0)
+  int lo = 0, hi = 0x7fffffff;       // shared windows: this wave's rows of the slice
+  if constexpr (kWin == 1) {
+    const ScalarI32Ptr ws = (ScalarI32Ptr)a.win_start, wl = (ScalarI32Ptr)a.win_len;
+    const int s0 = ws[t], l0 = wl[t];
+    L = (s0 >= 0 && l0 > 0 && (int64_t)s0 + l0 <= a.stream_len) ? l0 : 0;
+    part = a.kv_indices + (L > 0 ? s0 : 0);
+    if (L <= 0) {
+      zero_heads<D>(a.out, a.H, t, h0, 32, lane, 64);
+      return;
+    }
+  } else if constexpr (kWin == 2) {
+    // tokens t0 .. t0 + T - 1 share the workgroup; the slice is the union of
+    // their windows of the index stream, and wave w serves token
+    // t0 + 32 w / H, heads 32 w mod H .. + 31.  A window that is empty or
+    // leaves the stream counts as empty.
+    const int T = a.tokens_per_group;
+    const int t0 = item * T;
+    tok = t0 + (wave * 32) / a.H;
+    h0 = (wave * 32) % a.H;
+    const ScalarI32Ptr ws = (ScalarI32Ptr)a.win_start, wl = (ScalarI32Ptr)a.win_len;
+    auto window_ok = [&](int s0, int l0) {
+      return s0 >= 0 && l0 > 0 && (int64_t)s0 + l0 <= a.stream_len;
+    };
+    int u0 = 0x7fffffff, u1 = 0;
+    for (int k = 0; k < T; ++k) {
+      const int tk = t0 + k;
+      if (tk < a.N && window_ok(ws[tk], wl[tk])) {
+        u0 = min(u0, ws[tk]);
+        u1 = max(u1, ws[tk] + wl[tk]);
+      }
+    }
+    L = u1 > u0 ? u1 - u0 : 0;
+    part = a.kv_indices + (L > 0 ? u0 : 0);
+    lo = hi = 0;
+    if (tok < a.N && window_ok(ws[tok], wl[tok])) {
+      lo = ws[tok] - u0;
+      hi = lo + wl[tok];
+    }
+    if (L <= 0) {
+      if (tok < a.N) zero_heads<D>(a.out, a.H, tok, h0, 32, lane, 64);
+      return;
+    }
   } else {
-    const ScalarI32Ptr indptr = (ScalarI32Ptr)a.kv_indptr;
-    const int row0 = indptr[t];
-    L = indptr[t + 1] - row0;
-    part = a.kv_indices + row0;
-  }
-  const int h0 = hg * kHeads + wave * 32;  // first head of this wave (H % kHeads == 0)
-  if (L <= 0) {
-    zero_heads<D>(a.out, a.H, t, h0, 32, lane, 64);
-    return;
+    if constexpr (kPaged) {
+      L = stage_paged_list<64 * W>(a, t, sidx, scount);
+    } else {
+      const ScalarI32Ptr indptr = (ScalarI32Ptr)a.kv_indptr;
+      const int row0 = indptr[t];
+      L = indptr[t + 1] - row0;
+      part = a.kv_indices + row0;
+    }
+    if (L <= 0) {
+      zero_heads<D>(a.out, a.H, t, h0, 32, lane, 64);
+      return;
+    }
   }
 
   bf16x8 q0[kKSteps], q1[kKSteps];  // Q^T operands of head blocks 0 and 1
-  load_q<D>(a.q, (int64_t)t * a.H + h0 + n16, g, q0);
-  load_q<D>(a.q, (int64_t)t * a.H + h0 + 16 + n16, g, q1);
+  const int64_t qrow = (int64_t)(kWin == 2 ? (tok < a.N ? tok : a.N - 1) : t) * a.H + h0;
+  load_q<D>(a.q, qrow + n16, g, q0);
+  load_q<D>(a.q, qrow + 16 + n16, g, q1);
   if (wave == 0) {  // the workgroup's kHeads sinks (kHeads <= 128), one LDS-DMA per 64
 #pragma unroll
-    for (int c = 0; c < kHeads; c += 64)
-      dma_4B(a.sink + hg * kHeads + c + lane, __builtin_amdgcn_readfirstlane(lds_addr(ssink + c)));
+    for (int c = 0; c < kHeads; c += 64) {
+      const int hs = kWin == 2 ? (c + lane) % a.H : hg * kHeads + c + lane;
+      dma_4B(a.sink + hs, __builtin_amdgcn_readfirstlane(lds_addr(ssink + c)));
+    }
   }
 
   const TileOffsets<D, 1> off(n16, g);
@@ -500,15 +551,20 @@ __global__ void __launch_bounds__(64 * W) attn_wide_kernel(AttnArgs a) {
         float x0[8], x1[8];
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          const bool v0 = 4 * g + i4 < nvalid, v1 = 16 + 4 * g + i4 < nvalid;
+          bool v0 = 4 * g + i4 < nvalid, v1 = 16 + 4 * g + i4 < nvalid;
+          if constexpr (kWin == 2) {  // rows of the slice outside this wave's window
+            const int j = sc + i * kTile + 4 * g + i4;
+            v0 = v0 && j >= lo && j < hi;
+            v1 = v1 && j + 16 >= lo && j + 16 < hi;
+          }
           x0[i4] = v0 ? s00[i4] * a.qk_scale : -INFINITY;
           x0[4 + i4] = v1 ? s10[i4] * a.qk_scale : -INFINITY;
           x1[i4] = v0 ? s01[i4] * a.qk_scale : -INFINITY;
           x1[4 + i4] = v1 ? s11[i4] * a.qk_scale : -INFINITY;
         }
         __bf16 p0[8], p1[8];
-        over |= softmax_tile<8>(x0, sk0, g, first0, m0, mt0, l0, p0);
-        over |= softmax_tile<8>(x1, sk1, g, first1, m1, mt1, l1, p1);
+        over |= softmax_tile<8, kWin == 2>(x0, sk0, g, first0, m0, mt0, l0, p0);
+        over |= softmax_tile<8, kWin == 2>(x1, sk1, g, first1, m1, mt1, l1, p1);
         bf16x8 pb[2];  // B operands for rows 0-15 and 16-31
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
@@ -562,9 +618,16 @@ __global__ void __launch_bounds__(64 * W) attn_wide_kernel(AttnArgs a) {
   // 4 hf + e as element 4 e4 + e of acc[dt]; its denominator is block n / 16's
   // l of head n % 16, which every lane with lane % 16 == n % 16 holds.
   const float lb0 = group_sum4(l0), lb1 = group_sum4(l1);
+  if constexpr (kWin == 2) {
+    if (tok >= a.N) return;
+    if (hi <= lo) {  // this wave's token has an empty window: zeros
+      zero_heads<D>(a.out, a.H, tok, h0, 32, lane, 64);
+      return;
+    }
+  }
   const int n = lane & 31, hf = lane >> 5;
   const float inv = 1.0f / (n < 16 ? lb0 : lb1);
-  uint16_t* op = a.out + ((int64_t)t * a.H + h0 + n) * D + 4 * hf;
+  uint16_t* op = a.out + ((int64_t)tok * a.H + h0 + n) * D + 4 * hf;
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
@@ -826,6 +889,29 @@ hipError_t launch_wide(const AttnArgs& a, hipStream_t stream) {
 }
 
 template <int D>
+hipError_t launch_prefill_d(const AttnArgs& a, hipStream_t stream) {
+  // a workgroup's 32 * W query rows are tokens_per_group tokens x H heads
+  const long long groups = ((long long)a.N + a.tokens_per_group - 1) / a.tokens_per_group;
+  const int w = a.tokens_per_group * a.H / 32;
+  const bool shared = a.tokens_per_group > 1;
+  if (w == 4 && shared)
+    hipLaunchKernelGGL((attn_wide_kernel<D, 4, false, 2>), dim3((unsigned)groups), dim3(256), 0,
+                       stream, a);
+  else if (w == 4)
+    hipLaunchKernelGGL((attn_wide_kernel<D, 4, false, 1>), dim3((unsigned)groups), dim3(256), 0,
+                       stream, a);
+  else if (w == 2 && shared)
+    hipLaunchKernelGGL((attn_wide_kernel<D, 2, false, 2>), dim3((unsigned)groups), dim3(128), 0,
+                       stream, a);
+  else if (w == 2)
+    hipLaunchKernelGGL((attn_wide_kernel<D, 2, false, 1>), dim3((unsigned)groups), dim3(128), 0,
+                       stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream) {
   if (plan.mode == kModeRows) {
     if (a.paged)
@@ -944,6 +1030,16 @@ bool make_attn_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t sp
                                         (size_t)(D + 2) * sizeof(float)
                                   : 0;
   return true;
+}
+
+hipError_t launch_prefill(const AttnArgs& a, int D, hipStream_t stream) {
+  switch (D) {
+    case 64: return launch_prefill_d<64>(a, stream);
+    case 128: return launch_prefill_d<128>(a, stream);
+    case 256: return launch_prefill_d<256>(a, stream);
+    case 512: return launch_prefill_d<512>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_attention(const AttnArgs& a, int D, const AttnPlan& plan, hipStream_t stream) {

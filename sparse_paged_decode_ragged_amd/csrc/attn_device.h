@@ -367,7 +367,12 @@ __device__ __forceinline__ float group_sum4(float v) {
 // recomputes the whole state with m = mtrue, the running maximum tracked
 // here, which no score can exceed.  lpart is this lane's share of the
 // denominator: it sums the same bf16-rounded weights the PV product uses.
-template <int R>
+//
+// kGuard: the state may see tiles in which every row is masked before its
+// first unmasked one (windows that start inside a shared tile range); such a
+// tile with no sink leaves m at -inf, so the state stays "first" and its
+// weights are 0 instead of exp2(-inf - -inf).
+template <int R, bool kGuard = false>
 __device__ __forceinline__ bool softmax_tile(const float (&x)[R], float sink_l2, int g,
                                              bool& first, float& m, float& mtrue, float& lpart,
                                              __bf16 (&p)[R]) {
@@ -379,13 +384,14 @@ __device__ __forceinline__ bool softmax_tile(const float (&x)[R], float sink_l2,
   if (first) {
     m = fmaxf(sink_l2, mx);
     lpart = (g == 0 && sink_l2 > -INFINITY) ? __builtin_amdgcn_exp2f(sink_l2 - m) : 0.f;
-    first = false;
+    first = kGuard ? m == -INFINITY : false;
   }
   const bool over = __builtin_amdgcn_ballot_w64(mx > m + kRaise) != 0;
   float psum = 0.f;
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    p[j] = (__bf16)__builtin_amdgcn_exp2f(x[j] - m);
+    const float e = __builtin_amdgcn_exp2f(x[j] - m);
+    p[j] = (__bf16)(kGuard && m == -INFINITY ? 0.f : e);
     psum += (float)p[j];
   }
   lpart += psum;

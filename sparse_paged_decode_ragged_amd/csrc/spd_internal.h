@@ -52,6 +52,14 @@ struct AttnArgs {
   const int32_t* block_table;  // [N][max_blocks]
   int32_t topk, max_blocks, win, k_per_block, swa_pages;
   uint32_t comp_limit;         // min(max_blocks * k_per_block, 2^31)
+  // Shared-window prefill (sparse_prefill_attn): kv_indices is one index
+  // stream and token t attends to kv_indices[win_start[t] : + win_len[t]];
+  // a workgroup takes tokens_per_group consecutive tokens, whose
+  // tokens_per_group * H query rows fill its 2 or 4 waves of 32 heads.
+  const int32_t* win_start;    // [N]
+  const int32_t* win_len;      // [N]
+  int64_t stream_len;
+  int32_t tokens_per_group;
   // FP8 pool (sparse_decode_attn_fp8): row r is kv_scale[r] * e4m3(kv8[r][:]);
   // kv is not read.
   const uint8_t* kv8;          // [num_rows][D] OCP e4m3 codes
@@ -67,6 +75,10 @@ hipError_t launch_attention(const AttnArgs& args, int D, const AttnPlan& plan, h
 // Attention over an FP8 pool: rows mode (workgroup = token x 16 heads), no
 // split; args.kv8 / args.kv_scale replace args.kv.
 hipError_t launch_attention_fp8(const AttnArgs& args, int D, hipStream_t stream);
+
+// Shared-window prefill: 32-head waves, two or four per workgroup
+// (tokens_per_group x H = 64 or 128 query rows), no split.
+hipError_t launch_prefill(const AttnArgs& args, int D, hipStream_t stream);
 
 struct BuildArgs {
   const int32_t* state_slot;

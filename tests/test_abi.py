@@ -35,6 +35,8 @@ def lib():
     L.quantize_kv_fp8.argtypes = [P, P, i32, i32, P, P, i64, P]
     L.fused_qk_norm_rope_swa_store.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, i32, i32, P,
                                                i32, P, P, P, i64, i32, i32, i32, P]
+    L.sparse_prefill_attn.argtypes = [P, P, i64, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32,
+                                      i32, P]
     L.spd_status_string.argtypes = [ctypes.c_int]
     L.spd_status_string.restype = ctypes.c_char_p
     return L
@@ -274,3 +276,32 @@ def test_producer_rejects_bad_arguments(lib):
     assert _prod(lib, pool=FAKE * 16) == INVALID         # pool over q_out
     assert _prod(lib, pool=FAKE * 32 - 4096) == INVALID  # pool over kv
     assert _prod(lib, fp8=FAKE * 8192, sc=FAKE * 8192 + 1000) == INVALID   # scales in the codes
+
+
+def _pre(lib, q=FAKE, kv=FAKE * 64, rows=100, stream=FAKE * 128, slen=1000, ws=FAKE * 144,
+         wl=FAKE * 160, sink=FAKE * 176, scale=0.1, out=FAKE * 4096, N=4, H=64, D=512, T=0):
+    return lib.sparse_prefill_attn(q, kv, rows, stream, slen, ws, wl, sink, scale, out, N, H, D,
+                                   T, None)
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    assert _pre(lib, N=0) == OK
+    assert _pre(lib, N=-1) == INVALID
+    assert _pre(lib, rows=0) == INVALID
+    assert _pre(lib, slen=-1) == INVALID
+    assert _pre(lib, slen=1 << 31) == INVALID
+    assert _pre(lib, H=48) == UNSUPPORTED       # 128 / H tokens per workgroup: H in {32, 64, 128}
+    assert _pre(lib, H=256) == UNSUPPORTED
+    assert _pre(lib, T=-1) == INVALID
+    assert _pre(lib, T=3) == UNSUPPORTED         # 3 x 64 query rows fill no workgroup
+    assert _pre(lib, H=128, T=2) == UNSUPPORTED
+    assert _pre(lib, H=32, T=1) == UNSUPPORTED
+    assert _pre(lib, D=96) == UNSUPPORTED
+    assert _pre(lib, scale=float("inf")) == INVALID
+    assert _pre(lib, stream=None) == INVALID     # a non-empty stream needs its pointer
+    assert _pre(lib, ws=None) == INVALID
+    assert _pre(lib, wl=None) == INVALID
+    assert _pre(lib, kv=FAKE * 64 + 8) == INVALID
+    assert _pre(lib, stream=FAKE * 128 + 2) == INVALID
+    assert _pre(lib, out=FAKE) == INVALID         # over q
+    assert _pre(lib, out=FAKE * 128 - 1024) == INVALID   # over the stream

@@ -49,6 +49,13 @@ def test_prefill_sliding_reuse_small():
     w = W.prefill(N=64, H=2, D=64, P=1 << 16, max_len=640)
     L = np.diff(w.kv_indptr).astype(np.int64)
     assert L.min() >= 1 and L.max() <= 640
+    # the lists are exactly the windows of the stream (none cut at its end)
+    m = w.meta
+    assert np.array_equal(L, m["win_len"])
+    for t in range(64):
+        s0 = m["win_start"][t]
+        assert np.array_equal(w.kv_indices[w.kv_indptr[t]:w.kv_indptr[t + 1]],
+                              m["stream"][s0:s0 + m["win_len"][t]])
     # consecutive tokens share all but ceil(L_t/10) leading entries of the stream
     for t in range(63):
         a = w.kv_indices[w.kv_indptr[t]:w.kv_indptr[t + 1]]

@@ -34,6 +34,7 @@ Configurations (sizes from the benchmark definitions of this path):
                sliding reuse: one stream of uniform indices on [0, P); token t
                takes stream[a_t : a_t + L_t] with a_0 = 0 and
                a_{t+1} = a_t + ceil(L_t / 10); sink ~ N(0, 1); scale 1/sqrt(512).
+               meta holds the stream and each token's window (a_t, L_t).
 """
 from __future__ import annotations
 
@@ -263,11 +264,15 @@ def prefill(seed: int = SEEDS["prefill"], N: int = 8192, H: int = 64, D: int = 5
     starts = np.zeros(N, dtype=np.int64)
     for t in range(1, N):
         starts[t] = starts[t - 1] + (int(L[t - 1]) + 9) // 10
-    stream = rng.integers(0, P, size=int(starts[-1] + L[-1]))
+    stream = rng.integers(0, P, size=int((starts + L).max()))  # every window lies inside it
     lists = [stream[starts[t]: starts[t] + L[t]] for t in range(N)]
     idx, indptr = csr_from_lists(lists)
-    return _finish("prefill", rng, N, H, D, P, 1.0, 1.0 / math.sqrt(D), max_len, kv_indices=idx,
-                   kv_indptr=indptr)
+    w = _finish("prefill", rng, N, H, D, P, 1.0, 1.0 / math.sqrt(D), max_len, kv_indices=idx,
+                kv_indptr=indptr)
+    # the same lists as windows of the one stream they were cut from
+    w.meta.update(stream=stream.astype(np.int32), win_start=starts.astype(np.int32),
+                  win_len=L.astype(np.int32))
+    return w
 
 
 CONFIGS = {"tiny": tiny, "decode_base": decode_base, "ragged": ragged, "large": large,
