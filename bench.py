@@ -517,6 +517,8 @@ def main():
             "bytes_per_call": int(b_pf), "achieved_GBps": round(achf, 1),
             "frac": round(achf / HBM_PEAK_GBPS, 4),
             "speedup_vs_decode_call": round(us_attn / us_pf, 3),
+            "traffic": recorded_traffic("attn_wide_kernel<%d,%d, windows>" % (D, 4 if H == 128 else 2),
+                                        args.workload + "_windows"),
             "tokens_per_workgroup_%d_us" % shared_group: round(us_pf_shared, 3)}
     if us_prod is not None:
         # q read and written, each token's KV row read and stored, the two
