@@ -13,25 +13,26 @@
 // so small batches get one launch):
 //   batches of one workgroup (N <= 16, N * topk <= 2^16): one launch that
 //     counts every token, writes kv_indptr and scatters them;
-//   otherwise:
-//     1. count+scan (N <= 1024, N * topk <= 2^18): one 1024-thread workgroup
-//        counts every token's entries (window length + valid comp_pos entries)
-//        and writes kv_indptr; otherwise 1a. count (one wave per token) and
-//        1b. scan (one workgroup, in place);
-//     2. scatter: one wave per token writes the window slots, then the valid
-//        compressed slots compacted in comp_pos order (ballot + mbcnt).
+//   N <= 1024: 1. count (one wave per token, counts stored inverted in
+//     kv_indptr), 2. look-back scatter: each token's wave sums the counts
+//     below it down to the first entry an earlier wave has already made final,
+//     writes its own final entry and scatters its token -- no wave waits;
+//   otherwise: 1a. count (one wave per token), 1b. scan (one workgroup, in
+//     place), 2. scatter.
+//   A scatter writes the window slots, then the valid compressed slots
+//   compacted in comp_pos order (ballot + mbcnt).
 #include "spd_internal.h"
 
 namespace spd {
 namespace {
 
 constexpr int kBatch = 8;           // comp_pos entries per lane in flight (512 per wave)
-constexpr int kSmallN = 1024;       // largest batch counted by the single-workgroup kernel
+constexpr int kSmallN = 1024;       // largest batch of the look-back builder
 constexpr int kFusedEntries = 1 << 16;  // largest N * topk built by the one-launch kernel
 // Largest batch built by the one-launch kernel: one workgroup.  Beyond it each
 // workgroup recounts every earlier token and the launch saved no longer pays
-// (64 tokens x 512 entries: 10.1 us in one launch, 8.4 us as count+scan and
-// scatter).
+// (64 tokens x 512 entries: 10.1 us in one launch, 6.9 us as count and
+// look-back scatter).
 constexpr int kFusedMaxN = 16;
 
 __device__ __forceinline__ int clamp_swa(int v, int win) { return v < 0 ? 0 : (v > win ? win : v); }
@@ -137,7 +138,8 @@ __device__ __forceinline__ int block_scan_1024(int v, int* wsum, int lane, int w
   return r;
 }
 
-// Small batches (N <= kSmallN): counts and prefix sums in one workgroup.  Wave
+// Counts and prefix sums in one workgroup (used for N == 0, where it writes
+// kv_indptr[0]; correct for any N <= kSmallN).  Wave
 // w counts the tokens w + 16 i, four at a time; the counts meet in LDS and one
 // block scan produces kv_indptr[0..N].
 __global__ void __launch_bounds__(1024) build_count_scan_kernel(BuildArgs a) {
@@ -167,7 +169,10 @@ __global__ void __launch_bounds__(1024) build_count_scan_kernel(BuildArgs a) {
   if (i == 0) a.kv_indptr[0] = 0;
 }
 
-// Large batches, step 1a: one wave per token.
+// Large batches, step 1a: one wave per token.  With kFlagged the count is
+// stored inverted (~count < 0: "a count, not yet a prefix sum") for the
+// look-back scatter, and kv_indptr[0] = 0 is written here.
+template <bool kFlagged>
 __global__ void __launch_bounds__(256) build_count_kernel(BuildArgs a) {
   const int t = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -176,7 +181,11 @@ __global__ void __launch_bounds__(256) build_count_kernel(BuildArgs a) {
   const int tok[1] = {t};
   int n[1];
   count_compressed<1>(a, tok, lane, n);
-  if (lane == 0) a.kv_indptr[t + 1] = clamp_swa(sl, a.win) + n[0];
+  if (lane == 0) {
+    const int c = clamp_swa(sl, a.win) + n[0];
+    a.kv_indptr[t + 1] = kFlagged ? ~c : c;
+    if (kFlagged && t == 0) a.kv_indptr[0] = 0;
+  }
 }
 
 // Large batches, step 1b: kv_indptr[1..N] (counts) -> inclusive prefix sums,
@@ -389,6 +398,41 @@ __global__ void __launch_bounds__(256) validate_kernel(const int32_t* idx, int64
   }
 }
 
+// Step 2 of the look-back builder (N <= kSmallN): one wave per token.  On
+// entry kv_indptr[s+1] holds, for every token s, either ~count(s) (negative)
+// or, once token s's wave has passed this point, the final prefix sum through
+// s (>= 0).  Token t's start is kv_indptr[t] once final; the wave reads the
+// entries below t+1, 64 at a time from the top, adding counts down to the
+// first final entry (kv_indptr[0] = 0 always is one).  Every entry is either
+// kind at every moment and both are exact, so no wave ever waits for another
+// and any interleaving gives the same result.  The wave then writes its own
+// final entry and scatters its token.
+__global__ void __launch_bounds__(256) build_scatter_lookback_kernel(BuildArgs a) {
+  const int t = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= a.N) return;
+  const int32_t* src = lane == 0 ? a.kv_indptr + t + 1 : (lane == 1 ? a.swa_len + t : a.state_slot + t);
+  const int scal = __builtin_nontemporal_load(src);
+  const int own = ~__builtin_amdgcn_readlane(scal, 0);  // this token's count
+  const int sl = clamp_swa(__builtin_amdgcn_readlane(scal, 1), a.win);
+  const int64_t s0 = (int64_t)__builtin_amdgcn_readlane(scal, 2) * a.win;
+  int base = 0;
+  for (int top = t; top >= 0; top -= 64) {  // entries top, top-1, ..., top-63
+    const int e = top - lane;
+    const int v = e > 0 ? __builtin_nontemporal_load(a.kv_indptr + e) : 0;
+    const bool fin = e <= 0 || v >= 0;
+    const unsigned long long m = __ballot(fin);
+    if (m != 0) {
+      const int f = __builtin_ctzll(m);  // highest final entry of this chunk
+      base += wave_sum(lane < f ? ~v : (lane == f ? v : 0));
+      break;
+    }
+    base += wave_sum(~v);
+  }
+  if (lane == 0) a.kv_indptr[t + 1] = base + own;
+  scatter_token(a, t, base, sl, s0, lane);
+}
+
 }  // namespace
 
 hipError_t launch_build_indices(const BuildArgs& a, hipStream_t stream) {
@@ -402,10 +446,15 @@ hipError_t launch_build_indices(const BuildArgs& a, hipStream_t stream) {
                        stream, a);
     return hipGetLastError();
   }
-  if (a.N <= kSmallN && (int64_t)a.N * (a.comp_pos ? a.topk : 0) <= 4 * kFusedEntries) {
-    hipLaunchKernelGGL(build_count_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(build_count_kernel, dim3(blocks), dim3(256), 0, stream, a);
+  if (a.N <= kSmallN) {  // parallel counts, then the look-back scatter
+    hipLaunchKernelGGL(build_count_kernel<true>, dim3(blocks), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(build_scatter_lookback_kernel, dim3(blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  {
+    hipLaunchKernelGGL(build_count_kernel<false>, dim3(blocks), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(build_scan_kernel, dim3(1), dim3(1024), 0, stream, a.kv_indptr, a.N);
