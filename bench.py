@@ -49,7 +49,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="decode_base",
                    choices=["decode_base", "tiny", "ragged", "large", "prefill"])
-    p.add_argument("--mode", default="auto", choices=["auto", "heads", "rows"])
+    p.add_argument("--mode", default="auto", choices=["auto", "heads", "rows", "wide"])
     p.add_argument("--split-rows", type=int, default=0)
     p.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = automatic)")
     p.add_argument("--eager", action="store_true", help="launch kernels directly, no graphs")
@@ -151,6 +151,19 @@ def algorithmic_bytes(indptr: np.ndarray, N: int, H: int, D: int) -> dict:
     return {"sum_L": sum_l, "kv_bytes": kv, "qo_bytes": qo, "B_alg": total, "nonempty": nonempty}
 
 
+def covered_positions(stream_len: int, start: np.ndarray, length: np.ndarray) -> int:
+    """Stream positions that at least one window [start, start + length) covers,
+    counting only the windows the shared-window call reads (length > 0, inside
+    the stream; any other window is empty): that call reads each of them once."""
+    start = np.asarray(start, dtype=np.int64)
+    end = start + np.asarray(length, dtype=np.int64)
+    ok = (start >= 0) & (end > start) & (end <= stream_len)
+    cover = np.zeros(stream_len + 1, dtype=np.int64)
+    np.add.at(cover, start[ok], 1)
+    np.add.at(cover, end[ok], -1)
+    return int((np.cumsum(cover)[:-1] > 0).sum())
+
+
 def cpu_baseline(w, indptr, indices, seconds):
     """The oracle as it stands, on this host's cores, on a bounded token sample."""
     import oracle
@@ -201,7 +214,7 @@ def main():
         print(json.dumps({"per_kernel_KiB_per_dispatch": out, "scale": factors}, indent=1))
         return
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU; --gpus %d is not supported (the path would "
+        print("bench.py measures one GPU; --gpus %d is not supported (the path would "
               "shard by tokens with no exchange step)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
@@ -215,7 +228,8 @@ def main():
     w = W.make(args.workload)
     N, H, D = w.N, w.H, w.D
     max_len = w.max_len
-    mode = {"auto": spd.MODE_AUTO, "heads": spd.MODE_HEADS, "rows": spd.MODE_ROWS}[args.mode]
+    mode = {"auto": spd.MODE_AUTO, "heads": spd.MODE_HEADS, "rows": spd.MODE_ROWS,
+            "wide": spd.MODE_WIDE}[args.mode]
     plan = spd.sparse_decode_attn_plan_info(N, H, D, max_len, args.split_rows, mode)
     ws_bytes = spd.sparse_decode_attn_workspace_size(N, H, D, max_len, args.split_rows, mode)
     b = w.builder
@@ -502,11 +516,7 @@ def main():
         # each stream position some window covers once (its row and its index),
         # the windows and the sinks
         m = w.meta
-        cover = np.zeros(len(m["stream"]) + 1, dtype=np.int64)
-        ok = m["win_len"] > 0
-        np.add.at(cover, m["win_start"][ok], 1)
-        np.add.at(cover, m["win_start"][ok] + m["win_len"][ok], -1)
-        U = int((np.cumsum(cover)[:-1] > 0).sum())
+        U = covered_positions(len(m["stream"]), m["win_start"], m["win_len"])
         b_pf = ab["qo_bytes"] + U * (2 * D + 4) + 8 * N + 4 * H
         achf = b_pf / (us_pf * 1e-6) / 1e9
         rec["prefill"] = {

@@ -1,0 +1,42 @@
+"""Host logic of bench.py (no GPU): the algorithmic byte counts its roofline
+records divide by, the stream coverage of the shared-window record, and the
+refusal of more than one GPU."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_algorithmic_bytes_hand_count():
+    # three tokens with 2, 0, 3 rows; H = 4 heads, D = 8
+    indptr = np.array([0, 2, 2, 5])
+    ab = bench.algorithmic_bytes(indptr, N=3, H=4, D=8)
+    assert ab["sum_L"] == 5 and ab["nonempty"] == 2
+    assert ab["kv_bytes"] == 5 * 8 * 2
+    assert ab["qo_bytes"] == 2 * 4 * 8 * 2 + 3 * 4 * 8 * 2      # q of non-empty tokens, all of out
+    assert ab["B_alg"] == 80 + 320 + 4 * 5 + 4 * 4 + 4 * 4
+
+
+def test_covered_positions_matches_brute_force():
+    rng = np.random.default_rng(0)
+    for _ in range(50):
+        S = int(rng.integers(1, 200))
+        n = int(rng.integers(0, 30))
+        start = rng.integers(-20, S + 20, size=n)
+        length = rng.integers(-5, 60, size=n)
+        seen = set()
+        for s0, l0 in zip(start.tolist(), length.tolist()):
+            if s0 >= 0 and l0 > 0 and s0 + l0 <= S:
+                seen.update(range(s0, s0 + l0))
+        assert bench.covered_positions(S, start, length) == len(seen)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
