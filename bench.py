@@ -90,6 +90,15 @@ def kernel_sources_digest(kernel: str) -> str:
 
 
 
+def fp8_kernel(N: int, H: int, D: int) -> str:
+    """The kernel sparse_decode_attn_fp8 launches: 128-head workgroups on
+    32-head waves when D >= 128, H % 128 == 0 and N * H / 128 >= 256 (one
+    workgroup per CU), else the 16-head rows kernel."""
+    if D >= 128 and H % 128 == 0 and N * (H // 128) >= 256:
+        return "attn_wide_fp8_kernel<%d,4>" % D
+    return "attn_rows_fp8_kernel<%d>" % D
+
+
 def recorded_traffic(kernel: str, workload: str):
     """Per-launch HBM bytes of `kernel` from the committed counter summary
     profiles/hbm_traffic_<workload>.md, or None when there is none or the
@@ -506,9 +515,9 @@ def main():
         b_fp8 = ab["sum_L"] * (D + 4) + ab["qo_bytes"] + 4 * ab["sum_L"] + 4 * (N + 1) + 4 * H
         ach8 = b_fp8 / (us_fp8 * 1e-6) / 1e9
         rec["fp8_pool"] = {
-            "call": "sparse_decode_attn_fp8", "kernel": "attn_rows_fp8_kernel<%d>" % D,
+            "call": "sparse_decode_attn_fp8", "kernel": fp8_kernel(N, H, D),
             "rotating_sets": len(fp8_sets), "us_per_call": round(us_fp8, 3),
-            "traffic": recorded_traffic("attn_rows_fp8_kernel<%d>" % D, args.workload + "_fp8"),
+            "traffic": recorded_traffic(fp8_kernel(N, H, D), args.workload + "_fp8"),
             "tokens_per_s": round(N / (us_fp8 * 1e-6), 1), "bytes_per_call": int(b_fp8),
             "achieved_GBps": round(ach8, 1), "frac": round(ach8 / HBM_PEAK_GBPS, 4)}
     if us_pf is not None:

@@ -271,7 +271,12 @@ SPD_API spd_status sparse_decode_attn_fp8(const void* q, const void* kv_fp8,
       overlap(out, qo_bytes, attn_sink, (size_t)H * 4) ||
       overlap(out, qo_bytes, kv_indptr, (size_t)(N + 1) * 4))
     return SPD_ERR_INVALID_ARG;
-  const long long groups = (H + 15) / 16;
+  // Workgroups of 128 heads on 32-head waves when H % 128 == 0 and the batch
+  // gives every CU one (as for the bf16 pool); 16-head rows workgroups
+  // otherwise.
+  int wide = 0;
+  if (D >= 128 && H % 128 == 0 && (long long)N * (H / 128) >= 256) wide = 4;
+  const long long groups = wide ? H / (32 * wide) : (H + 15) / 16;
   if ((long long)N * groups > 0x7fffffffLL) return SPD_ERR_INVALID_ARG;
 
   spd::AttnArgs a{};
@@ -288,7 +293,7 @@ SPD_API spd_status sparse_decode_attn_fp8(const void* q, const void* kv_fp8,
   a.head_groups = (int32_t)groups;
   a.splits = 1;
   a.split_rows = 1 << 30;
-  const hipError_t e = spd::launch_attention_fp8(a, D, static_cast<hipStream_t>(stream));
+  const hipError_t e = spd::launch_attention_fp8(a, D, wide, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPD_OK : SPD_ERR_HIP;
 }
 

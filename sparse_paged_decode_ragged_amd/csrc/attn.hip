@@ -339,18 +339,6 @@ struct WideVtOffsets {
   __device__ __forceinline__ int at(int dt, int half) const { return v[half][dt & 3] + 256 * (dt >> 2); }
 };
 
-// B operand of the 32x32x16 PV product from the two head blocks' weights of
-// 16 rows (p0: block 0, p1: block 1, each this lane's 4 rows): see above.
-__device__ __forceinline__ bf16x8 wide_p_operand(bf16x4 p0, bf16x4 p1) {
-  const auto x = __builtin_bit_cast(HIP_vector_base<unsigned, 2>::Native_vec_, p0);
-  const auto y = __builtin_bit_cast(HIP_vector_base<unsigned, 2>::Native_vec_, p1);
-  const auto s0 = __builtin_amdgcn_permlane16_swap(x[0], y[0], false, false);
-  const auto s1 = __builtin_amdgcn_permlane16_swap(x[1], y[1], false, false);
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 r = {(unsigned)s0[0], (unsigned)s1[0], (unsigned)s0[1], (unsigned)s1[1]};
-  return __builtin_bit_cast(bf16x8, r);
-}
-
 // kWin: 0 = CSR slices; 1 = one token a workgroup whose slice is its window of
 // the index stream (no masks); 2 = tokens_per_group tokens share the union of
 // their windows, each wave masking the rows outside its token's window.

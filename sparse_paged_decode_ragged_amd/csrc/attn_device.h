@@ -156,6 +156,21 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// B operand of the 32x32x16 PV product (lane (n, kg): P of rows 8kg..8kg+7
+// for head n) from the two 16-head blocks' weights of 16 rows in the 16x16
+// score layout (p0: block 0, p1: block 1, each this lane's 4 rows 4g..4g+3):
+// one v_permlane16_swap per dword, lanes 16..31 of block 0's value trading
+// with lanes 0..15 of block 1's in each half-wave.
+__device__ __forceinline__ bf16x8 wide_p_operand(bf16x4 p0, bf16x4 p1) {
+  const auto x = __builtin_bit_cast(HIP_vector_base<unsigned, 2>::Native_vec_, p0);
+  const auto y = __builtin_bit_cast(HIP_vector_base<unsigned, 2>::Native_vec_, p1);
+  const auto s0 = __builtin_amdgcn_permlane16_swap(x[0], y[0], false, false);
+  const auto s1 = __builtin_amdgcn_permlane16_swap(x[1], y[1], false, false);
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 r = {(unsigned)s0[0], (unsigned)s1[0], (unsigned)s0[1], (unsigned)s1[1]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 __device__ __forceinline__ f32x4 mfma_k16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);

@@ -394,6 +394,263 @@ __global__ void __launch_bounds__(256) attn_rows_fp8_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Wide heads mode over an FP8 pool: workgroup = (token, 32 W heads), W waves
+// of 32 heads sharing every 32-row tile of codes (as attn_wide_kernel over
+// the bf16 pool; no split-L).  Per wave and tile, S^T = K Q^T on 16x16x32
+// MFMAs (K operand: one ds_read_b64 of 8 codes per k-step and 16-row half,
+// shared by both head blocks) and O^T += V^T P^T on 32x32x16 MFMAs (V^T
+// operand: one ds_read_b64_tr_b8 per d-tile and half, laid out below); codes
+// are decoded to bf16 in registers.  Each K and V^T code is read from LDS
+// once per 32 heads: a quarter of the LDS bytes per flop of the 16-head FP8
+// rows kernel.  The row scales multiply scores and weights as there.
+
+// Byte offsets of the 32x32x16 V^T operand reads of an FP8 tile (rows of D
+// codes; 16-byte chunk c of row r stored at c ^ (r & 15)).  Within each
+// 16-lane group the 8-bit transposing read gives destination lane i byte e
+// from source lane 2e + i/8, byte i % 8.  Source lane (G = lane / 16,
+// j = lane % 16) points at row 8 (G / 2) + j / 2, codes 32 dt + 16 (G % 2) +
+// 8 (j % 2) .. + 7; destination lane (G, i) then holds rows 8 (G / 2) .. + 7 of
+// column 32 dt + 16 (G % 2) + i, the A operand of the product (lane (d, kg):
+// rows 8 kg .. 8 kg + 7 of column d).  That is logical chunk 2 dt + G % 2 at
+// byte 8 (j % 2), stored at 2 (dt ^ (sw / 2)) + ((G % 2) ^ (sw % 2)) with sw
+// the row's swizzle: base + 16 ((2 dt) ^ x) with x = (G % 2) ^ sw, computed
+// per read (two VALU ops) rather than held in registers.  The 8 rows of a
+// group sit in 8 different 16-byte bank groups.  Rows 16..31 add 16 D bytes.
+template <int D>
+struct Fp8WideVtOffsets {
+  int base, x;
+  __device__ __forceinline__ explicit Fp8WideVtOffsets(int lane) {
+    const int G = lane >> 4, j = lane & 15;
+    const int row = 8 * (G >> 1) + (j >> 1);
+    const int sw = row_swizzle(row) & (D / 16 - 1);
+    base = row * D + 8 * (j & 1);
+    x = (G & 1) ^ sw;
+  }
+  __device__ __forceinline__ int at(int dt) const { return base + 16 * ((2 * dt) ^ x); }
+};
+
+template <int D, int W>
+__global__ void __launch_bounds__(64 * W) attn_wide_fp8_kernel(AttnArgs a) {
+  constexpr int kTile = 32;
+  constexpr int kStageBytes = kTile * D;
+  constexpr int kKSteps = D / 32;
+  constexpr int kDT = D / 32;                       // 32-wide d-tiles of the PV product
+  constexpr int kRowsPerLoad = 1024 / D;            // rows per LDS-DMA op
+  constexpr int kLoadsPerWave = kTile / kRowsPerLoad / W;
+  constexpr int kRowsPerWave = kTile / W;           // rows (and scales) each wave loads
+  constexpr int kPerTile = kLoadsPerWave + 1;       // and the scale load
+  constexpr int kHeads = 32 * W;
+  // W = 4: one workgroup per CU, three tiles in flight; W = 2: two per CU
+  constexpr int kAhead = W >= 4 ? 3 : 2;
+  constexpr int kStages = kAhead + 1;
+  static_assert(D >= 128 && D <= 512 && D % 64 == 0, "unsupported D");
+  static_assert(kLoadsPerWave >= 1 && kTile % (kRowsPerLoad * W) == 0, "loads must divide");
+  static_assert((kAhead - 1) * kPerTile < 64, "vmcnt range");
+  using Vt = Fp8WideVtOffsets<D>;
+
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(256))) int sidx[kIdxCap];
+  __shared__ __attribute__((aligned(256))) float ssink[kHeads];
+  __shared__ __attribute__((aligned(256))) float sscale[kStages][W][64];
+  __shared__ int sflag[W];
+
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const int hg = item % a.head_groups;
+  const int t = item / a.head_groups;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n16 = lane & 15;
+  const int g = lane >> 4;
+  const int h0 = hg * kHeads + wave * 32;  // first head of this wave (H % kHeads == 0)
+
+  const ScalarI32Ptr indptr = (ScalarI32Ptr)a.kv_indptr;
+  const int row0 = indptr[t];
+  const int L = indptr[t + 1] - row0;
+  const int32_t* part = a.kv_indices + row0;
+  if (L <= 0) {
+    zero_heads<D>(a.out, a.H, t, h0, 32, lane, 64);
+    return;
+  }
+
+  bf16x8 q0[kKSteps], q1[kKSteps];  // Q^T operands of head blocks 0 and 1
+  const int64_t qrow = (int64_t)t * a.H + h0;
+  load_q<D>(a.q, qrow + n16, g, q0);
+  load_q<D>(a.q, qrow + 16 + n16, g, q1);
+  if (wave == 0) {  // the workgroup's kHeads sinks, one LDS-DMA per 64
+#pragma unroll
+    for (int c = 0; c < kHeads; c += 64)
+      dma_4B(a.sink + hg * kHeads + c + lane, __builtin_amdgcn_readfirstlane(lds_addr(ssink + c)));
+  }
+
+  const uint16_t* kv8 = reinterpret_cast<const uint16_t*>(a.kv8);  // rows of D bytes
+  const Fp8Offsets<D> off8(n16, g);
+  const Vt voff(lane);
+
+  float m0 = -INFINITY, l0 = 0.f, mt0 = -INFINITY, sk0 = -INFINITY;
+  float m1 = -INFINITY, l1 = 0.f, mt1 = -INFINITY, sk1 = -INFINITY;
+  f32x16 acc[kDT];
+  for (int pass = 0; pass < 2; ++pass) {
+    bool first0 = pass == 0, first1 = pass == 0;
+    if (pass == 1) {
+      second_pass_state(sk0, mt0, g, m0, l0);
+      second_pass_state(sk1, mt1, g, m1, l1);
+    }
+#pragma unroll
+    for (int i = 0; i < kDT; ++i) acc[i] = f32x16{};
+    bool over = false;
+
+    for (int sc = 0; sc < L; sc += kIdxCap) {
+      const int n = L - sc < kIdxCap ? L - sc : kIdxCap;
+      if (sc > 0 || pass > 0) barrier_lds();  // every wave is done with the stages and indices
+      stage_indices(part, sc, n, sidx, wave, W, lane);
+      wait_vmcnt<0>();
+      barrier_lds();
+      if (pass == 0 && sc == 0) {
+        sk0 = ssink[wave * 32 + n16] * kLog2e;
+        sk1 = ssink[wave * 32 + 16 + n16] * kLog2e;
+      }
+      const int ntiles = (n + kTile - 1) / kTile;
+
+      // this wave's rows of a tile (codes, then their scales: lane l loads
+      // the scale of row l % kRowsPerWave of its part)
+      auto issue_tile = [&](int tile) {
+        const int st = tile % kStages;
+        const int p0 = tile * kTile + wave * kRowsPerWave;
+        issue_rows<D, kLoadsPerWave>(kv8, sidx, n, p0, wave * kRowsPerWave,
+                                     smem + st * kStageBytes + wave * kRowsPerWave * D, lane);
+        const int p = p0 + lane % kRowsPerWave;
+        const int grow = sidx[p < n ? p : n - 1];
+        dma_4B(a.kv_scale + grow, __builtin_amdgcn_readfirstlane(lds_addr(sscale[st][wave])));
+      };
+#pragma unroll
+      for (int k = 0; k < kAhead; ++k)
+        if (k < ntiles) issue_tile(k);
+
+      for (int i = 0; i < ntiles; ++i) {
+        // tile i has landed once at most min(kAhead - 1, ntiles - 1 - i) later
+        // tiles of this wave are still outstanding
+        const int later = ntiles - 1 - i;
+        if (later >= 2 && kAhead >= 3)
+          wait_vmcnt<(kAhead >= 3 ? 2 : 0) * kPerTile>();
+        else if (later >= 1)
+          wait_vmcnt<kPerTile>();
+        else
+          wait_vmcnt<0>();
+        barrier_lds();  // every wave's part of tile i is in LDS; tile i-1's stage is free
+        if (i + kAhead < ntiles) issue_tile(i + kAhead);
+
+        int stoff = (i % kStages) * kStageBytes;
+        asm volatile("" : "+v"(stoff));
+        const unsigned char* st = smem + stoff;
+        const float* scl = sscale[i % kStages][0];
+        const int nvalid = n - i * kTile;
+
+        // S^T = K Q^T: rows 0-15 and 16-31, head blocks 0 and 1.  Per k-step:
+        // the code reads of k-step u + 2, the decode of k-step u, its four
+        // MFMAs (the fence keeps each decode next to its MFMAs, so only two
+        // k-steps of codes are live).
+        f32x4 s00 = {0.f, 0.f, 0.f, 0.f}, s01 = s00, s10 = s00, s11 = s00;
+        {
+          constexpr int kPre = kKSteps < 2 ? kKSteps : 2;
+          u32x2 ra[kKSteps], rb[kKSteps];
+#pragma unroll
+          for (int u = 0; u < kPre; ++u) {
+            ra[u] = *reinterpret_cast<const u32x2*>(st + off8.kq(u));
+            rb[u] = *reinterpret_cast<const u32x2*>(st + off8.kq(u) + 16 * D);
+          }
+#pragma unroll
+          for (int u = 0; u < kKSteps; ++u) {
+            if (u + kPre < kKSteps) {
+              ra[u + kPre] = *reinterpret_cast<const u32x2*>(st + off8.kq(u + kPre));
+              rb[u + kPre] = *reinterpret_cast<const u32x2*>(st + off8.kq(u + kPre) + 16 * D);
+            }
+            const bf16x8 ka = e4m3x8_to_bf16(ra[u]);
+            const bf16x8 kb = e4m3x8_to_bf16(rb[u]);
+            s00 = mfma_k32(ka, q0[u], s00);
+            s01 = mfma_k32(ka, q1[u], s01);
+            s10 = mfma_k32(kb, q0[u], s10);
+            s11 = mfma_k32(kb, q1[u], s11);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+
+        // scales of this lane's rows 4g..4g+3 and 16+4g..16+4g+3 (row r was
+        // loaded by wave r / kRowsPerWave into entry r % kRowsPerWave)
+        const int r0 = 4 * g, r1 = 16 + 4 * g;
+        const f32x4 c0 = *reinterpret_cast<const f32x4*>(
+            scl + (r0 / kRowsPerWave) * 64 + r0 % kRowsPerWave);
+        const f32x4 c1 = *reinterpret_cast<const f32x4*>(
+            scl + (r1 / kRowsPerWave) * 64 + r1 % kRowsPerWave);
+        float x0[8], x1[8];
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const bool v0 = 4 * g + i4 < nvalid, v1 = 16 + 4 * g + i4 < nvalid;
+          x0[i4] = v0 ? s00[i4] * (a.qk_scale * c0[i4]) : -INFINITY;
+          x0[4 + i4] = v1 ? s10[i4] * (a.qk_scale * c1[i4]) : -INFINITY;
+          x1[i4] = v0 ? s01[i4] * (a.qk_scale * c0[i4]) : -INFINITY;
+          x1[4 + i4] = v1 ? s11[i4] * (a.qk_scale * c1[i4]) : -INFINITY;
+        }
+        float pf0[8], pf1[8];
+        over |= softmax_tile_f32<8>(x0, sk0, g, first0, m0, mt0, l0, pf0);
+        over |= softmax_tile_f32<8>(x1, sk1, g, first1, m1, mt1, l1, pf1);
+        bf16x8 pb[2];  // B operands for rows 0-15 and 16-31
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const f32x4 c = rb == 0 ? c0 : c1;
+          bf16x4 a0, a1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a0[e] = (__bf16)(pf0[4 * rb + e] * c[e]);
+            a1[e] = (__bf16)(pf1[4 * rb + e] * c[e]);
+          }
+          pb[rb] = wide_p_operand(a0, a1);
+        }
+
+        // O^T += V^T P^T: per d-tile, the transposing reads of d-tile u + 2,
+        // the decode of d-tile u and its two MFMAs.
+        {
+          constexpr int kPre = kDT < 2 ? kDT : 2;
+          u32x2 va[kDT], vb[kDT];
+          auto read_vt = [&](int u) {
+            const int o = voff.at(u);
+            va[u] = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((LdsV2i32*)(st + o)));
+            vb[u] = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((LdsV2i32*)(st + o + 16 * D)));
+          };
+#pragma unroll
+          for (int u = 0; u < kPre; ++u) read_vt(u);
+#pragma unroll
+          for (int u = 0; u < kDT; ++u) {
+            if (u + kPre < kDT) read_vt(u + kPre);
+            acc[u] = mfma32(e4m3x8_to_bf16(va[u]), pb[0], acc[u]);
+            acc[u] = mfma32(e4m3x8_to_bf16(vb[u]), pb[1], acc[u]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    }
+    if (!workgroup_any(over, sflag, wave, W)) break;
+  }
+
+  // lane (n, hf) = lane n + 32 hf holds, for head h0 + n, d = 32 dt + 8 e4 +
+  // 4 hf + e as element 4 e4 + e of acc[dt]; its denominator is block n / 16's
+  // l of head n % 16, which every lane with lane % 16 == n % 16 holds.
+  const float lb0 = group_sum4(l0), lb1 = group_sum4(l1);
+  const int nn = lane & 31, hf = lane >> 5;
+  const float inv = 1.0f / (nn < 16 ? lb0 : lb1);
+  uint16_t* op = a.out + ((int64_t)t * a.H + h0 + nn) * D + 4 * hf;
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const f32x4 v = {acc[dt][4 * e4], acc[dt][4 * e4 + 1], acc[dt][4 * e4 + 2], acc[dt][4 * e4 + 3]};
+      store_bf16x4(op + 32 * dt + 8 * e4, v, inv);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Quantising store: one wave per source row, D / 64 values per lane; row i
 // goes to pool row slots[i] (i when slots is null); a slot outside
 // [0, num_rows) skips the row.
@@ -412,9 +669,16 @@ __global__ void __launch_bounds__(256) quantize_fp8_kernel(QuantArgs a) {
 }
 
 template <int D>
-hipError_t launch_fp8_d(const AttnArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_rows_fp8_kernel<D>), dim3((unsigned)(a.N * a.head_groups)), dim3(256),
-                     0, stream, a);
+hipError_t launch_fp8_d(const AttnArgs& a, int wide_waves, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.N * a.head_groups));
+  if constexpr (D >= 128) {
+    if (wide_waves == 4) {
+      hipLaunchKernelGGL((attn_wide_fp8_kernel<D, 4>), grid, dim3(256), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
+  if (wide_waves != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_rows_fp8_kernel<D>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -427,12 +691,12 @@ hipError_t launch_quant_d(const QuantArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_attention_fp8(const AttnArgs& a, int D, hipStream_t stream) {
+hipError_t launch_attention_fp8(const AttnArgs& a, int D, int wide_waves, hipStream_t stream) {
   switch (D) {
-    case 64: return launch_fp8_d<64>(a, stream);
-    case 128: return launch_fp8_d<128>(a, stream);
-    case 256: return launch_fp8_d<256>(a, stream);
-    case 512: return launch_fp8_d<512>(a, stream);
+    case 64: return launch_fp8_d<64>(a, wide_waves, stream);
+    case 128: return launch_fp8_d<128>(a, wide_waves, stream);
+    case 256: return launch_fp8_d<256>(a, wide_waves, stream);
+    case 512: return launch_fp8_d<512>(a, wide_waves, stream);
     default: return hipErrorInvalidValue;
   }
 }

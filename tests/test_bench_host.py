@@ -40,3 +40,12 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_fp8_kernel_name_follows_the_plan():
+    # decode_base (H = 64): rows kernel; large (N = 1024, H = 128): one
+    # 128-head workgroup per token fills the chip
+    assert bench.fp8_kernel(64, 64, 512) == "attn_rows_fp8_kernel<512>"
+    assert bench.fp8_kernel(1024, 128, 512) == "attn_wide_fp8_kernel<512,4>"
+    assert bench.fp8_kernel(255, 128, 512) == "attn_rows_fp8_kernel<512>"
+    assert bench.fp8_kernel(256, 128, 64) == "attn_rows_fp8_kernel<64>"

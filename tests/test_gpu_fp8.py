@@ -195,3 +195,81 @@ def test_decode_base_config(spd):
     ref = oracle.sparse_decode_attn_fp8(w.q_bits[tokens], codes, scales, sidx, sptr, w.attn_sink,
                                         w.softmax_scale)
     assert_close(bf16_to_f64(out[torch.from_numpy(tokens).to(dev())]), ref, "fp8 decode_base")
+
+
+# --- 128-head workgroups on 32-head waves (H % 128 == 0, N * H / 128 >= 256) ---
+
+WIDE_N = 256  # the smallest batch that takes the 32-head-wave kernel at H = 128
+
+
+def wide_lengths(rng, n, long=()):
+    """Lengths of every kind: empty, 1, around the 32-row tile (31, 32, 33, 63,
+    64, 65), random up to 200, and the given long ones."""
+    L = rng.integers(0, 200, size=n)
+    edge = [0, 1, 31, 32, 33, 63, 64, 65, 0, 2]
+    L[:len(edge)] = edge
+    for i, v in enumerate(long):
+        L[len(edge) + i] = v
+    return L
+
+
+@pytest.mark.parametrize("D", [128, 256, 512])
+def test_wide_attention_matches_oracle(spd, D):
+    log("case fp8 wide attention D=%d" % D)
+    rng = np.random.default_rng(40 + D)
+    H, P = 128, 5000
+    lengths = wide_lengths(rng, WIDE_N, long=(2300,) if D == 512 else ())
+    _, codes, scales = fp8_pool(rng, P, D, zero_rows=rng.choice(P, size=20, replace=False))
+    idx, ptr = W.csr_from_lists([rng.integers(0, P, size=L) for L in lengths])
+    q_bits = W.normal_bf16(rng, (WIDE_N, H, D))
+    sink = rng.standard_normal(H).astype(np.float32)
+    sink[5] = -np.inf
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    out = run_fp8(spd, q_bits, codes, scales, idx, ptr, sink, scale)
+    ref = oracle.sparse_decode_attn_fp8(q_bits, codes, scales, idx, ptr, sink, scale)
+    assert_close(bf16_to_f64(out), ref, "fp8 wide D=%d" % D)
+    empty = np.nonzero(np.diff(ptr) == 0)[0]
+    assert torch.all(out[torch.from_numpy(empty).to(dev())].view(torch.int16) == 0)
+
+
+def test_wide_every_code_decodes_exactly(spd):
+    """As test_every_code_decodes_exactly, on the 32-head-wave kernel: each
+    token's slice is one row and there is no sink, so the output is the row,
+    scale * e4m3(code), exactly."""
+    log("case fp8 wide every code")
+    H, D, P = 128, 512, 8
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    codes = np.stack([np.resize(np.roll(finite, 37 * r), D) for r in range(P)]).astype(np.uint8)
+    scales = (2.0 ** np.arange(-4, 4)).astype(np.float32)
+    idx, ptr = W.csr_from_lists([[t % P] for t in range(WIDE_N)])
+    q_bits = W.normal_bf16(np.random.default_rng(6), (WIDE_N, H, D))
+    sink = np.full(H, -np.inf, dtype=np.float32)
+    out = run_fp8(spd, q_bits, codes, scales, idx, ptr, sink, 0.05)
+    ref = oracle.sparse_decode_attn_fp8(q_bits, codes, scales, idx, ptr, sink, 0.05)
+    assert np.array_equal(bf16_to_f64(out), ref)
+
+
+def test_wide_attention_second_pass(spd):
+    """Rows planted late in some slices score far above their first tile, on
+    the 32-head-wave kernel (as test_attention_second_pass)."""
+    log("case fp8 wide second pass")
+    rng = np.random.default_rng(12)
+    H, D, P = 128, 512, 6000
+    lengths = rng.integers(1, 120, size=WIDE_N)
+    lengths[[3, 77, 200]] = [300, 700, 2100]
+    lists = [rng.choice(P, size=L, replace=False) for L in lengths]
+    idx, ptr = W.csr_from_lists(lists)
+    q_bits = W.normal_bf16(rng, (WIDE_N, H, D))
+    q = W.bf16_to_f32(q_bits)
+    x = rng.standard_normal((P, D)).astype(np.float32)
+    for t, (p2, p1) in {3: (100, 290), 77: (150, 650), 200: (1000, 2090)}.items():
+        x[lists[t][p1]] = 4.0 * q[t, 0]            # score ~ 90 in log2 units
+        x[lists[t][p2]] = 3.9 * q[t, 0]            # about 2 lower
+    codes, scales = oracle.quantize_fp8(W.bf16_bits(x))
+    sink = rng.standard_normal(H).astype(np.float32)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    out = run_fp8(spd, q_bits, codes, scales, idx, ptr, sink, scale)
+    tokens = np.array([0, 3, 77, 200, 255])
+    sidx, sptr = W.csr_from_lists([lists[t] for t in tokens])
+    ref = oracle.sparse_decode_attn_fp8(q_bits[tokens], codes, scales, sidx, sptr, sink, scale)
+    assert_close(bf16_to_f64(out[torch.from_numpy(tokens).to(dev())]), ref, "fp8 wide second pass")
