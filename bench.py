@@ -91,11 +91,14 @@ def kernel_sources_digest(kernel: str) -> str:
 
 
 def fp8_kernel(N: int, H: int, D: int) -> str:
-    """The kernel sparse_decode_attn_fp8 launches: 128-head workgroups on
-    32-head waves when D >= 128, H % 128 == 0 and N * H / 128 >= 256 (one
-    workgroup per CU), else the 16-head rows kernel."""
-    if D >= 128 and H % 128 == 0 and N * (H // 128) >= 256:
-        return "attn_wide_fp8_kernel<%d,4>" % D
+    """The kernel sparse_decode_attn_fp8 launches: workgroups of 32 W heads
+    on 32-head waves when D >= 128 and H % 64 == 0 (W = 4 when H % 128 == 0,
+    else 2) and the batch gives one workgroup per CU (W = 4) or two (W = 2),
+    else the 16-head rows kernel."""
+    if D >= 128 and H % 64 == 0:
+        w = 4 if H % 128 == 0 else 2
+        if N * (H // (32 * w)) >= (256 if w == 4 else 512):
+            return "attn_wide_fp8_kernel<%d,%d>" % (D, w)
     return "attn_rows_fp8_kernel<%d>" % D
 
 

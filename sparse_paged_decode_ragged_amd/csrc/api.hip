@@ -271,11 +271,15 @@ SPD_API spd_status sparse_decode_attn_fp8(const void* q, const void* kv_fp8,
       overlap(out, qo_bytes, attn_sink, (size_t)H * 4) ||
       overlap(out, qo_bytes, kv_indptr, (size_t)(N + 1) * 4))
     return SPD_ERR_INVALID_ARG;
-  // Workgroups of 128 heads on 32-head waves when H % 128 == 0 and the batch
-  // gives every CU one (as for the bf16 pool); 16-head rows workgroups
-  // otherwise.
+  // As for the bf16 pool: 32-head waves (128 heads a workgroup when
+  // H % 128 == 0, else 64) once the batch gives every CU a workgroup (two
+  // per CU for 64-head workgroups); 16-head rows workgroups otherwise.
   int wide = 0;
-  if (D >= 128 && H % 128 == 0 && (long long)N * (H / 128) >= 256) wide = 4;
+  if (D >= 128 && H % 64 == 0) {
+    const int w = H % 128 == 0 ? 4 : 2;
+    const long long items = (long long)N * (H / (32 * w));
+    if (items >= (w == 4 ? 256 : 512)) wide = w;
+  }
   const long long groups = wide ? H / (32 * wide) : (H + 15) / 16;
   if ((long long)N * groups > 0x7fffffffLL) return SPD_ERR_INVALID_ARG;
 

@@ -676,6 +676,10 @@ hipError_t launch_fp8_d(const AttnArgs& a, int wide_waves, hipStream_t stream) {
       hipLaunchKernelGGL((attn_wide_fp8_kernel<D, 4>), grid, dim3(256), 0, stream, a);
       return hipGetLastError();
     }
+    if (wide_waves == 2) {
+      hipLaunchKernelGGL((attn_wide_fp8_kernel<D, 2>), grid, dim3(128), 0, stream, a);
+      return hipGetLastError();
+    }
   }
   if (wide_waves != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL((attn_rows_fp8_kernel<D>), grid, dim3(256), 0, stream, a);

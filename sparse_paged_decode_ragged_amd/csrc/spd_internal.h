@@ -74,8 +74,8 @@ hipError_t launch_attention(const AttnArgs& args, int D, const AttnPlan& plan, h
 
 // Attention over an FP8 pool: rows mode (workgroup = token x 16 heads), no
 // split; args.kv8 / args.kv_scale replace args.kv.
-// wide_waves: 0 = rows decomposition (16-head waves); 4 = workgroups of 128
-// heads on 32-head waves (H % 128 == 0, D >= 128)
+// wide_waves: 0 = rows decomposition (16-head waves); 2 or 4 = workgroups of
+// 32 * wide_waves heads on 32-head waves (H % (32 * wide_waves) == 0, D >= 128)
 hipError_t launch_attention_fp8(const AttnArgs& args, int D, int wide_waves, hipStream_t stream);
 
 // Shared-window prefill: 32-head waves, two or four per workgroup

@@ -197,9 +197,11 @@ def test_decode_base_config(spd):
     assert_close(bf16_to_f64(out[torch.from_numpy(tokens).to(dev())]), ref, "fp8 decode_base")
 
 
-# --- 128-head workgroups on 32-head waves (H % 128 == 0, N * H / 128 >= 256) ---
+# --- workgroups of 32-head waves: 128 heads (H % 128 == 0, N * H / 128 >= 256)
+# or 64 heads (H % 64 == 0, N * H / 64 >= 512) ---
 
 WIDE_N = 256  # the smallest batch that takes the 32-head-wave kernel at H = 128
+WIDE_SHAPES = [(128, 256), (64, 512)]  # (H, N): four and two waves a workgroup
 
 
 def wide_lengths(rng, n, long=()):
@@ -213,53 +215,56 @@ def wide_lengths(rng, n, long=()):
     return L
 
 
+@pytest.mark.parametrize("H,N", WIDE_SHAPES)
 @pytest.mark.parametrize("D", [128, 256, 512])
-def test_wide_attention_matches_oracle(spd, D):
-    log("case fp8 wide attention D=%d" % D)
-    rng = np.random.default_rng(40 + D)
-    H, P = 128, 5000
-    lengths = wide_lengths(rng, WIDE_N, long=(2300,) if D == 512 else ())
+def test_wide_attention_matches_oracle(spd, D, H, N):
+    log("case fp8 wide attention D=%d H=%d N=%d" % (D, H, N))
+    rng = np.random.default_rng(40 + D + H)
+    P = 5000
+    lengths = wide_lengths(rng, N, long=(2300,) if D == 512 else ())
     _, codes, scales = fp8_pool(rng, P, D, zero_rows=rng.choice(P, size=20, replace=False))
     idx, ptr = W.csr_from_lists([rng.integers(0, P, size=L) for L in lengths])
-    q_bits = W.normal_bf16(rng, (WIDE_N, H, D))
+    q_bits = W.normal_bf16(rng, (N, H, D))
     sink = rng.standard_normal(H).astype(np.float32)
     sink[5] = -np.inf
     scale = float(np.float32(1.0 / np.sqrt(D)))
     out = run_fp8(spd, q_bits, codes, scales, idx, ptr, sink, scale)
     ref = oracle.sparse_decode_attn_fp8(q_bits, codes, scales, idx, ptr, sink, scale)
-    assert_close(bf16_to_f64(out), ref, "fp8 wide D=%d" % D)
+    assert_close(bf16_to_f64(out), ref, "fp8 wide D=%d H=%d" % (D, H))
     empty = np.nonzero(np.diff(ptr) == 0)[0]
     assert torch.all(out[torch.from_numpy(empty).to(dev())].view(torch.int16) == 0)
 
 
-def test_wide_every_code_decodes_exactly(spd):
+@pytest.mark.parametrize("H,N", WIDE_SHAPES)
+def test_wide_every_code_decodes_exactly(spd, H, N):
     """As test_every_code_decodes_exactly, on the 32-head-wave kernel: each
     token's slice is one row and there is no sink, so the output is the row,
     scale * e4m3(code), exactly."""
-    log("case fp8 wide every code")
-    H, D, P = 128, 512, 8
+    log("case fp8 wide every code H=%d" % H)
+    D, P = 512, 8
     finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
     codes = np.stack([np.resize(np.roll(finite, 37 * r), D) for r in range(P)]).astype(np.uint8)
     scales = (2.0 ** np.arange(-4, 4)).astype(np.float32)
-    idx, ptr = W.csr_from_lists([[t % P] for t in range(WIDE_N)])
-    q_bits = W.normal_bf16(np.random.default_rng(6), (WIDE_N, H, D))
+    idx, ptr = W.csr_from_lists([[t % P] for t in range(N)])
+    q_bits = W.normal_bf16(np.random.default_rng(6), (N, H, D))
     sink = np.full(H, -np.inf, dtype=np.float32)
     out = run_fp8(spd, q_bits, codes, scales, idx, ptr, sink, 0.05)
     ref = oracle.sparse_decode_attn_fp8(q_bits, codes, scales, idx, ptr, sink, 0.05)
     assert np.array_equal(bf16_to_f64(out), ref)
 
 
-def test_wide_attention_second_pass(spd):
+@pytest.mark.parametrize("H,N", WIDE_SHAPES)
+def test_wide_attention_second_pass(spd, H, N):
     """Rows planted late in some slices score far above their first tile, on
     the 32-head-wave kernel (as test_attention_second_pass)."""
-    log("case fp8 wide second pass")
+    log("case fp8 wide second pass H=%d" % H)
     rng = np.random.default_rng(12)
-    H, D, P = 128, 512, 6000
-    lengths = rng.integers(1, 120, size=WIDE_N)
+    D, P = 512, 6000
+    lengths = rng.integers(1, 120, size=N)
     lengths[[3, 77, 200]] = [300, 700, 2100]
     lists = [rng.choice(P, size=L, replace=False) for L in lengths]
     idx, ptr = W.csr_from_lists(lists)
-    q_bits = W.normal_bf16(rng, (WIDE_N, H, D))
+    q_bits = W.normal_bf16(rng, (N, H, D))
     q = W.bf16_to_f32(q_bits)
     x = rng.standard_normal((P, D)).astype(np.float32)
     for t, (p2, p1) in {3: (100, 290), 77: (150, 650), 200: (1000, 2090)}.items():
