@@ -429,6 +429,19 @@ struct Fp8WideVtOffsets {
   __device__ __forceinline__ int at(int dt) const { return base + 16 * ((2 * dt) ^ x); }
 };
 
+// The K-operand reads of Fp8Offsets, computed per read: for k-step s the
+// address is base + 32 (s ^ x) (two VALU ops, no table in registers).
+template <int D>
+struct Fp8KOffsets {
+  int base, x;
+  __device__ __forceinline__ Fp8KOffsets(int n16, int g) {
+    const int w = (row_swizzle(n16) & (D / 16 - 1)) ^ (g >> 1);
+    base = n16 * D + 16 * (w & 1) + 8 * (g & 1);
+    x = w >> 1;
+  }
+  __device__ __forceinline__ int kq(int s) const { return base + 32 * (s ^ x); }
+};
+
 template <int D, int W>
 __global__ void __launch_bounds__(64 * W) attn_wide_fp8_kernel(AttnArgs a) {
   constexpr int kTile = 32;
@@ -484,7 +497,7 @@ __global__ void __launch_bounds__(64 * W) attn_wide_fp8_kernel(AttnArgs a) {
   }
 
   const uint16_t* kv8 = reinterpret_cast<const uint16_t*>(a.kv8);  // rows of D bytes
-  const Fp8Offsets<D> off8(n16, g);
+  const Fp8KOffsets<D> off8(n16, g);
   const Vt voff(lane);
 
   float m0 = -INFINITY, l0 = 0.f, mt0 = -INFINITY, sk0 = -INFINITY;
@@ -517,8 +530,13 @@ __global__ void __launch_bounds__(64 * W) attn_wide_fp8_kernel(AttnArgs a) {
       auto issue_tile = [&](int tile) {
         const int st = tile % kStages;
         const int p0 = tile * kTile + wave * kRowsPerWave;
+        // The lane id is made opaque per call: the loads' per-lane chunk
+        // addresses are loop-invariant, and hoisting them (two registers a
+        // load) would spill the 64-head workgroup's eight loads.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
         issue_rows<D, kLoadsPerWave>(kv8, sidx, n, p0, wave * kRowsPerWave,
-                                     smem + st * kStageBytes + wave * kRowsPerWave * D, lane);
+                                     smem + st * kStageBytes + wave * kRowsPerWave * D, ln);
         const int p = p0 + lane % kRowsPerWave;
         const int grow = sidx[p < n ? p : n - 1];
         dma_4B(a.kv_scale + grow, __builtin_amdgcn_readfirstlane(lds_addr(sscale[st][wave])));
