@@ -279,8 +279,10 @@ SPD_API spd_status sparse_prefill_attn(const void* q, const void* unified_kv, in
  * contract, sink and numerics) with the row value kv_scale[r] * e4m3(code),
  * used as both key and value.  fp32 accumulation; the codes are converted to
  * bf16 exactly, the scale multiplies the row's scores and its softmax weight.
- * Work decomposition: the rows mode of sparse_decode_attn_ex (workgroup =
- * token x 16 heads, no split, no workspace).
+ * Work decomposition (no split, no workspace): workgroups of 32 * W heads on
+ * 32-head waves (W = 4 when H % 128 == 0, else 2) when D >= 128, H % 64 == 0
+ * and N * H / (32 W) >= 256 (W = 4) or >= 512 (W = 2); otherwise the rows
+ * mode of sparse_decode_attn_ex (workgroup = token x 16 heads).
  *
  *   q, kv_indices, kv_indptr, attn_sink, softmax_scale, out, N, H, D:
  *                as sparse_decode_attn (same alignment and preconditions:
