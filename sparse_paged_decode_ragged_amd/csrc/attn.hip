@@ -359,6 +359,7 @@ __global__ void __launch_bounds__(64 * W) attn_wide_kernel(AttnArgs a) {
   // per CU (LDS <= 80 KiB each), one tile in flight per workgroup
   constexpr int kAhead = W >= 4 ? 2 : 1;
   constexpr int kStages = kAhead + 1;
+  constexpr bool kSpread = W == 4 && kRowsPerLoad == 1 && kLoadsPerWave <= kKSteps;
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
   __shared__ __attribute__((aligned(256))) int sidx[kIdxCap];
@@ -495,7 +496,21 @@ __global__ void __launch_bounds__(64 * W) attn_wide_kernel(AttnArgs a) {
         else
           wait_vmcnt<0>();
         barrier_lds();  // every wave's part of tile i is in LDS; tile i-1's stage is free
-        if (i + kAhead < ntiles) issue_tile(i + kAhead);
+        // At D = 512 (one row a load) the wave's loads of tile i + kAhead are
+        // spread over the QK k-steps, one after each step's MFMAs, so the
+        // address unit takes them while the MFMAs run; the row indices are
+        // read here.  Otherwise they are issued now.
+        const bool more = i + kAhead < ntiles;
+        int nidx = 0;
+        if (more) {
+          if constexpr (kSpread)
+            nidx = sidx[min((i + kAhead) * kTile + wave * (kTile / W) +
+                                (lane < kLoadsPerWave ? lane : 0), n - 1)];
+          else
+            issue_tile(i + kAhead);
+        }
+        const uint32_t ndst = __builtin_amdgcn_readfirstlane(
+            lds_addr(smem + ((i + kAhead) % kStages) * kStageBytes + wave * kLoadsPerWave * 1024));
 
         // The stage's offset is opaque to the compiler: it would otherwise keep
         // every lane offset precomputed for each stage (registers it lacks).
@@ -509,7 +524,35 @@ __global__ void __launch_bounds__(64 * W) attn_wide_kernel(AttnArgs a) {
         // (sched_group_barrier pins the interleave: four MFMAs per k-step,
         // each pair followed by one of the two reads of k-step s + 2).
         f32x4 s00 = {0.f, 0.f, 0.f, 0.f}, s01 = s00, s10 = s00, s11 = s00;
-        {
+        if constexpr (kSpread) {
+          // per k-step, in program order: the K reads of step u + 2, the four
+          // MFMAs of step u, then row load u of the next tile
+          bf16x8 ka[kKSteps], kb[kKSteps];
+          auto read_k = [&](int u) {
+            const int o = off.kq(u);
+            ka[u] = *reinterpret_cast<const bf16x8*>(st + o);
+            kb[u] = *reinterpret_cast<const bf16x8*>(st + o + 16 * kRowBytes);
+          };
+          read_k(0);
+          read_k(1);
+          const unsigned char* kvb = reinterpret_cast<const unsigned char*>(a.kv);
+#pragma unroll
+          for (int u = 0; u < kKSteps; ++u) {
+            if (u + 2 < kKSteps) read_k(u + 2);
+            s00 = mfma_k32(ka[u], q0[u], s00);
+            s01 = mfma_k32(ka[u], q1[u], s01);
+            s10 = mfma_k32(kb[u], q0[u], s10);
+            s11 = mfma_k32(kb[u], q1[u], s11);
+            if (u < kLoadsPerWave && more) {
+              const int grow = __builtin_amdgcn_readlane(nidx, u);
+              const int r = wave * (kTile / W) + u;
+              const uint32_t lane_off =
+                  (uint32_t)((lane ^ (wide_swizzle(r & 15) & (kRowBytes / 16 - 1))) << 4);
+              dma_16B_s(lane_off, kvb + (int64_t)grow * kRowBytes, ndst + u * 1024);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
           bf16x8 ka[kKSteps], kb[kKSteps];
 #pragma unroll
           for (int u = 0; u < kKSteps; ++u) {
