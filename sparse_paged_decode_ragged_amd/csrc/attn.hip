@@ -66,9 +66,28 @@ __global__ void __launch_bounds__(64 * W) attn_heads_kernel(AttnArgs a) {
   __shared__ int sflag[W];
   __shared__ int scount[8 * W];  // page transform: valid entries per (group slot, wave)
 
-  const int item = xcd_item(blockIdx.x, gridDim.x);
-  const int c = item % a.splits;
-  const int th = item / a.splits;
+  // Work item: partition c of (token, head group) th.  With split-L and a
+  // number of (token, head group) pairs divisible by 8, the k-th workgroup an
+  // XCD receives (the dispatcher deals workgroups to the 8 XCDs in turn)
+  // takes partition k / Tx of pair 8 (k mod Tx) + x.  Every XCD holds every
+  // 8th pair, so empty and short tokens (a padded batch tail, say) spread
+  // over all XCDs, and it dispatches the first partitions of all its pairs
+  // before any second one, so the later partitions of long slices fill the
+  // CUs those free on the same XCD, next to their token's other partitions.
+  int c, th;
+  {
+    const int T = a.N * a.head_groups;
+    if (a.splits > 1 && (T & 7) == 0) {
+      const int x = blockIdx.x & 7, k = blockIdx.x >> 3, tx = T >> 3;
+      c = k / tx;
+      th = 8 * (k - c * tx) + x;
+    } else {
+      const int it = xcd_item(blockIdx.x, gridDim.x);
+      c = it % a.splits;
+      th = it / a.splits;
+    }
+  }
+  const int item = th * a.splits + c;  // its workspace slot
   const int hg = th % a.head_groups;
   const int t = th / a.head_groups;
 

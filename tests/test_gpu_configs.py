@@ -70,7 +70,9 @@ def test_ragged_config(spd, device_data):
     ref = oracle_tokens(w, w.kv_indices, w.kv_indptr, tokens)
     q, kv, sink = device_inputs(w)
     idx, ptr = device_csr(w.kv_indices, w.kv_indptr)
-    for plan in [dict(max_len=w.max_len), dict(plain=True), dict(mode=2), dict(mode=1, max_len=w.max_len)]:
+    # the split plans take the XCD-strided partition order (256 tokens, one head group)
+    for plan in [dict(max_len=w.max_len), dict(plain=True), dict(mode=2), dict(mode=1, max_len=w.max_len),
+                 dict(max_len=w.max_len, split_rows=768), dict(max_len=w.max_len, split_rows=384)]:
         out = spd.sparse_decode_attn(q, kv, idx, ptr, sink, w.softmax_scale, **plan)
         torch.cuda.synchronize()
         assert_close(bf16_to_f64(out[torch.from_numpy(tokens).cuda()]), ref, "ragged %s" % plan)
