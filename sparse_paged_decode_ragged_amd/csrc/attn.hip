@@ -69,18 +69,20 @@ __global__ void __launch_bounds__(64 * W) attn_heads_kernel(AttnArgs a) {
   // Work item: partition c of (token, head group) th.  With split-L and a
   // number of (token, head group) pairs divisible by 8, the k-th workgroup an
   // XCD receives (the dispatcher deals workgroups to the 8 XCDs in turn)
-  // takes partition k / Tx of pair 8 (k mod Tx) + x.  Every XCD holds every
-  // 8th pair, so empty and short tokens (a padded batch tail, say) spread
-  // over all XCDs, and it dispatches the first partitions of all its pairs
-  // before any second one, so the later partitions of long slices fill the
-  // CUs those free on the same XCD, next to their token's other partitions.
+  // takes partition S - 1 - k / Tx of pair 8 (k mod Tx) + x.  Every XCD holds
+  // every 8th pair, so empty and short tokens (a padded batch tail, say)
+  // spread over all XCDs.  It deals the last partitions of all its pairs
+  // first: those exist only for the longest slices (the others exit at once),
+  // so the tails of long slices start at the beginning and the partitions
+  // every token has fill the CUs as they free.
   int c, th;
   {
     const int T = a.N * a.head_groups;
     if (a.splits > 1 && (T & 7) == 0) {
       const int x = blockIdx.x & 7, k = blockIdx.x >> 3, tx = T >> 3;
-      c = k / tx;
-      th = 8 * (k - c * tx) + x;
+      const int r = k / tx;
+      c = a.splits - 1 - r;
+      th = 8 * (k - r * tx) + x;
     } else {
       const int it = xcd_item(blockIdx.x, gridDim.x);
       c = it % a.splits;
