@@ -11,8 +11,10 @@ Cases: every supported D, head counts that are not a multiple of 16, empty and
 ragged slices, a slice longer than the 2048 indices staged at a time, zero
 rows (scale 0), a -inf sink, rows planted late in a slice whose scores lie
 far above the first tile (the fixed reference maximum then takes the second
-pass), slots that scatter, skip and leave rows untouched, and the decode-base
-configuration at full size on sampled tokens."""
+pass), slots that scatter, skip and leave rows untouched; the 32-head-wave
+kernel (128- and 64-head workgroups) on ragged tile edges, a restaged slice,
+every code and the second pass; and the decode-base, large and prefill
+configurations at full size on sampled tokens."""
 import numpy as np
 import pytest
 import torch
@@ -278,3 +280,68 @@ def test_wide_attention_second_pass(spd, H, N):
     sidx, sptr = W.csr_from_lists([lists[t] for t in tokens])
     ref = oracle.sparse_decode_attn_fp8(q_bits[tokens], codes, scales, sidx, sptr, sink, scale)
     assert_close(bf16_to_f64(out[torch.from_numpy(tokens).to(dev())]), ref, "fp8 wide second pass")
+
+
+# --- the large and prefill configurations at full size over FP8 pools, in the
+# launch configuration the benchmark times (32-head waves: 128 heads a
+# workgroup for large, 64 for prefill), on sampled tokens ---
+
+@pytest.fixture
+def device_data():
+    W.set_data_mode("device", dev())
+    yield
+    W.set_data_mode("host")
+
+
+def sampled(indptr, n, seed):
+    """n random tokens plus the longest, the shortest non-empty, the first and last."""
+    L = np.diff(indptr)
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(len(L), size=min(n, len(L)), replace=False).tolist())
+    pick |= {int(np.argmax(L)), 0, len(L) - 1}
+    nz = np.nonzero(L)[0]
+    if len(nz):
+        pick.add(int(nz[np.argmin(L[nz])]))
+    return np.array(sorted(pick))
+
+
+def check_fp8_config(spd, w, idx_np, ptr_np, tokens, what):
+    """Quantise the whole bf16 pool on the GPU, run the FP8 call over all
+    tokens, then check the sampled tokens: their rows' codes and scales bit for
+    bit against the oracle's quantiser, their outputs against the oracle's FP8
+    attention over those rows."""
+    from gpu_helpers import device_inputs
+    q, kv, sink = device_inputs(w)
+    kv8 = torch.empty((w.P, w.D), dtype=torch.uint8, device=dev())
+    ksc = torch.empty(w.P, dtype=torch.float32, device=dev())
+    spd.quantize_kv_fp8(kv, kv8, ksc)
+    idx, ptr = device_csr(idx_np, ptr_np)
+    out = spd.sparse_decode_attn_fp8(q, kv8, ksc, idx, ptr, sink, w.softmax_scale)
+    torch.cuda.synchronize()
+    lists = [idx_np[ptr_np[t]:ptr_np[t + 1]] for t in tokens]
+    uniq, inv = np.unique(np.concatenate(lists), return_inverse=True)
+    u = torch.from_numpy(uniq.astype(np.int64)).to(dev())
+    codes, scales = oracle.quantize_fp8(W.host_bits(kv[u]))
+    assert np.array_equal(kv8[u].cpu().numpy(), codes)
+    assert np.array_equal(ksc[u].cpu().numpy().view(np.uint32), scales.view(np.uint32))
+    sub_ptr = np.zeros(len(tokens) + 1, dtype=np.int32)
+    sub_ptr[1:] = np.cumsum([len(x) for x in lists])
+    tok = torch.from_numpy(np.asarray(tokens, dtype=np.int64)).to(dev())
+    ref = oracle.sparse_decode_attn_fp8(W.host_bits(q[tok]), codes, scales, inv.astype(np.int32),
+                                        sub_ptr, w.attn_sink, w.softmax_scale)
+    assert_close(bf16_to_f64(out[tok]), ref, what)
+
+
+def test_large_config_fp8(spd, device_data):
+    w = W.large()
+    log("case fp8 large: N=1024, H=128, 4 Mi rows quantised on the GPU")
+    b = w.builder
+    ptr, idx = oracle.build_decode_indices(b.state_slot, b.swa_len, b.comp_pos, b.block_table,
+                                           b.win, b.k_per_block, b.swa_pages)
+    check_fp8_config(spd, w, idx, ptr, sampled(ptr, 12, 5), "fp8 large")
+
+
+def test_prefill_config_fp8(spd, device_data):
+    w = W.prefill()
+    log("case fp8 prefill: N=8192, H=64, L up to 640")
+    check_fp8_config(spd, w, w.kv_indices, w.kv_indptr, sampled(w.kv_indptr, 20, 6), "fp8 prefill")
