@@ -408,14 +408,22 @@ __global__ void __launch_bounds__(256) attn_rows_fp8_kernel(AttnArgs a) {
 // codes; 16-byte chunk c of row r stored at c ^ (r & 15)).  Within each
 // 16-lane group the 8-bit transposing read gives destination lane i byte e
 // from source lane 2e + i/8, byte i % 8.  Source lane (G = lane / 16,
-// j = lane % 16) points at row 8 (G / 2) + j / 2, codes 32 dt + 16 (G % 2) +
-// 8 (j % 2) .. + 7; destination lane (G, i) then holds rows 8 (G / 2) .. + 7 of
-// column 32 dt + 16 (G % 2) + i, the A operand of the product (lane (d, kg):
-// rows 8 kg .. 8 kg + 7 of column d).  That is logical chunk 2 dt + G % 2 at
-// byte 8 (j % 2), stored at 2 (dt ^ (sw / 2)) + ((G % 2) ^ (sw % 2)) with sw
-// the row's swizzle: base + 16 ((2 dt) ^ x) with x = (G % 2) ^ sw, computed
-// per read (two VALU ops) rather than held in registers.  The 8 rows of a
-// group sit in 8 different 16-byte bank groups.  Rows 16..31 add 16 D bytes.
+// j = lane % 16) points at row 8 (G / 2) + j / 2, byte 8 (j % 2) of chunk
+// wide_vt_chunk(dt, G % 2); destination lane (G, i) then holds rows
+// 8 (G / 2) .. + 7 of that chunk's column i, the A operand of the product
+// (lane (d, kg): rows 8 kg .. 8 kg + 7 of column d of d-tile dt).  At D >= 256
+// d-tile dt is chunks a and a ^ 8 with a = dt % 8 + 16 (dt / 8): the 8 rows
+// of one group fall on 8 different 16-byte bank groups (the swizzle XORs the
+// low bits), and the two groups of a half-wave (chunks a and a ^ 8) on the
+// two other octets of the 16, so a half-wave's 256 bytes meet no conflict.
+// (Chunks 2 dt and 2 dt + 1, the columns in order, put both groups on the
+// same octet: two cycles a half-wave.)  At D = 128 the d-tiles stay 2 dt,
+// 2 dt + 1.  The output columns follow the same map.  Rows 16..31 add 16 D.
+template <int D>
+__device__ __forceinline__ constexpr int wide_vt_chunk(int dt, int half) {
+  return D >= 256 ? ((dt & 7) + 16 * (dt >> 3)) + 8 * half : 2 * dt + half;
+}
+
 template <int D>
 struct Fp8WideVtOffsets {
   int base, x;
@@ -424,9 +432,9 @@ struct Fp8WideVtOffsets {
     const int row = 8 * (G >> 1) + (j >> 1);
     const int sw = row_swizzle(row) & (D / 16 - 1);
     base = row * D + 8 * (j & 1);
-    x = (G & 1) ^ sw;
+    x = (wide_vt_chunk<D>(0, G & 1) - wide_vt_chunk<D>(0, 0)) ^ sw;  // chunk (a + h) ^ sw = a ^ x
   }
-  __device__ __forceinline__ int at(int dt) const { return base + 16 * ((2 * dt) ^ x); }
+  __device__ __forceinline__ int at(int dt) const { return base + 16 * (wide_vt_chunk<D>(dt, 0) ^ x); }
 };
 
 // The K-operand reads of Fp8Offsets, computed per read: for k-step s the
@@ -662,9 +670,9 @@ __global__ void __launch_bounds__(64 * W) attn_wide_fp8_kernel(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
+    for (int e4 = 0; e4 < 4; ++e4) {  // d = 8 e4 + 4 hf + e: chunk half e4 / 2 of d-tile dt
       const f32x4 v = {acc[dt][4 * e4], acc[dt][4 * e4 + 1], acc[dt][4 * e4 + 2], acc[dt][4 * e4 + 3]};
-      store_bf16x4(op + 32 * dt + 8 * e4, v, inv);
+      store_bf16x4(op + 16 * wide_vt_chunk<D>(dt, e4 >> 1) + 8 * (e4 & 1), v, inv);
     }
 }
 
