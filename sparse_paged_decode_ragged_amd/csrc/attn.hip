@@ -744,7 +744,6 @@ __global__ void __launch_bounds__(256) attn_rows_kernel(AttnArgs a) {
   }
 
   bf16x8 qreg[kKSteps];
-  load_q<D>(a.q, (int64_t)t * a.H + (hvalid ? h : 0), g, qreg);
   stage_sinks(a.sink, a.H, h0, ssink, wave, lane);
 
   unsigned char* mine = smem + wave * kWaveBytes;
@@ -790,6 +789,9 @@ __global__ void __launch_bounds__(256) attn_rows_kernel(AttnArgs a) {
       bf16x8 ka[kKSteps];
       if (my_tiles > 0) issue(0);
       if (my_tiles > 1) issue(1);
+      // q is loaded once its first two tiles are in flight: the index staging
+      // before them then waits for the indices alone
+      if (pass == 0 && sc == 0) load_q<D>(a.q, (int64_t)t * a.H + (hvalid ? h : 0), g, qreg);
       if (my_tiles > 0) {
         if (my_tiles > 1)
           wait_vmcnt<kLoads>();
