@@ -37,23 +37,29 @@ __global__ void __launch_bounds__(256) qk_norm_rope_store_kernel(ProducerArgs a)
   if (r >= nq + a.N) return;  // wave-uniform
   const bool is_kv = r >= nq;
   const int t = is_kv ? (int)(r - nq) : (int)(r / a.H);
-  const int p = a.positions[t];
-  // a position outside the table (when there is one to read): nothing is written
-  if (p < 0 || (a.rope_dim > 0 && p >= a.max_pos)) return;
-  int64_t slot = 0;
-  if (is_kv) {
-    slot = (int64_t)a.state_slot[t] * a.win + p % a.win;
-    if (slot < 0 || slot >= a.num_rows) return;  // outside the pool: nothing is written
-  }
+  // The row's address does not depend on the position: its load is issued
+  // with the position's (one memory round trip, not two), and its sum of
+  // squares is taken before the position is checked, so the load cannot be
+  // moved below that check.
   const uint16_t* src = is_kv ? a.kv + (int64_t)t * D : a.q + r * D;
   float x[E];
   load_bf16_lane<E>(src + lane * E, x);
+  const int p = a.positions[t];
+  const int64_t ring0 = is_kv ? (int64_t)a.state_slot[t] * a.win : 0;
 
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e) ss += x[e] * x[e];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+
+  // a position outside the table (when there is one to read): nothing is written
+  if (p < 0 || (a.rope_dim > 0 && p >= a.max_pos)) return;
+  int64_t slot = 0;
+  if (is_kv) {
+    slot = ring0 + p % a.win;
+    if (slot < 0 || slot >= a.num_rows) return;  // outside the pool: nothing is written
+  }
   const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
   const float* w = is_kv ? a.kv_weight : a.q_weight;
   float y[E];
