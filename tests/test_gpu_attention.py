@@ -57,7 +57,7 @@ LENGTHS = [0, 1, 5, 31, 32, 33, 64, 97, 200]
 
 
 @pytest.mark.parametrize("D", [64, 128, 256, 512])
-@pytest.mark.parametrize("H", [1, 8, 16, 24, 40, 64, 128])
+@pytest.mark.parametrize("H", [1, 8, 16, 24, 40, 64, 128, 256])
 def test_shapes(spd, H, D):
     seed = 100 + H * 7 + D
     w = W.random_csr("shapes", seed, len(LENGTHS), H, D, 700, LENGTHS)
