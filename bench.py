@@ -38,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA peak of the MI355X
 METRIC = "sparse decode attn tokens/s + gathered KV GB/s (% of MI355X HBM roofline)"
 MALL_BYTES = 256 << 20
 
@@ -161,6 +162,12 @@ def algorithmic_bytes(indptr: np.ndarray, N: int, H: int, D: int) -> dict:
     qo = nonempty * H * D * 2 + N * H * D * 2
     total = kv + qo + 4 * sum_l + 4 * (N + 1) + 4 * H
     return {"sum_L": sum_l, "kv_bytes": kv, "qo_bytes": qo, "B_alg": total, "nonempty": nonempty}
+
+
+def mfma_flops(sum_l: int, H: int, D: int) -> int:
+    """MFMA work the method must do per call: S = q K^T and O = P V, each
+    2 H D flop per gathered row (multiply and add)."""
+    return 4 * H * D * sum_l
 
 
 def covered_positions(stream_len: int, start: np.ndarray, length: np.ndarray) -> int:
@@ -491,7 +498,13 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": recorded_traffic(kernel, args.workload),
                      "kernel": kernel, "us_per_call": round(us_attn, 3),
-                     "bytes_per_call": ab["B_alg"]},
+                     "bytes_per_call": ab["B_alg"],
+                     # the secondary bound: the same call's MFMA work against the bf16 peak
+                     "mfma": {"flop_per_call": mfma_flops(ab["sum_L"], H, D),
+                              "achieved_TFLOPs": round(mfma_flops(ab["sum_L"], H, D) / us_attn / 1e6, 1),
+                              "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                              "frac": round(mfma_flops(ab["sum_L"], H, D) / us_attn / 1e6 /
+                                            MFMA_BF16_PEAK_TFLOPS, 4)}},
     }
     if us_paged is not None:
         pp = spd.sparse_decode_attn_plan_info(N, H, D, 0, 0, mode)  # the paged call never splits

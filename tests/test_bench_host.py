@@ -52,3 +52,11 @@ def test_fp8_kernel_name_follows_the_plan():
     # H = 64: two 32-head waves a workgroup once there are two per CU
     assert bench.fp8_kernel(8192, 64, 512) == "attn_wide_fp8_kernel<512,2>"
     assert bench.fp8_kernel(511, 64, 512) == "attn_rows_fp8_kernel<512>"
+
+
+def test_mfma_flops_hand_count():
+    # two tokens with 3 and 2 rows, H = 4, D = 8: per row and head, q.k takes
+    # D multiplies and D adds, and p.v the same again
+    assert bench.mfma_flops(5, H=4, D=8) == 5 * 4 * (2 * 8 + 2 * 8)
+    # decode_base: 40,960 rows, 64 heads, D = 512
+    assert bench.mfma_flops(40960, 64, 512) == 5368709120
