@@ -49,8 +49,10 @@ def parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="decode_base",
-                   choices=["decode_base", "tiny", "ragged", "large", "prefill"])
-    p.add_argument("--mode", default="auto", choices=["auto", "heads", "rows", "wide"])
+                   choices=["decode_base", "tiny", "ragged", "large", "prefill", "long_context"])
+    p.add_argument("--long-tokens", type=int, default=8, help="long_context: tokens")
+    p.add_argument("--long-rows", type=int, default=8192, help="long_context: rows per token")
+    p.add_argument("--mode", default="auto", choices=["auto", "heads", "rows", "wide", "split"])
     p.add_argument("--split-rows", type=int, default=0)
     p.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = automatic)")
     p.add_argument("--eager", action="store_true", help="launch kernels directly, no graphs")
@@ -73,7 +75,7 @@ def parse():
 
 def kernel_sources(kernel: str) -> tuple:
     """The source files an attention kernel is built from."""
-    main = "attn_fp8.hip" if "fp8" in kernel else "attn.hip"
+    main = "attn_fp8.hip" if "fp8" in kernel else ("attn_split.hip" if "split" in kernel else "attn.hip")
     return (main, "attn_device.h", "spd_internal.h")
 
 
@@ -242,13 +244,14 @@ def main():
     import workloads as W
 
     dev = torch.device("cuda:0")
-    if args.workload in ("ragged", "large", "prefill"):
+    if args.workload in ("ragged", "large", "prefill", "long_context"):
         W.set_data_mode("device", dev)
-    w = W.make(args.workload)
+    w = (W.make(args.workload, N=args.long_tokens, length=args.long_rows)
+         if args.workload == "long_context" else W.make(args.workload))
     N, H, D = w.N, w.H, w.D
     max_len = w.max_len
     mode = {"auto": spd.MODE_AUTO, "heads": spd.MODE_HEADS, "rows": spd.MODE_ROWS,
-            "wide": spd.MODE_WIDE}[args.mode]
+            "wide": spd.MODE_WIDE, "split": spd.MODE_SPLIT}[args.mode]
     plan = spd.sparse_decode_attn_plan_info(N, H, D, max_len, args.split_rows, mode)
     ws_bytes = spd.sparse_decode_attn_workspace_size(N, H, D, max_len, args.split_rows, mode)
     b = w.builder
@@ -263,7 +266,7 @@ def main():
         s = dict(q=q0 if r == 0 else q0.clone(), kv=kv0 if r == 0 else kv0.clone(),
                  sink=torch.from_numpy(w.attn_sink).to(dev),
                  out=torch.empty((N, H, D), dtype=torch.bfloat16, device=dev),
-                 ws=torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev))
+                 ws=torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev))
         if b is not None:
             s.update(ss=t(b.state_slot), sl=t(b.swa_len), cp=t(b.comp_pos), bt=t(b.block_table),
                      ptr=torch.zeros(N + 1, dtype=torch.int32, device=dev),
@@ -289,11 +292,15 @@ def main():
     # The same step with the page transform fused into the attention kernel
     # (builder-shaped workloads whose lists fit the paged call).
     has_paged = b is not None and b.win + b.topk <= 2048
+    # the paged call never splits a slice: it takes the mode asked for unless
+    # that is the split mode
+    paged_mode = mode if mode in (spd.MODE_AUTO, spd.MODE_HEADS, spd.MODE_ROWS,
+                                  spd.MODE_WIDE) else spd.MODE_AUTO
 
     def paged(s):
         spd.sparse_decode_attn_paged(s["q"], s["kv"], s["ss"], s["sl"], s["cp"], s["bt"], b.win,
                                      b.k_per_block, b.swa_pages, s["sink"], w.softmax_scale,
-                                     out=s["out"], mode=mode)
+                                     out=s["out"], mode=paged_mode)
 
     # The attention call over an FP8 pool (e4m3 codes + one fp32 scale per row),
     # each set's pool filled from its bf16 pool by the quantising store before
@@ -467,6 +474,8 @@ def main():
     achieved = ab["B_alg"] / (us_attn * 1e-6) / 1e9
     if plan["mode"] == "rows":
         kernel = "attn_rows_kernel<%d>" % D
+    elif plan["mode"] == "split":
+        kernel = "attn_split_kernel<%d,%d,%d>" % (D, plan["heads_per_group"] // 32, plan["parities"])
     elif plan.get("wide"):
         kernel = "attn_wide_kernel<%d,%d>" % (D, plan["heads_per_group"] // 32)
     else:
@@ -507,7 +516,7 @@ def main():
                                             MFMA_BF16_PEAK_TFLOPS, 4)}},
     }
     if us_paged is not None:
-        pp = spd.sparse_decode_attn_plan_info(N, H, D, 0, 0, mode)  # the paged call never splits
+        pp = spd.sparse_decode_attn_plan_info(N, H, D, 0, 0, paged_mode)  # the paged call never splits
         kernel_paged = ("attn_rows_kernel<%d, paged>" % D if pp["mode"] == "rows" else
                         "attn_wide_kernel<%d,%d, paged>" % (D, pp["heads_per_group"] // 32)
                         if pp.get("wide") else

@@ -47,7 +47,7 @@ typedef enum spd_status {
 /* Human-readable name of a status code (static string, never NULL). */
 SPD_API const char* spd_status_string(spd_status s);
 
-/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH (0.2.0: SPD_MODE_SPLIT). */
 SPD_API int spd_version(void);
 
 /*
@@ -109,14 +109,27 @@ SPD_API spd_status sparse_decode_attn(const void* q, const void* unified_kv, int
  *   SPD_MODE_WIDE:  SPD_MODE_HEADS on 32-head waves whatever the batch size:
  *                   needs H % 64 == 0 and no split-L (SPD_ERR_UNSUPPORTED
  *                   otherwise).
- *   SPD_MODE_AUTO:  ROWS when the batch gives fewer than 256 HEADS-mode
- *                   workgroups and split_rows == 0, else HEADS.
+ *   SPD_MODE_SPLIT: a workgroup takes (token, 64 heads, partition) -- 32
+ *                   heads when H <= 32 and D >= 128 -- its 4 waves two (or
+ *                   four) 16-row streams of each 32-head block; the
+ *                   partitions of one (token, head group) are merged inside
+ *                   the same kernel, by the workgroups that finish last
+ *                   (no combine kernel).  Up to 32 partitions; the plan
+ *                   chooses them (at least 64 rows each) when split_rows is
+ *                   0.  Its workspace holds arrival counters: see
+ *                   sparse_decode_attn_ex.
+ *   SPD_MODE_AUTO:  SPLIT when split_rows == 0, the batch gives fewer than
+ *                   256 HEADS-mode workgroups and max_len >= 2048 (a small
+ *                   batch of long slices); else ROWS when split_rows == 0
+ *                   and the batch gives fewer than 256 HEADS-mode
+ *                   workgroups; else HEADS.
  */
 typedef enum spd_mode {
   SPD_MODE_AUTO = 0,
   SPD_MODE_HEADS = 1,
   SPD_MODE_ROWS = 2,
-  SPD_MODE_WIDE = 3
+  SPD_MODE_WIDE = 3,
+  SPD_MODE_SPLIT = 4
 } spd_mode;
 
 /*
@@ -130,10 +143,12 @@ SPD_API size_t sparse_decode_attn_workspace_size(int32_t N, int32_t H, int32_t D
 /*
  * The plan sparse_decode_attn_ex would use for these arguments, for callers
  * that size buffers or report what runs: info[0] = mode actually used
- * (SPD_MODE_HEADS or SPD_MODE_ROWS), info[1] = heads per workgroup, info[2] =
- * head groups, info[3] = split-L partitions (1 = none), info[4] = rows per
- * partition, info[5] = 1 when the heads mode runs on 32-head waves (64 or 128
- * heads per workgroup) else 0.  info is a host array of 6 int32.  Returns
+ * (SPD_MODE_HEADS, SPD_MODE_ROWS or SPD_MODE_SPLIT), info[1] = heads per
+ * workgroup, info[2] = head groups, info[3] = split-L partitions (1 = none),
+ * info[4] = rows per partition, info[5] = 1 when the heads mode runs on
+ * 32-head waves (64 or 128 heads per workgroup) else 0, info[6] = waves per
+ * 16-head block (SPD_MODE_SPLIT: 2 when two waves take alternate tiles of the
+ * same heads, else 1).  info is a host array of 7 int32.  Returns
  * SPD_ERR_INVALID_ARG or SPD_ERR_UNSUPPORTED exactly when
  * sparse_decode_attn_ex would.
  */
@@ -146,11 +161,18 @@ SPD_API spd_status sparse_decode_attn_plan_info(int32_t N, int32_t H, int32_t D,
  * slice is still computed correctly, by its last partition); 0 = unknown.
  * split_rows fixes the split-L partition length (rounded up to a multiple of
  * 32, HEADS mode only; SPD_ERR_UNSUPPORTED with SPD_MODE_ROWS); 0 lets the
- * plan choose from N, H and max_len.  mode is an spd_mode.  Partitions of one
- * token are merged by a combine kernel (the attention sink is counted once).
+ * plan choose from N, H and max_len.  mode is an spd_mode.  HEADS-mode
+ * partitions of one token are merged by a combine kernel, SPLIT-mode ones
+ * inside the attention kernel (the attention sink is counted once either way).
  * workspace/workspace_bytes: a caller-owned device buffer of at least
  * sparse_decode_attn_workspace_size bytes, 16-byte aligned (may be NULL when
- * that size is 0); no state survives between calls.
+ * that size is 0).  HEADS-mode split-L keeps no state in it between calls.
+ * When the plan is SPD_MODE_SPLIT (asked for, or chosen by SPD_MODE_AUTO; see
+ * plan_info) the last N * ceil(H / heads per workgroup) * 16 bytes are
+ * arrival counters that must be zero when the call starts: zero the buffer
+ * once after allocating it (and again after another plan has used it).  Every
+ * call leaves them zero, so one buffer serves any number of calls issued one
+ * after another; two calls that run at the same time on one buffer race.
  */
 SPD_API spd_status sparse_decode_attn_ex(const void* q, const void* unified_kv, int64_t num_rows,
                                          const int32_t* kv_indices, const int32_t* kv_indptr,

@@ -137,7 +137,7 @@ def sparse_decode_attn_can_use(H: int, D: int) -> bool:
     return bool(lib.sparse_decode_attn_can_use(int(H), int(D)))
 
 
-MODE_AUTO, MODE_HEADS, MODE_ROWS, MODE_WIDE = 0, 1, 2, 3
+MODE_AUTO, MODE_HEADS, MODE_ROWS, MODE_WIDE, MODE_SPLIT = 0, 1, 2, 3, 4
 
 
 def sparse_decode_attn_workspace_size(N: int, H: int, D: int, max_len: int = 0,
@@ -148,13 +148,14 @@ def sparse_decode_attn_workspace_size(N: int, H: int, D: int, max_len: int = 0,
 
 def sparse_decode_attn_plan_info(N: int, H: int, D: int, max_len: int = 0, split_rows: int = 0,
                                  mode: int = MODE_AUTO) -> dict:
-    info = (ctypes.c_int32 * 6)()
+    info = (ctypes.c_int32 * 7)()
     st = lib.sparse_decode_attn_plan_info(int(N), int(H), int(D), int(max_len), int(split_rows),
                                           int(mode), info)
     _raise_on(st, "sparse_decode_attn_plan_info")
-    return {"mode": {1: "heads", 2: "rows"}[info[0]], "heads_per_group": info[1],
+    return {"mode": {1: "heads", 2: "rows", 4: "split"}[info[0]], "heads_per_group": info[1],
             "head_groups": info[2], "splits": info[3],
-            "split_rows": info[4] if info[3] > 1 else None, "wide": bool(info[5])}
+            "split_rows": info[4] if info[3] > 1 else None, "wide": bool(info[5]),
+            "parities": info[6]}
 
 
 def sparse_decode_attn(q: torch.Tensor, unified_kv: torch.Tensor, kv_indices: torch.Tensor,
@@ -195,7 +196,8 @@ def sparse_decode_attn(q: torch.Tensor, unified_kv: torch.Tensor, kv_indices: to
         return out
     need = sparse_decode_attn_workspace_size(N, H, D, max_len, split_rows, mode)
     if need > 0 and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        # zero-filled: a split-mode workspace's arrival counters must start at zero
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.sparse_decode_attn_ex(_ptr(q), _ptr(unified_kv), unified_kv.shape[0], _ptr(idx),
                                    _ptr(kv_indptr), _ptr(attn_sink), float(softmax_scale),

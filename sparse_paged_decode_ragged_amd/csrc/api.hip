@@ -36,7 +36,7 @@ SPD_API const char* spd_status_string(spd_status s) {
   return "SPD_ERR_UNKNOWN";
 }
 
-SPD_API int spd_version(void) { return 100; }
+SPD_API int spd_version(void) { return 200; }
 
 SPD_API int sparse_decode_attn_can_use(int32_t H, int32_t D) {
   return spd::attn_supported(H, D) ? 1 : 0;
@@ -53,7 +53,7 @@ SPD_API spd_status sparse_decode_attn_plan_info(int32_t N, int32_t H, int32_t D,
                                                 int32_t split_rows, int32_t mode, int32_t* info) {
   if (!info || N < 0 || H <= 0 || D <= 0 || max_len < 0 || split_rows < 0) return SPD_ERR_INVALID_ARG;
   if (mode != SPD_MODE_AUTO && mode != SPD_MODE_HEADS && mode != SPD_MODE_ROWS &&
-      mode != SPD_MODE_WIDE)
+      mode != SPD_MODE_WIDE && mode != SPD_MODE_SPLIT)
     return SPD_ERR_INVALID_ARG;
   if (!spd::attn_supported(H, D)) return SPD_ERR_UNSUPPORTED;
   if (mode == SPD_MODE_ROWS && split_rows != 0) return SPD_ERR_UNSUPPORTED;
@@ -66,6 +66,7 @@ SPD_API spd_status sparse_decode_attn_plan_info(int32_t N, int32_t H, int32_t D,
   info[3] = plan.splits;
   info[4] = plan.split_rows;
   info[5] = plan.wide;
+  info[6] = plan.parities;
   return SPD_OK;
 }
 
@@ -78,7 +79,7 @@ SPD_API spd_status sparse_decode_attn_ex(const void* q, const void* unified_kv, 
   if (N < 0 || H <= 0 || D <= 0 || num_rows <= 0 || max_len < 0 || split_rows < 0)
     return SPD_ERR_INVALID_ARG;
   if (mode != SPD_MODE_AUTO && mode != SPD_MODE_HEADS && mode != SPD_MODE_ROWS &&
-      mode != SPD_MODE_WIDE)
+      mode != SPD_MODE_WIDE && mode != SPD_MODE_SPLIT)
     return SPD_ERR_INVALID_ARG;
   if (mode == SPD_MODE_ROWS && split_rows != 0) return SPD_ERR_UNSUPPORTED;
   if (!isfinite(softmax_scale)) return SPD_ERR_INVALID_ARG;

@@ -334,32 +334,6 @@ __global__ void __launch_bounds__(64 * W) attn_combine_kernel(AttnArgs a) {
 //    holding rows 8kg..8kg+7 of column d) is two transposing reads.
 // The accumulator of a wave is 32 heads x D fp32 (256 AGPRs at D = 512).
 
-// Per-lane byte offsets of the 32x32x16 V^T operand reads within a stage:
-// lane (G = lane / 16, j = lane % 16) reads row 8 (G / 2) + 4 half + j / 4,
-// d = 32 dt + 16 (G % 2) + 4 (j % 4) .. +3, i.e. logical 16-byte chunk
-// 4 dt + b (b = 2 (G % 2) + (j / 2) % 2) at byte 8 (j % 2); stored at chunk
-// (4 dt + b) ^ sw with sw = wide_swizzle(row) < 16, that is
-// 4 ((dt % 4) ^ (sw / 4)) + 16 (dt / 4) ... split as v[half][dt % 4] + 256 (dt / 4).
-template <int D>
-struct WideVtOffsets {
-  static constexpr int kRowBytes = 2 * D;
-  static constexpr int kChunks = D / 8;
-  int v[2][4];
-  __device__ __forceinline__ explicit WideVtOffsets(int lane) {
-    const int G = lane >> 4, j = lane & 15;
-    const int b = 2 * (G & 1) + ((j >> 1) & 1);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int row = 8 * (G >> 1) + 4 * half + (j >> 2);
-      const int sw = wide_swizzle(row) & (kChunks - 1);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        v[half][u] = row * kRowBytes + 64 * (u ^ (sw >> 2)) + 16 * (b ^ (sw & 3)) + 8 * (j & 1);
-    }
-  }
-  __device__ __forceinline__ int at(int dt, int half) const { return v[half][dt & 3] + 256 * (dt >> 2); }
-};
-
 // kWin: 0 = CSR slices; 1 = one token a workgroup whose slice is its window of
 // the index stream (no masks); 2 = tokens_per_group tokens share the union of
 // their windows, each wave masking the rows outside its token's window.
@@ -967,6 +941,7 @@ hipError_t launch_prefill_d(const AttnArgs& a, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream) {
+  if (plan.mode == kModeSplit) return launch_split(a, D, plan, stream);
   if (plan.mode == kModeRows) {
     if (a.paged)
       hipLaunchKernelGGL((attn_rows_kernel<D, true>), dim3((unsigned)(a.N * a.head_groups)),
@@ -996,11 +971,67 @@ bool attn_supported(int32_t H, int32_t D) {
   return (D == 64 || D == 128 || D == 256 || D == 512) && H >= 1 && H <= 1024;
 }
 
+// Split mode: workgroups of 32 HB heads on 4 waves (HB head blocks x P
+// parities), slices cut into partitions of split_rows rows (at most
+// kSplitMax) so that the batch gives about one workgroup per CU.  Up to 32
+// heads (D >= 128) take HB = 1, P = 4; otherwise HB = 2, P = 2, so that a
+// token's rows enter one CU per partition for 64 heads.  (HB = 1, P = 4 for
+// 64 heads, a token's rows entering two CUs, measured 32.1 us against 28.5
+// us for N = 64 tokens of 640 rows, D = 512.)
+constexpr int kSplitMax = 32;
+// Shortest capacity bound for which the automatic plan of a small batch
+// splits the slices: below it the exchange of the partitions' states costs
+// more than the rows the head-split workgroups would share (measured at H =
+// 64, D = 512: N = 64 tokens of 1280 rows 37.7 us split against 36.0 us in
+// rows mode, of 2048 rows 46.4 us against 49.8 us; N = 8 of 8192 rows 58 us
+// against 150 us).
+constexpr int kSplitAutoLen = 2048;
+
+static bool make_split_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t split_rows,
+                            AttnPlan* p) {
+  const bool hb1 = H <= 32 && D >= 128;
+  p->mode = kModeSplit;
+  p->wide = 0;
+  p->parities = hb1 ? 4 : 2;
+  p->heads_per_group = hb1 ? 32 : 64;
+  p->waves = 4;
+  p->head_groups = (H + p->heads_per_group - 1) / p->heads_per_group;
+  const long long base = (long long)N * p->head_groups;
+  long long splits = 1, rows = 0;
+  if (split_rows > 0) {
+    rows = ((long long)split_rows + 31) / 32 * 32;
+    splits = max_len > rows ? (max_len + rows - 1) / rows : 1;
+  } else if (max_len > 0 && base > 0 && base < 256) {
+    const long long want = (256 + base - 1) / base;
+    const long long cap = (max_len + 63) / 64;  // partitions of at least 64 rows
+    splits = want < cap ? want : cap;
+    if (splits > kSplitMax) splits = kSplitMax;
+    if (splits > 1) {
+      rows = (max_len + splits - 1) / splits;
+      rows = (rows + 31) / 32 * 32;
+      splits = (max_len + rows - 1) / rows;
+    }
+  }
+  if (splits > kSplitMax) return false;
+  if (splits <= 1) {
+    splits = 1;
+    rows = 1 << 30;
+  }
+  if (base * splits > 0x7fffffffLL) return false;
+  p->splits = (int)splits;
+  p->split_rows = (int)rows;
+  p->workspace_bytes = splits > 1 ? split_workspace_bytes(N, D, *p) : 0;
+  return true;
+}
+
 bool make_attn_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t split_rows,
                     int32_t mode, AttnPlan* p) {
   if (!attn_supported(H, D) || N < 0 || max_len < 0 || split_rows < 0) return false;
-  if (mode != kModeAuto && mode != kModeHeads && mode != kModeRows && mode != kModeWide)
+  if (mode != kModeAuto && mode != kModeHeads && mode != kModeRows && mode != kModeWide &&
+      mode != kModeSplit)
     return false;
+  p->parities = 1;
+  if (mode == kModeSplit) return make_split_plan(N, H, D, max_len, split_rows, p);
   if (mode == kModeWide) {  // 32-head waves, no split-L
     if (H % 64 != 0 || split_rows != 0) return false;
     p->mode = kModeHeads;
@@ -1019,6 +1050,12 @@ bool make_attn_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t sp
   const long long heads_groups = (H + heads_per - 1) / heads_per;
   // Work items the heads mode provides without split-L; the chip has 256 CUs.
   const long long target = 256;
+  if (mode == kModeAuto && split_rows == 0 && (long long)N * heads_groups < target &&
+      max_len >= kSplitAutoLen) {
+    // a small batch of long slices: partitions merged in-kernel
+    if (make_split_plan(N, H, D, max_len, 0, p) && p->splits > 1) return true;
+    p->parities = 1;
+  }
   if (mode == kModeAuto)
     mode = (split_rows == 0 && (long long)N * heads_groups < target) ? kModeRows : kModeHeads;
   if (mode == kModeRows) {

@@ -96,6 +96,32 @@ struct TileOffsets {
   __device__ __forceinline__ int vt(int dt) const { return v[dt & 7] + 256 * (dt >> 3); }
 };
 
+// Per-lane byte offsets of the 32x32x16 V^T operand reads within a stage:
+// lane (G = lane / 16, j = lane % 16) reads row 8 (G / 2) + 4 half + j / 4,
+// d = 32 dt + 16 (G % 2) + 4 (j % 4) .. +3, i.e. logical 16-byte chunk
+// 4 dt + b (b = 2 (G % 2) + (j / 2) % 2) at byte 8 (j % 2); stored at chunk
+// (4 dt + b) ^ sw with sw = wide_swizzle(row) < 16, that is
+// 4 ((dt % 4) ^ (sw / 4)) + 16 (dt / 4) ... split as v[half][dt % 4] + 256 (dt / 4).
+template <int D>
+struct WideVtOffsets {
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kChunks = D / 8;
+  int v[2][4];
+  __device__ __forceinline__ explicit WideVtOffsets(int lane) {
+    const int G = lane >> 4, j = lane & 15;
+    const int b = 2 * (G & 1) + ((j >> 1) & 1);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = 8 * (G >> 1) + 4 * half + (j >> 2);
+      const int sw = wide_swizzle(row) & (kChunks - 1);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        v[half][u] = row * kRowBytes + 64 * (u ^ (sw >> 2)) + 16 * (b ^ (sw & 3)) + 8 * (j & 1);
+    }
+  }
+  __device__ __forceinline__ int at(int dt, int half) const { return v[half][dt & 3] + 256 * (dt >> 2); }
+};
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }

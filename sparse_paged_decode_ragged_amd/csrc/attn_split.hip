@@ -1,0 +1,728 @@
+// attn_split.hip -- split-L sparse decode attention with the partitions
+// merged inside the same kernel, gfx950.
+//
+// Operation (sglang PR #28392 summary page, "key source snippet": the
+// paged_decode.py module docstring): token t attends to the pool rows
+// kv_indices[kv_indptr[t] : kv_indptr[t+1]]; each bf16 row is both key and
+// value; attn_sink[H] is a virtual key of the softmax denominator; online
+// softmax in the log2 domain; an empty slice gives zeros.  Cutting a long
+// slice into partitions whose (m, l, O) states are merged afterwards is the
+// split-L plus combine design of the same path.
+//
+// Why this decomposition.  A small decode batch (tens of tokens, 64 heads,
+// D = 512) gives one workgroup per (token, head group) for a fraction of the
+// chip, and spreading the heads over several workgroups pulls every gathered
+// row into several CUs.  Here a workgroup is (token, 32 HB heads, partition c
+// of split_rows rows): every gathered row enters one CU (HB = 2: 64 heads) or
+// two (HB = 1, two head groups of a token), and each CU's rows are a quarter
+// or half of what a head-split workgroup would take in.
+//
+// Inside a workgroup: 4 waves of 32 heads (two 16-head MFMA blocks per wave,
+// as in the 32-head-wave heads kernel): HB head blocks x P parities.  A
+// super-tile of 16 P rows sits in an LDS ring (LDS-DMA gathers, XOR-swizzled
+// rows); wave (hb, par) computes heads 32 hb .. of rows [16 par, 16 par + 16):
+//   S^T = K Q^T on 16x16x32 MFMAs (one K read feeds both head blocks),
+//   O^T += V^T P^T on 32x32x16 MFMAs over the 16 rows (P^T from the two
+//   blocks' weights after one v_permlane16_swap per dword),
+// so each K and V^T byte read from LDS feeds 32 heads.  At the end the P
+// parity states of a head block merge in LDS (a butterfly over the parities),
+// leaving each wave the merged state of its 32 heads on D / P columns: the
+// wave's piece.
+//
+// Merging the partitions without a second launch.  Piece w of a (token, head
+// group) is merged by partition w mod nparts (a reduce-scatter: every
+// partition merges a share).  The others publish their piece to the workspace
+// with agent-scope coherent stores (sc1), wait until the stores are complete
+// and count themselves in with one atomic add on the piece's counter; the
+// merging wave polls the counter (read-modify-writes at agent scope), then
+// reads the pieces (sc1 loads), sums them in partition order (every arrival
+// order gives the same bits), writes the output and resets the counter to
+// zero.  It waits only when the whole grid fits on the chip at once (one
+// workgroup per CU), and then for a bounded number of polls: past the bound,
+// or at once on a larger grid, it publishes its own piece and counts itself
+// in as well, and whichever arrival completes the count merges instead -- so
+// no wave ever waits on a workgroup that cannot be scheduled.  No whole-cache
+// write-back or invalidation is involved: only these sc1 accesses carry data
+// between workgroups, and an sc1 load is served at agent scope, never from a
+// line an XCD's L2 kept from before the publishing stores.
+#include <atomic>
+
+#include "attn_device.h"
+
+namespace spd {
+namespace {
+
+constexpr int kSplitIdx = 1024;  // row indices staged at a time
+constexpr int kSpinLimit = 1000; // polls (each a memory round trip plus a short sleep)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const void* base) {
+  // raw buffer over a piece's slot (< 2 GiB), untyped 32-bit format
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+
+constexpr int kSc1 = 16;  // cache policy bit of an agent-scope coherent access
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void store_sc1(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kSc1);
+}
+__device__ __forceinline__ f32x4 load_sc1(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
+}
+__device__ __forceinline__ void store1_sc1(__amdgpu_buffer_rsrc_t r, int off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, off, 0, kSc1);
+}
+__device__ __forceinline__ float load1_sc1(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSc1));
+}
+
+// Weight 2^(m - M) of a state with reference maximum m in a merge whose
+// maximum is M >= m; a state that saw no row (m = -inf) weighs exactly 0, also
+// when every merged state is empty (M = -inf, where 2^(m - M) would be NaN).
+__device__ __forceinline__ float state_weight(float m, float M) {
+  return m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+}
+
+__device__ __forceinline__ f32x4 quarter(const f32x16& v, int e4) {
+  return f32x4{v[4 * e4], v[4 * e4 + 1], v[4 * e4 + 2], v[4 * e4 + 3]};
+}
+
+__device__ __forceinline__ void set_quarter(f32x16& v, int e4, f32x4 q) {
+  v[4 * e4] = q[0];
+  v[4 * e4 + 1] = q[1];
+  v[4 * e4 + 2] = q[2];
+  v[4 * e4 + 3] = q[3];
+}
+
+// A piece's slot in the workspace: its kDTw d-tiles as the register image of
+// the accumulators (each f32x16 stored as four 16-byte columns of 64 lanes),
+// then m of its 32 heads, then l.
+template <int D, int P>
+struct Piece {
+  static constexpr int kDTw = D / 32 / P;
+  static constexpr int kOBytes = kDTw * 4 * 64 * 16;
+  static constexpr int kBytes = kOBytes + 2 * 32 * 4;
+};
+
+template <int D, int HB, int P>
+__global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
+  constexpr int kWaves = 4;
+  static_assert(HB * P == kWaves, "four waves: head blocks x parities");
+  constexpr int kHeads = 32 * HB;
+  constexpr int kRowBytes = 2 * D;
+  constexpr int kSuper = 16 * P;  // rows per super-tile
+  constexpr int kStageBytes = kSuper * kRowBytes;
+  constexpr int kKSteps = D / 32;
+  constexpr int kDT = D / 32;    // 32-wide d-tiles of the PV product
+  constexpr int kDTw = kDT / P;  // d-tiles of this wave's piece
+  constexpr int kRowsPerLoad = 1024 / kRowBytes;
+  constexpr int kLoadsPerStage = kSuper / kRowsPerLoad;
+  constexpr int kLoadsPerWave = kLoadsPerStage / kWaves;
+  constexpr int kRing = 128 * 1024;
+  // stages of the ring: what kRing holds, at most 4, and no more loads in
+  // flight per wave than the 6-bit vmcnt counts
+  constexpr int kFit = kRing / kStageBytes < 4 ? kRing / kStageBytes : 4;
+  constexpr int kCount = 63 / kLoadsPerWave;
+  constexpr int kStages0 = kFit < kCount ? kFit : kCount;
+  constexpr int kStages = kStages0 < 2 ? 2 : kStages0;
+  using Pc = Piece<D, P>;
+  // LDS read lead of the QK (k-steps) and PV (d-tiles) loops
+  constexpr int kKA = 2, kVA = 2;
+  // super-tiles in flight when the loop starts
+  constexpr int kBurst = 2 < kStages ? 2 : kStages;
+  static_assert(D % 64 == 0 && D <= 512, "unsupported D");
+  static_assert(kDTw >= 1, "a piece holds at least one d-tile");
+  static_assert(kLoadsPerStage % kWaves == 0, "loads must divide among waves");
+  static_assert(kStages * kLoadsPerWave <= 63, "outstanding loads must fit vmcnt");
+  static_assert(P == 1 || kStages * kStageBytes >= kWaves * (kDT / 2) * 64 * 64,
+                "the parity exchange reuses the ring");
+
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(256))) int sidx[kSplitIdx];
+  __shared__ __attribute__((aligned(256))) float ssink[64];
+  __shared__ float sml[kWaves][4][16];  // per wave: m0, m1, l0, l1 of its 32 heads
+  __shared__ int sflag[kWaves];
+
+  // Work item (token, head group, partition), partition fastest: the
+  // partitions and head groups of a token are consecutive items, which
+  // xcd_item keeps on one XCD (one L2) and dispatches together.
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const int c = item % a.splits;
+  const int th = item / a.splits;
+  const int hg = th % a.head_groups;
+  const int t = th / a.head_groups;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hb = wave / P;
+  const int par = wave % P;
+  const int n16 = lane & 15;
+  const int g = lane >> 4;
+  const int h0 = hg * kHeads + hb * 32;  // first head of this wave (32 heads)
+
+  // q of the workgroup's heads is staged once into the last kQStages stages of
+  // the ring (rows XOR-swizzled like the tiles, so that the Q^T reads below
+  // put 16 heads' same chunk in 16 bank groups), read into registers, and the
+  // stages are handed back to the row tiles; rows of heads past H repeat a
+  // valid row.  Its loads go out first, with the sinks: neither depends on the
+  // slice, so their latency overlaps the kv_indptr and index round trips.
+  constexpr int kQBytes = kHeads * kRowBytes;
+  constexpr int kQStages = (kQBytes + kStageBytes - 1) / kStageBytes;
+  static_assert(kQStages < kStages, "q staging must leave a stage for the first tiles");
+  constexpr int kQLoads = kQBytes / 1024;
+  static_assert(kQLoads % kWaves == 0, "q loads must divide among waves");
+  constexpr int kQLoadsPerWave = kQLoads / kWaves;
+  unsigned char* sq = smem + (kStages - kQStages) * kStageBytes;
+  {
+    constexpr int kRowsPerLd = 1024 / kRowBytes;
+    constexpr int kChunksQ = kRowBytes / 16;
+    const unsigned char* qb = reinterpret_cast<const unsigned char*>(a.q);
+    const int64_t qrow0 = (int64_t)t * a.H + hg * kHeads;
+#pragma unroll
+    for (int k = 0; k < kQLoadsPerWave; ++k) {
+      const int ld = k * kWaves + wave;
+      const int r = ld * kRowsPerLd + lane / kChunksQ;  // head row within the group
+      const int hr = hg * kHeads + r < a.H ? r : 0;
+      const int chunk = (lane % kChunksQ) ^ (row_swizzle(r) & (kChunksQ - 1));
+      dma_16B(qb + ((qrow0 + hr) * kRowBytes + chunk * 16),
+              __builtin_amdgcn_readfirstlane(lds_addr(sq + ld * 1024)));
+    }
+    if (wave == 0) {
+      const int hs = hg * kHeads + lane;
+      dma_4B(a.sink + (hs < a.H ? hs : a.H - 1), __builtin_amdgcn_readfirstlane(lds_addr(ssink)));
+    }
+  }
+
+  const ScalarI32Ptr indptr = (ScalarI32Ptr)a.kv_indptr;
+  const int row0 = indptr[t];
+  const int L = indptr[t + 1] - row0;
+  const int nparts = partitions_of(L, a.splits, a.split_rows);
+  if (c >= nparts || L <= 0) {
+    wait_vmcnt<0>();  // no LDS-DMA load may outlive the workgroup
+    // partition 0 of an empty slice: zeros
+    if (c == 0 && L <= 0 && par == 0)
+      zero_heads<D>(a.out, a.H, t, h0, a.H - h0 < 32 ? a.H - h0 : 32, lane, 64);
+    return;
+  }
+  const int cb = c * a.split_rows;
+  const int nrows = (c == nparts - 1) ? L - cb : a.split_rows;
+  const int32_t* part = a.kv_indices + row0 + cb;
+
+  const TileOffsets<D, 1> off(n16, g);
+  const WideVtOffsets<D> voff(lane);
+
+  // wait until at most `tiles` (< kStages) later super-tiles of this wave are in flight
+  auto wait_outstanding = [](int tiles) {
+    constexpr int k2 = kStages > 2 ? 2 : 1, k3 = kStages > 3 ? 3 : k2;
+    switch (tiles) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<kLoadsPerWave>(); break;
+      case 2: wait_vmcnt<k2 * kLoadsPerWave>(); break;
+      default: wait_vmcnt<k3 * kLoadsPerWave>(); break;
+    }
+  };
+
+  // The first chunk's indices; once they (and q, issued before them) are in,
+  // the first tiles go out into the stages q does not use, then q is read.
+  const int n0 = nrows < kSplitIdx ? nrows : kSplitIdx;
+  const int ntiles0 = (n0 + kSuper - 1) / kSuper;
+  const int burst0 = ntiles0 < kBurst ? ntiles0 : kBurst;  // tiles in flight before the loop
+  const int pre = burst0 < kStages - kQStages ? burst0 : kStages - kQStages;
+  auto issue_tile0 = [&](int tile) {
+    issue_rows<kRowBytes, kLoadsPerWave, 1>(
+        a.kv, sidx, n0, tile * kSuper + wave * (kSuper / kWaves), wave * (kSuper / kWaves),
+        smem + (tile % kStages) * kStageBytes + wave * kLoadsPerWave * 1024, lane);
+  };
+  stage_indices(part, 0, n0, sidx, wave, kWaves, lane);
+  wait_vmcnt<0>();
+  barrier_lds();
+  for (int k = 0; k < pre; ++k) issue_tile0(k);
+  bf16x8 q0[kKSteps], q1[kKSteps];  // Q^T operands of head blocks 0 and 1
+  {
+    // lane (n16, g) of the k-step u operand holds q[h, 32 u + 8 g .. +7]:
+    // logical chunk 4 u + g of head row h, stored at chunk ^ swizzle(h)
+    const int r0 = hb * 32 + n16, r1 = r0 + 16;
+    constexpr int kChunksQ = kRowBytes / 16;
+    const int sw = row_swizzle(n16) & (kChunksQ - 1);  // r0 & 15 == r1 & 15 == n16
+#pragma unroll
+    for (int u = 0; u < kKSteps; ++u) {
+      const int ch = ((4 * u + g) ^ sw) * 16;
+      q0[u] = *reinterpret_cast<const bf16x8*>(sq + r0 * kRowBytes + ch);
+      q1[u] = *reinterpret_cast<const bf16x8*>(sq + r1 * kRowBytes + ch);
+    }
+    barrier_lds();  // every wave has its q: the stages go back to the tiles
+    for (int k = pre; k < burst0; ++k) issue_tile0(k);
+  }
+  float m0 = -INFINITY, l0 = 0.f, mt0 = -INFINITY, sk0 = -INFINITY;
+  float m1 = -INFINITY, l1 = 0.f, mt1 = -INFINITY, sk1 = -INFINITY;
+  f32x16 acc[kDT];
+  for (int pass = 0; pass < 2; ++pass) {
+    bool first0 = pass == 0, first1 = pass == 0;
+    if (pass == 1) {
+      second_pass_state(sk0, mt0, g, m0, l0);
+      second_pass_state(sk1, mt1, g, m1, l1);
+    }
+#pragma unroll
+    for (int i = 0; i < kDT; ++i) acc[i] = f32x16{};
+    bool over = false;
+
+    for (int sc = 0; sc < nrows; sc += kSplitIdx) {
+      const int n = nrows - sc < kSplitIdx ? nrows - sc : kSplitIdx;
+      if (sc > 0 || pass > 0) barrier_lds();  // every wave is done with the ring and indices
+      if (sc > 0 || pass > 0) {
+        stage_indices(part, sc, n, sidx, wave, kWaves, lane);
+        wait_vmcnt<0>();
+        barrier_lds();
+      }
+      if (pass == 0 && sc == 0) {  // the sink belongs to partition 0, parity 0
+        const bool own = c == 0 && par == 0;
+        sk0 = own && h0 + n16 < a.H ? ssink[hb * 32 + n16] * kLog2e : -INFINITY;
+        sk1 = own && h0 + 16 + n16 < a.H ? ssink[hb * 32 + 16 + n16] * kLog2e : -INFINITY;
+      }
+      const int ntiles = (n + kSuper - 1) / kSuper;
+
+      auto issue_tile = [&](int tile) {
+        issue_rows<kRowBytes, kLoadsPerWave, 1>(
+            a.kv, sidx, n, tile * kSuper + wave * (kSuper / kWaves), wave * (kSuper / kWaves),
+            smem + (tile % kStages) * kStageBytes + wave * kLoadsPerWave * 1024, lane);
+      };
+      const int first_burst = ntiles < kBurst ? ntiles : kBurst;
+      if (sc > 0 || pass > 0)  // the first chunk's burst went out in the prologue
+        for (int k = 0; k < first_burst; ++k) issue_tile(k);
+
+      for (int i = 0; i < ntiles; ++i) {
+        // before this wait, tiles [0, first_burst) went out together and one
+        // more after each barrier from i = 1 on: min(ntiles, kBurst + i - 1)
+        const int issued = i == 0 ? first_burst : min(ntiles, kBurst + i - 1);
+        wait_outstanding(issued - i - 1);
+        barrier_lds();  // super-tile i is in LDS; every wave is done with i-1's stage
+        // the next tile goes into the stage tile i - 1 left (kBurst <= kStages)
+        if (i >= 1 && i - 1 + kBurst < ntiles) issue_tile(i - 1 + kBurst);
+
+        const int nvalid = n - i * kSuper - 16 * par;  // rows of this wave's 16 that exist
+        if (nvalid <= 0) continue;                     // (wave-uniform: a ragged tail)
+        // The stage's offset is opaque to the compiler: it would otherwise keep
+        // every lane offset precomputed for each stage (registers it lacks).
+        int stoff = (i % kStages) * kStageBytes + 16 * par * kRowBytes;
+        asm volatile("" : "+v"(stoff));
+        const unsigned char* st = smem + stoff;
+
+        // S^T = K Q^T for both head blocks; the K reads run kKA k-steps ahead
+        // of the MFMAs that consume them (one read issued after each step's
+        // MFMA pair), two chains per block.
+        bf16x8 ka[kKSteps];
+        f32x4 s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
+#pragma unroll
+        for (int u = 0; u < kKA && u < kKSteps; ++u) ka[u] = *reinterpret_cast<const bf16x8*>(st + off.kq(u));
+#pragma unroll
+        for (int u = 0; u < kKSteps; ++u) {
+          if (u & 1) {
+            s0b = mfma_k32(ka[u], q0[u], s0b);
+            s1b = mfma_k32(ka[u], q1[u], s1b);
+          } else {
+            s0a = mfma_k32(ka[u], q0[u], s0a);
+            s1a = mfma_k32(ka[u], q1[u], s1a);
+          }
+          if (u + kKA < kKSteps) ka[u + kKA] = *reinterpret_cast<const bf16x8*>(st + off.kq(u + kKA));
+        }
+        {
+          constexpr int kPre = kKA < kKSteps ? kKA : kKSteps;
+          __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+#pragma unroll
+          for (int u = 0; u < kKSteps; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if (u + kPre < kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        const f32x4 s0 = s0a + s0b, s1 = s1a + s1b;
+
+        float x0[4], x1[4];
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const bool v = 4 * g + i4 < nvalid;
+          x0[i4] = v ? s0[i4] * a.qk_scale : -INFINITY;
+          x1[i4] = v ? s1[i4] * a.qk_scale : -INFINITY;
+        }
+        __bf16 p0[4], p1[4];
+        over |= softmax_tile<4>(x0, sk0, g, first0, m0, mt0, l0, p0);
+        over |= softmax_tile<4>(x1, sk1, g, first1, m1, mt1, l1, p1);
+        bf16x4 pa, pbk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pa[e] = p0[e];
+          pbk[e] = p1[e];
+        }
+        const bf16x8 pb = wide_p_operand(pa, pbk);
+
+        // O^T += V^T P^T over the 16 rows: the two transposing reads of d-tile
+        // u + kVA run under the MFMA of d-tile u.
+        {
+          bf16x8 va[kDT];
+          auto read_vt = [&](int u) {
+            const bf16x4 vl = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + voff.at(u, 0)));
+            const bf16x4 vh = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + voff.at(u, 1)));
+            va[u] = __builtin_shufflevector(vl, vh, 0, 1, 2, 3, 4, 5, 6, 7);
+          };
+#pragma unroll
+          for (int u = 0; u < kVA && u < kDT; ++u) read_vt(u);
+#pragma unroll
+          for (int u = 0; u < kDT; ++u) {
+            acc[u] = mfma32(va[u], pb, acc[u]);
+            if (u + kVA < kDT) read_vt(u + kVA);
+          }
+          constexpr int kPre = kVA < kDT ? kVA : kDT;
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre, 0);
+#pragma unroll
+          for (int u = 0; u < kDT; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (u + kPre < kDT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    if (!workgroup_any(over, sflag, wave, kWaves)) break;
+  }
+
+  // This wave's states: head n16 of block 0 (m0, l0) and of block 1 (m1, l1);
+  // m is -inf for a parity that saw no row.  Accumulator layout: lane
+  // (n = lane % 32, hf = lane / 32) holds, for head h0 + n, d = 32 dt + 8 e4 +
+  // 4 hf + e as element 4 e4 + e of acc[dt]; head h0 + n is head n % 16 =
+  // lane % 16 of block n / 16, whose softmax state this lane holds too.
+  const int n = lane & 31, hf = lane >> 5;
+  float lb0 = group_sum4(l0), lb1 = group_sum4(l1);
+
+  // Merge the P parity states of head block hb in LDS: a butterfly over the
+  // parity bits.  At stride s a wave keeps the lower half of its current
+  // d-tile range when bit s of its parity is 0 (the upper one otherwise),
+  // hands the other half to its partner par ^ s, and combines the partner's
+  // half with its own, the lower parity's state first.
+  int lo = 0;  // first d-tile of the range this wave holds; acc[0, kDTw) is the piece
+  if constexpr (P > 1) {
+#pragma unroll
+    for (int s = 1; s < P; s <<= 1) {
+      constexpr int kHalfMax = kDT / 2;
+      const int half = kDT / (2 * s);  // compile-time per unrolled round
+      const bool upper = (par & s) != 0;
+      const int partner = hb * P + (par ^ s);
+      barrier_lds();  // the ring is free, and the previous round's reads are done
+      if (g == 0) {
+        sml[wave][0][n16] = m0;
+        sml[wave][1][n16] = m1;
+        sml[wave][2][n16] = lb0;
+        sml[wave][3][n16] = lb1;
+      }
+      // hand over the half this wave gives away (register image); the
+      // branches are wave-uniform and keep every accumulator index constant
+      f32x4* mine = reinterpret_cast<f32x4*>(smem) + wave * kHalfMax * 256 + lane;
+      if (upper) {
+#pragma unroll
+        for (int i = 0; i < half; ++i)
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) mine[(i * 4 + e4) * 64] = quarter(acc[i], e4);
+      } else {
+#pragma unroll
+        for (int i = 0; i < half; ++i)
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) mine[(i * 4 + e4) * 64] = quarter(acc[half + i], e4);
+      }
+      barrier_lds();
+      const float pm0 = sml[partner][0][n16], pm1 = sml[partner][1][n16];
+      const float pl0 = sml[partner][2][n16], pl1 = sml[partner][3][n16];
+      const float M0 = fmaxf(m0, pm0), M1 = fmaxf(m1, pm1);
+      const float ws0 = state_weight(m0, M0), wp0 = state_weight(pm0, M0);
+      const float ws1 = state_weight(m1, M1), wp1 = state_weight(pm1, M1);
+      const float wself = n < 16 ? ws0 : ws1, wpart = n < 16 ? wp0 : wp1;
+      const f32x4* tp = reinterpret_cast<const f32x4*>(smem) + partner * kHalfMax * 256 + lane;
+      // the kept half moves to the front, the lower parity's state first
+      if (upper) {
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+          f32x16 other;
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) set_quarter(other, e4, tp[(i * 4 + e4) * 64]);
+          acc[i] = wpart * other + wself * acc[half + i];
+        }
+        lb0 = wp0 * pl0 + ws0 * lb0;
+        lb1 = wp1 * pl1 + ws1 * lb1;
+        lo += half;
+      } else {
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+          f32x16 other;
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) set_quarter(other, e4, tp[(i * 4 + e4) * 64]);
+          acc[i] = wself * acc[i] + wpart * other;
+        }
+        lb0 = ws0 * lb0 + wp0 * pl0;
+        lb1 = ws1 * lb1 + wp1 * pl1;
+      }
+      m0 = M0;
+      m1 = M1;
+    }
+  }
+
+  // Cross-workgroup merge.  Piece w (held by wave w: head block w / P,
+  // d-tiles [piece_lo(w % P), + kDTw)) of every partition of (token, head
+  // group) is merged by workgroup w mod nparts, all four of its waves sharing
+  // the piece's d-tiles.  The other partitions publish it and count
+  // themselves in; the merging workgroup waits for the count (bounded), then
+  // loads every partition's share at once and sums in partition order.
+  auto piece_lo = [](int pr) {  // first d-tile a parity keeps after the butterfly
+    int l = 0;
+#pragma unroll
+    for (int s2 = 1; s2 < P; s2 <<= 1) l += (pr & s2) ? kDT / (2 * s2) : 0;
+    return l;
+  };
+  if (nparts == 1) {
+    // out = O / l for heads h0 + n, d-tiles [lo, lo + kDTw)
+    if (h0 + n < a.H) {
+      const float inv = 1.0f / (n < 16 ? lb0 : lb1);
+      uint16_t* op = a.out + ((int64_t)t * a.H + h0 + n) * D + 4 * hf + 32 * lo;
+#pragma unroll
+      for (int i = 0; i < kDTw; ++i)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) store_bf16x4(op + 32 * i + 8 * e4, quarter(acc[i], e4), inv);
+    }
+    return;
+  }
+
+  const int64_t slot = (int64_t)Pc::kBytes;
+  const int64_t item_bytes = kWaves * slot;
+  unsigned char* ws = reinterpret_cast<unsigned char*>(a.ws);
+  unsigned char* ws_th = ws + (int64_t)th * a.splits * item_bytes;  // partition 0's slots
+  int* ctr_th = reinterpret_cast<int*>(ws + (int64_t)a.N * a.head_groups * a.splits * item_bytes) +
+                (int64_t)th * kWaves;
+  const int others = nparts - 1;
+
+  // publishing: this wave's piece to its slot, complete before the count
+  auto publish = [&]() {
+    const __amdgpu_buffer_rsrc_t r = ws_rsrc(ws_th + c * item_bytes + wave * slot);
+#pragma unroll
+    for (int i = 0; i < kDTw; ++i)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) store_sc1(r, ((i * 4 + e4) * 64 + lane) * 16, quarter(acc[i], e4));
+    if (g == 0) {
+      store1_sc1(r, Pc::kOBytes + n16 * 4, m0);
+      store1_sc1(r, Pc::kOBytes + (16 + n16) * 4, m1);
+      store1_sc1(r, Pc::kOBytes + 128 + n16 * 4, lb0);
+      store1_sc1(r, Pc::kOBytes + 128 + (16 + n16) * 4, lb1);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  auto arrive = [&](int w) {
+    int old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(ctr_th + w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    asm volatile("" ::: "memory");
+    return old;
+  };
+
+  // Merge of piece w over d-tiles [i0, i0 + ni) of it, by one wave: partition
+  // c's share comes from `own` (a register image in LDS, or this wave's own
+  // accumulators when own_regs), the others' from their slots.  Writes out.
+  auto merge_range = [&](int w, int i0, const f32x4* own_lds, bool own_regs, float om0, float om1,
+                         float ol0, float ol1, auto ni_tag) {
+    constexpr int kNi = decltype(ni_tag)::value;
+    // partitions whose shares are loaded together (registers: kBatch * kNi
+    // accumulator images)
+    constexpr int kBatch = kNi <= 2 ? 4 : 1;
+    // pass 1: the largest m over the partitions (partition c's own from the
+    // arguments), kMB partitions' loads in flight at a time
+    constexpr int kMB = 8;
+    float M0 = -INFINITY, M1 = -INFINITY;
+    for (int k0 = 0; k0 < nparts; k0 += kMB) {
+      float x0[kMB], x1[kMB];
+#pragma unroll
+      for (int b = 0; b < kMB; ++b) {
+        const int k = k0 + b < nparts ? k0 + b : 0;
+        const __amdgpu_buffer_rsrc_t r = ws_rsrc(ws_th + k * item_bytes + w * slot);
+        x0[b] = load1_sc1(r, Pc::kOBytes + n16 * 4);
+        x1[b] = load1_sc1(r, Pc::kOBytes + (16 + n16) * 4);
+      }
+#pragma unroll
+      for (int b = 0; b < kMB; ++b) {
+        const int k = k0 + b;
+        if (k < nparts) {
+          M0 = fmaxf(M0, k == c ? om0 : x0[b]);
+          M1 = fmaxf(M1, k == c ? om1 : x1[b]);
+        }
+      }
+    }
+    // pass 2: each partition's share weighted by 2^(m - M), summed in
+    // partition order (every arrival order gives the same bits)
+    float ls0 = 0.f, ls1 = 0.f;
+    f32x16 tot[kNi];
+#pragma unroll
+    for (int i = 0; i < kNi; ++i) tot[i] = f32x16{};
+    for (int k0 = 0; k0 < nparts; k0 += kBatch) {
+      f32x16 x[kBatch][kNi];
+      float bm0[kBatch], bm1[kBatch], bl0[kBatch], bl1[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {  // the batch's loads go out before any is used
+        const int k = k0 + b < nparts ? k0 + b : 0;
+        if (k == c) {
+          bm0[b] = om0;
+          bm1[b] = om1;
+          bl0[b] = ol0;
+          bl1[b] = ol1;
+#pragma unroll
+          for (int i = 0; i < kNi; ++i) {
+            if (own_regs) {
+              x[b][i] = acc[i0 + i];
+            } else {
+#pragma unroll
+              for (int e4 = 0; e4 < 4; ++e4) set_quarter(x[b][i], e4, own_lds[((i0 + i) * 4 + e4) * 64 + lane]);
+            }
+          }
+        } else {
+          const __amdgpu_buffer_rsrc_t r = ws_rsrc(ws_th + k * item_bytes + w * slot);
+          bm0[b] = load1_sc1(r, Pc::kOBytes + n16 * 4);
+          bm1[b] = load1_sc1(r, Pc::kOBytes + (16 + n16) * 4);
+          bl0[b] = load1_sc1(r, Pc::kOBytes + 128 + n16 * 4);
+          bl1[b] = load1_sc1(r, Pc::kOBytes + 128 + (16 + n16) * 4);
+#pragma unroll
+          for (int i = 0; i < kNi; ++i)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+              set_quarter(x[b][i], e4, load_sc1(r, (((i0 + i) * 4 + e4) * 64 + lane) * 16));
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        if (k0 + b < nparts) {
+          const float w0 = state_weight(bm0[b], M0);
+          const float w1 = state_weight(bm1[b], M1);
+          ls0 += w0 * bl0[b];
+          ls1 += w1 * bl1[b];
+          const float wk = n < 16 ? w0 : w1;
+#pragma unroll
+          for (int i = 0; i < kNi; ++i) tot[i] += wk * x[b][i];
+        }
+      }
+    }
+    const int hw0 = hg * kHeads + (w / P) * 32;  // first head of piece w
+    if (hw0 + n < a.H) {
+      const float inv = 1.0f / (n < 16 ? ls0 : ls1);
+      uint16_t* op = a.out + ((int64_t)t * a.H + hw0 + n) * D + 4 * hf + 32 * (piece_lo(w % P) + i0);
+#pragma unroll
+      for (int i = 0; i < kNi; ++i)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) store_bf16x4(op + 32 * i + 8 * e4, quarter(tot[i], e4), inv);
+    }
+  };
+
+  // 1. publish the pieces another workgroup merges; an arrival that completes
+  //    a count whose merger gave up merges that piece alone
+  if (wave % nparts != c) {
+    publish();
+    if (arrive(wave) == others) {
+      merge_range(wave, 0, nullptr, true, m0, m1, lb0, lb1, std::integral_constant<int, kDTw>{});
+      if (lane == 0) __hip_atomic_store(ctr_th + wave, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // 2. merge this workgroup's pieces, all four waves sharing each
+  constexpr int kShare = kDTw >= kWaves ? kDTw / kWaves : 1;  // d-tiles per wave
+  f32x4* spiece = reinterpret_cast<f32x4*>(smem);
+  int* sdec = sflag;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (w % nparts != c) continue;  // (workgroup-uniform)
+    barrier_lds();  // the ring is free; the previous piece's reads are done
+    if (wave == w) {  // the holder: its share to LDS, then wait for the others
+      if (g == 0) {
+        sml[w][0][n16] = m0;
+        sml[w][1][n16] = m1;
+        sml[w][2][n16] = lb0;
+        sml[w][3][n16] = lb1;
+      }
+#pragma unroll
+      for (int i = 0; i < kDTw; ++i)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) spiece[(i * 4 + e4) * 64 + lane] = quarter(acc[i], e4);
+      int v = 0;
+      for (int it = 0; a.split_wait && it < kSpinLimit; ++it) {
+        // polled with a read-modify-write (max with 0 leaves the count as it
+        // is): it is served where the arrivals' adds are, which a plain
+        // agent-scope load is not guaranteed to be promptly
+        if (lane == 0) v = __hip_atomic_fetch_max(ctr_th + w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v = __builtin_amdgcn_readfirstlane(v);
+        if (v >= others) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      asm volatile("" ::: "memory");
+      int decision = 1;
+      if (v < others) {  // (waited long enough, or not at all) the arrival that completes the count merges
+        publish();
+        decision = arrive(w) == others ? 1 : 0;
+      }
+      if (decision && lane == 0)
+        __hip_atomic_store(ctr_th + w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) sdec[0] = decision;
+    }
+    barrier_lds();
+    if (sdec[0] == 0) continue;  // (workgroup-uniform) a later arrival merges it
+    if (kDTw >= kWaves || wave < kDTw) {
+      merge_range(w, wave * kShare, spiece, false, sml[w][0][n16], sml[w][1][n16], sml[w][2][n16],
+                  sml[w][3][n16], std::integral_constant<int, kShare>{});
+    }
+  }
+}
+
+// Compute units of the current device, read once per device.
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cus[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+template <int D, int HB, int P>
+hipError_t launch_split_d(const AttnArgs& a0, hipStream_t stream) {
+  const long long items = (long long)a0.N * a0.head_groups * a0.splits;
+  AttnArgs a = a0;
+  // one workgroup per CU (the LDS ring and 512 registers a wave): the grid is
+  // resident at once when it has no more workgroups than CUs
+  a.split_wait = items <= device_cus() ? 1 : 0;
+  hipLaunchKernelGGL((attn_split_kernel<D, HB, P>), dim3((unsigned)items), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_split_shape(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
+  const int hb = p.heads_per_group / 32;
+  if (hb == 2 && p.parities == 2) return launch_split_d<D, 2, 2>(a, stream);
+  if constexpr (D >= 128) {
+    if (hb == 1 && p.parities == 4) return launch_split_d<D, 1, 4>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t split_workspace_bytes(int32_t N, int32_t D, const AttnPlan& p) {
+  const size_t slot = (size_t)(D / 32 / p.parities) * 4 * 64 * 16 + 2 * 32 * 4;
+  const size_t states = (size_t)N * p.head_groups * p.splits * 4 * slot;
+  return states + (size_t)N * p.head_groups * 4 * sizeof(int);
+}
+
+hipError_t launch_split(const AttnArgs& a, int D, const AttnPlan& p, hipStream_t stream) {
+  switch (D) {
+    case 64: return launch_split_shape<64>(a, p, stream);
+    case 128: return launch_split_shape<128>(a, p, stream);
+    case 256: return launch_split_shape<256>(a, p, stream);
+    case 512: return launch_split_shape<512>(a, p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace spd

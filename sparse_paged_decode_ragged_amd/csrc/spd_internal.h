@@ -13,17 +13,19 @@ constexpr int kModeAuto = 0;
 constexpr int kModeHeads = 1;  // waves of a workgroup split the heads, share the rows
 constexpr int kModeRows = 2;   // waves of a workgroup split the rows, share 16 heads
 constexpr int kModeWide = 3;   // heads mode on 32-head waves, asked for explicitly
+constexpr int kModeSplit = 4;  // (token, heads, partition) workgroups merged in-kernel
 
 // Work decomposition of one attention call, fixed by scalar arguments only so
 // that the grid never depends on device data.
 struct AttnPlan {
-  int mode;            // kModeHeads or kModeRows
+  int mode;            // kModeHeads, kModeRows or kModeSplit
   int waves;           // waves per workgroup
   int heads_per_group; // heads per workgroup
   int head_groups;     // ceil(H / heads_per_group)
   int wide;            // heads mode with 32-head waves (attn_wide_kernel)
   int splits;          // partitions of a slice (1 = no split-L)
   int split_rows;      // rows per partition (multiple of 32); huge when splits == 1
+  int parities;        // split mode: waves per head block (1 or 2)
   size_t workspace_bytes;
 };
 
@@ -42,6 +44,10 @@ struct AttnArgs {
   float* ws;                 // split partials (splits > 1)
   float qk_scale;            // softmax_scale * log2(e)
   int32_t N, H, head_groups, splits, split_rows;
+  // split mode: 1 when the whole grid can be resident at once (one
+  // workgroup per CU), so that a merging workgroup may wait a bounded time
+  // for the other partitions; 0 = never wait (the last arrival merges)
+  int32_t split_wait;
   // Page transform (sparse_decode_attn_paged): when paged != 0 each token's
   // rows are derived from these, as build_decode_indices derives them, and
   // kv_indices / kv_indptr are not read.  win + topk <= kPagedMaxLen, no split.
@@ -71,6 +77,14 @@ struct AttnArgs {
 constexpr int kPagedMaxLen = 2048;
 
 hipError_t launch_attention(const AttnArgs& args, int D, const AttnPlan& plan, hipStream_t stream);
+
+// Split mode (attn_split.hip): workgroup = (token, 16 * heads_per_group / 16
+// heads, partition), the partitions of a (token, head group) merged by the
+// last to finish.  The workspace holds one softmax state per work item and
+// one arrival counter per (token, head group, wave); the counters must be
+// zero before the first call and every call leaves them zero.
+size_t split_workspace_bytes(int32_t N, int32_t D, const AttnPlan& plan);
+hipError_t launch_split(const AttnArgs& args, int D, const AttnPlan& plan, hipStream_t stream);
 
 // Attention over an FP8 pool: rows mode (workgroup = token x 16 heads), no
 // split; args.kv8 / args.kv_scale replace args.kv.

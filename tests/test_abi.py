@@ -70,7 +70,7 @@ def test_binding_lists_the_same_symbols():
 def test_status_strings(lib):
     assert lib.spd_status_string(0) == b"SPD_OK"
     assert lib.spd_status_string(3) == b"SPD_ERR_WORKSPACE"
-    assert lib.spd_version() >= 100
+    assert lib.spd_version() >= 200
 
 
 @pytest.mark.parametrize("H,D,ok", [(64, 512, 1), (128, 512, 1), (8, 64, 1), (1, 128, 1),
@@ -102,9 +102,27 @@ def test_attn_rejects_bad_arguments(lib):
 
 
 def test_attn_ex_workspace_checks(lib):
-    AUTO, HEADS, ROWS = 0, 1, 2
-    # decode_base shape: the automatic plan uses the rows mode, which needs no workspace
+    AUTO, HEADS, ROWS, SPLIT = 0, 1, 2, 4
+    # decode_base shape: the automatic plan is the split mode, 64 heads a
+    # workgroup (4 waves of 32 heads: 2 head blocks x 2 parities), 4
+    # partitions of 160 rows: one piece slot per (token, partition, wave) of
+    # 32 heads x 256 fp32 + 32 m + 32 l, then one int32 arrival counter per
+    # (token, wave)
+    split_need = 64 * 4 * 4 * (32 * 256 * 4 + 2 * 32 * 4) + 64 * 4 * 4
+    assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 0, SPLIT) == split_need
+    # the automatic plan keeps rows mode for 640-row slices (no workspace) and
+    # splits small batches of slices of 2048 rows and more: 16 tokens x 8
+    # partitions of 256 rows
     assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 0, AUTO) == 0
+    # 16 tokens of up to 2048 rows: 16 partitions of 128 rows (256 workgroups)
+    assert lib.sparse_decode_attn_workspace_size(16, 64, 512, 2048, 0, AUTO) == \
+        16 * 16 * 4 * (32 * 256 * 4 + 2 * 32 * 4) + 16 * 4 * 4
+    # at most 32 partitions
+    assert lib.sparse_decode_attn_workspace_size(2, 64, 512, 65536, 0, SPLIT) == \
+        2 * 32 * 4 * (32 * 256 * 4 + 2 * 32 * 4) + 2 * 4 * 4
+    assert lib.sparse_decode_attn_workspace_size(2, 64, 512, 65536, 1024, SPLIT) == 0
+    # without a capacity bound the automatic plan cannot split: rows mode, no workspace
+    assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 0, 0, AUTO) == 0
     assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 0, ROWS) == 0
     # heads mode splits a 640-row slice into 4 partitions of 160 rows:
     # 64 tokens x 1 head group x 4 partitions x 64 heads x (512 + 2) floats

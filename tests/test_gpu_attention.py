@@ -32,10 +32,11 @@ def run(spd, w, idx_np, ptr_np, sink=None, **plan):
     return out
 
 
-ROWS, HEADS, WIDE = 2, 1, 3
+ROWS, HEADS, WIDE, SPLIT = 2, 1, 3, 4
 PLANS = [dict(plain=True), dict(mode=ROWS), dict(mode=HEADS),
          dict(mode=HEADS, max_len=200, split_rows=32), dict(mode=HEADS, max_len=200, split_rows=64),
-         dict(max_len=200)]
+         dict(max_len=200), dict(mode=SPLIT, max_len=200), dict(mode=SPLIT, max_len=200, split_rows=32),
+         dict(mode=SPLIT, max_len=200, split_rows=64)]
 
 
 def plans(H):
@@ -107,7 +108,8 @@ def test_single_row_without_sink_is_bit_exact(spd, H):
     sink = np.full(H, -np.inf, dtype=np.float32)
     log("case single row H=%d" % H)
     extra = [dict(mode=WIDE)] if H % 64 == 0 else []
-    for plan in [dict(mode=ROWS), dict(mode=HEADS), dict(max_len=32, split_rows=32)] + extra:
+    for plan in [dict(mode=ROWS), dict(mode=HEADS), dict(max_len=32, split_rows=32),
+                 dict(mode=SPLIT, max_len=32)] + extra:
         out = run(spd, w, w.kv_indices, w.kv_indptr, sink=sink, **plan)
         kv = W.device_bits(w.kv_bits, torch.device("cuda:0"))
         for t in range(5):
@@ -133,7 +135,7 @@ def test_permutation_and_duplicates(spd):
         perm[a:b] = rng.permutation(perm[a:b])
     log("case permutation")
     ref = oracle_tokens(w, w.kv_indices, w.kv_indptr)
-    for plan in [dict(mode=ROWS), dict(mode=HEADS), dict(mode=WIDE)]:
+    for plan in [dict(mode=ROWS), dict(mode=HEADS), dict(mode=WIDE), dict(mode=SPLIT, max_len=130)]:
         o1 = bf16_to_f64(run(spd, w, w.kv_indices, w.kv_indptr, **plan))
         o2 = bf16_to_f64(run(spd, w, perm, w.kv_indptr, **plan))
         assert_close(o1, ref, "original order %s" % plan)
@@ -150,6 +152,8 @@ def test_repeated_rows_closed_form(spd):
     assert_close(out, ref_closed_form(w, L), "repeated row, split")
     out = bf16_to_f64(run(spd, w, w.kv_indices, w.kv_indptr, mode=ROWS))
     assert_close(out, ref_closed_form(w, L), "repeated row, rows mode")
+    out = bf16_to_f64(run(spd, w, w.kv_indices, w.kv_indptr, mode=SPLIT, max_len=L, split_rows=64))
+    assert_close(out, ref_closed_form(w, L), "repeated row, split mode")
 
 
 def ref_closed_form(w, L):
@@ -165,7 +169,8 @@ def ref_closed_form(w, L):
 def test_deterministic(spd):
     w = W.random_csr("det", 16, 8, 64, 512, 3000, [640, 1, 0, 333, 1000, 64, 65, 2000])
     log("case determinism")
-    for plan in [dict(mode=ROWS), dict(mode=HEADS), dict(mode=WIDE), dict(max_len=2000, mode=HEADS)]:
+    for plan in [dict(mode=ROWS), dict(mode=HEADS), dict(mode=WIDE), dict(max_len=2000, mode=HEADS),
+                 dict(max_len=2000, mode=SPLIT)]:
         a = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
         b = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
@@ -200,7 +205,8 @@ def test_late_large_scores_take_the_second_pass(spd):
     w.kv_bits = kv
     log("case late large scores")
     ref = oracle_tokens(w, w.kv_indices, w.kv_indptr)
-    for plan in plans(w.H) + [dict(mode=HEADS, max_len=2100, split_rows=256)]:
+    for plan in plans(w.H) + [dict(mode=HEADS, max_len=2100, split_rows=256),
+                              dict(mode=SPLIT, max_len=2100, split_rows=512)]:
         out = run(spd, w, w.kv_indices, w.kv_indptr, **plan)
         assert_close(bf16_to_f64(out), ref, "late large %s" % plan)
 

@@ -1,6 +1,8 @@
-"""GPU parity at the benchmark configurations' full sizes (decode_base fully;
-ragged, large and prefill on sampled tokens that always include the longest,
-shortest and empty slices), in the launch configuration the benchmark times,
+"""GPU parity at the benchmark configurations' full sizes: every token of
+decode_base, ragged, large and prefill against the fp64 oracle (in chunks of
+tokens, to bound host memory), in the launch configuration the benchmark
+times; the other plans on sampled tokens that always include the longest,
+shortest and empty slices; a small batch of long slices on the split plan;
 plus HIP-graph capture and replay of builder + attention with fixed-shape
 buffers whose contents change between replays."""
 import numpy as np
@@ -39,6 +41,21 @@ def sample_tokens(indptr: np.ndarray, n: int, seed: int) -> np.ndarray:
     return np.array(sorted(pick))
 
 
+def check_all_tokens(w, indices, indptr, out, what, chunk=512):
+    """Every token of `out` against the oracle, chunk tokens at a time."""
+    N = len(indptr) - 1
+    worst = 0.0
+    for t0 in range(0, N, chunk):
+        toks = np.arange(t0, min(N, t0 + chunk))
+        ref = oracle_tokens(w, indices, indptr, toks)
+        got = bf16_to_f64(out[t0:t0 + len(toks)])
+        err = np.abs(got - ref)
+        bound = 1e-2 + 1e-2 * np.abs(ref)
+        assert_close(got, ref, "%s tokens %d..%d" % (what, t0, toks[-1]))
+        worst = max(worst, float((err / bound).max()) if err.size else 0.0)
+    log("  %s: all %d tokens, max err/bound %.3f" % (what, N, worst))
+
+
 def build_on_gpu(spd, b):
     ss, sl, cp, bt = device_builder_inputs(b)
     ptr, idx = spd.build_decode_indices(ss, sl, cp, bt, b.win, b.k_per_block, b.swa_pages)
@@ -57,7 +74,8 @@ def test_decode_base_end_to_end(spd):
     ref = oracle_tokens(w, oidx, optr)
     q, kv, sink = device_inputs(w)
     for plan in [dict(max_len=640), dict(plain=True), dict(mode=1, max_len=640),
-                 dict(max_len=640, split_rows=64), dict(max_len=640, split_rows=320)]:
+                 dict(max_len=640, split_rows=64), dict(max_len=640, split_rows=320),
+                 dict(mode=4, max_len=640), dict(mode=4, max_len=640, split_rows=128)]:
         out = spd.sparse_decode_attn(q, kv, idx, ptr, sink, w.softmax_scale, **plan)
         torch.cuda.synchronize()
         assert_close(bf16_to_f64(out), ref, "decode_base %s" % plan)
@@ -70,9 +88,14 @@ def test_ragged_config(spd, device_data):
     ref = oracle_tokens(w, w.kv_indices, w.kv_indptr, tokens)
     q, kv, sink = device_inputs(w)
     idx, ptr = device_csr(w.kv_indices, w.kv_indptr)
+    # the launch the benchmark times: every token
+    out = spd.sparse_decode_attn(q, kv, idx, ptr, sink, w.softmax_scale, max_len=w.max_len)
+    torch.cuda.synchronize()
+    check_all_tokens(w, w.kv_indices, w.kv_indptr, out, "ragged")
     # the split plans take the XCD-strided partition order (256 tokens, one head group)
-    for plan in [dict(max_len=w.max_len), dict(plain=True), dict(mode=2), dict(mode=1, max_len=w.max_len),
-                 dict(max_len=w.max_len, split_rows=768), dict(max_len=w.max_len, split_rows=384)]:
+    for plan in [dict(plain=True), dict(mode=2), dict(mode=1, max_len=w.max_len),
+                 dict(max_len=w.max_len, split_rows=768), dict(max_len=w.max_len, split_rows=384),
+                 dict(mode=4, max_len=w.max_len, split_rows=512)]:
         out = spd.sparse_decode_attn(q, kv, idx, ptr, sink, w.softmax_scale, **plan)
         torch.cuda.synchronize()
         assert_close(bf16_to_f64(out[torch.from_numpy(tokens).cuda()]), ref, "ragged %s" % plan)
@@ -83,24 +106,36 @@ def test_large_config(spd, device_data):
     w = W.large()
     log("case large: N=1024, H=128, 4 GiB pool, K_PER_BLOCK=64")
     ptr, idx, optr, oidx = build_on_gpu(spd, w.builder)
-    tokens = sample_tokens(optr, 20, 3)
-    ref = oracle_tokens(w, oidx, optr, tokens)
     q, kv, sink = device_inputs(w)
     out = spd.sparse_decode_attn(q, kv, idx, ptr, sink, w.softmax_scale, max_len=w.max_len)
     torch.cuda.synchronize()
-    assert_close(bf16_to_f64(out[torch.from_numpy(tokens).cuda()]), ref, "large")
+    check_all_tokens(w, oidx, optr, out, "large", chunk=256)
 
 
 def test_prefill_config(spd, device_data):
     w = W.prefill()
     log("case prefill: N=8192, L up to 640, sliding reuse")
-    tokens = sample_tokens(w.kv_indptr, 30, 4)
-    ref = oracle_tokens(w, w.kv_indices, w.kv_indptr, tokens)
     q, kv, sink = device_inputs(w)
     idx, ptr = device_csr(w.kv_indices, w.kv_indptr)
     out = spd.sparse_decode_attn(q, kv, idx, ptr, sink, w.softmax_scale, max_len=w.max_len)
     torch.cuda.synchronize()
-    assert_close(bf16_to_f64(out[torch.from_numpy(tokens).cuda()]), ref, "prefill")
+    check_all_tokens(w, w.kv_indices, w.kv_indptr, out, "prefill", chunk=1024)
+
+
+def test_long_slices_small_batch_split(spd):
+    """A few long slices (the case the automatic plan splits): every token
+    against the oracle, on the automatic (split) plan and on rows mode."""
+    lengths = [2048, 4000, 0, 3333, 1, 4096, 2500, 129]
+    w = W.random_csr("long_small", 41, len(lengths), 64, 512, 40000, lengths)
+    log("case long slices, small batch")
+    plan = spd.sparse_decode_attn_plan_info(w.N, w.H, w.D, 4096)
+    assert plan["mode"] == "split" and plan["splits"] > 1
+    q, kv, sink = device_inputs(w)
+    idx, ptr = device_csr(w.kv_indices, w.kv_indptr)
+    for p in [dict(max_len=4096), dict(mode=2)]:
+        out = spd.sparse_decode_attn(q, kv, idx, ptr, sink, w.softmax_scale, **p)
+        torch.cuda.synchronize()
+        check_all_tokens(w, w.kv_indices, w.kv_indptr, out, "long small %s" % p)
 
 
 @pytest.mark.parametrize("mode", [1, 2])

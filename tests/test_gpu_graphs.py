@@ -1,5 +1,6 @@
 """Graph capture of the calls added beside the decode attention (FP8 attention,
-the quantising store, the producer, the shared-window prefill): each is
+the quantising store, the producer, the shared-window prefill, the split
+plan with its in-kernel merge on a reused workspace): each is
 captured once into a HIP graph and replayed several times, with new inputs
 copied into the captured buffers and eager work between replays; every replay
 must equal the eager call on the same inputs bit for bit."""
@@ -138,3 +139,42 @@ def test_prefill(spd, group):
         wl.copy_(torch.from_numpy(np.maximum(L - r.integers(0, 50, size=N), 0).astype(np.int32)))
 
     replay_equals_eager(g, step, [out], refresh)
+
+
+def test_split_plan_reused_workspace(spd):
+    """The split plan in a graph: 5 tokens x 5 partitions of 96 rows (25
+    workgroups, so a token's partitions fall on different XCDs), one
+    workspace for the eager calls and the replays (its arrival counters must
+    come back to zero after every call)."""
+    import math
+    log("case graph split")
+    rng = np.random.default_rng(33)
+    N, H, D, P, max_len = 5, 64, 512, 3000, 400
+    q = bits_tensor(rng, (N, H, D))
+    kv = bits_tensor(rng, (P, D))
+    sink = torch.from_numpy(rng.standard_normal(H).astype(np.float32)).to(dev())
+    lengths = np.array([400, 97, 0, 333, 250], dtype=np.int64)
+    indptr = np.zeros(N + 1, dtype=np.int32)
+    indptr[1:] = np.cumsum(lengths)
+    idx = torch.from_numpy(rng.integers(0, P, size=int(lengths.sum())).astype(np.int32)).to(dev())
+    ptr = torch.from_numpy(indptr).to(dev())
+    plan = spd.sparse_decode_attn_plan_info(N, H, D, max_len, 96, spd.MODE_SPLIT)
+    assert plan["mode"] == "split" and plan["splits"] == 5
+    ws = torch.zeros(spd.sparse_decode_attn_workspace_size(N, H, D, max_len, 96, spd.MODE_SPLIT),
+                     dtype=torch.uint8, device=dev())
+    out = torch.empty((N, H, D), dtype=torch.bfloat16, device=dev())
+
+    def fn():
+        spd.sparse_decode_attn(q, kv, idx, ptr, sink, 1 / math.sqrt(D), out=out, max_len=max_len,
+                               split_rows=96, mode=spd.MODE_SPLIT, workspace=ws)
+
+    g = capture(fn)
+
+    def refresh(rep):
+        idx.copy_(torch.from_numpy(rng.integers(0, P, size=idx.numel()).astype(np.int32)))
+        q.copy_(bits_tensor(rng, (N, H, D)))
+
+    replay_equals_eager(g, fn, [out], refresh, reps=4)
+    torch.cuda.synchronize()
+    nctr = N * 4
+    assert torch.all(ws[-4 * nctr:].view(torch.int32) == 0), "arrival counters left nonzero"

@@ -46,7 +46,7 @@ import numpy as np
 
 _CHUNK = 1 << 24
 
-SEEDS = {"tiny": 0, "decode_base": 1, "ragged": 2, "large": 3, "prefill": 4}
+SEEDS = {"tiny": 0, "decode_base": 1, "ragged": 2, "large": 3, "prefill": 4, "long_context": 5}
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -275,8 +275,21 @@ def prefill(seed: int = SEEDS["prefill"], N: int = 8192, H: int = 64, D: int = 5
     return w
 
 
+def long_context(seed: int = SEEDS["long_context"], N: int = 8, H: int = 64, D: int = 512,
+                 P: int = 1048576, length: int = 8192) -> Workload:
+    """A small batch of long slices (the case that splits a slice across
+    workgroups): N tokens of `length` rows each, rows uniform in [0, P),
+    q, kv ~ N(0, 1), sinks ~ N(0, 1).  Not one of the pages' batches: a
+    measurement case for the split plan, beside the ragged batch's lengths."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lists = [rng.integers(0, P, size=length) for _ in range(N)]
+    idx, indptr = csr_from_lists(lists)
+    return _finish("long_context", rng, N, H, D, P, 1.0, 1.0 / math.sqrt(D), length,
+                   kv_indices=idx, kv_indptr=indptr)
+
+
 CONFIGS = {"tiny": tiny, "decode_base": decode_base, "ragged": ragged, "large": large,
-           "prefill": prefill}
+           "prefill": prefill, "long_context": long_context}
 
 
 def make(name: str, **kw) -> Workload:
