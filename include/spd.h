@@ -182,6 +182,32 @@ SPD_API spd_status sparse_decode_attn_ex(const void* q, const void* unified_kv, 
                                          size_t workspace_bytes, void* stream);
 
 /*
+ * sparse_decode_attn_ex for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments but the workspace, the same plans, kernels
+ * and results, bit for bit.  A plan that needs a workspace (split-L, split
+ * mode) uses a static device array of SPD_NOALLOC_WORKSPACE_BYTES (96 MiB)
+ * that the library holds on each GPU it runs on until the process ends; the
+ * call allocates and frees nothing.  A split-mode call first clears the
+ * plan's arrival counters in that array with a small kernel on `stream`.
+ *
+ * Every call on one GPU shares that GPU's array: two calls that may run at
+ * the same time (other streams, other host threads) race on it and give
+ * wrong results.  stream must belong to the current device
+ * (SPD_ERR_INVALID_ARG otherwise).  SPD_ERR_WORKSPACE when the plan needs
+ * more than SPD_NOALLOC_WORKSPACE_BYTES (sparse_decode_attn_workspace_size
+ * reports the need; the automatic plans need at most about 68 MB); other
+ * errors as sparse_decode_attn_ex.
+ */
+#define SPD_NOALLOC_WORKSPACE_BYTES ((size_t)96 << 20)
+SPD_API spd_status sparse_decode_attn_noalloc(const void* q, const void* unified_kv,
+                                              int64_t num_rows, const int32_t* kv_indices,
+                                              const int32_t* kv_indptr, const float* attn_sink,
+                                              float softmax_scale, void* out, int32_t N, int32_t H,
+                                              int32_t D, int32_t max_len, int32_t split_rows,
+                                              int32_t mode, void* stream);
+
+/*
  * Decode index builder, the page's write_v4_paged_decode_indices ("paged
  * decode index scatter kernel"): packs sliding-window ring slots and
  * compressed paged slots into ragged CSR indices with no sentinels.

@@ -51,7 +51,7 @@ EXPORTED_SYMBOLS = (
     "sparse_decode_attn_workspace_size", "sparse_decode_attn_ex", "build_decode_indices",
     "spd_validate_indices", "sparse_decode_attn_plan_info", "sparse_decode_attn_paged",
     "sparse_decode_attn_fp8", "quantize_kv_fp8", "fused_qk_norm_rope_swa_store",
-    "sparse_prefill_attn",
+    "sparse_prefill_attn", "sparse_decode_attn_noalloc",
 )
 
 
@@ -80,6 +80,9 @@ def _load() -> ctypes.CDLL:
     lib.sparse_decode_attn_ex.argtypes = [P, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32, i32,
                                           i32, i32, P, sz, P]
     lib.sparse_decode_attn_ex.restype = ctypes.c_int
+    lib.sparse_decode_attn_noalloc.argtypes = [P, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32,
+                                               i32, i32, i32, P]
+    lib.sparse_decode_attn_noalloc.restype = ctypes.c_int
     lib.sparse_decode_attn_paged.argtypes = [P, P, i64, P, P, P, i32, P, i32, i32, i32, i32, P,
                                              ctypes.c_float, P, i32, i32, i32, i32, P]
     lib.sparse_decode_attn_paged.restype = ctypes.c_int
@@ -204,6 +207,38 @@ def sparse_decode_attn(q: torch.Tensor, unified_kv: torch.Tensor, kv_indices: to
                                    _ptr(out), N, H, D, int(max_len), int(split_rows), int(mode),
                                    _ptr(workspace), ws_bytes, stream)
     _raise_on(st, "sparse_decode_attn_ex")
+    return out
+
+
+# Workspace the library holds per GPU for sparse_decode_attn_noalloc.
+NOALLOC_WORKSPACE_BYTES = 96 << 20
+
+
+def sparse_decode_attn_noalloc(q: torch.Tensor, unified_kv: torch.Tensor,
+                               kv_indices: torch.Tensor, kv_indptr: torch.Tensor,
+                               attn_sink: torch.Tensor, softmax_scale: float, out: torch.Tensor,
+                               *, max_len: int = 0, split_rows: int = 0,
+                               mode: int = MODE_AUTO) -> torch.Tensor:
+    """``sparse_decode_attn_noalloc``: sparse_decode_attn_ex with the library's
+    per-GPU workspace, so the call allocates nothing (``out`` is required).
+    Calls that may overlap on one GPU race on that workspace."""
+    _check(q, "q", torch.bfloat16, 3)
+    _check(unified_kv, "unified_kv", torch.bfloat16, 2)
+    _check(kv_indices, "kv_indices", torch.int32, 1)
+    _check(kv_indptr, "kv_indptr", torch.int32, 1)
+    _check(attn_sink, "attn_sink", torch.float32, 1)
+    _check(out, "out", torch.bfloat16, 3)
+    N, H, D = q.shape
+    if unified_kv.shape[1] != D or kv_indptr.shape[0] != N + 1 or attn_sink.shape[0] != H:
+        raise ValueError("shape mismatch between q, unified_kv, kv_indptr and attn_sink")
+    if tuple(out.shape) != (N, H, D):
+        raise ValueError("out must be [N, H, D]")
+    idx = kv_indices if kv_indices.numel() > 0 else kv_indptr  # any valid pointer; never read
+    st = lib.sparse_decode_attn_noalloc(_ptr(q), _ptr(unified_kv), unified_kv.shape[0], _ptr(idx),
+                                        _ptr(kv_indptr), _ptr(attn_sink), float(softmax_scale),
+                                        _ptr(out), N, H, D, int(max_len), int(split_rows),
+                                        int(mode), _stream(q.device))
+    _raise_on(st, "sparse_decode_attn_noalloc")
     return out
 
 

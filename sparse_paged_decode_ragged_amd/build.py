@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libspd.so")
-SOURCES = ["api.hip", "attn.hip", "attn_split.hip", "attn_fp8.hip", "indices.hip", "producer.hip"]
+SOURCES = ["api.hip", "attn.hip", "attn_split.hip", "attn_fp8.hip", "indices.hip", "producer.hip",
+           "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -6,6 +6,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "api_internal.h"
 #include "spd.h"
 #include "spd_internal.h"
 #include "store_internal.h"
@@ -22,6 +23,58 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 constexpr double kLog2eD = 1.4426950408889634073599;
 
 }  // namespace
+
+namespace spd {
+
+spd_status prepare_attn_ex(const void* q, const void* unified_kv, int64_t num_rows,
+                           const int32_t* kv_indices, const int32_t* kv_indptr,
+                           const float* attn_sink, float softmax_scale, void* out, int32_t N,
+                           int32_t H, int32_t D, int32_t max_len, int32_t split_rows, int32_t mode,
+                           AttnArgs* a, AttnPlan* plan, bool* empty) {
+  *empty = false;
+  if (N < 0 || H <= 0 || D <= 0 || num_rows <= 0 || max_len < 0 || split_rows < 0)
+    return SPD_ERR_INVALID_ARG;
+  if (mode != SPD_MODE_AUTO && mode != SPD_MODE_HEADS && mode != SPD_MODE_ROWS &&
+      mode != SPD_MODE_WIDE && mode != SPD_MODE_SPLIT)
+    return SPD_ERR_INVALID_ARG;
+  if (mode == SPD_MODE_ROWS && split_rows != 0) return SPD_ERR_UNSUPPORTED;
+  if (!isfinite(softmax_scale)) return SPD_ERR_INVALID_ARG;
+  if (!attn_supported(H, D)) return SPD_ERR_UNSUPPORTED;
+  if (mode == SPD_MODE_WIDE && (split_rows != 0 || H % 64 != 0)) return SPD_ERR_UNSUPPORTED;
+  if (N == 0) {
+    *empty = true;
+    return SPD_OK;
+  }
+  if (!q || !unified_kv || !kv_indices || !kv_indptr || !attn_sink || !out)
+    return SPD_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(unified_kv, 16) || !aligned(out, 16) || !aligned(kv_indices, 4) ||
+      !aligned(kv_indptr, 4) || !aligned(attn_sink, 4))
+    return SPD_ERR_INVALID_ARG;
+  if (num_rows > (int64_t)1 << 40) return SPD_ERR_INVALID_ARG;
+  const size_t qo_bytes = (size_t)N * H * D * 2;
+  if (overlap(out, qo_bytes, q, qo_bytes) ||
+      overlap(out, qo_bytes, unified_kv, (size_t)num_rows * D * 2) ||
+      overlap(out, qo_bytes, attn_sink, (size_t)H * 4) ||
+      overlap(out, qo_bytes, kv_indptr, (size_t)(N + 1) * 4))
+    return SPD_ERR_INVALID_ARG;
+  if (!make_attn_plan(N, H, D, max_len, split_rows, mode, plan)) return SPD_ERR_INVALID_ARG;
+  a->q = static_cast<const uint16_t*>(q);
+  a->kv = static_cast<const uint16_t*>(unified_kv);
+  a->kv_indices = kv_indices;
+  a->kv_indptr = kv_indptr;
+  a->sink = attn_sink;
+  a->out = static_cast<uint16_t*>(out);
+  a->ws = nullptr;
+  a->qk_scale = (float)((double)softmax_scale * kLog2eD);
+  a->N = N;
+  a->H = H;
+  a->head_groups = plan->head_groups;
+  a->splits = plan->splits;
+  a->split_rows = plan->split_rows;
+  return SPD_OK;
+}
+
+}  // namespace spd
 
 extern "C" {
 
@@ -76,50 +129,18 @@ SPD_API spd_status sparse_decode_attn_ex(const void* q, const void* unified_kv, 
                                          int32_t N, int32_t H, int32_t D, int32_t max_len,
                                          int32_t split_rows, int32_t mode, void* workspace,
                                          size_t workspace_bytes, void* stream) {
-  if (N < 0 || H <= 0 || D <= 0 || num_rows <= 0 || max_len < 0 || split_rows < 0)
-    return SPD_ERR_INVALID_ARG;
-  if (mode != SPD_MODE_AUTO && mode != SPD_MODE_HEADS && mode != SPD_MODE_ROWS &&
-      mode != SPD_MODE_WIDE && mode != SPD_MODE_SPLIT)
-    return SPD_ERR_INVALID_ARG;
-  if (mode == SPD_MODE_ROWS && split_rows != 0) return SPD_ERR_UNSUPPORTED;
-  if (!isfinite(softmax_scale)) return SPD_ERR_INVALID_ARG;
-  if (!spd::attn_supported(H, D)) return SPD_ERR_UNSUPPORTED;
-  if (mode == SPD_MODE_WIDE && (split_rows != 0 || H % 64 != 0)) return SPD_ERR_UNSUPPORTED;
-  if (N == 0) return SPD_OK;
-  if (!q || !unified_kv || !kv_indices || !kv_indptr || !attn_sink || !out)
-    return SPD_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(unified_kv, 16) || !aligned(out, 16) || !aligned(kv_indices, 4) ||
-      !aligned(kv_indptr, 4) || !aligned(attn_sink, 4))
-    return SPD_ERR_INVALID_ARG;
-  if (num_rows > (int64_t)1 << 40) return SPD_ERR_INVALID_ARG;
-  const size_t qo_bytes = (size_t)N * H * D * 2;
-  if (overlap(out, qo_bytes, q, qo_bytes) ||
-      overlap(out, qo_bytes, unified_kv, (size_t)num_rows * D * 2) ||
-      overlap(out, qo_bytes, attn_sink, (size_t)H * 4) ||
-      overlap(out, qo_bytes, kv_indptr, (size_t)(N + 1) * 4))
-    return SPD_ERR_INVALID_ARG;
-
-  spd::AttnPlan plan;
-  if (!spd::make_attn_plan(N, H, D, max_len, split_rows, mode, &plan)) return SPD_ERR_INVALID_ARG;
+  spd::AttnArgs a{};
+  spd::AttnPlan plan{};
+  bool empty = false;
+  const spd_status st =
+      spd::prepare_attn_ex(q, unified_kv, num_rows, kv_indices, kv_indptr, attn_sink, softmax_scale,
+                           out, N, H, D, max_len, split_rows, mode, &a, &plan, &empty);
+  if (st != SPD_OK || empty) return st;
   if (plan.workspace_bytes > 0) {
     if (!workspace || workspace_bytes < plan.workspace_bytes) return SPD_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return SPD_ERR_INVALID_ARG;
   }
-
-  spd::AttnArgs a{};
-  a.q = static_cast<const uint16_t*>(q);
-  a.kv = static_cast<const uint16_t*>(unified_kv);
-  a.kv_indices = kv_indices;
-  a.kv_indptr = kv_indptr;
-  a.sink = attn_sink;
-  a.out = static_cast<uint16_t*>(out);
   a.ws = static_cast<float*>(workspace);
-  a.qk_scale = (float)((double)softmax_scale * kLog2eD);
-  a.N = N;
-  a.H = H;
-  a.head_groups = plan.head_groups;
-  a.splits = plan.splits;
-  a.split_rows = plan.split_rows;
   const hipError_t e = spd::launch_attention(a, D, plan, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPD_OK : SPD_ERR_HIP;
 }

@@ -709,10 +709,13 @@ hipError_t launch_split_shape(const AttnArgs& a, const AttnPlan& p, hipStream_t 
 
 }  // namespace
 
-size_t split_workspace_bytes(int32_t N, int32_t D, const AttnPlan& p) {
+size_t split_counters_offset(int32_t N, int32_t D, const AttnPlan& p) {
   const size_t slot = (size_t)(D / 32 / p.parities) * 4 * 64 * 16 + 2 * 32 * 4;
-  const size_t states = (size_t)N * p.head_groups * p.splits * 4 * slot;
-  return states + (size_t)N * p.head_groups * 4 * sizeof(int);
+  return (size_t)N * p.head_groups * p.splits * 4 * slot;
+}
+
+size_t split_workspace_bytes(int32_t N, int32_t D, const AttnPlan& p) {
+  return split_counters_offset(N, D, p) + (size_t)N * p.head_groups * 4 * sizeof(int);
 }
 
 hipError_t launch_split(const AttnArgs& a, int D, const AttnPlan& p, hipStream_t stream) {

@@ -84,6 +84,9 @@ hipError_t launch_attention(const AttnArgs& args, int D, const AttnPlan& plan, h
 // one arrival counter per (token, head group, wave); the counters must be
 // zero before the first call and every call leaves them zero.
 size_t split_workspace_bytes(int32_t N, int32_t D, const AttnPlan& plan);
+// Offset of the arrival counters in that workspace (N * head_groups * 4 int32
+// from there to its end).
+size_t split_counters_offset(int32_t N, int32_t D, const AttnPlan& plan);
 hipError_t launch_split(const AttnArgs& args, int D, const AttnPlan& plan, hipStream_t stream);
 
 // Attention over an FP8 pool: rows mode (workgroup = token x 16 heads), no

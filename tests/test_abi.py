@@ -24,6 +24,8 @@ def lib():
     L.sparse_decode_attn.argtypes = [P, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32, P]
     L.sparse_decode_attn_ex.argtypes = [P, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32, i32,
                                         i32, i32, P, sz, P]
+    L.sparse_decode_attn_noalloc.argtypes = [P, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32,
+                                             i32, i32, i32, P]
     L.sparse_decode_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     L.sparse_decode_attn_workspace_size.restype = sz
     L.sparse_decode_attn_can_use.argtypes = [i32, i32]
@@ -323,3 +325,31 @@ def test_prefill_rejects_bad_arguments(lib):
     assert _pre(lib, stream=FAKE * 128 + 2) == INVALID
     assert _pre(lib, out=FAKE) == INVALID         # over q
     assert _pre(lib, out=FAKE * 128 - 1024) == INVALID   # over the stream
+
+
+def test_noalloc_rejects_plans_beyond_its_workspace(lib):
+    """The allocation-free call checks every argument, then the plan's
+    workspace against the 96 MiB it holds per GPU, before any HIP call."""
+    AUTO, HEADS, SPLIT = 0, 1, 4
+    limit = 96 << 20
+    args = lambda N, max_len, split_rows, mode, scale=0.1, q=FAKE: (
+        q, FAKE, 1 << 20, FAKE, FAKE, FAKE, scale, 1 << 40, N, 64, 512, max_len, split_rows,
+        mode, None)
+    # 4096 tokens of 64 heads in 8 partitions of 256 rows: 4096 * 8 * 64 * 514 * 4 bytes
+    need = lib.sparse_decode_attn_workspace_size(4096, 64, 512, 2048, 256, HEADS)
+    assert need > limit
+    assert lib.sparse_decode_attn_noalloc(*args(4096, 2048, 256, HEADS)) == WORKSPACE
+    # split mode past the limit too
+    assert lib.sparse_decode_attn_workspace_size(1024, 64, 512, 4096, 256, SPLIT) > limit
+    assert lib.sparse_decode_attn_noalloc(*args(1024, 4096, 256, SPLIT)) == WORKSPACE
+    # argument errors come first, as in sparse_decode_attn_ex
+    assert lib.sparse_decode_attn_noalloc(*args(4096, 2048, 256, HEADS, scale=float("nan"))) == INVALID
+    assert lib.sparse_decode_attn_noalloc(*args(4096, 2048, 256, 7)) == INVALID
+    assert lib.sparse_decode_attn_noalloc(*args(4096, 2048, 256, HEADS, q=None)) == INVALID
+    # nothing to do
+    assert lib.sparse_decode_attn_noalloc(*args(0, 2048, 256, HEADS)) == OK
+    # the automatic plans fit: every batch of up to 255 heads-mode workgroups
+    worst = max(lib.sparse_decode_attn_workspace_size(N, H, 512, L, 0, m)
+                for N in (1, 2, 3, 5, 63, 64, 127, 255) for H in (64, 128, 256)
+                for L in (2048, 8192, 65536) for m in (AUTO, HEADS, SPLIT))
+    assert 0 < worst <= limit

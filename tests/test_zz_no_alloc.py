@@ -1,0 +1,79 @@
+"""sparse_decode_attn_noalloc (the library's per-GPU workspace, no allocation)
+against sparse_decode_attn_ex (a caller workspace) through the C ABI: the
+same plan on the same inputs gives the same bits, on calls in a row whose
+plans differ and shrink (so each call finds the array as the previous call
+left it), with every token also checked against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_helpers import assert_close, bf16_to_f64, device_csr, device_inputs, log, oracle_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def spd():
+    import sparse_paged_decode_ragged_amd as m
+    return m
+
+
+def run_pair(spd, w, **plan):
+    """One call of each entry point with the same plan; returns both outputs."""
+    q, kv, sink = device_inputs(w)
+    idx, ptr = device_csr(w.kv_indices, w.kv_indptr)
+    info = spd.sparse_decode_attn_plan_info(w.N, w.H, w.D, plan.get("max_len", 0),
+                                            plan.get("split_rows", 0), plan.get("mode", 0))
+    log("  noalloc %s: N=%d plan %s" % (w.name, w.N, info))
+    need = spd.sparse_decode_attn_workspace_size(w.N, w.H, w.D, plan.get("max_len", 0),
+                                                 plan.get("split_rows", 0), plan.get("mode", 0))
+    assert need <= spd.NOALLOC_WORKSPACE_BYTES
+    out_na = torch.full((w.N, w.H, w.D), float("nan"), dtype=torch.bfloat16, device=q.device)
+    spd.sparse_decode_attn_noalloc(q, kv, idx, ptr, sink, w.softmax_scale, out_na, **plan)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
+    out_ex = spd.sparse_decode_attn(q, kv, idx, ptr, sink, w.softmax_scale, workspace=ws, **plan)
+    torch.cuda.synchronize()
+    return info, out_na, out_ex
+
+
+def check(w, info, out_na, out_ex, what):
+    assert torch.equal(out_na.view(torch.int16), out_ex.view(torch.int16)), \
+        "%s: noalloc and ex differ (plan %s)" % (what, info)
+    ref = oracle_tokens(w, w.kv_indices, w.kv_indptr)
+    assert_close(bf16_to_f64(out_na), ref, what)
+
+
+def test_noalloc_matches_ex_on_calls_in_a_row(spd):
+    MODE_HEADS, MODE_SPLIT = spd.MODE_HEADS, spd.MODE_SPLIT
+    cases = [
+        # heads-mode split-L first: its partials fill the array where the
+        # split plans below keep their arrival counters
+        # (64 tokens x 8 partitions x 64 heads x 514 floats: 67 MB, past the
+        # 34 MB at which the next plan's counters start)
+        ("heads_big", dict(N=64, lengths=None, max_len=2048),
+         dict(max_len=2048, split_rows=256, mode=MODE_HEADS), "heads"),
+        # the automatic plan of a small batch of long slices: split mode, 32 partitions
+        ("split_big", dict(N=8, lengths=[4096, 0, 3000, 1, 4095, 2222, 4096, 777], max_len=4096),
+         dict(max_len=4096), "split"),
+        # the same entry point again, smaller: 3 tokens, 6 partitions of 256 rows
+        ("split_small", dict(N=3, lengths=[1500, 64, 0], max_len=1500),
+         dict(max_len=1500, split_rows=256, mode=MODE_SPLIT), "split"),
+        # and heads-mode split-L, smaller
+        ("heads_small", dict(N=5, lengths=None, max_len=600),
+         dict(max_len=600, split_rows=128, mode=MODE_HEADS), "heads"),
+        # a plan with no workspace at all
+        ("rows", dict(N=4, lengths=[640, 0, 17, 300], max_len=640), dict(max_len=640), "rows"),
+    ]
+    for i, (name, shape, plan, mode_name) in enumerate(cases):
+        rng = np.random.default_rng(100 + i)
+        lengths = shape["lengths"]
+        if lengths is None:
+            lengths = rng.integers(0, shape["max_len"] + 1, size=shape["N"]).tolist()
+            lengths[0] = shape["max_len"]
+        w = W.random_csr(name, 200 + i, shape["N"], 64, 512, 50000, lengths)
+        info, out_na, out_ex = run_pair(spd, w, **plan)
+        assert info["mode"] == mode_name, info
+        if mode_name != "rows":
+            assert info["splits"] > 1, info
+        check(w, info, out_na, out_ex, name)
