@@ -61,6 +61,9 @@ def parse():
     p.add_argument("--no-producer", action="store_true", help="skip the producer measurement")
     p.add_argument("--no-prefill", action="store_true", help="skip the shared-window measurement")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-floor", action="store_true",
+                   help="skip the floor legs (gather without arithmetic, empty launch, output "
+                        "store, device copy)")
     p.add_argument("--calibration-copy-mib", type=int, default=0,
                    help="also run a kernel of known traffic three times (bitwise_not over this "
                         "many MiB of int32: reads and writes exactly that much), which scales "
@@ -212,20 +215,73 @@ def cpu_baseline(w, indptr, indices, seconds):
         oracle.sparse_decode_attn(qb, rows, inv.astype(np.int32), sub, w.attn_sink, w.softmax_scale)
         return time.perf_counter() - t0
 
-    # size the sample from a short probe, then time whole passes over it
-    probe = order[: min(N, 8)]
-    dt = max(run(probe), 1e-4)
-    n = int(min(N, max(len(probe), len(probe) * 0.5 * seconds / dt)))
-    sample = order[:n]
-    reps, el = 0, 0.0
-    while el < seconds:
-        el += run(sample)
-        reps += 1
-    toks = reps * n
-    return {"value": round(toks / el, 2), "unit": "tokens/s", "cores": oracle.get_threads(),
-            "kind": "oracle",
-            "sample": "%d of %d tokens (%d pool rows gathered each pass, fp64 two-pass attention "
-                      "only), %d passes, %.1f s" % (n, N, int(L[sample].sum()), reps, el)}
+    def median_rate(threads, budget):
+        """Median tokens/s of three timed passes on `threads` threads, each
+        pass about budget / 3 seconds: a sample of tokens (the whole batch
+        when it is quick), repeated k times."""
+        oracle.set_threads(threads)
+        probe = order[: min(N, 8)]
+        dt = max(run(probe), 1e-4)
+        per = (budget / 3) / dt * len(probe)  # tokens one pass can take
+        n = int(min(N, max(len(probe), per)))
+        sample = order[:n]
+        k = max(1, int(round(per / n)))
+        rates, el = [], 0.0
+        for _ in range(3):
+            d = sum(run(sample) for _ in range(k))
+            el += d
+            rates.append(k * n / d)
+        return float(np.median(rates)), rates, n, k, int(L[sample].sum()), el
+
+    def describe(n, k, rows, el, threads):
+        return ("3 passes, each %d x %d of %d tokens (%d pool rows gathered), %.1f s on %d "
+                "thread%s" % (k, n, N, rows, el, threads, "" if threads == 1 else "s"))
+
+    all_cores = os.cpu_count() or 1
+    v, rates, n, k, rows, el = median_rate(all_cores, seconds)
+    used = oracle.get_threads()
+    v1, rates1, n1, k1, rows1, el1 = median_rate(1, seconds)
+    oracle.set_threads(all_cores)
+    return {"value": round(v, 2), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "passes_tokens_per_s": [round(r, 2) for r in rates],
+            "value_1core": round(v1, 2), "passes_1core_tokens_per_s": [round(r, 2) for r in rates1],
+            "sample": "fp64 two-pass attention only, median of " + describe(n, k, rows, el, used) +
+                      "; one core: " + describe(n1, k1, rows1, el1, 1)}
+
+
+def load_probe():
+    """libspd_probe.so (include/spd_probe.h): the measurement kernels."""
+    import ctypes
+    path = os.path.join(ROOT, "sparse_paged_decode_ragged_amd", "_lib", "libspd_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError("libspd_probe.so not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(path)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.spd_probe_gather.argtypes = [P, P, P, i32, i32, i32, i32, P, P]
+    L.spd_probe_null.argtypes = [i32, P]
+    L.spd_probe_store.argtypes = [P, i64, i32, P]
+    return L
+
+
+def probe_call(st: int, what: str) -> None:
+    if st != 0:
+        raise RuntimeError("%s failed with status %d" % (what, st))
+
+
+def one_cu_parts(N: int) -> int:
+    """Partitions per token that give each CU (256 of them) one share of a
+    token's rows: every gathered row then enters exactly one CU."""
+    return max(1, min(32, round(256 / max(N, 1))))
+
+
+def touched_bytes(indices: np.ndarray, N: int, H: int, D: int) -> dict:
+    """Bytes one set's attention call touches: its distinct pool rows, q, out,
+    the indices and kv_indptr (the footprint that must exceed the Infinity
+    Cache across the rotating sets)."""
+    uniq = int(len(np.unique(indices))) if len(indices) else 0
+    tb = uniq * 2 * D + 2 * N * H * D * 2 + 4 * len(indices) + 4 * (N + 1)
+    return {"unique_rows": uniq, "gathered_rows": int(len(indices)),
+            "unique_row_fraction": round(uniq / max(len(indices), 1), 4), "bytes": int(tb)}
 
 
 def main():
@@ -257,12 +313,11 @@ def main():
     b = w.builder
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
 
-    pool_bytes = w.P * D * 2
-    n_sets = args.sets or max(2, min(16, math.ceil(2 * MALL_BYTES / pool_bytes)))
     q0 = W.device_bits(w.q_bits, dev)
     kv0 = W.device_bits(w.kv_bits, dev)
     sets = []
-    for r in range(n_sets):
+
+    def new_set(r):
         s = dict(q=q0 if r == 0 else q0.clone(), kv=kv0 if r == 0 else kv0.clone(),
                  sink=torch.from_numpy(w.attn_sink).to(dev),
                  out=torch.empty((N, H, D), dtype=torch.bfloat16, device=dev),
@@ -273,7 +328,28 @@ def main():
                      idx=torch.zeros(b.capacity, dtype=torch.int32, device=dev))
         else:
             s.update(ptr=t(w.kv_indptr), idx=t(w.kv_indices))
+        s["gw"] = torch.zeros(N * max(plan["head_groups"] * plan["splits"], one_cu_parts(N)) + 1,
+                              dtype=torch.int32, device=dev)  # the gather probe's words
         sets.append(s)
+
+    # The rotating sets: enough that the bytes the attention calls touch
+    # (distinct rows, q, out, indices) exceed three times the 256 MB Infinity
+    # Cache, so each call finds its rows in HBM.  Set 0's lists (built on the
+    # GPU for builder-shaped workloads) size the rotation.
+    new_set(0)
+    if b is not None:
+        spd.build_decode_indices(sets[0]["ss"], sets[0]["sl"], sets[0]["cp"], sets[0]["bt"], b.win,
+                                 b.k_per_block, b.swa_pages, kv_indptr=sets[0]["ptr"],
+                                 kv_indices=sets[0]["idx"])
+        torch.cuda.synchronize()
+        ptr0 = sets[0]["ptr"].cpu().numpy()
+        idx0 = sets[0]["idx"].cpu().numpy()[: ptr0[-1]]
+    else:
+        idx0 = w.kv_indices
+    touched = touched_bytes(idx0, N, H, D)
+    n_sets = args.sets or max(2, min(32, math.ceil(3 * MALL_BYTES / touched["bytes"])))
+    for r in range(1, n_sets):
+        new_set(r)
 
     def build(s):
         spd.build_decode_indices(s["ss"], s["sl"], s["cp"], s["bt"], b.win, b.k_per_block,
@@ -362,6 +438,41 @@ def main():
         spd.sparse_decode_attn_fp8(s["q"], s["kv8"], s["ksc"], s["idx"], s["ptr"], s["sink"],
                                    w.softmax_scale, out=s["out"])
 
+    # Floor legs (libspd_probe.so): the same rows gathered by the same LDS-DMA
+    # pattern with no arithmetic, in the plan's decomposition (head groups x
+    # partitions: each group re-reads a token's rows) and in one where every
+    # row enters one CU; an empty 256-workgroup launch; the output written by
+    # 256 workgroups.  Each runs on the same rotating sets as the calls.
+    has_floor = not args.no_floor
+    if has_floor:
+        probe = load_probe()
+    g_plan, p_plan, p_one = plan["head_groups"], plan["splits"], one_cu_parts(N)
+    out_bytes = N * H * D * 2
+
+    def cur_stream():
+        import ctypes
+        return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def gather_plan(s):
+        probe_call(probe.spd_probe_gather(s["kv"].data_ptr(), s["idx"].data_ptr(), s["ptr"].data_ptr(),
+                                          N, D, g_plan, p_plan, s["gw"].data_ptr(), cur_stream()),
+                   "spd_probe_gather")
+
+    def gather_one(s):
+        probe_call(probe.spd_probe_gather(s["kv"].data_ptr(), s["idx"].data_ptr(), s["ptr"].data_ptr(),
+                                          N, D, 1, p_one, s["gw"].data_ptr(), cur_stream()),
+                   "spd_probe_gather")
+
+    def null_leg(s):
+        probe_call(probe.spd_probe_null(256, cur_stream()), "spd_probe_null")
+
+    def store_leg(s):
+        probe_call(probe.spd_probe_store(s["out"].data_ptr(), out_bytes, 256, cur_stream()),
+                   "spd_probe_store")
+
+    floor_kinds = ((("gather_plan", gather_plan), ("gather_one", gather_one), ("null", null_leg),
+                    ("store", store_leg)) if has_floor else ())
+
     for s in sets:  # eager warm-up (and the indices the graphs will rebuild)
         step(s)
     for s in fp8_sets:
@@ -371,13 +482,14 @@ def main():
     # holds every set's call back to back: the timed loops replay the latter,
     # so consecutive calls are not separated by per-graph launch gaps.
     single = {"step": [], "attn": [], "paged": [], "producer": [], "prefill": [],
-              "prefill_shared": []}
+              "prefill_shared": [], "gather_plan": [], "gather_one": [], "null": [], "store": []}
     chain = {}
     cs = torch.cuda.Stream()
     if not args.eager:
         kinds = ((("step", step), ("attn", attn)) + ((("paged", paged),) if has_paged else ()) +
                  ((("producer", producer),) if has_producer else ()) +
-                 ((("prefill", prefill), ("prefill_shared", prefill_shared)) if has_prefill else ()))
+                 ((("prefill", prefill), ("prefill_shared", prefill_shared)) if has_prefill else ()) +
+                 floor_kinds)
         for name, fn in kinds:
             for s in sets:
                 g = torch.cuda.CUDAGraph()
@@ -466,6 +578,28 @@ def main():
         run_calls(min(args.warmup, 64), "fp8", attn_fp8)
         us_fp8 = timed(n_attn, "fp8", attn_fp8) * 1e3 / n_attn
 
+    floor = {}
+    if has_floor:
+        for name, fn in floor_kinds:
+            run_calls(min(args.warmup, 64), name, fn)
+            floor[name] = timed(n_attn, name, fn) * 1e3 / n_attn
+        # a plain device copy of 512 MiB (reads and writes that much)
+        n_copy = 512 << 20
+        src = torch.ones(n_copy // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(20):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        floor["copy"] = e0.elapsed_time(e1) * 1e3 / 20
+        del src, dst
+
     indptr = sets[0]["ptr"].cpu().numpy()
     indices = sets[0]["idx"].cpu().numpy()[: indptr[-1]]
     ab = algorithmic_bytes(indptr, N, H, D)
@@ -499,6 +633,10 @@ def main():
         "config": {"workload": args.workload, "N": N, "H": H, "D": D, "pool_rows": w.P,
                    "max_len": max_len, "sum_L": ab["sum_L"], "nonempty_tokens": ab["nonempty"],
                    "plan": plan, "rotating_sets": n_sets,
+                   "touched_bytes_per_set": touched["bytes"],
+                   "touched_bytes_all_sets": touched["bytes"] * n_sets,
+                   "unique_rows": touched["unique_rows"],
+                   "unique_row_fraction": touched["unique_row_fraction"],
                    "launch": "eager" if args.eager else "hip_graph_of_%d_steps" % n_sets,
                    "step": ("build_decode_indices + " if b is not None else "") + "sparse_decode_attn"},
         "gathered_kv_GBps": round(gathered_gbps, 1),
@@ -515,6 +653,23 @@ def main():
                               "frac": round(mfma_flops(ab["sum_L"], H, D) / us_attn / 1e6 /
                                             MFMA_BF16_PEAK_TFLOPS, 4)}},
     }
+    if floor:
+        kvb = ab["kv_bytes"]
+
+        def gleg(us, groups, parts):
+            return {"groups": groups, "parts": parts, "us_per_call": round(us, 3),
+                    "kv_bytes": kvb, "bytes_into_cus": groups * kvb,
+                    "GBps": round(kvb / (us * 1e-6) / 1e9, 1),
+                    "frac": round(kvb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+        cgb = 2 * (512 << 20) / (floor["copy"] * 1e-6) / 1e9
+        rec["floor"] = {
+            "kernels": "libspd_probe.so (include/spd_probe.h), same rotating sets and graphs",
+            "launch_us": round(floor["null"], 3),
+            "output_store_us": round(floor["store"], 3), "output_bytes": out_bytes,
+            "gather_plan": gleg(floor["gather_plan"], g_plan, p_plan),
+            "gather_one_cu": gleg(floor["gather_one"], 1, p_one),
+            "copy": {"bytes_read_plus_written": 2 * (512 << 20), "us": round(floor["copy"], 2),
+                     "GBps": round(cgb, 1), "frac": round(cgb / HBM_PEAK_GBPS, 4)}}
     if us_paged is not None:
         pp = spd.sparse_decode_attn_plan_info(N, H, D, 0, 0, paged_mode)  # the paged call never splits
         kernel_paged = ("attn_rows_kernel<%d, paged>" % D if pp["mode"] == "rows" else

@@ -1,8 +1,9 @@
-"""Build libspd.so (HIP, gfx950) in-tree with hipcc.
+"""Build libspd.so (HIP, gfx950) in-tree with hipcc, and beside it
+libspd_probe.so (the benchmark's measurement kernels, include/spd_probe.h).
 
 Every call compiles from source (the build check must really build); the
 objects are compiled in parallel and linked into
-``sparse_paged_decode_ragged_amd/_lib/libspd.so``.
+``sparse_paged_decode_ragged_amd/_lib/``.
 """
 from __future__ import annotations
 
@@ -16,6 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libspd.so")
+PROBE_LIB = os.path.join(OUT_DIR, "libspd_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 SOURCES = ["api.hip", "attn.hip", "attn_split.hip", "attn_fp8.hip", "indices.hip", "producer.hip",
            "noalloc.hip"]
 
@@ -44,19 +47,25 @@ def _compile(src: str, obj_dir: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    obj_dir = os.path.join(OUT_DIR, "obj")
-    os.makedirs(obj_dir, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, obj_dir), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    obj_dir = os.path.join(OUT_DIR, "obj")
+    os.makedirs(obj_dir, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, obj_dir), srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

@@ -353,3 +353,34 @@ def test_noalloc_rejects_plans_beyond_its_workspace(lib):
                 for N in (1, 2, 3, 5, 63, 64, 127, 255) for H in (64, 128, 256)
                 for L in (2048, 8192, 65536) for m in (AUTO, HEADS, SPLIT))
     assert 0 < worst <= limit
+
+
+PROBE_LIB = os.path.join(ROOT, "sparse_paged_decode_ragged_amd", "_lib", "libspd_probe.so")
+PROBE_HEADER = os.path.join(ROOT, "include", "spd_probe.h")
+
+
+def test_probe_library_exports_and_host_checks():
+    """libspd_probe.so exports what include/spd_probe.h declares and rejects
+    bad arguments before any HIP call."""
+    if not os.path.exists(PROBE_LIB):
+        pytest.fail("libspd_probe.so not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(PROBE_LIB)
+    names = re.findall(r"SPD_PROBE_API\s+[\w\s\*]+?\b(\w+)\s*\(", open(PROBE_HEADER).read())
+    assert set(names) == {"spd_probe_gather", "spd_probe_null", "spd_probe_store"}
+    for n in names:
+        assert hasattr(L, n), n
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.spd_probe_gather.argtypes = [P, P, P, i32, i32, i32, i32, P, P]
+    L.spd_probe_null.argtypes = [i32, P]
+    L.spd_probe_store.argtypes = [P, i64, i32, P]
+    g = lambda **k: L.spd_probe_gather(k.get("kv", FAKE), FAKE, FAKE, k.get("N", 4), k.get("D", 512),
+                                       k.get("groups", 1), k.get("parts", 1), FAKE, None)
+    assert g(D=96) == 1 and g(groups=0) == 1 and g(parts=0) == 1 and g(N=-1) == 1
+    assert g(kv=FAKE + 8) == 1 and g(kv=None) == 1
+    assert g(N=1 << 20, groups=64, parts=64) == 1
+    assert g(N=0) == 0
+    assert L.spd_probe_null(0, None) == 1
+    assert L.spd_probe_store(FAKE, 100, 256, None) == 1
+    assert L.spd_probe_store(FAKE, 64, 0, None) == 1
+    assert L.spd_probe_store(None, 64, 256, None) == 1
+    assert L.spd_probe_store(FAKE, 0, 256, None) == 0

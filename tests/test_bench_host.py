@@ -60,3 +60,16 @@ def test_mfma_flops_hand_count():
     assert bench.mfma_flops(5, H=4, D=8) == 5 * 4 * (2 * 8 + 2 * 8)
     # decode_base: 40,960 rows, 64 heads, D = 512
     assert bench.mfma_flops(40960, 64, 512) == 5368709120
+
+
+def test_touched_bytes_and_one_cu_parts():
+    import bench
+    idx = np.array([5, 7, 5, 9, 7, 7], dtype=np.int32)
+    tb = bench.touched_bytes(idx, N=2, H=3, D=8)
+    assert tb["unique_rows"] == 3 and tb["gathered_rows"] == 6
+    assert tb["unique_row_fraction"] == 0.5
+    # 3 rows of 16 bytes, q and out of 2*3*8 bf16 each, 6 indices, 3 indptr entries
+    assert tb["bytes"] == 3 * 16 + 2 * 2 * 3 * 8 * 2 + 4 * 6 + 4 * 3
+    assert bench.touched_bytes(np.zeros(0, np.int32), 1, 1, 8)["unique_rows"] == 0
+    assert bench.one_cu_parts(64) == 4 and bench.one_cu_parts(1024) == 1
+    assert bench.one_cu_parts(1) == 32 and bench.one_cu_parts(8) == 32
