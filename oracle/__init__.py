@@ -51,6 +51,9 @@ def _load() -> ctypes.CDLL:
         lib.spd_oracle_build_decode_indices.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i32, P,
                                                         P, i64]
         lib.spd_oracle_build_decode_indices.restype = ctypes.c_int
+        lib.spd_oracle_build_decode_indices_clamped.argtypes = \
+            lib.spd_oracle_build_decode_indices.argtypes
+        lib.spd_oracle_build_decode_indices_clamped.restype = ctypes.c_int
         lib.spd_oracle_sparse_decode_attn_fp8.argtypes = [P, P, P, i64, P, P, P, ctypes.c_float,
                                                           i32, i32, i32, P, i32, P]
         lib.spd_oracle_sparse_decode_attn_fp8.restype = ctypes.c_int
@@ -193,11 +196,15 @@ def qk_norm_rope(q_bits: np.ndarray, kv_bits: np.ndarray, q_weight: np.ndarray,
 
 def build_decode_indices(state_slot: np.ndarray, swa_len: np.ndarray,
                          comp_pos: Optional[np.ndarray], block_table: Optional[np.ndarray],
-                         win: int, k_per_block: int, swa_pages: int) -> Tuple[np.ndarray, np.ndarray]:
+                         win: int, k_per_block: int, swa_pages: int,
+                         clamp: bool = False) -> Tuple[np.ndarray, np.ndarray]:
     """Ragged-packed ``(kv_indptr [N+1], kv_indices [kv_indptr[N]])``, both int32.
 
     comp_pos ``[N, topk]`` int32 (negative = no entry) or None; block_table
-    ``[N, max_blocks]`` int32 (unused when comp_pos is None).
+    ``[N, max_blocks]`` int32 (unused when comp_pos is None).  Input outside
+    the builder's preconditions raises, unless clamp: then a ring length
+    counts as its nearest bound in [0, win] and an entry whose block lies
+    past the table counts as no entry (spd_oracle_build_decode_indices_clamped).
     """
     state_slot = np.ascontiguousarray(state_slot, dtype=np.int32)
     swa_len = np.ascontiguousarray(swa_len, dtype=np.int32)
@@ -211,9 +218,10 @@ def build_decode_indices(state_slot: np.ndarray, swa_len: np.ndarray,
     capacity = N * (max(int(win), 0) + topk)
     indptr = np.zeros(N + 1, dtype=np.int32)
     indices = np.zeros(max(capacity, 1), dtype=np.int32)
-    rc = _load().spd_oracle_build_decode_indices(
-        _ptr(state_slot), _ptr(swa_len), _ptr(comp_pos), topk, _ptr(block_table), max_blocks, N,
-        int(win), int(k_per_block), int(swa_pages), _ptr(indptr), _ptr(indices), capacity)
+    fn = (_load().spd_oracle_build_decode_indices_clamped if clamp
+          else _load().spd_oracle_build_decode_indices)
+    rc = fn(_ptr(state_slot), _ptr(swa_len), _ptr(comp_pos), topk, _ptr(block_table), max_blocks, N,
+            int(win), int(k_per_block), int(swa_pages), _ptr(indptr), _ptr(indices), capacity)
     if rc != 0:
         raise ValueError("oracle builder rejected its input (code %d)" % rc)
     return indptr, indices[: indptr[-1]].copy()

@@ -339,6 +339,46 @@ int spd_oracle_build_decode_indices(const int32_t* state_slot, const int32_t* sw
 }
 
 /*
+ * The builder over metadata that breaks its preconditions (the pages say
+ * nothing of such input; this is the rule the library's builder and its fused
+ * page transform document): a ring length outside [0, win] counts as the
+ * nearest bound, and a compressed entry c >= 0 whose block c / k_per_block
+ * lies outside [0, max_blocks) counts as no entry.  The inputs are mapped by
+ * that rule, then built exactly as spd_oracle_build_decode_indices does.
+ * Same return codes, except that -5 and -6 cannot occur; -7 when the copies
+ * cannot be allocated.
+ */
+int spd_oracle_build_decode_indices_clamped(const int32_t* state_slot, const int32_t* swa_len,
+                                            const int32_t* comp_pos, int32_t topk,
+                                            const int32_t* block_table, int32_t max_blocks,
+                                            int32_t N, int32_t win, int32_t k_per_block,
+                                            int32_t swa_pages, int32_t* kv_indptr,
+                                            int32_t* kv_indices, int64_t capacity) {
+  if (N < 0 || win <= 0 || k_per_block <= 0 || topk < 0 || swa_pages < 0) return -3;
+  int32_t* len = (int32_t*)malloc(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
+  int32_t* pos = comp_pos ? (int32_t*)malloc(sizeof(int32_t) * (size_t)((int64_t)N * topk + 1))
+                          : NULL;
+  if (!len || (comp_pos && !pos)) {
+    free(len);
+    free(pos);
+    return -7;
+  }
+  for (int32_t t = 0; t < N; ++t) len[t] = swa_len[t] < 0 ? 0 : (swa_len[t] > win ? win : swa_len[t]);
+  if (comp_pos) {
+    for (int64_t i = 0; i < (int64_t)N * topk; ++i) {
+      const int32_t c = comp_pos[i];
+      pos[i] = (c >= 0 && c / k_per_block >= max_blocks) ? -1 : c;
+    }
+  }
+  const int rc = spd_oracle_build_decode_indices(state_slot, len, pos, topk, block_table, max_blocks,
+                                                 N, win, k_per_block, swa_pages, kv_indptr,
+                                                 kv_indices, capacity);
+  free(len);
+  free(pos);
+  return rc;
+}
+
+/*
  * Producer of the decode step: per-head RMSNorm of q, RMSNorm of the token's
  * new KV row, rotary embedding of both, and the ring slot the KV row is
  * stored in (sglang PR #25898 summary page, "key files": one kernel does the

@@ -40,8 +40,8 @@ def attention_cases():
     return out
 
 
-def builder_case():
-    with open(os.path.join(HERE, "builder_worked_example.json")) as f:
+def builder_case(name: str = "builder_worked_example.json"):
+    with open(os.path.join(HERE, name)) as f:
         c = json.load(f)
     a = lambda k: np.array(c[k], dtype=np.int32)
     return dict(win=c["win"], k_per_block=c["k_per_block"], swa_pages=c["swa_pages"],

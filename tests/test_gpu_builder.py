@@ -79,7 +79,7 @@ def test_defensive_rules_and_unaligned_rows(spd):
     """Out-of-contract metadata takes the documented device rule: swa_len is
     clamped to [0, win] and a comp_pos entry whose block lookup falls outside
     [0, max_blocks) (or any negative entry) is dropped.  Expected output: the
-    oracle on the sanitised input.  The comp_pos rows are passed as a view one
+    oracle's builder under that rule (clamp=True).  The comp_pos rows are passed as a view one
     int32 past a 16-byte boundary with topk % 4 == 0, so the 4-entries-per-load
     path must not be taken."""
     rng = np.random.default_rng(77)
@@ -90,10 +90,8 @@ def test_defensive_rules_and_unaligned_rows(spd):
     cp[rng.random(cp.shape) < 0.05] = -7
     sl = b.swa_len.copy()
     sl[:3] = [-2, win + 5, win]
-    clean_cp = np.where((cp >= 0) & (cp < mb * k), cp, -1).astype(np.int32)
-    clean_sl = np.clip(sl, 0, win).astype(np.int32)
-    optr, oidx = oracle.build_decode_indices(b.state_slot, clean_sl, clean_cp, b.block_table,
-                                             win, k, b.swa_pages)
+    optr, oidx = oracle.build_decode_indices(b.state_slot, sl, cp, b.block_table, win, k,
+                                             b.swa_pages, clamp=True)
     log("case builder defensive rules")
     d = torch.device("cuda:0")
     flat = torch.zeros(cp.size + 1, dtype=torch.int32, device=d)

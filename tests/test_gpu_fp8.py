@@ -13,8 +13,8 @@ rows (scale 0), a -inf sink, rows planted late in a slice whose scores lie
 far above the first tile (the fixed reference maximum then takes the second
 pass), slots that scatter, skip and leave rows untouched; the 32-head-wave
 kernel (128- and 64-head workgroups) on ragged tile edges, a restaged slice,
-every code and the second pass; and the decode-base, large and prefill
-configurations at full size on sampled tokens."""
+every code and the second pass; and the decode-base, ragged, large and
+prefill configurations at full size, every token."""
 import numpy as np
 import pytest
 import torch
@@ -183,7 +183,7 @@ def test_attention_second_pass(spd):
 
 def test_decode_base_config(spd):
     """decode_base (N=64, H=64, D=512, 640 rows a token) with its pool
-    quantised by the oracle; sampled tokens against the oracle."""
+    quantised by the oracle; every token against the oracle."""
     log("case fp8 decode_base")
     w = W.decode_base()
     b = w.builder
@@ -191,12 +191,9 @@ def test_decode_base_config(spd):
                                            b.win, b.k_per_block, b.swa_pages)
     codes, scales = oracle.quantize_fp8(w.kv_bits)
     out = run_fp8(spd, w.q_bits, codes, scales, idx, ptr, w.attn_sink, w.softmax_scale)
-    tokens = np.array([0, 13, 40, 63])
-    sub = [idx[ptr[t]:ptr[t + 1]] for t in tokens]
-    sidx, sptr = W.csr_from_lists(sub)
-    ref = oracle.sparse_decode_attn_fp8(w.q_bits[tokens], codes, scales, sidx, sptr, w.attn_sink,
+    ref = oracle.sparse_decode_attn_fp8(w.q_bits, codes, scales, idx, ptr, w.attn_sink,
                                         w.softmax_scale)
-    assert_close(bf16_to_f64(out[torch.from_numpy(tokens).to(dev())]), ref, "fp8 decode_base")
+    assert_close(bf16_to_f64(out), ref, "fp8 decode_base")
 
 
 # --- workgroups of 32-head waves: 128 heads (H % 128 == 0, N * H / 128 >= 256)
@@ -283,9 +280,9 @@ def test_wide_attention_second_pass(spd, H, N):
     assert_close(bf16_to_f64(out[torch.from_numpy(tokens).to(dev())]), ref, "fp8 wide second pass")
 
 
-# --- the large and prefill configurations at full size over FP8 pools, in the
-# launch configuration the benchmark times (32-head waves: 128 heads a
-# workgroup for large, 64 for prefill), on sampled tokens ---
+# --- the ragged, large and prefill configurations at full size over FP8 pools,
+# in the launch configuration the benchmark times (32-head waves: 128 heads a
+# workgroup for large, 64 for prefill; rows mode for ragged), every token ---
 
 @pytest.fixture
 def device_data():
@@ -294,23 +291,11 @@ def device_data():
     W.set_data_mode("host")
 
 
-def sampled(indptr, n, seed):
-    """n random tokens plus the longest, the shortest non-empty, the first and last."""
-    L = np.diff(indptr)
-    rng = np.random.default_rng(seed)
-    pick = set(rng.choice(len(L), size=min(n, len(L)), replace=False).tolist())
-    pick |= {int(np.argmax(L)), 0, len(L) - 1}
-    nz = np.nonzero(L)[0]
-    if len(nz):
-        pick.add(int(nz[np.argmin(L[nz])]))
-    return np.array(sorted(pick))
-
-
-def check_fp8_config(spd, w, idx_np, ptr_np, tokens, what):
+def check_fp8_config(spd, w, idx_np, ptr_np, what, chunk=512):
     """Quantise the whole bf16 pool on the GPU, run the FP8 call over all
-    tokens, then check the sampled tokens: their rows' codes and scales bit for
-    bit against the oracle's quantiser, their outputs against the oracle's FP8
-    attention over those rows."""
+    tokens, then check every token, chunk tokens at a time: the codes and
+    scales of the rows they read bit for bit against the oracle's quantiser,
+    their outputs against the oracle's FP8 attention over those rows."""
     from gpu_helpers import device_inputs
     q, kv, sink = device_inputs(w)
     kv8 = torch.empty((w.P, w.D), dtype=torch.uint8, device=dev())
@@ -319,18 +304,26 @@ def check_fp8_config(spd, w, idx_np, ptr_np, tokens, what):
     idx, ptr = device_csr(idx_np, ptr_np)
     out = spd.sparse_decode_attn_fp8(q, kv8, ksc, idx, ptr, sink, w.softmax_scale)
     torch.cuda.synchronize()
-    lists = [idx_np[ptr_np[t]:ptr_np[t + 1]] for t in tokens]
-    uniq, inv = np.unique(np.concatenate(lists), return_inverse=True)
-    u = torch.from_numpy(uniq.astype(np.int64)).to(dev())
-    codes, scales = oracle.quantize_fp8(W.host_bits(kv[u]))
-    assert np.array_equal(kv8[u].cpu().numpy(), codes)
-    assert np.array_equal(ksc[u].cpu().numpy().view(np.uint32), scales.view(np.uint32))
-    sub_ptr = np.zeros(len(tokens) + 1, dtype=np.int32)
-    sub_ptr[1:] = np.cumsum([len(x) for x in lists])
-    tok = torch.from_numpy(np.asarray(tokens, dtype=np.int64)).to(dev())
-    ref = oracle.sparse_decode_attn_fp8(W.host_bits(q[tok]), codes, scales, inv.astype(np.int32),
-                                        sub_ptr, w.attn_sink, w.softmax_scale)
-    assert_close(bf16_to_f64(out[tok]), ref, what)
+    for t0 in range(0, w.N, chunk):
+        tokens = np.arange(t0, min(w.N, t0 + chunk))
+        lists = [idx_np[ptr_np[t]:ptr_np[t + 1]] for t in tokens]
+        allidx = np.concatenate(lists) if lists else np.zeros(0, np.int32)
+        uniq, inv = np.unique(allidx, return_inverse=True)
+        if len(uniq) == 0:
+            uniq, inv = np.zeros(1, np.int64), np.zeros(0, np.int64)
+        u = torch.from_numpy(uniq.astype(np.int64)).to(dev())
+        codes, scales = oracle.quantize_fp8(W.host_bits(kv[u]))
+        assert np.array_equal(kv8[u].cpu().numpy(), codes), "%s: codes, tokens %d.." % (what, t0)
+        assert np.array_equal(ksc[u].cpu().numpy().view(np.uint32), scales.view(np.uint32)), \
+            "%s: scales, tokens %d.." % (what, t0)
+        sub_ptr = np.zeros(len(tokens) + 1, dtype=np.int32)
+        sub_ptr[1:] = np.cumsum([len(x) for x in lists])
+        tok = torch.from_numpy(tokens.astype(np.int64)).to(dev())
+        ref = oracle.sparse_decode_attn_fp8(W.host_bits(q[tok]), codes, scales,
+                                            inv.astype(np.int32), sub_ptr, w.attn_sink,
+                                            w.softmax_scale)
+        assert_close(bf16_to_f64(out[tok]), ref, "%s tokens %d..%d" % (what, t0, tokens[-1]))
+    log("  %s: all %d tokens" % (what, w.N))
 
 
 def test_large_config_fp8(spd, device_data):
@@ -339,10 +332,16 @@ def test_large_config_fp8(spd, device_data):
     b = w.builder
     ptr, idx = oracle.build_decode_indices(b.state_slot, b.swa_len, b.comp_pos, b.block_table,
                                            b.win, b.k_per_block, b.swa_pages)
-    check_fp8_config(spd, w, idx, ptr, sampled(ptr, 12, 5), "fp8 large")
+    check_fp8_config(spd, w, idx, ptr, "fp8 large", chunk=256)
 
 
 def test_prefill_config_fp8(spd, device_data):
     w = W.prefill()
     log("case fp8 prefill: N=8192, H=64, L up to 640")
-    check_fp8_config(spd, w, w.kv_indices, w.kv_indptr, sampled(w.kv_indptr, 20, 6), "fp8 prefill")
+    check_fp8_config(spd, w, w.kv_indices, w.kv_indptr, "fp8 prefill", chunk=1024)
+
+
+def test_ragged_config_fp8(spd, device_data):
+    w = W.ragged()
+    log("case fp8 ragged: N=256, H=64, L up to 2048, 25 % empty")
+    check_fp8_config(spd, w, w.kv_indices, w.kv_indptr, "fp8 ragged", chunk=64)

@@ -37,18 +37,6 @@ def workload_for(b: W.BuilderInputs, H: int, D: int, seed: int, n_blocks: int) -
                       max_len=b.win + b.topk, builder=b)
 
 
-def sanitized(b: W.BuilderInputs) -> W.BuilderInputs:
-    """b with the device-side rules of build_decode_indices applied on the host
-    (swa_len clamped to [0, win], comp_pos entries outside [0, max_blocks * K)
-    dropped), which the oracle's builder requires of its input."""
-    cp = None
-    if b.comp_pos is not None:
-        cp = b.comp_pos.copy()
-        cp[(cp < 0) | (cp >= b.block_table.shape[1] * b.k_per_block)] = -1
-    return W.BuilderInputs(b.state_slot, np.clip(b.swa_len, 0, b.win).astype(np.int32), cp,
-                           b.block_table, b.win, b.k_per_block, b.swa_pages)
-
-
 def run_both(spd, w: W.Workload, mode: int):
     """(paged output, two-call output, oracle kv_indptr, oracle kv_indices)."""
     b = w.builder
@@ -62,9 +50,11 @@ def run_both(spd, w: W.Workload, mode: int):
     ptr, idx = spd.build_decode_indices(ss, sl, cp, bt, b.win, b.k_per_block, b.swa_pages)
     two = spd.sparse_decode_attn(q, kv, idx, ptr, sink, w.softmax_scale, mode=mode)
     torch.cuda.synchronize()
-    c = sanitized(b)
-    optr, oidx = oracle.build_decode_indices(c.state_slot, c.swa_len, c.comp_pos, c.block_table,
-                                             c.win, c.k_per_block, c.swa_pages)
+    # the builder's device-side rule for metadata outside its preconditions
+    # (swa_len clamped to [0, win], entries past the block table dropped) is
+    # the oracle's clamping form
+    optr, oidx = oracle.build_decode_indices(b.state_slot, b.swa_len, b.comp_pos, b.block_table,
+                                             b.win, b.k_per_block, b.swa_pages, clamp=True)
     return fused, two, optr, oidx
 
 

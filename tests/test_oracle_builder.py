@@ -124,3 +124,45 @@ def test_decode_base_structure(oracle_mod):
         assert np.array_equal(seg[:128], t * 128 + np.arange(128))
         comp = seg[128:]
         assert len(np.unique(comp)) == 512 and comp.min() >= 8192 and comp.max() < 65536
+
+
+def test_clamped_builder_hand_worked_example(oracle_mod):
+    """Metadata outside the builder's preconditions (ring lengths below 0 and
+    above win, entries whose block lies past the table): the hand-derived
+    fixture tests/golden/builder_clamp_example.json (reading R27)."""
+    c = golden_cases.builder_case("builder_clamp_example.json")
+    args = (c["state_slot"], c["swa_len"], c["comp_pos"], c["block_table"], c["win"],
+            c["k_per_block"], c["swa_pages"])
+    indptr, indices = oracle_mod.build_decode_indices(*args, clamp=True)
+    assert indptr.tolist() == c["kv_indptr"].tolist()
+    assert indices.tolist() == c["kv_indices"].tolist()
+    with pytest.raises(ValueError):  # the strict builder rejects the same input
+        oracle_mod.build_decode_indices(*args)
+
+
+def test_clamped_builder_equals_strict_on_valid_input(oracle_mod):
+    """Within the preconditions the clamping form changes nothing."""
+    for seed in range(5):
+        ss, sl, cp, bt, swa_pages, _ = _random_builder(40 + seed, 7, 8, 12, 4, 5, 11)
+        a = oracle_mod.build_decode_indices(ss, sl, cp, bt, 8, 4, swa_pages)
+        b = oracle_mod.build_decode_indices(ss, sl, cp, bt, 8, 4, swa_pages, clamp=True)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_clamped_builder_counts(oracle_mod):
+    """Each token gets min(max(swa_len, 0), win) window rows and one row per
+    entry c with 0 <= c < max_blocks * K, and nothing else."""
+    rng = np.random.default_rng(77)
+    N, win, topk, K, mb = 9, 6, 7, 3, 4
+    ss = rng.integers(0, 20, size=N).astype(np.int32)
+    sl = rng.integers(-5, 12, size=N).astype(np.int32)
+    cp = rng.integers(-3, 2 * mb * K, size=(N, topk)).astype(np.int32)
+    bt = rng.integers(0, 50, size=(N, mb)).astype(np.int32)
+    indptr, indices = oracle_mod.build_decode_indices(ss, sl, cp, bt, win, K, 200, clamp=True)
+    for t in range(N):
+        n_win = min(max(int(sl[t]), 0), win)
+        n_comp = int(((cp[t] >= 0) & (cp[t] < mb * K)).sum())
+        assert indptr[t + 1] - indptr[t] == n_win + n_comp
+        rows = indices[indptr[t]:indptr[t + 1]]
+        assert rows[:n_win].tolist() == [int(ss[t]) * win + r for r in range(n_win)]
+        assert np.all(rows[n_win:] >= 200)
