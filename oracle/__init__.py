@@ -22,12 +22,31 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "spd_oracle.c")
 _BUILD_DIR = os.path.join(_HERE, "_build")
 _LIB_PATH = os.path.join(_BUILD_DIR, "libspd_oracle.so")
+# ASan + UBSan build (clang, the sanitizer runtime the HIP library's host code
+# uses too, so both load into one process); SPD_ORACLE_LIB selects it
+_SAN_PATH = os.path.join(_BUILD_DIR, "sanitize", "libspd_oracle.so")
+_CLANG = "/opt/rocm/llvm/bin/clang"
 
 _lib: Optional[ctypes.CDLL] = None
 
 
-def build(force: bool = False) -> str:
-    """Compile the C oracle with gcc (generic x86-64, OpenMP).  Returns the path."""
+def build(force: bool = False, sanitize: bool = False) -> str:
+    """Compile the C oracle with gcc (generic x86-64, OpenMP).  Returns the path.
+
+    sanitize: an AddressSanitizer + UndefinedBehaviorSanitizer build with
+    clang instead (any finding aborts), for the sanitized CPU test run."""
+    if sanitize:
+        os.makedirs(os.path.dirname(_SAN_PATH), exist_ok=True)
+        tmp = _SAN_PATH + ".tmp%d" % os.getpid()
+        cmd = [_CLANG, "-O1", "-g", "-fPIC", "-shared", "-fopenmp", "-std=c99", "-Wall",
+               "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+               "-fno-omit-frame-pointer", "-shared-libsan", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _SAN_PATH)
+        return _SAN_PATH
+    env = os.environ.get("SPD_ORACLE_LIB")
+    if env:
+        return env
     if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
         return _LIB_PATH
     os.makedirs(_BUILD_DIR, exist_ok=True)

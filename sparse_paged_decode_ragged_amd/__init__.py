@@ -40,7 +40,10 @@ from typing import Optional, Tuple
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "_lib", "libspd.so")
+# SPD_LIB_DIR selects another build of the same library (build.py --sanitize
+# writes a host-sanitized one to _lib/sanitize)
+LIB_DIR = os.environ.get("SPD_LIB_DIR") or os.path.join(_PKG, "_lib")
+LIB_PATH = os.path.join(LIB_DIR, "libspd.so")
 
 SPD_OK = 0
 _STATUS = {0: "SPD_OK", 1: "SPD_ERR_INVALID_ARG", 2: "SPD_ERR_UNSUPPORTED", 3: "SPD_ERR_WORKSPACE",

@@ -8,7 +8,8 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-LIB = os.path.join(ROOT, "sparse_paged_decode_ragged_amd", "_lib", "libspd.so")
+LIB_DIR = os.environ.get("SPD_LIB_DIR") or os.path.join(ROOT, "sparse_paged_decode_ragged_amd", "_lib")
+LIB = os.path.join(LIB_DIR, "libspd.so")
 HEADER = os.path.join(ROOT, "include", "spd.h")
 
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
@@ -355,7 +356,7 @@ def test_noalloc_rejects_plans_beyond_its_workspace(lib):
     assert 0 < worst <= limit
 
 
-PROBE_LIB = os.path.join(ROOT, "sparse_paged_decode_ragged_amd", "_lib", "libspd_probe.so")
+PROBE_LIB = os.path.join(LIB_DIR, "libspd_probe.so")
 PROBE_HEADER = os.path.join(ROOT, "include", "spd_probe.h")
 
 
@@ -384,3 +385,18 @@ def test_probe_library_exports_and_host_checks():
     assert L.spd_probe_store(FAKE, 64, 0, None) == 1
     assert L.spd_probe_store(None, 64, 256, None) == 1
     assert L.spd_probe_store(FAKE, 0, 256, None) == 0
+
+
+@pytest.mark.skipif(not os.environ.get("SPD_EXPECT_SANITIZED"),
+                    reason="only in the sanitized run (tests/run_sanitized.sh)")
+def test_sanitized_builds_are_the_ones_loaded(lib):
+    """In the sanitized run the process has loaded the instrumented libspd and
+    oracle (their sanitizer hooks are present), not the plain builds."""
+    import oracle
+    oracle.sparse_decode_attn  # noqa: B018  (module loaded)
+    oracle._load()
+    maps = open("/proc/self/maps").read()
+    assert os.path.join(LIB_DIR, "libspd.so") in maps
+    assert os.path.basename(os.path.normpath(LIB_DIR)) == "sanitize"
+    assert os.environ["SPD_ORACLE_LIB"] in maps and "/sanitize/" in os.environ["SPD_ORACLE_LIB"]
+    assert hasattr(ctypes.CDLL(None), "__asan_init")
