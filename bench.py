@@ -105,6 +105,8 @@ def fp8_kernel(N: int, H: int, D: int) -> str:
         w = 4 if H % 128 == 0 else 2
         if N * (H // (32 * w)) >= (256 if w == 4 else 512):
             return "attn_wide_fp8_kernel<%d,%d>" % (D, w)
+        if w == 2 and N * (H // 64) >= 256:
+            return "attn_wide_fp8_kernel<%d,4,2>" % D
     return "attn_rows_fp8_kernel<%d>" % D
 
 

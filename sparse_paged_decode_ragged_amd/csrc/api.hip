@@ -295,14 +295,19 @@ SPD_API spd_status sparse_decode_attn_fp8(const void* q, const void* kv_fp8,
     return SPD_ERR_INVALID_ARG;
   // As for the bf16 pool: 32-head waves (128 heads a workgroup when
   // H % 128 == 0, else 64) once the batch gives every CU a workgroup (two
-  // per CU for 64-head workgroups); 16-head rows workgroups otherwise.
+  // per CU for 64-head workgroups on two waves); 64-head workgroups on four
+  // waves (two parities of each head block) when it gives one per CU; 16-head
+  // rows workgroups otherwise.
   int wide = 0;
   if (D >= 128 && H % 64 == 0) {
     const int w = H % 128 == 0 ? 4 : 2;
     const long long items = (long long)N * (H / (32 * w));
-    if (items >= (w == 4 ? 256 : 512)) wide = w;
+    if (items >= (w == 4 ? 256 : 512))
+      wide = w;
+    else if (w == 2 && items >= 256)
+      wide = 3;
   }
-  const long long groups = wide ? H / (32 * wide) : (H + 15) / 16;
+  const long long groups = wide ? H / (wide == 4 ? 128 : 64) : (H + 15) / 16;
   if ((long long)N * groups > 0x7fffffffLL) return SPD_ERR_INVALID_ARG;
 
   spd::AttnArgs a{};

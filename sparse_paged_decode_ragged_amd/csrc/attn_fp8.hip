@@ -450,7 +450,19 @@ struct Fp8KOffsets {
   __device__ __forceinline__ int kq(int s) const { return base + 32 * (s ^ x); }
 };
 
-template <int D, int W>
+// Weight 2^(m - M) of a state with reference maximum m in a merge whose
+// maximum is M >= m; a state that saw no row (m = -inf) weighs exactly 0.
+__device__ __forceinline__ float fp8_state_weight(float m, float M) {
+  return m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+}
+
+// P = 1: workgroups of 32 W heads, each wave 32 heads over all 32 rows of a
+// tile.  P = 2 (W = 4): workgroups of 64 heads, waves (head block hb, parity
+// par) = (wave / 2, wave % 2); a wave takes rows [16 par, 16 par + 16) of
+// each tile for its 32 heads, so all four SIMDs work when H is 64; at the
+// end the two parity states of a head block merge in LDS, each wave keeping
+// half of D.
+template <int D, int W, int P = 1>
 __global__ void __launch_bounds__(64 * W) attn_wide_fp8_kernel(AttnArgs a) {
   constexpr int kTile = 32;
   constexpr int kStageBytes = kTile * D;
@@ -460,19 +472,26 @@ __global__ void __launch_bounds__(64 * W) attn_wide_fp8_kernel(AttnArgs a) {
   constexpr int kLoadsPerWave = kTile / kRowsPerLoad / W;
   constexpr int kRowsPerWave = kTile / W;           // rows (and scales) each wave loads
   constexpr int kPerTile = kLoadsPerWave + 1;       // and the scale load
-  constexpr int kHeads = 32 * W;
+  constexpr int kHB = W / P;  // 32-head blocks of the workgroup
+  constexpr int kHeads = 32 * kHB;
   // W = 4: one workgroup per CU, three tiles in flight; W = 2: two per CU
   constexpr int kAhead = W >= 4 ? 3 : 2;
   constexpr int kStages = kAhead + 1;
+  static_assert(P == 1 || (P == 2 && W == 4), "parities: P = 2 with four waves");
+  // LDS of the stages, and of the parity merge (each wave hands over half of
+  // its accumulators)
+  constexpr int kMergeBytes = P > 1 ? W * (kDT / 2) * 64 * 64 : 0;
+  constexpr int kSmem = kStages * kStageBytes > kMergeBytes ? kStages * kStageBytes : kMergeBytes;
   static_assert(D >= 128 && D <= 512 && D % 64 == 0, "unsupported D");
   static_assert(kLoadsPerWave >= 1 && kTile % (kRowsPerLoad * W) == 0, "loads must divide");
   static_assert((kAhead - 1) * kPerTile < 64, "vmcnt range");
   using Vt = Fp8WideVtOffsets<D>;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem];
   __shared__ __attribute__((aligned(256))) int sidx[kIdxCap];
   __shared__ __attribute__((aligned(256))) float ssink[kHeads];
   __shared__ __attribute__((aligned(256))) float sscale[kStages][W][64];
+  __shared__ float sml[W][4][16];  // parity merge: m0, m1, l0, l1 of each wave's 32 heads
   __shared__ int sflag[W];
 
   const int item = xcd_item(blockIdx.x, gridDim.x);
@@ -483,14 +502,16 @@ __global__ void __launch_bounds__(64 * W) attn_wide_fp8_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n16 = lane & 15;
   const int g = lane >> 4;
-  const int h0 = hg * kHeads + wave * 32;  // first head of this wave (H % kHeads == 0)
+  const int hb = wave / P;    // head block
+  const int par = wave % P;   // parity: rows [16 par, 16 par + 16) of each tile (P = 2)
+  const int h0 = hg * kHeads + hb * 32;  // first head of this wave (H % kHeads == 0)
 
   const ScalarI32Ptr indptr = (ScalarI32Ptr)a.kv_indptr;
   const int row0 = indptr[t];
   const int L = indptr[t + 1] - row0;
   const int32_t* part = a.kv_indices + row0;
   if (L <= 0) {
-    zero_heads<D>(a.out, a.H, t, h0, 32, lane, 64);
+    if (par == 0) zero_heads<D>(a.out, a.H, t, h0, 32, lane, 64);
     return;
   }
 
@@ -527,9 +548,9 @@ __global__ void __launch_bounds__(64 * W) attn_wide_fp8_kernel(AttnArgs a) {
       stage_indices(part, sc, n, sidx, wave, W, lane);
       wait_vmcnt<0>();
       barrier_lds();
-      if (pass == 0 && sc == 0) {
-        sk0 = ssink[wave * 32 + n16] * kLog2e;
-        sk1 = ssink[wave * 32 + 16 + n16] * kLog2e;
+      if (pass == 0 && sc == 0) {  // (with parities, the sink belongs to parity 0)
+        sk0 = par == 0 ? ssink[hb * 32 + n16] * kLog2e : -INFINITY;
+        sk1 = par == 0 ? ssink[hb * 32 + 16 + n16] * kLog2e : -INFINITY;
       }
       const int ntiles = (n + kTile - 1) / kTile;
 
@@ -572,6 +593,64 @@ __global__ void __launch_bounds__(64 * W) attn_wide_fp8_kernel(AttnArgs a) {
         const float* scl = sscale[i % kStages][0];
         const int nvalid = n - i * kTile;
 
+        if constexpr (P == 2) {
+          const int nv = nvalid - 16 * par;  // rows of this wave's 16 that exist
+          if (nv <= 0) continue;             // (wave-uniform: a ragged tail)
+          const unsigned char* sp = st + 16 * D * par;  // the parity's 16 rows
+          // S^T = K Q^T over the parity's rows, head blocks 0 and 1
+          f32x4 s00 = {0.f, 0.f, 0.f, 0.f}, s01 = s00;
+          {
+            constexpr int kPre = kKSteps < 2 ? kKSteps : 2;
+            u32x2 ra[kKSteps];
+#pragma unroll
+            for (int u = 0; u < kPre; ++u) ra[u] = *reinterpret_cast<const u32x2*>(sp + off8.kq(u));
+#pragma unroll
+            for (int u = 0; u < kKSteps; ++u) {
+              if (u + kPre < kKSteps) ra[u + kPre] = *reinterpret_cast<const u32x2*>(sp + off8.kq(u + kPre));
+              const bf16x8 ka = e4m3x8_to_bf16(ra[u]);
+              s00 = mfma_k32(ka, q0[u], s00);
+              s01 = mfma_k32(ka, q1[u], s01);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          const int r0 = 16 * par + 4 * g;
+          const f32x4 c0 = *reinterpret_cast<const f32x4*>(
+              scl + (r0 / kRowsPerWave) * 64 + r0 % kRowsPerWave);
+          float x0[4], x1[4];
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const bool v = 4 * g + i4 < nv;
+            x0[i4] = v ? s00[i4] * (a.qk_scale * c0[i4]) : -INFINITY;
+            x1[i4] = v ? s01[i4] * (a.qk_scale * c0[i4]) : -INFINITY;
+          }
+          float pf0[4], pf1[4];
+          over |= softmax_tile_f32<4>(x0, sk0, g, first0, m0, mt0, l0, pf0);
+          over |= softmax_tile_f32<4>(x1, sk1, g, first1, m1, mt1, l1, pf1);
+          bf16x4 a0, a1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a0[e] = (__bf16)(pf0[e] * c0[e]);
+            a1[e] = (__bf16)(pf1[e] * c0[e]);
+          }
+          const bf16x8 pb = wide_p_operand(a0, a1);
+          // O^T += V^T P^T over the parity's 16 rows
+          {
+            constexpr int kPre = kDT < 2 ? kDT : 2;
+            u32x2 va[kDT];
+            auto read_vt = [&](int u) {
+              va[u] = __builtin_bit_cast(
+                  u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((LdsV2i32*)(sp + voff.at(u))));
+            };
+#pragma unroll
+            for (int u = 0; u < kPre; ++u) read_vt(u);
+#pragma unroll
+            for (int u = 0; u < kDT; ++u) {
+              if (u + kPre < kDT) read_vt(u + kPre);
+              acc[u] = mfma32(e4m3x8_to_bf16(va[u]), pb, acc[u]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        } else {
         // S^T = K Q^T: rows 0-15 and 16-31, head blocks 0 and 1.  Per k-step:
         // the code reads of k-step u + 2, the decode of k-step u, its four
         // MFMAs (the fence keeps each decode next to its MFMAs, so only two
@@ -655,6 +734,7 @@ __global__ void __launch_bounds__(64 * W) attn_wide_fp8_kernel(AttnArgs a) {
             __builtin_amdgcn_sched_barrier(0);
           }
         }
+        }
       }
     }
     if (!workgroup_any(over, sflag, wave, W)) break;
@@ -663,16 +743,86 @@ __global__ void __launch_bounds__(64 * W) attn_wide_fp8_kernel(AttnArgs a) {
   // lane (n, hf) = lane n + 32 hf holds, for head h0 + n, d = 32 dt + 8 e4 +
   // 4 hf + e as element 4 e4 + e of acc[dt]; its denominator is block n / 16's
   // l of head n % 16, which every lane with lane % 16 == n % 16 holds.
-  const float lb0 = group_sum4(l0), lb1 = group_sum4(l1);
+  float lb0 = group_sum4(l0), lb1 = group_sum4(l1);
   const int nn = lane & 31, hf = lane >> 5;
+  // P = 2: the two parity states of the head block merge in LDS; the lower
+  // parity keeps d-tiles [0, kDT / 2), the upper one the rest, each combining
+  // its own half with the half its partner hands over (the lower parity's
+  // state first).  A parity that saw no row has m = -inf and weighs 0.
+  int lo = 0;
+  if constexpr (P == 2) {
+    constexpr int kHalf = kDT / 2;
+    const bool upper = par != 0;
+    const int partner = hb * P + (par ^ 1);
+    barrier_lds();  // the stages are free
+    if (g == 0) {
+      sml[wave][0][n16] = m0;
+      sml[wave][1][n16] = m1;
+      sml[wave][2][n16] = lb0;
+      sml[wave][3][n16] = lb1;
+    }
+    f32x4* mine = reinterpret_cast<f32x4*>(smem) + wave * kHalf * 256 + lane;
+    if (upper) {
+#pragma unroll
+      for (int i = 0; i < kHalf; ++i)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+          mine[(i * 4 + e4) * 64] = f32x4{acc[i][4 * e4], acc[i][4 * e4 + 1], acc[i][4 * e4 + 2], acc[i][4 * e4 + 3]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < kHalf; ++i)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+          mine[(i * 4 + e4) * 64] = f32x4{acc[kHalf + i][4 * e4], acc[kHalf + i][4 * e4 + 1],
+                                          acc[kHalf + i][4 * e4 + 2], acc[kHalf + i][4 * e4 + 3]};
+    }
+    barrier_lds();
+    const float pm0 = sml[partner][0][n16], pm1 = sml[partner][1][n16];
+    const float pl0 = sml[partner][2][n16], pl1 = sml[partner][3][n16];
+    const float M0 = fmaxf(m0, pm0), M1 = fmaxf(m1, pm1);
+    const float ws0 = fp8_state_weight(m0, M0), wp0 = fp8_state_weight(pm0, M0);
+    const float ws1 = fp8_state_weight(m1, M1), wp1 = fp8_state_weight(pm1, M1);
+    const float wself = nn < 16 ? ws0 : ws1, wpart = nn < 16 ? wp0 : wp1;
+    const f32x4* tp = reinterpret_cast<const f32x4*>(smem) + partner * kHalf * 256 + lane;
+    if (upper) {
+#pragma unroll
+      for (int i = 0; i < kHalf; ++i) {
+        f32x16 other;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const f32x4 q4 = tp[(i * 4 + e4) * 64];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) other[4 * e4 + e] = q4[e];
+        }
+        acc[i] = wpart * other + wself * acc[kHalf + i];
+      }
+      lb0 = wp0 * pl0 + ws0 * lb0;
+      lb1 = wp1 * pl1 + ws1 * lb1;
+      lo = kHalf;
+    } else {
+#pragma unroll
+      for (int i = 0; i < kHalf; ++i) {
+        f32x16 other;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const f32x4 q4 = tp[(i * 4 + e4) * 64];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) other[4 * e4 + e] = q4[e];
+        }
+        acc[i] = wself * acc[i] + wpart * other;
+      }
+      lb0 = ws0 * lb0 + wp0 * pl0;
+      lb1 = ws1 * lb1 + wp1 * pl1;
+    }
+  }
   const float inv = 1.0f / (nn < 16 ? lb0 : lb1);
   uint16_t* op = a.out + ((int64_t)t * a.H + h0 + nn) * D + 4 * hf;
 #pragma unroll
-  for (int dt = 0; dt < kDT; ++dt)
+  for (int dt = 0; dt < kDT / P; ++dt)
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {  // d = 8 e4 + 4 hf + e: chunk half e4 / 2 of d-tile dt
+    for (int e4 = 0; e4 < 4; ++e4) {  // d = 8 e4 + 4 hf + e: chunk half e4 / 2 of d-tile lo + dt
       const f32x4 v = {acc[dt][4 * e4], acc[dt][4 * e4 + 1], acc[dt][4 * e4 + 2], acc[dt][4 * e4 + 3]};
-      store_bf16x4(op + 16 * wide_vt_chunk<D>(dt, e4 >> 1) + 8 * (e4 & 1), v, inv);
+      store_bf16x4(op + 16 * wide_vt_chunk<D>(lo + dt, e4 >> 1) + 8 * (e4 & 1), v, inv);
     }
 }
 
@@ -704,6 +854,10 @@ hipError_t launch_fp8_d(const AttnArgs& a, int wide_waves, hipStream_t stream) {
     }
     if (wide_waves == 2) {
       hipLaunchKernelGGL((attn_wide_fp8_kernel<D, 2>), grid, dim3(128), 0, stream, a);
+      return hipGetLastError();
+    }
+    if (wide_waves == 3) {  // 64 heads on four waves: two head blocks x two parities
+      hipLaunchKernelGGL((attn_wide_fp8_kernel<D, 4, 2>), grid, dim3(256), 0, stream, a);
       return hipGetLastError();
     }
   }

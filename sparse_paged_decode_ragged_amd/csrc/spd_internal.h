@@ -92,7 +92,9 @@ hipError_t launch_split(const AttnArgs& args, int D, const AttnPlan& plan, hipSt
 // Attention over an FP8 pool: rows mode (workgroup = token x 16 heads), no
 // split; args.kv8 / args.kv_scale replace args.kv.
 // wide_waves: 0 = rows decomposition (16-head waves); 2 or 4 = workgroups of
-// 32 * wide_waves heads on 32-head waves (H % (32 * wide_waves) == 0, D >= 128)
+// 32 * wide_waves heads on 32-head waves (H % (32 * wide_waves) == 0, D >= 128);
+// 3 = workgroups of 64 heads on four 32-head waves, two parities of each head
+// block (H % 64 == 0, D >= 128)
 hipError_t launch_attention_fp8(const AttnArgs& args, int D, int wide_waves, hipStream_t stream);
 
 // Shared-window prefill: 32-head waves, two or four per workgroup

@@ -200,8 +200,10 @@ def test_decode_base_config(spd):
 # or 64 heads (H % 64 == 0, N * H / 64 >= 512) ---
 
 WIDE_N = 256  # the smallest batch that takes the 32-head-wave kernel at H = 128
-# (H, N): four waves a workgroup, two, and four with two head groups a token
-WIDE_SHAPES = [(128, 256), (64, 512), (256, 128)]
+# (H, N): 128-head workgroups on four waves, 64-head ones on two, four waves
+# with two head groups a token, and 64-head workgroups on four waves (two
+# parities of each head block: a batch of one workgroup per CU at H = 64)
+WIDE_SHAPES = [(128, 256), (64, 512), (256, 128), (64, 256)]
 
 
 def wide_lengths(rng, n, long=()):
