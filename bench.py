@@ -220,9 +220,10 @@ def cpu_baseline(w, indptr, indices, seconds):
     def median_rate(threads, budget):
         """Median tokens/s of three timed passes on `threads` threads, each
         pass about budget / 3 seconds: a sample of tokens (the whole batch
-        when it is quick), repeated k times."""
+        when it is quick), repeated k times, after one untimed pass."""
         oracle.set_threads(threads)
         probe = order[: min(N, 8)]
+        run(probe)  # warm-up
         dt = max(run(probe), 1e-4)
         per = (budget / 3) / dt * len(probe)  # tokens one pass can take
         n = int(min(N, max(len(probe), per)))
@@ -244,11 +245,24 @@ def cpu_baseline(w, indptr, indices, seconds):
     used = oracle.get_threads()
     v1, rates1, n1, k1, rows1, el1 = median_rate(1, seconds)
     oracle.set_threads(all_cores)
+    # gathered KV GB/s at the median rate: the sample's rows per token
+    row_bytes = 2 * w.D * rows / max(n, 1)
     return {"value": round(v, 2), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "cpu_model": cpu_model(), "gathered_kv_GBps": round(v * row_bytes / 1e9, 3),
             "passes_tokens_per_s": [round(r, 2) for r in rates],
             "value_1core": round(v1, 2), "passes_1core_tokens_per_s": [round(r, 2) for r in rates1],
             "sample": "fp64 two-pass attention only, median of " + describe(n, k, rows, el, used) +
                       "; one core: " + describe(n1, k1, rows1, el1, 1)}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def load_probe():
@@ -639,9 +653,15 @@ def main():
                    "touched_bytes_all_sets": touched["bytes"] * n_sets,
                    "unique_rows": touched["unique_rows"],
                    "unique_row_fraction": touched["unique_row_fraction"],
+                   "seed": W.SEEDS.get(args.workload), "torch": torch.__version__,
+                   "hip": getattr(torch.version, "hip", None),
+                   # sum of set 0's q and pool bit patterns (as int16): identifies the inputs
+                   "input_checksum": int(q0.view(torch.int16).sum(dtype=torch.int64).item() +
+                                         kv0.view(torch.int16).sum(dtype=torch.int64).item()),
                    "launch": "eager" if args.eager else "hip_graph_of_%d_steps" % n_sets,
                    "step": ("build_decode_indices + " if b is not None else "") + "sparse_decode_attn"},
         "gathered_kv_GBps": round(gathered_gbps, 1),
+        "nonempty_tokens_per_s": round(ab["nonempty"] / (ms_per_step * 1e-3), 1),
         "gathered_kv_frac_of_hbm_peak": round(gathered_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -655,6 +675,11 @@ def main():
                               "frac": round(mfma_flops(ab["sum_L"], H, D) / us_attn / 1e6 /
                                             MFMA_BF16_PEAK_TFLOPS, 4)}},
     }
+    # the rows the call touches once each (prefill's windows overlap: its
+    # gathered-byte rate can exceed HBM through cache reuse, this one cannot)
+    ub = touched["unique_rows"] * 2 * D
+    rec["unique_kv"] = {"bytes": ub, "GBps": round(ub / (us_attn * 1e-6) / 1e9, 1),
+                        "frac": round(ub / (us_attn * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
     if floor:
         kvb = ab["kv_bytes"]
 

@@ -49,9 +49,13 @@ def test_fp8_kernel_name_follows_the_plan():
     assert bench.fp8_kernel(1024, 128, 512) == "attn_wide_fp8_kernel<512,4>"
     assert bench.fp8_kernel(255, 128, 512) == "attn_rows_fp8_kernel<512>"
     assert bench.fp8_kernel(256, 128, 64) == "attn_rows_fp8_kernel<64>"
-    # H = 64: two 32-head waves a workgroup once there are two per CU
+    # H = 64: two 32-head waves a workgroup once there are two per CU; four
+    # waves (two parities of each head block) when there is one per CU
     assert bench.fp8_kernel(8192, 64, 512) == "attn_wide_fp8_kernel<512,2>"
-    assert bench.fp8_kernel(511, 64, 512) == "attn_rows_fp8_kernel<512>"
+    assert bench.fp8_kernel(511, 64, 512) == "attn_wide_fp8_kernel<512,4,2>"
+    assert bench.fp8_kernel(256, 64, 512) == "attn_wide_fp8_kernel<512,4,2>"
+    assert bench.fp8_kernel(255, 64, 512) == "attn_rows_fp8_kernel<512>"
+    assert bench.fp8_kernel(256, 64, 64) == "attn_rows_fp8_kernel<64>"
 
 
 def test_mfma_flops_hand_count():
