@@ -77,3 +77,61 @@ def test_noalloc_matches_ex_on_calls_in_a_row(spd):
         if mode_name != "rows":
             assert info["splits"] > 1, info
         check(w, info, out_na, out_ex, name)
+
+
+def test_noalloc_split_plan_in_a_graph(spd):
+    """The allocation-free call captured in a HIP graph (its use case): the
+    split plan of 6 tokens of up to 3000 rows, whose counter-clearing kernel
+    and attention kernel are both graph nodes, replayed four times on new
+    inputs, each replay equal bit for bit to sparse_decode_attn_ex on the
+    same inputs; an eager call of another plan between replays reuses the
+    array in between."""
+    rng = np.random.default_rng(77)
+    N, H, D, P, max_len = 6, 64, 512, 20000, 3000
+    lengths = np.array([3000, 17, 0, 2500, 1, 2999])
+    indptr = np.zeros(N + 1, dtype=np.int32)
+    indptr[1:] = np.cumsum(lengths)
+    dev = torch.device("cuda:0")
+    bits = lambda shape: torch.from_numpy(
+        W.normal_bf16(rng, shape).view(np.int16)).to(dev).view(torch.bfloat16)
+    q, kv = bits((N, H, D)), bits((P, D))
+    sink = torch.from_numpy(rng.standard_normal(H).astype(np.float32)).to(dev)
+    idx = torch.from_numpy(rng.integers(0, P, size=int(lengths.sum())).astype(np.int32)).to(dev)
+    ptr = torch.from_numpy(indptr).to(dev)
+    scale = 1.0 / np.sqrt(D)
+    info = spd.sparse_decode_attn_plan_info(N, H, D, max_len)
+    assert info["mode"] == "split" and info["splits"] > 1, info
+    out = torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)
+
+    def call():
+        spd.sparse_decode_attn_noalloc(q, kv, idx, ptr, sink, scale, out, max_len=max_len)
+
+    # warm-up outside capture, then capture on a side stream
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    ws = torch.zeros(spd.sparse_decode_attn_workspace_size(N, H, D, max_len), dtype=torch.uint8,
+                     device=dev)
+    other = torch.empty((3, H, D), dtype=torch.bfloat16, device=dev)
+    for rep in range(4):
+        log("  noalloc graph replay %d" % rep)
+        q.copy_(bits((N, H, D)))
+        idx.copy_(torch.from_numpy(rng.integers(0, P, size=idx.numel()).astype(np.int32)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref = spd.sparse_decode_attn(q, kv, idx, ptr, sink, scale, max_len=max_len, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), "replay %d" % rep
+        # another plan through the same array between replays (heads-mode split-L)
+        spd.sparse_decode_attn_noalloc(q[:3], kv, idx, ptr[:4], sink, scale, other, max_len=3000,
+                                       split_rows=256, mode=spd.MODE_HEADS)
+        torch.cuda.synchronize()
