@@ -54,6 +54,10 @@ namespace {
 
 constexpr int kSplitIdx = 1024;  // row indices staged at a time
 constexpr int kSpinLimit = 1000; // polls (each a memory round trip plus a short sleep)
+// ... and at most this long, on the 100 MHz real-time counter: partners that
+// are resident arrive within a few microseconds; one that is not (a kernel on
+// another stream holding CUs) is not waited for past this
+constexpr uint64_t kSpinTicks = 2000;  // 20 us
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const void* base) {
   // raw buffer over a piece's slot (< 2 GiB), untyped 32-bit format
@@ -644,6 +648,7 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) spiece[(i * 4 + e4) * 64 + lane] = quarter(acc[i], e4);
       int v = 0;
+      const uint64_t t_spin = __builtin_amdgcn_s_memrealtime();
       for (int it = 0; a.split_wait && it < kSpinLimit; ++it) {
         // polled with a read-modify-write (max with 0 leaves the count as it
         // is): it is served where the arrivals' adds are, which a plain
@@ -651,6 +656,7 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
         if (lane == 0) v = __hip_atomic_fetch_max(ctr_th + w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         v = __builtin_amdgcn_readfirstlane(v);
         if (v >= others) break;
+        if (__builtin_amdgcn_s_memrealtime() - t_spin > kSpinTicks) break;
         __builtin_amdgcn_s_sleep(2);
       }
       asm volatile("" ::: "memory");
