@@ -78,8 +78,11 @@ def parse():
 
 def kernel_sources(kernel: str) -> tuple:
     """The source files an attention kernel is built from."""
-    main = "attn_fp8.hip" if "fp8" in kernel else ("attn_split.hip" if "split" in kernel else "attn.hip")
-    return (main, "attn_device.h", "spd_internal.h")
+    if "split" in kernel:
+        return ("attn_split.hip", "fp8_device.h", "attn_device.h", "spd_internal.h")
+    if "fp8" in kernel:
+        return ("attn_fp8.hip", "fp8_device.h", "attn_device.h", "spd_internal.h")
+    return ("attn.hip", "attn_device.h", "spd_internal.h")
 
 
 def kernel_sources_digest(kernel: str) -> str:
@@ -96,17 +99,19 @@ def kernel_sources_digest(kernel: str) -> str:
 
 
 
-def fp8_kernel(N: int, H: int, D: int) -> str:
-    """The kernel sparse_decode_attn_fp8 launches: workgroups of 32 W heads
-    on 32-head waves when D >= 128 and H % 64 == 0 (W = 4 when H % 128 == 0,
-    else 2) and the batch gives one workgroup per CU (W = 4) or two (W = 2),
-    else the 16-head rows kernel."""
-    if D >= 128 and H % 64 == 0:
-        w = 4 if H % 128 == 0 else 2
-        if N * (H // (32 * w)) >= (256 if w == 4 else 512):
-            return "attn_wide_fp8_kernel<%d,%d>" % (D, w)
-        if w == 2 and N * (H // 64) >= 256:
-            return "attn_wide_fp8_kernel<%d,4,2>" % D
+def fp8_kernel(plan: dict, D: int) -> str:
+    """The kernel sparse_decode_attn_fp8_ex launches for a plan of
+    sparse_decode_attn_fp8_plan_info: the split kernel over codes, workgroups
+    of 32 W heads on 32-head waves (W = 3: 64 heads on four waves, two
+    parities), or the 16-head rows kernel."""
+    if plan["mode"] == "split":
+        return "attn_split_kernel<%d,%d,%d,true>" % (D, plan["heads_per_group"] // 32,
+                                                      plan["parities"])
+    w = plan["wide_waves"]
+    if w == 3:
+        return "attn_wide_fp8_kernel<%d,4,2>" % D
+    if w:
+        return "attn_wide_fp8_kernel<%d,%d>" % (D, w)
     return "attn_rows_fp8_kernel<%d>" % D
 
 
@@ -394,13 +399,16 @@ def main():
                                      b.k_per_block, b.swa_pages, s["sink"], w.softmax_scale,
                                      out=s["out"], mode=paged_mode)
 
-    # The attention call over an FP8 pool (e4m3 codes + one fp32 scale per row),
-    # each set's pool filled from its bf16 pool by the quantising store before
-    # timing; an FP8 pool is half the bytes, so twice the sets keep the touched
-    # footprint out of the Infinity Cache.
+    # The attention call over an FP8 pool (e4m3 codes + one fp32 scale per row)
+    # in its automatic plan for the same capacity bound, each set's pool filled
+    # from its bf16 pool by the quantising store before timing; an FP8 pool is
+    # half the bytes, so twice the sets keep the touched footprint out of the
+    # Infinity Cache.
     has_fp8 = not args.no_fp8 and args.split_rows == 0
     fp8_sets = []
     if has_fp8:
+        plan8 = spd.sparse_decode_attn_fp8_plan_info(N, H, D, max_len)
+        ws8_bytes = spd.sparse_decode_attn_fp8_workspace_size(N, H, D, max_len)
         n8 = max(2, min(32, math.ceil(2 * MALL_BYTES / (w.P * D))))
         for r in range(n8):
             base = sets[r % n_sets]
@@ -408,7 +416,9 @@ def main():
             ksc = torch.empty(w.P, dtype=torch.float32, device=dev)
             spd.quantize_kv_fp8(base["kv"], kv8, ksc)
             fp8_sets.append(dict(base, q=base["q"].clone(), kv8=kv8, ksc=ksc,
-                                 out=torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)))
+                                 out=torch.empty((N, H, D), dtype=torch.bfloat16, device=dev),
+                                 ws8=torch.zeros(max(ws8_bytes, 16), dtype=torch.uint8,
+                                                 device=dev)))
 
     # The decode-step producer (builder-shaped workloads): RMSNorm + RoPE of q
     # and of each token's new KV row, the KV row stored into its window-ring
@@ -452,7 +462,8 @@ def main():
 
     def attn_fp8(s):
         spd.sparse_decode_attn_fp8(s["q"], s["kv8"], s["ksc"], s["idx"], s["ptr"], s["sink"],
-                                   w.softmax_scale, out=s["out"])
+                                   w.softmax_scale, out=s["out"], max_len=max_len,
+                                   workspace=s["ws8"])
 
     # Floor legs (libspd_probe.so): the same rows gathered by the same LDS-DMA
     # pattern with no arithmetic, in the plan's decomposition (head groups x
@@ -625,7 +636,8 @@ def main():
     if plan["mode"] == "rows":
         kernel = "attn_rows_kernel<%d>" % D
     elif plan["mode"] == "split":
-        kernel = "attn_split_kernel<%d,%d,%d>" % (D, plan["heads_per_group"] // 32, plan["parities"])
+        kernel = "attn_split_kernel<%d,%d,%d,false>" % (D, plan["heads_per_group"] // 32,
+                                                        plan["parities"])
     elif plan.get("wide"):
         kernel = "attn_wide_kernel<%d,%d>" % (D, plan["heads_per_group"] // 32)
     else:
@@ -721,10 +733,12 @@ def main():
         # gathered row, q, out, the indices, kv_indptr and the sinks
         b_fp8 = ab["sum_L"] * (D + 4) + ab["qo_bytes"] + 4 * ab["sum_L"] + 4 * (N + 1) + 4 * H
         ach8 = b_fp8 / (us_fp8 * 1e-6) / 1e9
+        k8 = fp8_kernel(plan8, D)
         rec["fp8_pool"] = {
-            "call": "sparse_decode_attn_fp8", "kernel": fp8_kernel(N, H, D),
-            "rotating_sets": len(fp8_sets), "us_per_call": round(us_fp8, 3),
-            "traffic": recorded_traffic(fp8_kernel(N, H, D), args.workload + "_fp8"),
+            "call": "sparse_decode_attn_fp8_ex", "kernel": k8, "max_len": max_len,
+            "splits": plan8["splits"], "rotating_sets": len(fp8_sets),
+            "us_per_call": round(us_fp8, 3),
+            "traffic": recorded_traffic(k8, args.workload + "_fp8"),
             "tokens_per_s": round(N / (us_fp8 * 1e-6), 1), "bytes_per_call": int(b_fp8),
             "achieved_GBps": round(ach8, 1), "frac": round(ach8 / HBM_PEAK_GBPS, 4)}
     if us_pf is not None:

@@ -47,7 +47,8 @@ typedef enum spd_status {
 /* Human-readable name of a status code (static string, never NULL). */
 SPD_API const char* spd_status_string(spd_status s);
 
-/* Library version as MAJOR*10000 + MINOR*100 + PATCH (0.2.0: SPD_MODE_SPLIT). */
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH (0.2.0: SPD_MODE_SPLIT;
+ * 0.3.0: sparse_decode_attn_fp8_ex and its split mode). */
 SPD_API int spd_version(void);
 
 /*
@@ -147,8 +148,9 @@ SPD_API size_t sparse_decode_attn_workspace_size(int32_t N, int32_t H, int32_t D
  * workgroup, info[2] = head groups, info[3] = split-L partitions (1 = none),
  * info[4] = rows per partition, info[5] = 1 when the heads mode runs on
  * 32-head waves (64 or 128 heads per workgroup) else 0, info[6] = waves per
- * 16-head block (SPD_MODE_SPLIT: 2 when two waves take alternate tiles of the
- * same heads, else 1).  info is a host array of 7 int32.  Returns
+ * 32-head block (SPD_MODE_SPLIT: 2, or 4 when a workgroup takes 32 heads,
+ * the waves taking alternate 16-row tiles of the same heads; else 1).  info is
+ * a host array of 7 int32.  Returns
  * SPD_ERR_INVALID_ARG or SPD_ERR_UNSUPPORTED exactly when
  * sparse_decode_attn_ex would.
  */
@@ -327,10 +329,8 @@ SPD_API spd_status sparse_prefill_attn(const void* q, const void* unified_kv, in
  * contract, sink and numerics) with the row value kv_scale[r] * e4m3(code),
  * used as both key and value.  fp32 accumulation; the codes are converted to
  * bf16 exactly, the scale multiplies the row's scores and its softmax weight.
- * Work decomposition (no split, no workspace): workgroups of 32 * W heads on
- * 32-head waves (W = 4 when H % 128 == 0, else 2) when D >= 128, H % 64 == 0
- * and N * H / (32 W) >= 256 (W = 4) or >= 512 (W = 2); otherwise the rows
- * mode of sparse_decode_attn_ex (workgroup = token x 16 heads).
+ * Work decomposition as sparse_decode_attn_fp8_ex with max_len 0 and
+ * SPD_MODE_AUTO (no split, no workspace).
  *
  *   q, kv_indices, kv_indptr, attn_sink, softmax_scale, out, N, H, D:
  *                as sparse_decode_attn (same alignment and preconditions:
@@ -345,6 +345,54 @@ SPD_API spd_status sparse_decode_attn_fp8(const void* q, const void* kv_fp8,
                                           const int32_t* kv_indices, const int32_t* kv_indptr,
                                           const float* attn_sink, float softmax_scale, void* out,
                                           int32_t N, int32_t H, int32_t D, void* stream);
+
+/*
+ * sparse_decode_attn_fp8 with a chosen plan, as sparse_decode_attn_ex is
+ * for the bf16 pool (same max_len, split_rows, workspace and arrival-counter
+ * rules).  Modes:
+ *   SPD_MODE_ROWS:  workgroup = (token, 16 heads), its 4 waves splitting the
+ *                   rows (any supported H and D).
+ *   SPD_MODE_WIDE:  workgroups of 128 heads (H % 128 == 0) or 64 heads on
+ *                   32-head waves sharing 32-row tiles of codes; D >= 128,
+ *                   H % 64 == 0.
+ *   SPD_MODE_SPLIT: the split mode of sparse_decode_attn_ex over codes
+ *                   (D >= 128): partitions of a slice merged inside the
+ *                   kernel, each gathered row entering one CU per 64 heads.
+ *   SPD_MODE_AUTO:  SPLIT when split_rows != 0, or when D >= 128, the batch
+ *                   gives fewer than 256 workgroups of 64 heads (16 or 32
+ *                   when H is smaller) and max_len >= 2048; else WIDE on 128-head
+ *                   workgroups when H % 128 == 0, D >= 128 and N * H / 128 >=
+ *                   256; on 64-head workgroups of two waves when H % 64 == 0
+ *                   and N * H / 64 >= 512, or of four waves (two parities of
+ *                   each 32-head block) when it is in [256, 512); else ROWS.
+ * SPD_MODE_HEADS (no FP8 kernel), SPLIT, WIDE or split_rows != 0 with
+ * D < 128, WIDE with H % 64 != 0 and split_rows != 0 with ROWS or WIDE give
+ * SPD_ERR_UNSUPPORTED.  Other arguments and errors as sparse_decode_attn_fp8
+ * and sparse_decode_attn_ex.
+ */
+SPD_API spd_status sparse_decode_attn_fp8_ex(const void* q, const void* kv_fp8,
+                                             const float* kv_scale, int64_t num_rows,
+                                             const int32_t* kv_indices, const int32_t* kv_indptr,
+                                             const float* attn_sink, float softmax_scale,
+                                             void* out, int32_t N, int32_t H, int32_t D,
+                                             int32_t max_len, int32_t split_rows, int32_t mode,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* stream);
+
+/*
+ * Workspace bytes sparse_decode_attn_fp8_ex needs (0 when its plan does not
+ * split, or for arguments it rejects), and its plan in the layout of
+ * sparse_decode_attn_plan_info, except info[5] = 0 (ROWS), 2 or 4 (WIDE:
+ * waves of 32 heads a workgroup) or 3 (64 heads on four waves, two parities).
+ * plan_info returns SPD_ERR_UNSUPPORTED for every mode and shape the call
+ * rejects as unsupported, SPD_ERR_INVALID_ARG for invalid sizes or modes.
+ */
+SPD_API size_t sparse_decode_attn_fp8_workspace_size(int32_t N, int32_t H, int32_t D,
+                                                     int32_t max_len, int32_t split_rows,
+                                                     int32_t mode);
+SPD_API spd_status sparse_decode_attn_fp8_plan_info(int32_t N, int32_t H, int32_t D,
+                                                    int32_t max_len, int32_t split_rows,
+                                                    int32_t mode, int32_t* info);
 
 /*
  * Quantising store into an FP8 pool: bf16 row i of src goes to pool row

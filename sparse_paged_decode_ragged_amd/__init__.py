@@ -20,8 +20,11 @@ Call names follow the C ABI:
   softmax_scale, out=None)`` -- the same attention for tokens whose row lists
   are windows of one index stream (consecutive tokens sharing rows)
 * ``sparse_decode_attn_fp8(q, kv_fp8, kv_scale, kv_indices, kv_indptr,
-  attn_sink, softmax_scale, out=None)`` -- the same attention over an FP8 pool
-  (e4m3 codes times a per-row fp32 scale)
+  attn_sink, softmax_scale, out=None, *, max_len=0, split_rows=0, mode=0,
+  workspace=None)`` -- the same attention over an FP8 pool (e4m3 codes times a
+  per-row fp32 scale), with the plans of ``sparse_decode_attn_fp8_ex``
+  (split mode included); ``sparse_decode_attn_fp8_workspace_size`` and
+  ``sparse_decode_attn_fp8_plan_info`` as for the bf16 pool
 * ``quantize_kv_fp8(src, kv_fp8, kv_scale, slots=None)`` -- the quantising
   store that fills such a pool
 * ``fused_qk_norm_rope_swa_store(q, kv, q_weight, kv_weight, eps, positions,
@@ -54,7 +57,8 @@ EXPORTED_SYMBOLS = (
     "sparse_decode_attn_workspace_size", "sparse_decode_attn_ex", "build_decode_indices",
     "spd_validate_indices", "sparse_decode_attn_plan_info", "sparse_decode_attn_paged",
     "sparse_decode_attn_fp8", "quantize_kv_fp8", "fused_qk_norm_rope_swa_store",
-    "sparse_prefill_attn", "sparse_decode_attn_noalloc",
+    "sparse_prefill_attn", "sparse_decode_attn_noalloc", "sparse_decode_attn_fp8_ex",
+    "sparse_decode_attn_fp8_workspace_size", "sparse_decode_attn_fp8_plan_info",
 )
 
 
@@ -92,6 +96,14 @@ def _load() -> ctypes.CDLL:
     lib.sparse_decode_attn_fp8.argtypes = [P, P, P, i64, P, P, P, ctypes.c_float, P, i32, i32, i32,
                                            P]
     lib.sparse_decode_attn_fp8.restype = ctypes.c_int
+    lib.sparse_decode_attn_fp8_ex.argtypes = [P, P, P, i64, P, P, P, ctypes.c_float, P, i32, i32,
+                                              i32, i32, i32, i32, P, sz, P]
+    lib.sparse_decode_attn_fp8_ex.restype = ctypes.c_int
+    lib.sparse_decode_attn_fp8_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.sparse_decode_attn_fp8_workspace_size.restype = sz
+    lib.sparse_decode_attn_fp8_plan_info.argtypes = [i32, i32, i32, i32, i32, i32,
+                                                     ctypes.POINTER(ctypes.c_int32)]
+    lib.sparse_decode_attn_fp8_plan_info.restype = ctypes.c_int
     lib.quantize_kv_fp8.argtypes = [P, P, i32, i32, P, P, i64, P]
     lib.sparse_prefill_attn.argtypes = [P, P, i64, P, i64, P, P, P, ctypes.c_float, P, i32, i32,
                                         i32, i32, P]
@@ -361,13 +373,37 @@ def _fp8_codes(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+def sparse_decode_attn_fp8_workspace_size(N: int, H: int, D: int, max_len: int = 0,
+                                          split_rows: int = 0, mode: int = MODE_AUTO) -> int:
+    return int(lib.sparse_decode_attn_fp8_workspace_size(int(N), int(H), int(D), int(max_len),
+                                                         int(split_rows), int(mode)))
+
+
+def sparse_decode_attn_fp8_plan_info(N: int, H: int, D: int, max_len: int = 0,
+                                     split_rows: int = 0, mode: int = MODE_AUTO) -> dict:
+    info = (ctypes.c_int32 * 7)()
+    st = lib.sparse_decode_attn_fp8_plan_info(int(N), int(H), int(D), int(max_len),
+                                              int(split_rows), int(mode), info)
+    _raise_on(st, "sparse_decode_attn_fp8_plan_info")
+    return {"mode": {1: "heads", 2: "rows", 4: "split"}[info[0]], "heads_per_group": info[1],
+            "head_groups": info[2], "splits": info[3],
+            "split_rows": info[4] if info[3] > 1 else None, "wide_waves": info[5],
+            "parities": info[6]}
+
+
 def sparse_decode_attn_fp8(q: torch.Tensor, kv_fp8: torch.Tensor, kv_scale: torch.Tensor,
                            kv_indices: torch.Tensor, kv_indptr: torch.Tensor,
                            attn_sink: torch.Tensor, softmax_scale: float,
-                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                           out: Optional[torch.Tensor] = None, *, max_len: int = 0,
+                           split_rows: int = 0, mode: int = MODE_AUTO,
+                           workspace: Optional[torch.Tensor] = None,
+                           plain: bool = False) -> torch.Tensor:
     """out[N, H, D] (bf16): sparse decode attention over an FP8 pool whose row r
     is kv_scale[r] * e4m3(kv_fp8[r]) (uint8 codes or a float8_e4m3fn tensor);
-    see include/spd.h."""
+    see include/spd.h.  plain=True calls ``sparse_decode_attn_fp8`` (automatic
+    plan, no split); otherwise ``sparse_decode_attn_fp8_ex`` runs with
+    (max_len, split_rows, mode), and a zero-filled workspace is allocated here
+    when its plan needs one and none is given."""
     _check(q, "q", torch.bfloat16, 3)
     codes = _fp8_codes(kv_fp8, "kv_fp8")
     _check(kv_scale, "kv_scale", torch.float32, 1)
@@ -385,10 +421,24 @@ def sparse_decode_attn_fp8(q: torch.Tensor, kv_fp8: torch.Tensor, kv_scale: torc
         if tuple(out.shape) != (N, H, D):
             raise ValueError("out must be [N, H, D]")
     idx = kv_indices if kv_indices.numel() > 0 else kv_indptr  # any valid pointer; never read
-    st = lib.sparse_decode_attn_fp8(_ptr(q), _ptr(codes), _ptr(kv_scale), codes.shape[0],
-                                    _ptr(idx), _ptr(kv_indptr), _ptr(attn_sink),
-                                    float(softmax_scale), _ptr(out), N, H, D, _stream(q.device))
-    _raise_on(st, "sparse_decode_attn_fp8")
+    stream = _stream(q.device)
+    if plain:
+        st = lib.sparse_decode_attn_fp8(_ptr(q), _ptr(codes), _ptr(kv_scale), codes.shape[0],
+                                        _ptr(idx), _ptr(kv_indptr), _ptr(attn_sink),
+                                        float(softmax_scale), _ptr(out), N, H, D, stream)
+        _raise_on(st, "sparse_decode_attn_fp8")
+        return out
+    need = sparse_decode_attn_fp8_workspace_size(N, H, D, max_len, split_rows, mode)
+    if need > 0 and workspace is None:
+        # zero-filled: a split-mode workspace's arrival counters must start at zero
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.sparse_decode_attn_fp8_ex(_ptr(q), _ptr(codes), _ptr(kv_scale), codes.shape[0],
+                                       _ptr(idx), _ptr(kv_indptr), _ptr(attn_sink),
+                                       float(softmax_scale), _ptr(out), N, H, D, int(max_len),
+                                       int(split_rows), int(mode), _ptr(workspace), ws_bytes,
+                                       stream)
+    _raise_on(st, "sparse_decode_attn_fp8_ex")
     return out
 
 

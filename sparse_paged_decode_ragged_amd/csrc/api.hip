@@ -22,6 +22,21 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 constexpr double kLog2eD = 1.4426950408889634073599;
 
+// The mode and shape checks of sparse_decode_attn_fp8_ex (host only).
+spd_status fp8_mode_status(int32_t H, int32_t D, int32_t split_rows, int32_t mode) {
+  if (mode != SPD_MODE_AUTO && mode != SPD_MODE_HEADS && mode != SPD_MODE_ROWS &&
+      mode != SPD_MODE_WIDE && mode != SPD_MODE_SPLIT)
+    return SPD_ERR_INVALID_ARG;
+  if (!spd::attn_supported(H, D) || mode == SPD_MODE_HEADS) return SPD_ERR_UNSUPPORTED;
+  // split and wide modes need D >= 128 (wide: H % 64 == 0); only split mode
+  // (asked for, or taken by the automatic plan) cuts slices into split_rows
+  if ((mode == SPD_MODE_SPLIT || mode == SPD_MODE_WIDE || split_rows != 0) && D < 128)
+    return SPD_ERR_UNSUPPORTED;
+  if (mode == SPD_MODE_WIDE && H % 64 != 0) return SPD_ERR_UNSUPPORTED;
+  if (mode != SPD_MODE_SPLIT && mode != SPD_MODE_AUTO && split_rows != 0) return SPD_ERR_UNSUPPORTED;
+  return SPD_OK;
+}
+
 }  // namespace
 
 namespace spd {
@@ -89,7 +104,7 @@ SPD_API const char* spd_status_string(spd_status s) {
   return "SPD_ERR_UNKNOWN";
 }
 
-SPD_API int spd_version(void) { return 200; }
+SPD_API int spd_version(void) { return 300; }
 
 SPD_API int sparse_decode_attn_can_use(int32_t H, int32_t D) {
   return spd::attn_supported(H, D) ? 1 : 0;
@@ -271,14 +286,45 @@ SPD_API spd_status sparse_prefill_attn(const void* q, const void* unified_kv, in
   return e == hipSuccess ? SPD_OK : SPD_ERR_HIP;
 }
 
-SPD_API spd_status sparse_decode_attn_fp8(const void* q, const void* kv_fp8,
-                                          const float* kv_scale, int64_t num_rows,
-                                          const int32_t* kv_indices, const int32_t* kv_indptr,
-                                          const float* attn_sink, float softmax_scale, void* out,
-                                          int32_t N, int32_t H, int32_t D, void* stream) {
-  if (N < 0 || H <= 0 || D <= 0 || num_rows <= 0) return SPD_ERR_INVALID_ARG;
+SPD_API size_t sparse_decode_attn_fp8_workspace_size(int32_t N, int32_t H, int32_t D,
+                                                     int32_t max_len, int32_t split_rows,
+                                                     int32_t mode) {
+  spd::AttnPlan plan;
+  if (!spd::make_fp8_plan(N, H, D, max_len, split_rows, mode, &plan)) return 0;
+  return plan.workspace_bytes;
+}
+
+SPD_API spd_status sparse_decode_attn_fp8_plan_info(int32_t N, int32_t H, int32_t D,
+                                                    int32_t max_len, int32_t split_rows,
+                                                    int32_t mode, int32_t* info) {
+  if (!info || N < 0 || H <= 0 || D <= 0 || max_len < 0 || split_rows < 0) return SPD_ERR_INVALID_ARG;
+  const spd_status ms = fp8_mode_status(H, D, split_rows, mode);
+  if (ms != SPD_OK) return ms;
+  spd::AttnPlan plan;
+  if (!spd::make_fp8_plan(N, H, D, max_len, split_rows, mode, &plan)) return SPD_ERR_INVALID_ARG;
+  info[0] = plan.mode;
+  info[1] = plan.heads_per_group;
+  info[2] = plan.head_groups;
+  info[3] = plan.splits;
+  info[4] = plan.split_rows;
+  info[5] = plan.wide;
+  info[6] = plan.parities;
+  return SPD_OK;
+}
+
+SPD_API spd_status sparse_decode_attn_fp8_ex(const void* q, const void* kv_fp8,
+                                             const float* kv_scale, int64_t num_rows,
+                                             const int32_t* kv_indices, const int32_t* kv_indptr,
+                                             const float* attn_sink, float softmax_scale,
+                                             void* out, int32_t N, int32_t H, int32_t D,
+                                             int32_t max_len, int32_t split_rows, int32_t mode,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  if (N < 0 || H <= 0 || D <= 0 || num_rows <= 0 || max_len < 0 || split_rows < 0)
+    return SPD_ERR_INVALID_ARG;
   if (!isfinite(softmax_scale)) return SPD_ERR_INVALID_ARG;
-  if (!spd::attn_supported(H, D)) return SPD_ERR_UNSUPPORTED;
+  const spd_status ms = fp8_mode_status(H, D, split_rows, mode);
+  if (ms != SPD_OK) return ms;
   if (N == 0) return SPD_OK;
   if (!q || !kv_fp8 || !kv_scale || !kv_indices || !kv_indptr || !attn_sink || !out)
     return SPD_ERR_INVALID_ARG;
@@ -293,22 +339,12 @@ SPD_API spd_status sparse_decode_attn_fp8(const void* q, const void* kv_fp8,
       overlap(out, qo_bytes, attn_sink, (size_t)H * 4) ||
       overlap(out, qo_bytes, kv_indptr, (size_t)(N + 1) * 4))
     return SPD_ERR_INVALID_ARG;
-  // As for the bf16 pool: 32-head waves (128 heads a workgroup when
-  // H % 128 == 0, else 64) once the batch gives every CU a workgroup (two
-  // per CU for 64-head workgroups on two waves); 64-head workgroups on four
-  // waves (two parities of each head block) when it gives one per CU; 16-head
-  // rows workgroups otherwise.
-  int wide = 0;
-  if (D >= 128 && H % 64 == 0) {
-    const int w = H % 128 == 0 ? 4 : 2;
-    const long long items = (long long)N * (H / (32 * w));
-    if (items >= (w == 4 ? 256 : 512))
-      wide = w;
-    else if (w == 2 && items >= 256)
-      wide = 3;
+  spd::AttnPlan plan;
+  if (!spd::make_fp8_plan(N, H, D, max_len, split_rows, mode, &plan)) return SPD_ERR_INVALID_ARG;
+  if (plan.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.workspace_bytes) return SPD_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return SPD_ERR_INVALID_ARG;
   }
-  const long long groups = wide ? H / (wide == 4 ? 128 : 64) : (H + 15) / 16;
-  if ((long long)N * groups > 0x7fffffffLL) return SPD_ERR_INVALID_ARG;
 
   spd::AttnArgs a{};
   a.q = static_cast<const uint16_t*>(q);
@@ -318,14 +354,25 @@ SPD_API spd_status sparse_decode_attn_fp8(const void* q, const void* kv_fp8,
   a.kv_indptr = kv_indptr;
   a.sink = attn_sink;
   a.out = static_cast<uint16_t*>(out);
+  a.ws = static_cast<float*>(workspace);
   a.qk_scale = (float)((double)softmax_scale * kLog2eD);
   a.N = N;
   a.H = H;
-  a.head_groups = (int32_t)groups;
-  a.splits = 1;
-  a.split_rows = 1 << 30;
-  const hipError_t e = spd::launch_attention_fp8(a, D, wide, static_cast<hipStream_t>(stream));
+  a.head_groups = plan.head_groups;
+  a.splits = plan.splits;
+  a.split_rows = plan.split_rows;
+  const hipError_t e = spd::launch_attention_fp8(a, D, plan, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPD_OK : SPD_ERR_HIP;
+}
+
+SPD_API spd_status sparse_decode_attn_fp8(const void* q, const void* kv_fp8,
+                                          const float* kv_scale, int64_t num_rows,
+                                          const int32_t* kv_indices, const int32_t* kv_indptr,
+                                          const float* attn_sink, float softmax_scale, void* out,
+                                          int32_t N, int32_t H, int32_t D, void* stream) {
+  return sparse_decode_attn_fp8_ex(q, kv_fp8, kv_scale, num_rows, kv_indices, kv_indptr,
+                                   attn_sink, softmax_scale, out, N, H, D, 0, 0, SPD_MODE_AUTO,
+                                   nullptr, 0, stream);
 }
 
 SPD_API spd_status quantize_kv_fp8(const void* src, const int32_t* slots, int32_t n, int32_t D,

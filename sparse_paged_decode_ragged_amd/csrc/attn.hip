@@ -941,7 +941,7 @@ hipError_t launch_prefill_d(const AttnArgs& a, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream) {
-  if (plan.mode == kModeSplit) return launch_split(a, D, plan, stream);
+  if (plan.mode == kModeSplit) return launch_split(a, D, plan, false, stream);
   if (plan.mode == kModeRows) {
     if (a.paged)
       hipLaunchKernelGGL((attn_rows_kernel<D, true>), dim3((unsigned)(a.N * a.head_groups)),
@@ -1126,6 +1126,52 @@ bool make_attn_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t sp
                                         (size_t)(D + 2) * sizeof(float)
                                   : 0;
   return true;
+}
+
+bool make_fp8_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t split_rows,
+                   int32_t mode, AttnPlan* p) {
+  if (!attn_supported(H, D) || N < 0 || max_len < 0 || split_rows < 0) return false;
+  if (mode != kModeAuto && mode != kModeRows && mode != kModeWide && mode != kModeSplit)
+    return false;
+  p->parities = 1;
+  // the batch's workgroups without split-L, counted as for the bf16 pool
+  const int heads_per = H <= 16 ? 16 : (H <= 32 ? 32 : 64);
+  const long long base = (long long)N * ((H + heads_per - 1) / heads_per);
+  // split mode when asked for, when the automatic plan is given a partition
+  // length, or for a small batch of long slices
+  const bool chosen = mode == kModeSplit || (mode == kModeAuto && split_rows > 0);
+  if (chosen || (mode == kModeAuto && base < 256 && max_len >= kSplitAutoLen && D >= 128)) {
+    if (D < 128) return false;
+    if (make_split_plan(N, H, D, max_len, split_rows, p) && (chosen || p->splits > 1)) return true;
+    if (chosen) return false;
+    p->parities = 1;
+  }
+  if (split_rows != 0) return false;  // only split mode cuts slices
+  // 32-head waves (128 heads a workgroup when H % 128 == 0, else 64) once the
+  // batch gives every CU a workgroup (two per CU for 64-head workgroups on
+  // two waves); 64-head workgroups on four waves (two parities of each head
+  // block) when it gives one per CU; 16-head rows workgroups otherwise.
+  int wide = 0;
+  if (mode == kModeWide) {
+    if (D < 128 || H % 64 != 0) return false;
+    wide = H % 128 == 0 ? 4 : 2;
+  } else if (mode == kModeAuto && D >= 128 && H % 64 == 0) {
+    const int w = H % 128 == 0 ? 4 : 2;
+    const long long items = (long long)N * (H / (32 * w));
+    if (items >= (w == 4 ? 256 : 512))
+      wide = w;
+    else if (w == 2 && items >= 256)
+      wide = 3;
+  }
+  p->mode = wide ? kModeHeads : kModeRows;
+  p->wide = wide;
+  p->waves = wide == 2 ? 2 : 4;
+  p->heads_per_group = wide == 4 ? 128 : (wide ? 64 : 16);
+  p->head_groups = (H + p->heads_per_group - 1) / p->heads_per_group;
+  p->splits = 1;
+  p->split_rows = 1 << 30;
+  p->workspace_bytes = 0;
+  return (long long)N * p->head_groups <= 0x7fffffffLL;
 }
 
 hipError_t launch_prefill(const AttnArgs& a, int D, hipStream_t stream) {

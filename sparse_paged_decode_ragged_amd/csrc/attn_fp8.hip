@@ -32,33 +32,12 @@
 //   * the scale multiplies its row's scores and its softmax weight, which
 //     becomes P' = bf16(p * scale); the denominator sums the unscaled p.
 #include "attn_device.h"
+#include "fp8_device.h"
 #include "row_device.h"
 #include "store_internal.h"
 
 namespace spd {
 namespace {
-
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) i32x2 LdsV2i32;
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Four e4m3 codes (bytes of raw, in order) -> four bf16 values, exactly
-// (v_cvt_scalef32_pk_bf16_fp8 with scale 1 decodes two codes per instruction;
-// an e4m3 value has at most 4 significant bits and an exponent well inside
-// the bf16 range).
-__device__ __forceinline__ bf16x4 e4m3x4_to_bf16(unsigned raw) {
-  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw, 1.0f, false);  // bytes 0, 1
-  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw, 1.0f, true);   // bytes 2, 3
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
-}
-
-__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 raw) {
-  return __builtin_shufflevector(e4m3x4_to_bf16(raw[0]), e4m3x4_to_bf16(raw[1]), 0, 1, 2, 3, 4,
-                                 5, 6, 7);
-}
 
 // Byte offsets of the K-operand read of an FP8 tile (16 rows of D codes; the
 // 16-byte chunk c of row r is stored at c ^ (r & 15), within the row's D / 16
@@ -118,35 +97,6 @@ __device__ __forceinline__ void issue_scales(const float* kv_scale, const int* s
   const int p = p0 + (lane & 15);
   const int grow = sidx[p < n ? p : n - 1];
   dma_4B(kv_scale + grow, __builtin_amdgcn_readfirstlane(lds_addr(sc)));
-}
-
-// softmax_tile with fp32 weights: pf[j] = 2^(x[j] - m), unrounded, for the
-// caller to scale by its row's FP8 scale before rounding to bf16; lpart sums
-// them.  Reference maximum, its headroom and the second-pass flag as in
-// softmax_tile.
-template <int R>
-__device__ __forceinline__ bool softmax_tile_f32(const float (&x)[R], float sink_l2, int g,
-                                                 bool& first, float& m, float& mtrue,
-                                                 float& lpart, float (&pf)[R]) {
-  float mx = x[0];
-#pragma unroll
-  for (int j = 1; j < R; ++j) mx = fmaxf(mx, x[j]);
-  mx = group_max4(mx);
-  mtrue = fmaxf(mtrue, mx);
-  if (first) {
-    m = fmaxf(sink_l2, mx);
-    lpart = (g == 0 && sink_l2 > -INFINITY) ? __builtin_amdgcn_exp2f(sink_l2 - m) : 0.f;
-    first = false;
-  }
-  const bool over = __builtin_amdgcn_ballot_w64(mx > m + kRaise) != 0;
-  float psum = 0.f;
-#pragma unroll
-  for (int j = 0; j < R; ++j) {
-    pf[j] = __builtin_amdgcn_exp2f(x[j] - m);
-    psum += pf[j];
-  }
-  lpart += psum;
-  return over;
 }
 
 template <int D>
@@ -399,56 +349,10 @@ __global__ void __launch_bounds__(256) attn_rows_fp8_kernel(AttnArgs a) {
 // the bf16 pool; no split-L).  Per wave and tile, S^T = K Q^T on 16x16x32
 // MFMAs (K operand: one ds_read_b64 of 8 codes per k-step and 16-row half,
 // shared by both head blocks) and O^T += V^T P^T on 32x32x16 MFMAs (V^T
-// operand: one ds_read_b64_tr_b8 per d-tile and half, laid out below); codes
+// operand: one ds_read_b64_tr_b8 per d-tile and half, fp8_device.h); codes
 // are decoded to bf16 in registers.  Each K and V^T code is read from LDS
 // once per 32 heads: a quarter of the LDS bytes per flop of the 16-head FP8
 // rows kernel.  The row scales multiply scores and weights as there.
-
-// Byte offsets of the 32x32x16 V^T operand reads of an FP8 tile (rows of D
-// codes; 16-byte chunk c of row r stored at c ^ (r & 15)).  Within each
-// 16-lane group the 8-bit transposing read gives destination lane i byte e
-// from source lane 2e + i/8, byte i % 8.  Source lane (G = lane / 16,
-// j = lane % 16) points at row 8 (G / 2) + j / 2, byte 8 (j % 2) of chunk
-// wide_vt_chunk(dt, G % 2); destination lane (G, i) then holds rows
-// 8 (G / 2) .. + 7 of that chunk's column i, the A operand of the product
-// (lane (d, kg): rows 8 kg .. 8 kg + 7 of column d of d-tile dt).  At D >= 256
-// d-tile dt is chunks a and a ^ 8 with a = dt % 8 + 16 (dt / 8): the 8 rows
-// of one group fall on 8 different 16-byte bank groups (the swizzle XORs the
-// low bits), and the two groups of a half-wave (chunks a and a ^ 8) on the
-// two other octets of the 16, so a half-wave's 256 bytes meet no conflict.
-// (Chunks 2 dt and 2 dt + 1, the columns in order, put both groups on the
-// same octet: two cycles a half-wave.)  At D = 128 the d-tiles stay 2 dt,
-// 2 dt + 1.  The output columns follow the same map.  Rows 16..31 add 16 D.
-template <int D>
-__device__ __forceinline__ constexpr int wide_vt_chunk(int dt, int half) {
-  return D >= 256 ? ((dt & 7) + 16 * (dt >> 3)) + 8 * half : 2 * dt + half;
-}
-
-template <int D>
-struct Fp8WideVtOffsets {
-  int base, x;
-  __device__ __forceinline__ explicit Fp8WideVtOffsets(int lane) {
-    const int G = lane >> 4, j = lane & 15;
-    const int row = 8 * (G >> 1) + (j >> 1);
-    const int sw = row_swizzle(row) & (D / 16 - 1);
-    base = row * D + 8 * (j & 1);
-    x = (wide_vt_chunk<D>(0, G & 1) - wide_vt_chunk<D>(0, 0)) ^ sw;  // chunk (a + h) ^ sw = a ^ x
-  }
-  __device__ __forceinline__ int at(int dt) const { return base + 16 * (wide_vt_chunk<D>(dt, 0) ^ x); }
-};
-
-// The K-operand reads of Fp8Offsets, computed per read: for k-step s the
-// address is base + 32 (s ^ x) (two VALU ops, no table in registers).
-template <int D>
-struct Fp8KOffsets {
-  int base, x;
-  __device__ __forceinline__ Fp8KOffsets(int n16, int g) {
-    const int w = (row_swizzle(n16) & (D / 16 - 1)) ^ (g >> 1);
-    base = n16 * D + 16 * (w & 1) + 8 * (g & 1);
-    x = w >> 1;
-  }
-  __device__ __forceinline__ int kq(int s) const { return base + 32 * (s ^ x); }
-};
 
 // Weight 2^(m - M) of a state with reference maximum m in a merge whose
 // maximum is M >= m; a state that saw no row (m = -inf) weighs exactly 0.
@@ -875,7 +779,10 @@ hipError_t launch_quant_d(const QuantArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_attention_fp8(const AttnArgs& a, int D, int wide_waves, hipStream_t stream) {
+hipError_t launch_attention_fp8(const AttnArgs& a, int D, const AttnPlan& plan,
+                                hipStream_t stream) {
+  if (plan.mode == kModeSplit) return launch_split(a, D, plan, true, stream);
+  const int wide_waves = plan.wide;
   switch (D) {
     case 64: return launch_fp8_d<64>(a, wide_waves, stream);
     case 128: return launch_fp8_d<128>(a, wide_waves, stream);

@@ -47,7 +47,7 @@
 // line an XCD's L2 kept from before the publishing stores.
 #include <atomic>
 
-#include "attn_device.h"
+#include "fp8_device.h"
 
 namespace spd {
 namespace {
@@ -65,8 +65,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const void* base) {
 }
 
 constexpr int kSc1 = 16;  // cache policy bit of an agent-scope coherent access
-
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void store_sc1(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kSc1);
@@ -109,12 +107,14 @@ struct Piece {
   static constexpr int kBytes = kOBytes + 2 * 32 * 4;
 };
 
-template <int D, int HB, int P>
+template <int D, int HB, int P, bool kFp8>
 __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
   constexpr int kWaves = 4;
   static_assert(HB * P == kWaves, "four waves: head blocks x parities");
+  static_assert(!kFp8 || D >= 128, "FP8 rows: D >= 128");
   constexpr int kHeads = 32 * HB;
-  constexpr int kRowBytes = 2 * D;
+  constexpr int kRowBytes = kFp8 ? D : 2 * D;  // a gathered row: D codes, or D bf16
+  constexpr int kQRowBytes = 2 * D;            // a row of q (bf16)
   constexpr int kSuper = 16 * P;  // rows per super-tile
   constexpr int kStageBytes = kSuper * kRowBytes;
   constexpr int kKSteps = D / 32;
@@ -123,28 +123,35 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
   constexpr int kRowsPerLoad = 1024 / kRowBytes;
   constexpr int kLoadsPerStage = kSuper / kRowsPerLoad;
   constexpr int kLoadsPerWave = kLoadsPerStage / kWaves;
+  constexpr int kRowsPerWave = kSuper / kWaves;  // rows (and FP8 scales) a wave loads
+  constexpr int kPerTile = kLoadsPerWave + (kFp8 ? 1 : 0);  // with the scales' load
   constexpr int kRing = 128 * 1024;
-  // stages of the ring: what kRing holds, at most 4, and no more loads in
-  // flight per wave than the 6-bit vmcnt counts
-  constexpr int kFit = kRing / kStageBytes < 4 ? kRing / kStageBytes : 4;
-  constexpr int kCount = 63 / kLoadsPerWave;
+  // stages of the ring: what kRing holds, at most 4 bf16 or 8 FP8 super-tiles
+  // (the same bytes), and no more loads in flight per wave than the 6-bit
+  // vmcnt counts
+  constexpr int kMaxStages = kFp8 ? 8 : 4;
+  constexpr int kFit = kRing / kStageBytes < kMaxStages ? kRing / kStageBytes : kMaxStages;
+  constexpr int kCount = 63 / kPerTile;
   constexpr int kStages0 = kFit < kCount ? kFit : kCount;
   constexpr int kStages = kStages0 < 2 ? 2 : kStages0;
   using Pc = Piece<D, P>;
   // LDS read lead of the QK (k-steps) and PV (d-tiles) loops
   constexpr int kKA = 2, kVA = 2;
-  // super-tiles in flight when the loop starts
-  constexpr int kBurst = 2 < kStages ? 2 : kStages;
+  // super-tiles in flight when the loop starts (FP8: twice as many, the same bytes)
+  constexpr int kBurstWant = kFp8 ? 4 : 2;
+  constexpr int kBurst = kBurstWant < kStages ? kBurstWant : kStages;
   static_assert(D % 64 == 0 && D <= 512, "unsupported D");
   static_assert(kDTw >= 1, "a piece holds at least one d-tile");
   static_assert(kLoadsPerStage % kWaves == 0, "loads must divide among waves");
-  static_assert(kStages * kLoadsPerWave <= 63, "outstanding loads must fit vmcnt");
+  static_assert(kStages * kPerTile <= 63, "outstanding loads must fit vmcnt");
+  static_assert(kBurst <= 4, "wait_outstanding counts up to three later super-tiles");
   static_assert(P == 1 || kStages * kStageBytes >= kWaves * (kDT / 2) * 64 * 64,
                 "the parity exchange reuses the ring");
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
   __shared__ __attribute__((aligned(256))) int sidx[kSplitIdx];
   __shared__ __attribute__((aligned(256))) float ssink[64];
+  __shared__ __attribute__((aligned(256))) float sscale[kFp8 ? kStages : 1][kWaves][64];
   __shared__ float sml[kWaves][4][16];  // per wave: m0, m1, l0, l1 of its 32 heads
   __shared__ int sflag[kWaves];
 
@@ -171,7 +178,7 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
   // stages are handed back to the row tiles; rows of heads past H repeat a
   // valid row.  Its loads go out first, with the sinks: neither depends on the
   // slice, so their latency overlaps the kv_indptr and index round trips.
-  constexpr int kQBytes = kHeads * kRowBytes;
+  constexpr int kQBytes = kHeads * kQRowBytes;
   constexpr int kQStages = (kQBytes + kStageBytes - 1) / kStageBytes;
   static_assert(kQStages < kStages, "q staging must leave a stage for the first tiles");
   constexpr int kQLoads = kQBytes / 1024;
@@ -179,8 +186,8 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
   constexpr int kQLoadsPerWave = kQLoads / kWaves;
   unsigned char* sq = smem + (kStages - kQStages) * kStageBytes;
   {
-    constexpr int kRowsPerLd = 1024 / kRowBytes;
-    constexpr int kChunksQ = kRowBytes / 16;
+    constexpr int kRowsPerLd = 1024 / kQRowBytes;
+    constexpr int kChunksQ = kQRowBytes / 16;
     const unsigned char* qb = reinterpret_cast<const unsigned char*>(a.q);
     const int64_t qrow0 = (int64_t)t * a.H + hg * kHeads;
 #pragma unroll
@@ -189,7 +196,7 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
       const int r = ld * kRowsPerLd + lane / kChunksQ;  // head row within the group
       const int hr = hg * kHeads + r < a.H ? r : 0;
       const int chunk = (lane % kChunksQ) ^ (row_swizzle(r) & (kChunksQ - 1));
-      dma_16B(qb + ((qrow0 + hr) * kRowBytes + chunk * 16),
+      dma_16B(qb + ((qrow0 + hr) * kQRowBytes + chunk * 16),
               __builtin_amdgcn_readfirstlane(lds_addr(sq + ld * 1024)));
     }
     if (wave == 0) {
@@ -213,17 +220,39 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
   const int nrows = (c == nparts - 1) ? L - cb : a.split_rows;
   const int32_t* part = a.kv_indices + row0 + cb;
 
+  // LDS read offsets of the K and V^T operands: bf16 tiles in the wide
+  // swizzle, FP8 tiles in the row swizzle (one set is dead code)
   const TileOffsets<D, 1> off(n16, g);
   const WideVtOffsets<D> voff(lane);
+  const Fp8KOffsets<D> off8(n16, g);
+  const Fp8WideVtOffsets<D> voff8(lane);
 
   // wait until at most `tiles` (< kStages) later super-tiles of this wave are in flight
   auto wait_outstanding = [](int tiles) {
     constexpr int k2 = kStages > 2 ? 2 : 1, k3 = kStages > 3 ? 3 : k2;
     switch (tiles) {
       case 0: wait_vmcnt<0>(); break;
-      case 1: wait_vmcnt<kLoadsPerWave>(); break;
-      case 2: wait_vmcnt<k2 * kLoadsPerWave>(); break;
-      default: wait_vmcnt<k3 * kLoadsPerWave>(); break;
+      case 1: wait_vmcnt<kPerTile>(); break;
+      case 2: wait_vmcnt<k2 * kPerTile>(); break;
+      default: wait_vmcnt<k3 * kPerTile>(); break;
+    }
+  };
+
+  // This wave's rows of super-tile `tile` of a chunk of n staged indices;
+  // FP8: then their scales (lane l loads the scale of row l % kRowsPerWave of
+  // the wave's part; positions past n repeat the last row).
+  auto issue_super = [&](int n, int tile) {
+    const int p0 = tile * kSuper + wave * kRowsPerWave;
+    unsigned char* dst = smem + (tile % kStages) * kStageBytes + wave * kLoadsPerWave * 1024;
+    if constexpr (kFp8) {
+      issue_rows<kRowBytes, kLoadsPerWave>(reinterpret_cast<const uint16_t*>(a.kv8), sidx, n, p0,
+                                           wave * kRowsPerWave, dst, lane);
+      const int p = p0 + lane % kRowsPerWave;
+      const int grow = sidx[p < n ? p : n - 1];
+      dma_4B(a.kv_scale + grow,
+             __builtin_amdgcn_readfirstlane(lds_addr(sscale[tile % (kFp8 ? kStages : 1)][wave])));
+    } else {
+      issue_rows<kRowBytes, kLoadsPerWave, 1>(a.kv, sidx, n, p0, wave * kRowsPerWave, dst, lane);
     }
   };
 
@@ -233,11 +262,7 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
   const int ntiles0 = (n0 + kSuper - 1) / kSuper;
   const int burst0 = ntiles0 < kBurst ? ntiles0 : kBurst;  // tiles in flight before the loop
   const int pre = burst0 < kStages - kQStages ? burst0 : kStages - kQStages;
-  auto issue_tile0 = [&](int tile) {
-    issue_rows<kRowBytes, kLoadsPerWave, 1>(
-        a.kv, sidx, n0, tile * kSuper + wave * (kSuper / kWaves), wave * (kSuper / kWaves),
-        smem + (tile % kStages) * kStageBytes + wave * kLoadsPerWave * 1024, lane);
-  };
+  auto issue_tile0 = [&](int tile) { issue_super(n0, tile); };
   stage_indices(part, 0, n0, sidx, wave, kWaves, lane);
   wait_vmcnt<0>();
   barrier_lds();
@@ -247,13 +272,13 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
     // lane (n16, g) of the k-step u operand holds q[h, 32 u + 8 g .. +7]:
     // logical chunk 4 u + g of head row h, stored at chunk ^ swizzle(h)
     const int r0 = hb * 32 + n16, r1 = r0 + 16;
-    constexpr int kChunksQ = kRowBytes / 16;
+    constexpr int kChunksQ = kQRowBytes / 16;
     const int sw = row_swizzle(n16) & (kChunksQ - 1);  // r0 & 15 == r1 & 15 == n16
 #pragma unroll
     for (int u = 0; u < kKSteps; ++u) {
       const int ch = ((4 * u + g) ^ sw) * 16;
-      q0[u] = *reinterpret_cast<const bf16x8*>(sq + r0 * kRowBytes + ch);
-      q1[u] = *reinterpret_cast<const bf16x8*>(sq + r1 * kRowBytes + ch);
+      q0[u] = *reinterpret_cast<const bf16x8*>(sq + r0 * kQRowBytes + ch);
+      q1[u] = *reinterpret_cast<const bf16x8*>(sq + r1 * kQRowBytes + ch);
     }
     barrier_lds();  // every wave has its q: the stages go back to the tiles
     for (int k = pre; k < burst0; ++k) issue_tile0(k);
@@ -286,11 +311,7 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
       }
       const int ntiles = (n + kSuper - 1) / kSuper;
 
-      auto issue_tile = [&](int tile) {
-        issue_rows<kRowBytes, kLoadsPerWave, 1>(
-            a.kv, sidx, n, tile * kSuper + wave * (kSuper / kWaves), wave * (kSuper / kWaves),
-            smem + (tile % kStages) * kStageBytes + wave * kLoadsPerWave * 1024, lane);
-      };
+      auto issue_tile = [&](int tile) { issue_super(n, tile); };
       const int first_burst = ntiles < kBurst ? ntiles : kBurst;
       if (sc > 0 || pass > 0)  // the first chunk's burst went out in the prologue
         for (int k = 0; k < first_burst; ++k) issue_tile(k);
@@ -312,78 +333,143 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
         asm volatile("" : "+v"(stoff));
         const unsigned char* st = smem + stoff;
 
-        // S^T = K Q^T for both head blocks; the K reads run kKA k-steps ahead
-        // of the MFMAs that consume them (one read issued after each step's
-        // MFMA pair), two chains per block.
-        bf16x8 ka[kKSteps];
-        f32x4 s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
+        if constexpr (kFp8) {
+          // S^T = K Q^T for both head blocks over codes: per k-step the code
+          // read of step u + kKA, the exact decode of step u and its two
+          // MFMAs (a fence per step keeps kKA + 1 steps of codes live)
+          u32x2 ra[kKSteps];
+          f32x4 s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
 #pragma unroll
-        for (int u = 0; u < kKA && u < kKSteps; ++u) ka[u] = *reinterpret_cast<const bf16x8*>(st + off.kq(u));
-#pragma unroll
-        for (int u = 0; u < kKSteps; ++u) {
-          if (u & 1) {
-            s0b = mfma_k32(ka[u], q0[u], s0b);
-            s1b = mfma_k32(ka[u], q1[u], s1b);
-          } else {
-            s0a = mfma_k32(ka[u], q0[u], s0a);
-            s1a = mfma_k32(ka[u], q1[u], s1a);
-          }
-          if (u + kKA < kKSteps) ka[u + kKA] = *reinterpret_cast<const bf16x8*>(st + off.kq(u + kKA));
-        }
-        {
-          constexpr int kPre = kKA < kKSteps ? kKA : kKSteps;
-          __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+          for (int u = 0; u < kKA && u < kKSteps; ++u) ra[u] = *reinterpret_cast<const u32x2*>(st + off8.kq(u));
 #pragma unroll
           for (int u = 0; u < kKSteps; ++u) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            if (u + kPre < kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (u + kKA < kKSteps) ra[u + kKA] = *reinterpret_cast<const u32x2*>(st + off8.kq(u + kKA));
+            const bf16x8 ka = e4m3x8_to_bf16(ra[u]);
+            if (u & 1) {
+              s0b = mfma_k32(ka, q0[u], s0b);
+              s1b = mfma_k32(ka, q1[u], s1b);
+            } else {
+              s0a = mfma_k32(ka, q0[u], s0a);
+              s1a = mfma_k32(ka, q1[u], s1a);
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        const f32x4 s0 = s0a + s0b, s1 = s1a + s1b;
+          const f32x4 s0 = s0a + s0b, s1 = s1a + s1b;
 
-        float x0[4], x1[4];
+          // the scales of this lane's rows 16 par + 4 g .. + 3 (row r of the
+          // super-tile was loaded by wave r / kRowsPerWave into its entry
+          // r % kRowsPerWave); they multiply the scores, and the weights
+          // before these are rounded to bf16
+          const int r0 = 16 * par + 4 * g;
+          const f32x4 c0 = *reinterpret_cast<const f32x4*>(
+              &sscale[i % (kFp8 ? kStages : 1)][r0 / kRowsPerWave][r0 % kRowsPerWave]);
+          float x0[4], x1[4];
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const bool v = 4 * g + i4 < nvalid;
-          x0[i4] = v ? s0[i4] * a.qk_scale : -INFINITY;
-          x1[i4] = v ? s1[i4] * a.qk_scale : -INFINITY;
-        }
-        __bf16 p0[4], p1[4];
-        over |= softmax_tile<4>(x0, sk0, g, first0, m0, mt0, l0, p0);
-        over |= softmax_tile<4>(x1, sk1, g, first1, m1, mt1, l1, p1);
-        bf16x4 pa, pbk;
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const bool v = 4 * g + i4 < nvalid;
+            x0[i4] = v ? s0[i4] * (a.qk_scale * c0[i4]) : -INFINITY;
+            x1[i4] = v ? s1[i4] * (a.qk_scale * c0[i4]) : -INFINITY;
+          }
+          float pf0[4], pf1[4];
+          over |= softmax_tile_f32<4>(x0, sk0, g, first0, m0, mt0, l0, pf0);
+          over |= softmax_tile_f32<4>(x1, sk1, g, first1, m1, mt1, l1, pf1);
+          bf16x4 pa, pbk;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pa[e] = p0[e];
-          pbk[e] = p1[e];
-        }
-        const bf16x8 pb = wide_p_operand(pa, pbk);
+          for (int e = 0; e < 4; ++e) {
+            pa[e] = (__bf16)(pf0[e] * c0[e]);
+            pbk[e] = (__bf16)(pf1[e] * c0[e]);
+          }
+          const bf16x8 pb = wide_p_operand(pa, pbk);
 
-        // O^T += V^T P^T over the 16 rows: the two transposing reads of d-tile
-        // u + kVA run under the MFMA of d-tile u.
-        {
-          bf16x8 va[kDT];
+          // O^T += V^T P^T over the 16 rows: the 8-bit transposing read of
+          // d-tile u + kVA, the decode of d-tile u and its MFMA
+          u32x2 va[kDT];
           auto read_vt = [&](int u) {
-            const bf16x4 vl = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + voff.at(u, 0)));
-            const bf16x4 vh = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + voff.at(u, 1)));
-            va[u] = __builtin_shufflevector(vl, vh, 0, 1, 2, 3, 4, 5, 6, 7);
+            va[u] = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((LdsV2i32*)(st + voff8.at(u))));
           };
 #pragma unroll
           for (int u = 0; u < kVA && u < kDT; ++u) read_vt(u);
 #pragma unroll
           for (int u = 0; u < kDT; ++u) {
-            acc[u] = mfma32(va[u], pb, acc[u]);
             if (u + kVA < kDT) read_vt(u + kVA);
+            acc[u] = mfma32(e4m3x8_to_bf16(va[u]), pb, acc[u]);
+            __builtin_amdgcn_sched_barrier(0);
           }
-          constexpr int kPre = kVA < kDT ? kVA : kDT;
-          __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre, 0);
+        } else {
+          // S^T = K Q^T for both head blocks; the K reads run kKA k-steps ahead
+          // of the MFMAs that consume them (one read issued after each step's
+          // MFMA pair), two chains per block.
+          bf16x8 ka[kKSteps];
+          f32x4 s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
 #pragma unroll
-          for (int u = 0; u < kDT; ++u) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (u + kPre < kDT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          for (int u = 0; u < kKA && u < kKSteps; ++u) ka[u] = *reinterpret_cast<const bf16x8*>(st + off.kq(u));
+#pragma unroll
+          for (int u = 0; u < kKSteps; ++u) {
+            if (u & 1) {
+              s0b = mfma_k32(ka[u], q0[u], s0b);
+              s1b = mfma_k32(ka[u], q1[u], s1b);
+            } else {
+              s0a = mfma_k32(ka[u], q0[u], s0a);
+              s1a = mfma_k32(ka[u], q1[u], s1a);
+            }
+            if (u + kKA < kKSteps) ka[u + kKA] = *reinterpret_cast<const bf16x8*>(st + off.kq(u + kKA));
           }
-          __builtin_amdgcn_sched_barrier(0);
+          {
+            constexpr int kPre = kKA < kKSteps ? kKA : kKSteps;
+            __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+#pragma unroll
+            for (int u = 0; u < kKSteps; ++u) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+              if (u + kPre < kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          const f32x4 s0 = s0a + s0b, s1 = s1a + s1b;
+
+          float x0[4], x1[4];
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const bool v = 4 * g + i4 < nvalid;
+            x0[i4] = v ? s0[i4] * a.qk_scale : -INFINITY;
+            x1[i4] = v ? s1[i4] * a.qk_scale : -INFINITY;
+          }
+          __bf16 p0[4], p1[4];
+          over |= softmax_tile<4>(x0, sk0, g, first0, m0, mt0, l0, p0);
+          over |= softmax_tile<4>(x1, sk1, g, first1, m1, mt1, l1, p1);
+          bf16x4 pa, pbk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pa[e] = p0[e];
+            pbk[e] = p1[e];
+          }
+          const bf16x8 pb = wide_p_operand(pa, pbk);
+
+          // O^T += V^T P^T over the 16 rows: the two transposing reads of d-tile
+          // u + kVA run under the MFMA of d-tile u.
+          {
+            bf16x8 va[kDT];
+            auto read_vt = [&](int u) {
+              const bf16x4 vl = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + voff.at(u, 0)));
+              const bf16x4 vh = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsBf16x4*)(st + voff.at(u, 1)));
+              va[u] = __builtin_shufflevector(vl, vh, 0, 1, 2, 3, 4, 5, 6, 7);
+            };
+#pragma unroll
+            for (int u = 0; u < kVA && u < kDT; ++u) read_vt(u);
+#pragma unroll
+            for (int u = 0; u < kDT; ++u) {
+              acc[u] = mfma32(va[u], pb, acc[u]);
+              if (u + kVA < kDT) read_vt(u + kVA);
+            }
+            constexpr int kPre = kVA < kDT ? kVA : kDT;
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre, 0);
+#pragma unroll
+            for (int u = 0; u < kDT; ++u) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              if (u + kPre < kDT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
     }
@@ -392,10 +478,18 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
 
   // This wave's states: head n16 of block 0 (m0, l0) and of block 1 (m1, l1);
   // m is -inf for a parity that saw no row.  Accumulator layout: lane
-  // (n = lane % 32, hf = lane / 32) holds, for head h0 + n, d = 32 dt + 8 e4 +
-  // 4 hf + e as element 4 e4 + e of acc[dt]; head h0 + n is head n % 16 =
+  // (n = lane % 32, hf = lane / 32) holds, for head h0 + n, d = out_col(dt,
+  // e4) + 4 hf + e as element 4 e4 + e of acc[dt]; head h0 + n is head n % 16 =
   // lane % 16 of block n / 16, whose softmax state this lane holds too.
   const int n = lane & 31, hf = lane >> 5;
+  // bf16 rows: the columns in order; FP8 rows: the 16-column chunks in the
+  // order of the transposing reads (wide_vt_chunk)
+  auto out_col = [](int dt, int e4) {
+    if constexpr (kFp8)
+      return 16 * wide_vt_chunk<D>(dt, e4 >> 1) + 8 * (e4 & 1);
+    else
+      return 32 * dt + 8 * e4;
+  };
   float lb0 = group_sum4(l0), lb1 = group_sum4(l1);
 
   // Merge the P parity states of head block hb in LDS: a butterfly over the
@@ -484,11 +578,11 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
     // out = O / l for heads h0 + n, d-tiles [lo, lo + kDTw)
     if (h0 + n < a.H) {
       const float inv = 1.0f / (n < 16 ? lb0 : lb1);
-      uint16_t* op = a.out + ((int64_t)t * a.H + h0 + n) * D + 4 * hf + 32 * lo;
+      uint16_t* op = a.out + ((int64_t)t * a.H + h0 + n) * D + 4 * hf;
 #pragma unroll
       for (int i = 0; i < kDTw; ++i)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) store_bf16x4(op + 32 * i + 8 * e4, quarter(acc[i], e4), inv);
+        for (int e4 = 0; e4 < 4; ++e4) store_bf16x4(op + out_col(lo + i, e4), quarter(acc[i], e4), inv);
     }
     return;
   }
@@ -610,11 +704,12 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
     const int hw0 = hg * kHeads + (w / P) * 32;  // first head of piece w
     if (hw0 + n < a.H) {
       const float inv = 1.0f / (n < 16 ? ls0 : ls1);
-      uint16_t* op = a.out + ((int64_t)t * a.H + hw0 + n) * D + 4 * hf + 32 * (piece_lo(w % P) + i0);
+      uint16_t* op = a.out + ((int64_t)t * a.H + hw0 + n) * D + 4 * hf;
+      const int dt0 = piece_lo(w % P) + i0;
 #pragma unroll
       for (int i = 0; i < kNi; ++i)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) store_bf16x4(op + 32 * i + 8 * e4, quarter(tot[i], e4), inv);
+        for (int e4 = 0; e4 < 4; ++e4) store_bf16x4(op + out_col(dt0 + i, e4), quarter(tot[i], e4), inv);
     }
   };
 
@@ -692,23 +787,23 @@ int device_cus() {
   return n;
 }
 
-template <int D, int HB, int P>
+template <int D, int HB, int P, bool kFp8>
 hipError_t launch_split_d(const AttnArgs& a0, hipStream_t stream) {
   const long long items = (long long)a0.N * a0.head_groups * a0.splits;
   AttnArgs a = a0;
   // one workgroup per CU (the LDS ring and 512 registers a wave): the grid is
   // resident at once when it has no more workgroups than CUs
   a.split_wait = items <= device_cus() ? 1 : 0;
-  hipLaunchKernelGGL((attn_split_kernel<D, HB, P>), dim3((unsigned)items), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((attn_split_kernel<D, HB, P, kFp8>), dim3((unsigned)items), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool kFp8>
 hipError_t launch_split_shape(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
   const int hb = p.heads_per_group / 32;
-  if (hb == 2 && p.parities == 2) return launch_split_d<D, 2, 2>(a, stream);
+  if (hb == 2 && p.parities == 2) return launch_split_d<D, 2, 2, kFp8>(a, stream);
   if constexpr (D >= 128) {
-    if (hb == 1 && p.parities == 4) return launch_split_d<D, 1, 4>(a, stream);
+    if (hb == 1 && p.parities == 4) return launch_split_d<D, 1, 4, kFp8>(a, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -724,12 +819,20 @@ size_t split_workspace_bytes(int32_t N, int32_t D, const AttnPlan& p) {
   return split_counters_offset(N, D, p) + (size_t)N * p.head_groups * 4 * sizeof(int);
 }
 
-hipError_t launch_split(const AttnArgs& a, int D, const AttnPlan& p, hipStream_t stream) {
+hipError_t launch_split(const AttnArgs& a, int D, const AttnPlan& p, bool fp8, hipStream_t stream) {
+  if (fp8) {
+    switch (D) {
+      case 128: return launch_split_shape<128, true>(a, p, stream);
+      case 256: return launch_split_shape<256, true>(a, p, stream);
+      case 512: return launch_split_shape<512, true>(a, p, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (D) {
-    case 64: return launch_split_shape<64>(a, p, stream);
-    case 128: return launch_split_shape<128>(a, p, stream);
-    case 256: return launch_split_shape<256>(a, p, stream);
-    case 512: return launch_split_shape<512>(a, p, stream);
+    case 64: return launch_split_shape<64, false>(a, p, stream);
+    case 128: return launch_split_shape<128, false>(a, p, stream);
+    case 256: return launch_split_shape<256, false>(a, p, stream);
+    case 512: return launch_split_shape<512, false>(a, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -22,10 +22,11 @@ struct AttnPlan {
   int waves;           // waves per workgroup
   int heads_per_group; // heads per workgroup
   int head_groups;     // ceil(H / heads_per_group)
-  int wide;            // heads mode with 32-head waves (attn_wide_kernel)
+  int wide;            // heads mode with 32-head waves (attn_wide_kernel); FP8 plans:
+                       // the wide_waves of launch_attention_fp8 (0, 2, 3 or 4)
   int splits;          // partitions of a slice (1 = no split-L)
   int split_rows;      // rows per partition (multiple of 32); huge when splits == 1
-  int parities;        // split mode: waves per head block (1 or 2)
+  int parities;        // split mode: waves per head block (2 or 4); 1 otherwise
   size_t workspace_bytes;
 };
 
@@ -33,6 +34,12 @@ bool attn_supported(int32_t H, int32_t D);
 // Returns false when the arguments cannot form a plan.
 bool make_attn_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t split_rows,
                     int32_t mode, AttnPlan* plan);
+// Plan of an attention call over an FP8 pool: split mode as make_attn_plan
+// chooses it (D >= 128), else rows mode or one of the 32-head-wave
+// decompositions (plan->wide).  mode: kModeAuto, kModeRows, kModeWide or
+// kModeSplit.  False when the arguments cannot form a plan.
+bool make_fp8_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t split_rows,
+                   int32_t mode, AttnPlan* plan);
 
 struct AttnArgs {
   const uint16_t* q;         // [N][H][D] bf16 bits
@@ -87,15 +94,18 @@ size_t split_workspace_bytes(int32_t N, int32_t D, const AttnPlan& plan);
 // Offset of the arrival counters in that workspace (N * head_groups * 4 int32
 // from there to its end).
 size_t split_counters_offset(int32_t N, int32_t D, const AttnPlan& plan);
-hipError_t launch_split(const AttnArgs& args, int D, const AttnPlan& plan, hipStream_t stream);
+// fp8: the rows are args.kv8 / args.kv_scale (D >= 128), else args.kv.
+hipError_t launch_split(const AttnArgs& args, int D, const AttnPlan& plan, bool fp8,
+                        hipStream_t stream);
 
-// Attention over an FP8 pool: rows mode (workgroup = token x 16 heads), no
-// split; args.kv8 / args.kv_scale replace args.kv.
-// wide_waves: 0 = rows decomposition (16-head waves); 2 or 4 = workgroups of
-// 32 * wide_waves heads on 32-head waves (H % (32 * wide_waves) == 0, D >= 128);
-// 3 = workgroups of 64 heads on four 32-head waves, two parities of each head
-// block (H % 64 == 0, D >= 128)
-hipError_t launch_attention_fp8(const AttnArgs& args, int D, int wide_waves, hipStream_t stream);
+// Attention over an FP8 pool (args.kv8 / args.kv_scale replace args.kv), in
+// the plan of make_fp8_plan: split mode (attn_split.hip), or no split with
+// plan.wide = 0: rows decomposition (workgroup = token x 16 heads); 2 or 4:
+// workgroups of 32 * wide heads on 32-head waves (H % (32 * wide) == 0,
+// D >= 128); 3: workgroups of 64 heads on four 32-head waves, two parities of
+// each head block (H % 64 == 0, D >= 128).
+hipError_t launch_attention_fp8(const AttnArgs& args, int D, const AttnPlan& plan,
+                                hipStream_t stream);
 
 // Shared-window prefill: 32-head waves, two or four per workgroup
 // (tokens_per_group x H = 64 or 128 query rows), no split.

@@ -73,7 +73,7 @@ def test_binding_lists_the_same_symbols():
 def test_status_strings(lib):
     assert lib.spd_status_string(0) == b"SPD_OK"
     assert lib.spd_status_string(3) == b"SPD_ERR_WORKSPACE"
-    assert lib.spd_version() >= 200
+    assert lib.spd_version() >= 300
 
 
 @pytest.mark.parametrize("H,D,ok", [(64, 512, 1), (128, 512, 1), (8, 64, 1), (1, 128, 1),
@@ -236,6 +236,75 @@ def test_fp8_attn_rejects_bad_arguments(lib):
     assert _fp8(lib, out=FAKE) == INVALID               # out overlaps q (both at FAKE)
     assert _fp8(lib, out=FAKE * 8192) == INVALID        # out overlaps the scales
     assert _fp8(lib, rows=1 << 41) == INVALID
+
+
+def test_fp8_plans_and_ex_checks(lib):
+    """The FP8 pool's plans (host only): split mode for small batches of long
+    slices as for the bf16 pool, the 32-head-wave decompositions by batch
+    size, and the mode, shape and workspace checks of sparse_decode_attn_fp8_ex."""
+    P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.sparse_decode_attn_fp8_ex.argtypes = [P, P, P, ctypes.c_int64, P, P, P, ctypes.c_float, P,
+                                              i32, i32, i32, i32, i32, i32, P, sz, P]
+    lib.sparse_decode_attn_fp8_workspace_size.argtypes = [i32] * 6
+    lib.sparse_decode_attn_fp8_workspace_size.restype = sz
+    lib.sparse_decode_attn_fp8_plan_info.argtypes = [i32] * 6 + [ctypes.POINTER(ctypes.c_int32)]
+    AUTO, HEADS, ROWS, WIDE, SPLIT = 0, 1, 2, 3, 4
+
+    def info(N, H, D, max_len=0, split=0, mode=AUTO):
+        out = (ctypes.c_int32 * 7)()
+        st = lib.sparse_decode_attn_fp8_plan_info(N, H, D, max_len, split, mode, out)
+        return st, list(out)
+
+    # 8 tokens of 8192 rows: split mode, 64 heads a workgroup, 32 partitions
+    # of 256 rows; the same workspace layout as the bf16 pool's split mode
+    st, i = info(8, 64, 512, 8192)
+    assert st == OK and i == [SPLIT, 64, 1, 32, 256, 0, 2]
+    assert lib.sparse_decode_attn_fp8_workspace_size(8, 64, 512, 8192, 0, AUTO) == \
+        lib.sparse_decode_attn_workspace_size(8, 64, 512, 8192, 0, AUTO) == \
+        8 * 32 * 4 * (32 * 256 * 4 + 2 * 32 * 4) + 8 * 4 * 4
+    assert info(8, 32, 256, 8192)[1][:7] == [SPLIT, 32, 1, 32, 256, 0, 4]
+    # no capacity bound, or slices under 2048 rows: no split
+    assert info(8, 64, 512)[1][0] == ROWS
+    assert info(64, 64, 512, 640)[1][0] == ROWS
+    assert info(8, 64, 64, 8192)[1][0] == ROWS            # D = 64: no FP8 split kernel
+    # the batch sizes of the 32-head-wave decompositions
+    assert info(1024, 128, 512, 640)[1][:6] == [HEADS, 128, 1, 1, 1 << 30, 4]
+    assert info(8192, 64, 512, 640)[1][:6] == [HEADS, 64, 1, 1, 1 << 30, 2]
+    assert info(256, 64, 512, 2048)[1][:6] == [HEADS, 64, 1, 1, 1 << 30, 3]
+    assert info(255, 64, 512)[1][0] == ROWS
+    # explicit modes
+    assert info(8, 64, 512, 0, 0, WIDE)[1][5] == 2
+    assert info(8, 128, 512, 0, 0, WIDE)[1][5] == 4
+    assert info(64, 64, 512, 640, 0, ROWS)[1][0] == ROWS
+    assert info(64, 64, 512, 640, 0, SPLIT)[1][:4] == [SPLIT, 64, 1, 4]
+    assert info(8, 64, 512, 8192, 1024, AUTO)[1][:5] == [SPLIT, 64, 1, 8, 1024]  # split_rows: split
+    assert info(8, 64, 512, 0, 0, HEADS)[0] == UNSUPPORTED     # no FP8 heads kernel
+    assert info(8, 64, 64, 0, 0, SPLIT)[0] == UNSUPPORTED
+    assert info(8, 64, 64, 0, 0, WIDE)[0] == UNSUPPORTED
+    assert info(8, 40, 512, 0, 0, WIDE)[0] == UNSUPPORTED      # H % 64
+    assert info(8, 64, 512, 640, 64, ROWS)[0] == UNSUPPORTED
+    assert info(8, 64, 64, 640, 64, AUTO)[0] == UNSUPPORTED
+    assert info(8, 64, 512, 0, 0, 7)[0] == INVALID
+    assert info(8, 64, 512, 65536, 1024, SPLIT)[0] == INVALID  # over 32 partitions
+    assert lib.sparse_decode_attn_fp8_workspace_size(8, 64, 512, 0, 0, HEADS) == 0
+
+    def ex(N=8, H=64, D=512, max_len=8192, split=0, mode=AUTO, ws=None, ws_bytes=0, scale=0.1):
+        return lib.sparse_decode_attn_fp8_ex(FAKE, FAKE, FAKE * 8192, 100, FAKE, FAKE, FAKE, scale,
+                                             FAKE * 4096, N, H, D, max_len, split, mode, ws,
+                                             ws_bytes, None)
+    need = lib.sparse_decode_attn_fp8_workspace_size(8, 64, 512, 8192, 0, AUTO)
+    assert ex() == WORKSPACE
+    assert ex(ws=FAKE * 16384, ws_bytes=need - 1) == WORKSPACE
+    assert ex(ws=FAKE * 16384 + 8, ws_bytes=need) == INVALID    # workspace 16-byte aligned
+    assert ex(max_len=-1) == INVALID
+    assert ex(split=-1) == INVALID
+    assert ex(mode=7) == INVALID
+    assert ex(mode=HEADS) == UNSUPPORTED
+    assert ex(D=64, mode=SPLIT) == UNSUPPORTED
+    assert ex(mode=ROWS, split=64) == UNSUPPORTED
+    assert ex(H=40, mode=WIDE, max_len=0) == UNSUPPORTED
+    assert ex(scale=float("inf")) == INVALID
+    assert ex(N=0) == OK
 
 
 def _quant(lib, src=FAKE, slots=None, n=4, D=64, kv=FAKE * 4096, sc=FAKE * 8192, rows=100):

@@ -43,19 +43,26 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_fp8_kernel_name_follows_the_plan():
+    import sparse_paged_decode_ragged_amd as spd
+
+    def name(N, H, D, max_len=0):
+        return bench.fp8_kernel(spd.sparse_decode_attn_fp8_plan_info(N, H, D, max_len), D)
     # decode_base (H = 64): rows kernel; large (N = 1024, H = 128): one
     # 128-head workgroup per token fills the chip
-    assert bench.fp8_kernel(64, 64, 512) == "attn_rows_fp8_kernel<512>"
-    assert bench.fp8_kernel(1024, 128, 512) == "attn_wide_fp8_kernel<512,4>"
-    assert bench.fp8_kernel(255, 128, 512) == "attn_rows_fp8_kernel<512>"
-    assert bench.fp8_kernel(256, 128, 64) == "attn_rows_fp8_kernel<64>"
+    assert name(64, 64, 512, 640) == "attn_rows_fp8_kernel<512>"
+    assert name(1024, 128, 512, 640) == "attn_wide_fp8_kernel<512,4>"
+    assert name(255, 128, 512) == "attn_rows_fp8_kernel<512>"
+    assert name(256, 128, 64) == "attn_rows_fp8_kernel<64>"
     # H = 64: two 32-head waves a workgroup once there are two per CU; four
     # waves (two parities of each head block) when there is one per CU
-    assert bench.fp8_kernel(8192, 64, 512) == "attn_wide_fp8_kernel<512,2>"
-    assert bench.fp8_kernel(511, 64, 512) == "attn_wide_fp8_kernel<512,4,2>"
-    assert bench.fp8_kernel(256, 64, 512) == "attn_wide_fp8_kernel<512,4,2>"
-    assert bench.fp8_kernel(255, 64, 512) == "attn_rows_fp8_kernel<512>"
-    assert bench.fp8_kernel(256, 64, 64) == "attn_rows_fp8_kernel<64>"
+    assert name(8192, 64, 512, 640) == "attn_wide_fp8_kernel<512,2>"
+    assert name(511, 64, 512) == "attn_wide_fp8_kernel<512,4,2>"
+    assert name(256, 64, 512, 2048) == "attn_wide_fp8_kernel<512,4,2>"
+    assert name(255, 64, 512) == "attn_rows_fp8_kernel<512>"
+    assert name(256, 64, 64) == "attn_rows_fp8_kernel<64>"
+    # a small batch of long slices: split mode over codes
+    assert name(8, 64, 512, 8192) == "attn_split_kernel<512,2,2,true>"
+    assert name(8, 32, 256, 8192) == "attn_split_kernel<256,1,4,true>"
 
 
 def test_mfma_flops_hand_count():

@@ -347,3 +347,145 @@ def test_ragged_config_fp8(spd, device_data):
     w = W.ragged()
     log("case fp8 ragged: N=256, H=64, L up to 2048, 25 % empty")
     check_fp8_config(spd, w, w.kv_indices, w.kv_indptr, "fp8 ragged", chunk=64)
+
+
+# --- split mode over an FP8 pool: partitions of a slice merged inside the
+# kernel (64-head workgroups on two parities of each 32-head block, or
+# 32-head workgroups on four parities when H <= 32) ---
+
+SPLIT = 4
+# (H, D): 64 heads (one head group), 96 (two, the second half padding), 32
+# and 24 heads (32-head workgroups, four parities)
+SPLIT_SHAPES = [(64, 128), (64, 256), (64, 512), (96, 512), (32, 512), (24, 256), (32, 128)]
+
+
+def split_lengths(rng, n):
+    """Empty, one row, around the 32- and 64-row super-tiles and the
+    partition length, random, and one slice over the 1024 indices staged at a
+    time."""
+    L = rng.integers(0, 700, size=n)
+    L[:9] = [0, 1, 31, 32, 33, 95, 96, 97, 2300]
+    return L
+
+
+@pytest.mark.parametrize("H,D", SPLIT_SHAPES)
+def test_split_attention_matches_oracle(spd, H, D):
+    """Partitions of 96 rows (up to 24 of a slice) merged in-kernel: every
+    token against the oracle; a second call on the same workspace gives the
+    same bits (its arrival counters end every call at zero, and the merge
+    sums in partition order whatever the arrival order)."""
+    log("case fp8 split H=%d D=%d" % (H, D))
+    rng = np.random.default_rng(60 + H + D)
+    N, P = 12, 5000
+    lengths = split_lengths(rng, N)
+    _, codes, scales = fp8_pool(rng, P, D, zero_rows=rng.choice(P, size=20, replace=False))
+    idx, ptr = W.csr_from_lists([rng.integers(0, P, size=L) for L in lengths])
+    q_bits = W.normal_bf16(rng, (N, H, D))
+    sink = rng.standard_normal(H).astype(np.float32)
+    sink[3] = -np.inf
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    max_len = int(lengths.max())
+    plan = spd.sparse_decode_attn_fp8_plan_info(N, H, D, max_len, 96, SPLIT)
+    assert plan["mode"] == "split" and plan["splits"] == (max_len + 95) // 96
+    assert plan["parities"] == (4 if H <= 32 else 2)
+    q = to_dev_bits(q_bits)
+    kv8 = torch.from_numpy(codes).to(dev())
+    ksc = torch.from_numpy(scales).to(dev())
+    di, dp = device_csr(idx, ptr)
+    sk = torch.from_numpy(sink).to(dev())
+    need = spd.sparse_decode_attn_fp8_workspace_size(N, H, D, max_len, 96, SPLIT)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    outs = []
+    for _ in range(2):
+        outs.append(spd.sparse_decode_attn_fp8(q, kv8, ksc, di, dp, sk, scale, max_len=max_len,
+                                               split_rows=96, mode=SPLIT, workspace=ws))
+        torch.cuda.synchronize()
+    ref = oracle.sparse_decode_attn_fp8(q_bits, codes, scales, idx, ptr, sink, scale)
+    assert_close(bf16_to_f64(outs[0]), ref, "fp8 split H=%d D=%d" % (H, D))
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    empty = np.nonzero(np.diff(ptr) == 0)[0]
+    assert torch.all(outs[0][torch.from_numpy(empty).to(dev())].view(torch.int16) == 0)
+
+
+@pytest.mark.parametrize("H", [64, 32])
+def test_split_every_code_decodes_exactly(spd, H):
+    """Each slice is one row repeated 300 times (four partitions of 96 rows)
+    and there is no sink: every weight is exactly 1, so each partition's state
+    and their merge hold exact sums and the output is the row, scale *
+    e4m3(code), bit for bit (the rows hold every finite code)."""
+    log("case fp8 split every code H=%d" % H)
+    D, P = 512, 8
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    codes = np.stack([np.resize(np.roll(finite, 37 * r), D) for r in range(P)]).astype(np.uint8)
+    scales = (2.0 ** np.arange(-4, 4)).astype(np.float32)
+    idx, ptr = W.csr_from_lists([[r] * 300 for r in range(P)])
+    q_bits = W.normal_bf16(np.random.default_rng(8), (P, H, D))
+    sink = np.full(H, -np.inf, dtype=np.float32)
+    q = to_dev_bits(q_bits)
+    di, dp = device_csr(idx, ptr)
+    out = spd.sparse_decode_attn_fp8(q, torch.from_numpy(codes).to(dev()),
+                                     torch.from_numpy(scales).to(dev()), di, dp,
+                                     torch.from_numpy(sink).to(dev()), 0.05, max_len=300,
+                                     split_rows=96, mode=SPLIT)
+    torch.cuda.synchronize()
+    ref = np.stack([np.broadcast_to(np.array([oracle.e4m3_value(c) for c in codes[r]]) * scales[r],
+                                    (H, D)) for r in range(P)])
+    assert np.array_equal(bf16_to_f64(out), ref)
+
+
+def test_split_attention_second_pass(spd):
+    """Rows planted in late partitions of long slices score far above the
+    partitions' first tiles, so those partitions take the second pass; their
+    states then merge with partitions that did not."""
+    log("case fp8 split second pass")
+    rng = np.random.default_rng(13)
+    H, D, P = 64, 512, 6000
+    lengths = [300, 700, 40, 2100]
+    lists = [rng.choice(P, size=L, replace=False) for L in lengths]
+    idx, ptr = W.csr_from_lists(lists)
+    q_bits = W.normal_bf16(rng, (len(lengths), H, D))
+    q = W.bf16_to_f32(q_bits)
+    x = rng.standard_normal((P, D)).astype(np.float32)
+    for t, (p2, p1) in {0: (100, 290), 1: (150, 650), 3: (1000, 2090)}.items():
+        x[lists[t][p1]] = 4.0 * q[t, 0]            # score ~ 90 in log2 units
+        x[lists[t][p2]] = 3.9 * q[t, 0]            # about 2 lower
+    codes, scales = oracle.quantize_fp8(W.bf16_bits(x))
+    sink = rng.standard_normal(H).astype(np.float32)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    q = to_dev_bits(q_bits)
+    di, dp = device_csr(idx, ptr)
+    out = spd.sparse_decode_attn_fp8(q, torch.from_numpy(codes).to(dev()),
+                                     torch.from_numpy(scales).to(dev()), di, dp,
+                                     torch.from_numpy(sink).to(dev()), scale, max_len=2100,
+                                     split_rows=128, mode=SPLIT)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_decode_attn_fp8(q_bits, codes, scales, idx, ptr, sink, scale)
+    assert_close(bf16_to_f64(out), ref, "fp8 split second pass")
+
+
+def test_long_context_config_fp8(spd, device_data):
+    """The long-slice batch (N = 8 tokens of 8192 rows, H = 64, D = 512, a
+    2^20-row pool) over an FP8 pool in the launch configuration the benchmark
+    times: the automatic plan with max_len 8192 (split mode, 32 partitions),
+    every token against the oracle."""
+    w = W.long_context()
+    log("case fp8 long_context: N=%d, L=%d, automatic split plan" % (w.N, w.max_len))
+    plan = spd.sparse_decode_attn_fp8_plan_info(w.N, w.H, w.D, w.max_len)
+    assert plan["mode"] == "split" and plan["splits"] == 32
+    from gpu_helpers import device_inputs
+    q, kv, sink = device_inputs(w)
+    kv8 = torch.empty((w.P, w.D), dtype=torch.uint8, device=dev())
+    ksc = torch.empty(w.P, dtype=torch.float32, device=dev())
+    spd.quantize_kv_fp8(kv, kv8, ksc)
+    idx, ptr = device_csr(w.kv_indices, w.kv_indptr)
+    out = spd.sparse_decode_attn_fp8(q, kv8, ksc, idx, ptr, sink, w.softmax_scale,
+                                     max_len=w.max_len)
+    torch.cuda.synchronize()
+    allidx = w.kv_indices
+    uniq, inv = np.unique(allidx, return_inverse=True)
+    u = torch.from_numpy(uniq.astype(np.int64)).to(dev())
+    codes, scales = oracle.quantize_fp8(W.host_bits(kv[u]))
+    assert np.array_equal(kv8[u].cpu().numpy(), codes)
+    ref = oracle.sparse_decode_attn_fp8(W.host_bits(q), codes, scales, inv.astype(np.int32),
+                                        w.kv_indptr, w.attn_sink, w.softmax_scale)
+    assert_close(bf16_to_f64(out), ref, "fp8 long_context")
