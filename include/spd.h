@@ -114,8 +114,8 @@ SPD_API spd_status sparse_decode_attn(const void* q, const void* unified_kv, int
  *                   heads when H <= 32 and D >= 128 -- its 4 waves two (or
  *                   four) 16-row streams of each 32-head block; the
  *                   partitions of one (token, head group) are merged inside
- *                   the same kernel, by the workgroups that finish last
- *                   (no combine kernel).  Up to 32 partitions; the plan
+ *                   the same kernel, each partition merging a share of the
+ *                   columns (no combine kernel).  Up to 32 partitions; the plan
  *                   chooses them (at least 64 rows each) when split_rows is
  *                   0.  Its workspace holds arrival counters: see
  *                   sparse_decode_attn_ex.
@@ -170,8 +170,8 @@ SPD_API spd_status sparse_decode_attn_plan_info(int32_t N, int32_t H, int32_t D,
  * sparse_decode_attn_workspace_size bytes, 16-byte aligned (may be NULL when
  * that size is 0).  HEADS-mode split-L keeps no state in it between calls.
  * When the plan is SPD_MODE_SPLIT (asked for, or chosen by SPD_MODE_AUTO; see
- * plan_info) the last N * ceil(H / heads per workgroup) * 16 bytes are
- * arrival counters that must be zero when the call starts: zero the buffer
+ * plan_info) the last N * ceil(H / heads per workgroup) * D / (2 * info[6])
+ * bytes are arrival counters that must be zero when the call starts: zero the buffer
  * once after allocating it (and again after another plan has used it).  Every
  * call leaves them zero, so one buffer serves any number of calls issued one
  * after another; two calls that run at the same time on one buffer race.

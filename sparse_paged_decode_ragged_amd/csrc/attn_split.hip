@@ -69,14 +69,14 @@ constexpr int kSc1 = 16;  // cache policy bit of an agent-scope coherent access
 __device__ __forceinline__ void store_sc1(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kSc1);
 }
-__device__ __forceinline__ f32x4 load_sc1(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
+__device__ __forceinline__ f32x4 load_sc1(__amdgpu_buffer_rsrc_t r, int off, int soff = 0) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, kSc1));
 }
 __device__ __forceinline__ void store1_sc1(__amdgpu_buffer_rsrc_t r, int off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, off, 0, kSc1);
 }
-__device__ __forceinline__ float load1_sc1(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSc1));
+__device__ __forceinline__ float load1_sc1(__amdgpu_buffer_rsrc_t r, int off, int soff = 0) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, kSc1));
 }
 
 // Weight 2^(m - M) of a state with reference maximum m in a merge whose
@@ -562,12 +562,15 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
     }
   }
 
-  // Cross-workgroup merge.  Piece w (held by wave w: head block w / P,
-  // d-tiles [piece_lo(w % P), + kDTw)) of every partition of (token, head
-  // group) is merged by workgroup w mod nparts, all four of its waves sharing
-  // the piece's d-tiles.  The other partitions publish it and count
-  // themselves in; the merging workgroup waits for the count (bounded), then
-  // loads every partition's share at once and sums in partition order.
+  // Cross-workgroup merge, a reduce-scatter.  Piece w (held by wave w: head
+  // block w / P, d-tiles [piece_lo(w % P), + kDTw)) is cut into U units of
+  // du = kDTw / U d-tiles, U the least power of two with 4 U >= nparts (at
+  // most kDTw), and unit u = w U + j is merged by partition u mod nparts: the
+  // merge reads spread over up to 4 U workgroups instead of four.  Every
+  // partition publishes its pieces and counts itself in on each unit another
+  // partition merges; a merging workgroup waits for its unit's count
+  // (bounded), then each of its waves sums a quarter of the unit's columns
+  // over every partition's share, in partition order.
   auto piece_lo = [](int pr) {  // first d-tile a parity keeps after the butterfly
     int l = 0;
 #pragma unroll
@@ -591,11 +594,16 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
   const int64_t item_bytes = kWaves * slot;
   unsigned char* ws = reinterpret_cast<unsigned char*>(a.ws);
   unsigned char* ws_th = ws + (int64_t)th * a.splits * item_bytes;  // partition 0's slots
+  // kDTw arrival counters a piece (one a unit at the finest cut)
   int* ctr_th = reinterpret_cast<int*>(ws + (int64_t)a.N * a.head_groups * a.splits * item_bytes) +
-                (int64_t)th * kWaves;
+                (int64_t)th * kWaves * kDTw;
   const int others = nparts - 1;
+  int U = 1;
+  while (U < kDTw && 4 * U < nparts) U <<= 1;
+  const int du = kDTw / U;
+  auto ctr_of = [&](int u) { return ctr_th + (u / U) * kDTw + u % U; };
 
-  // publishing: this wave's piece to its slot, complete before the count
+  // publishing: this wave's piece to its slot, complete before any count
   auto publish = [&]() {
     const __amdgpu_buffer_rsrc_t r = ws_rsrc(ws_th + c * item_bytes + wave * slot);
 #pragma unroll
@@ -610,94 +618,54 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
-  auto arrive = [&](int w) {
-    int old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(ctr_th + w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __builtin_amdgcn_readfirstlane(old);
-    asm volatile("" ::: "memory");
-    return old;
-  };
 
-  // Merge of piece w over d-tiles [i0, i0 + ni) of it, by one wave: partition
-  // c's share comes from `own` (a register image in LDS, or this wave's own
-  // accumulators when own_regs), the others' from their slots.  Writes out.
-  auto merge_range = [&](int w, int i0, const f32x4* own_lds, bool own_regs, float om0, float om1,
-                         float ol0, float ol1, auto ni_tag) {
-    constexpr int kNi = decltype(ni_tag)::value;
-    // partitions whose shares are loaded together (registers: kBatch * kNi
-    // accumulator images)
-    constexpr int kBatch = kNi <= 2 ? 4 : 1;
-    // pass 1: the largest m over the partitions (partition c's own from the
-    // arguments), kMB partitions' loads in flight at a time
-    constexpr int kMB = 8;
-    float M0 = -INFINITY, M1 = -INFINITY;
-    for (int k0 = 0; k0 < nparts; k0 += kMB) {
-      float x0[kMB], x1[kMB];
+  // Merge of quarter-columns [v kQ, (v + 1) kQ) of unit u (kQ = du) by one
+  // wave: every partition's share of them, this one's included, from the
+  // slots, summed in partition order with a running maximum (so every arrival
+  // order gives the same bits).  Writes out.
+  auto merge_part = [&](int u, int v, auto q_tag) {
+    constexpr int kQ = decltype(q_tag)::value;
+    // partitions whose shares are loaded together
+    constexpr int kB = kQ == 1 ? 16 : (kQ == 2 ? 8 : 32 / kQ);
+    const int w = u / U;
+    const int i0 = (u % U) * du;  // the unit's first d-tile within the piece
+    float M0 = -INFINITY, M1 = -INFINITY, ls0 = 0.f, ls1 = 0.f;
+    f32x4 tot[kQ];
 #pragma unroll
-      for (int b = 0; b < kMB; ++b) {
-        const int k = k0 + b < nparts ? k0 + b : 0;
-        const __amdgpu_buffer_rsrc_t r = ws_rsrc(ws_th + k * item_bytes + w * slot);
-        x0[b] = load1_sc1(r, Pc::kOBytes + n16 * 4);
-        x1[b] = load1_sc1(r, Pc::kOBytes + (16 + n16) * 4);
-      }
+    for (int q = 0; q < kQ; ++q) tot[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // one descriptor over the (token, head group)'s slots; a partition's slot
+    // is a scalar offset from it (< 2^31: at most 32 partitions of 4 slots)
+    const __amdgpu_buffer_rsrc_t r = ws_rsrc(ws_th);
+    for (int k0 = 0; k0 < nparts; k0 += kB) {
+      f32x4 x[kB][kQ];
+      float bm0[kB], bm1[kB], bl0[kB], bl1[kB];
 #pragma unroll
-      for (int b = 0; b < kMB; ++b) {
-        const int k = k0 + b;
-        if (k < nparts) {
-          M0 = fmaxf(M0, k == c ? om0 : x0[b]);
-          M1 = fmaxf(M1, k == c ? om1 : x1[b]);
-        }
-      }
-    }
-    // pass 2: each partition's share weighted by 2^(m - M), summed in
-    // partition order (every arrival order gives the same bits)
-    float ls0 = 0.f, ls1 = 0.f;
-    f32x16 tot[kNi];
+      for (int b = 0; b < kB; ++b) {  // the batch's loads go out before any is used
+        const int k = k0 + b < nparts ? k0 + b : k0;  // (past nparts: a repeat, unused)
+        const int so = __builtin_amdgcn_readfirstlane((int)(k * item_bytes + w * slot));
+        bm0[b] = load1_sc1(r, Pc::kOBytes + n16 * 4, so);
+        bm1[b] = load1_sc1(r, Pc::kOBytes + (16 + n16) * 4, so);
+        bl0[b] = load1_sc1(r, Pc::kOBytes + 128 + n16 * 4, so);
+        bl1[b] = load1_sc1(r, Pc::kOBytes + 128 + (16 + n16) * 4, so);
 #pragma unroll
-    for (int i = 0; i < kNi; ++i) tot[i] = f32x16{};
-    for (int k0 = 0; k0 < nparts; k0 += kBatch) {
-      f32x16 x[kBatch][kNi];
-      float bm0[kBatch], bm1[kBatch], bl0[kBatch], bl1[kBatch];
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) {  // the batch's loads go out before any is used
-        const int k = k0 + b < nparts ? k0 + b : 0;
-        if (k == c) {
-          bm0[b] = om0;
-          bm1[b] = om1;
-          bl0[b] = ol0;
-          bl1[b] = ol1;
-#pragma unroll
-          for (int i = 0; i < kNi; ++i) {
-            if (own_regs) {
-              x[b][i] = acc[i0 + i];
-            } else {
-#pragma unroll
-              for (int e4 = 0; e4 < 4; ++e4) set_quarter(x[b][i], e4, own_lds[((i0 + i) * 4 + e4) * 64 + lane]);
-            }
-          }
-        } else {
-          const __amdgpu_buffer_rsrc_t r = ws_rsrc(ws_th + k * item_bytes + w * slot);
-          bm0[b] = load1_sc1(r, Pc::kOBytes + n16 * 4);
-          bm1[b] = load1_sc1(r, Pc::kOBytes + (16 + n16) * 4);
-          bl0[b] = load1_sc1(r, Pc::kOBytes + 128 + n16 * 4);
-          bl1[b] = load1_sc1(r, Pc::kOBytes + 128 + (16 + n16) * 4);
-#pragma unroll
-          for (int i = 0; i < kNi; ++i)
-#pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4)
-              set_quarter(x[b][i], e4, load_sc1(r, (((i0 + i) * 4 + e4) * 64 + lane) * 16));
+        for (int q = 0; q < kQ; ++q) {
+          const int qc = v * kQ + q;
+          x[b][q] = load_sc1(r, (((i0 + qc / 4) * 4 + qc % 4) * 64 + lane) * 16, so);
         }
       }
 #pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
+      for (int b = 0; b < kB; ++b) {
         if (k0 + b < nparts) {
-          const float w0 = state_weight(bm0[b], M0);
-          const float w1 = state_weight(bm1[b], M1);
-          ls0 += w0 * bl0[b];
-          ls1 += w1 * bl1[b];
-          const float wk = n < 16 ? w0 : w1;
+          const float N0 = fmaxf(M0, bm0[b]), N1 = fmaxf(M1, bm1[b]);
+          const float s0 = state_weight(M0, N0), s1 = state_weight(M1, N1);
+          const float w0 = state_weight(bm0[b], N0), w1 = state_weight(bm1[b], N1);
+          ls0 = s0 * ls0 + w0 * bl0[b];
+          ls1 = s1 * ls1 + w1 * bl1[b];
+          const float sk = n < 16 ? s0 : s1, wk = n < 16 ? w0 : w1;
 #pragma unroll
-          for (int i = 0; i < kNi; ++i) tot[i] += wk * x[b][i];
+          for (int q = 0; q < kQ; ++q) tot[q] = sk * tot[q] + wk * x[b][q];
+          M0 = N0;
+          M1 = N1;
         }
       }
     }
@@ -707,48 +675,68 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
       uint16_t* op = a.out + ((int64_t)t * a.H + hw0 + n) * D + 4 * hf;
       const int dt0 = piece_lo(w % P) + i0;
 #pragma unroll
-      for (int i = 0; i < kNi; ++i)
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) store_bf16x4(op + out_col(dt0 + i, e4), quarter(tot[i], e4), inv);
+      for (int q = 0; q < kQ; ++q) {
+        const int qc = v * kQ + q;
+        store_bf16x4(op + out_col(dt0 + qc / 4, qc % 4), tot[q], inv);
+      }
+    }
+  };
+  auto merge_unit_part = [&](int u, int v) {  // du: a power of two, at most kDTw
+    if (du == 1) {
+      merge_part(u, v, std::integral_constant<int, 1>{});
+    } else if (du == 2) {
+      if constexpr (kDTw >= 2) merge_part(u, v, std::integral_constant<int, 2>{});
+    } else if (du == 4) {
+      if constexpr (kDTw >= 4) merge_part(u, v, std::integral_constant<int, 4>{});
+    } else {
+      if constexpr (kDTw >= 8) merge_part(u, v, std::integral_constant<int, 8>{});
     }
   };
 
-  // 1. publish the pieces another workgroup merges; an arrival that completes
-  //    a count whose merger gave up merges that piece alone
-  if (wave % nparts != c) {
-    publish();
-    if (arrive(wave) == others) {
-      merge_range(wave, 0, nullptr, true, m0, m1, lb0, lb1, std::integral_constant<int, kDTw>{});
-      if (lane == 0) __hip_atomic_store(ctr_th + wave, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // 1. every wave publishes its piece, then counts itself in on each unit of
+  //    it that another partition merges (lane j on unit j, all at once); an
+  //    arrival that completes a count whose merger gave up merges that unit
+  //    alone
+  publish();
+  {
+    const int u = wave * U + lane;
+    int old = -1;
+    if (lane < U && u % nparts != c)
+      old = __hip_atomic_fetch_add(ctr_of(u), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t done = __builtin_amdgcn_ballot_w64(old == others);
+    asm volatile("" ::: "memory");
+    while (done != 0) {  // (wave-uniform)
+      const int uj = wave * U + __builtin_ctzll(done);
+      done &= done - 1;
+      // one wave takes all 4 du quarter-columns, at most four a call (wider
+      // calls here would hold more registers than the kernel has)
+      if (du >= 4) {
+        if constexpr (kDTw >= 4)
+          for (int v = 0; v < du; ++v) merge_part(uj, v, std::integral_constant<int, 4>{});
+      } else if (du == 2) {
+        if constexpr (kDTw >= 2)
+          for (int v = 0; v < 4; ++v) merge_part(uj, v, std::integral_constant<int, 2>{});
+      } else {
+        for (int v = 0; v < 4; ++v) merge_part(uj, v, std::integral_constant<int, 1>{});
+      }
+      if (lane == 0) __hip_atomic_store(ctr_of(uj), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
-  // 2. merge this workgroup's pieces, all four waves sharing each
-  constexpr int kShare = kDTw >= kWaves ? kDTw / kWaves : 1;  // d-tiles per wave
-  f32x4* spiece = reinterpret_cast<f32x4*>(smem);
+  // 2. the units this workgroup merges (u = c, c + nparts, ...), its four
+  //    waves sharing the columns of each
   int* sdec = sflag;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    if (w % nparts != c) continue;  // (workgroup-uniform)
-    barrier_lds();  // the ring is free; the previous piece's reads are done
-    if (wave == w) {  // the holder: its share to LDS, then wait for the others
-      if (g == 0) {
-        sml[w][0][n16] = m0;
-        sml[w][1][n16] = m1;
-        sml[w][2][n16] = lb0;
-        sml[w][3][n16] = lb1;
-      }
-#pragma unroll
-      for (int i = 0; i < kDTw; ++i)
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) spiece[(i * 4 + e4) * 64 + lane] = quarter(acc[i], e4);
+  for (int u = c; u < kWaves * U; u += nparts) {  // (workgroup-uniform)
+    barrier_lds();  // every wave has read the previous unit's decision
+    if (wave == 0) {  // wait for the other partitions' counts
+      int* cu = ctr_of(u);
       int v = 0;
       const uint64_t t_spin = __builtin_amdgcn_s_memrealtime();
       for (int it = 0; a.split_wait && it < kSpinLimit; ++it) {
         // polled with a read-modify-write (max with 0 leaves the count as it
         // is): it is served where the arrivals' adds are, which a plain
         // agent-scope load is not guaranteed to be promptly
-        if (lane == 0) v = __hip_atomic_fetch_max(ctr_th + w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) v = __hip_atomic_fetch_max(cu, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         v = __builtin_amdgcn_readfirstlane(v);
         if (v >= others) break;
         if (__builtin_amdgcn_s_memrealtime() - t_spin > kSpinTicks) break;
@@ -757,19 +745,17 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
       asm volatile("" ::: "memory");
       int decision = 1;
       if (v < others) {  // (waited long enough, or not at all) the arrival that completes the count merges
-        publish();
-        decision = arrive(w) == others ? 1 : 0;
+        int old = 0;
+        if (lane == 0) old = __hip_atomic_fetch_add(cu, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        decision = __builtin_amdgcn_readfirstlane(old) == others ? 1 : 0;
+        asm volatile("" ::: "memory");
       }
-      if (decision && lane == 0)
-        __hip_atomic_store(ctr_th + w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (decision && lane == 0) __hip_atomic_store(cu, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (lane == 0) sdec[0] = decision;
     }
     barrier_lds();
     if (sdec[0] == 0) continue;  // (workgroup-uniform) a later arrival merges it
-    if (kDTw >= kWaves || wave < kDTw) {
-      merge_range(w, wave * kShare, spiece, false, sml[w][0][n16], sml[w][1][n16], sml[w][2][n16],
-                  sml[w][3][n16], std::integral_constant<int, kShare>{});
-    }
+    merge_unit_part(u, wave);
   }
 }
 
@@ -816,7 +802,9 @@ size_t split_counters_offset(int32_t N, int32_t D, const AttnPlan& p) {
 }
 
 size_t split_workspace_bytes(int32_t N, int32_t D, const AttnPlan& p) {
-  return split_counters_offset(N, D, p) + (size_t)N * p.head_groups * 4 * sizeof(int);
+  // one arrival counter per unit at the finest cut: D / 32 / parities a piece
+  return split_counters_offset(N, D, p) +
+         (size_t)N * p.head_groups * 4 * (D / 32 / p.parities) * sizeof(int);
 }
 
 hipError_t launch_split(const AttnArgs& a, int D, const AttnPlan& p, bool fp8, hipStream_t stream) {
