@@ -176,6 +176,25 @@ def test_deterministic(spd):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("H,D", [(64, 512), (32, 512), (64, 128)])
+def test_split_every_unit_width_without_waiting(spd, H, D):
+    """Split mode on a grid larger than the chip (16 tokens x 32 partitions of
+    64 rows), so no merging workgroup waits and the arrival that completes
+    each count merges its unit alone; the lengths give 1 to 32 partitions, so
+    units of every width (a piece cut into 1, 2, 4 or 8) are merged.  Every
+    token against the oracle, and the same bits on a second call."""
+    lengths = [1, 64, 65, 130, 256, 257, 400, 520, 700, 1000, 1030, 1500, 2000, 2048, 0, 33]
+    w = W.random_csr("split_units", 23, len(lengths), H, D, 9000, lengths)
+    log("case split units H=%d D=%d" % (H, D))
+    plan = spd.sparse_decode_attn_plan_info(w.N, H, D, 2048, 64, SPLIT)
+    assert plan["splits"] == 32 and w.N * plan["head_groups"] * 32 > 256
+    ref = oracle_tokens(w, w.kv_indices, w.kv_indptr)
+    a = run(spd, w, w.kv_indices, w.kv_indptr, mode=SPLIT, max_len=2048, split_rows=64)
+    b = run(spd, w, w.kv_indices, w.kv_indptr, mode=SPLIT, max_len=2048, split_rows=64)
+    assert_close(bf16_to_f64(a), ref, "split units H=%d D=%d" % (H, D))
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 def test_validate_indices(spd):
     d = torch.device("cuda:0")
     ptr = torch.tensor([0, 2, 2, 5], dtype=torch.int32, device=d)

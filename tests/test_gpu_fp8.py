@@ -361,10 +361,10 @@ SPLIT_SHAPES = [(64, 128), (64, 256), (64, 512), (96, 512), (32, 512), (24, 256)
 
 def split_lengths(rng, n):
     """Empty, one row, around the 32- and 64-row super-tiles and the
-    partition length, random, and one slice over the 1024 indices staged at a
-    time."""
+    partition length, random, one slice over the 1024 indices staged at a
+    time, and slices of 1 to 24 partitions of 96 rows (units of every width)."""
     L = rng.integers(0, 700, size=n)
-    L[:9] = [0, 1, 31, 32, 33, 95, 96, 97, 2300]
+    L[:10] = [0, 1, 31, 32, 33, 95, 96, 97, 2300, 1000]
     return L
 
 
