@@ -29,22 +29,28 @@
 // leaving each wave the merged state of its 32 heads on D / P columns: the
 // wave's piece.
 //
-// Merging the partitions without a second launch.  Piece w of a (token, head
-// group) is merged by partition w mod nparts (a reduce-scatter: every
-// partition merges a share).  The others publish their piece to the workspace
-// with agent-scope coherent stores (sc1), wait until the stores are complete
-// and count themselves in with one atomic add on the piece's counter; the
-// merging wave polls the counter (read-modify-writes at agent scope), then
-// reads the pieces (sc1 loads), sums them in partition order (every arrival
-// order gives the same bits), writes the output and resets the counter to
-// zero.  It waits only when the whole grid fits on the chip at once (one
-// workgroup per CU), and then for a bounded number of polls: past the bound,
-// or at once on a larger grid, it publishes its own piece and counts itself
-// in as well, and whichever arrival completes the count merges instead -- so
-// no wave ever waits on a workgroup that cannot be scheduled.  No whole-cache
+// Merging the partitions without a second launch.  Each of the four pieces
+// of a (token, head group) is cut into U units of whole d-tiles, U the least
+// power of two with 4 U >= nparts, and unit u of the 4 U is merged by
+// partition u mod nparts (a reduce-scatter: every partition merges a share).  Every partition publishes its pieces to the workspace with
+// agent-scope coherent stores (sc1), waits until the stores are complete and
+// counts itself in with one atomic add on each unit another partition merges;
+// the merging workgroup polls the unit's counter (read-modify-writes at agent
+// scope), then reads every partition's share of the unit (sc1 loads), sums
+// them in partition order (every arrival order gives the same bits), writes
+// the output and resets the counter to zero.  It waits only when the whole
+// grid fits on the chip at once (one workgroup per CU), and then for a bounded
+// time: past the bound, or at once on a larger grid, it counts itself in as
+// well, and whichever arrival completes the count merges instead -- so no wave
+// ever waits on a workgroup that cannot be scheduled.  No whole-cache
 // write-back or invalidation is involved: only these sc1 accesses carry data
 // between workgroups, and an sc1 load is served at agent scope, never from a
 // line an XCD's L2 kept from before the publishing stores.
+//
+// FP8 rows (kFp8): the same kernel over D code bytes a row with an fp32 scale
+// a row (sglang PR #25898 summary page, "key files": the FP8 caches), the
+// codes decoded to bf16 exactly before each MFMA and the scale applied to the
+// row's scores and weights, as in attn_fp8.hip.
 #include <atomic>
 
 #include "fp8_device.h"
