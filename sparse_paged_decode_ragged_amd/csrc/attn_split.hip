@@ -72,11 +72,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const void* base) {
 
 constexpr int kSc1 = 16;  // cache policy bit of an agent-scope coherent access
 
-__device__ __forceinline__ void store_sc1(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kSc1);
+// Four accumulator values as four bf16 (round to nearest even), stored and
+// loaded as 8 bytes; the load widens them back to fp32 exactly.
+__device__ __forceinline__ void store_bf16x4_sc1(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
+  const bf16x4 h = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), r, off, 0, kSc1);
 }
-__device__ __forceinline__ f32x4 load_sc1(__amdgpu_buffer_rsrc_t r, int off, int soff = 0) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, kSc1));
+__device__ __forceinline__ f32x4 load_bf16x4_sc1(__amdgpu_buffer_rsrc_t r, int off, int soff = 0) {
+  const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, kSc1);
+  return f32x4{__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xffff0000u),
+               __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xffff0000u)};
 }
 __device__ __forceinline__ void store1_sc1(__amdgpu_buffer_rsrc_t r, int off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, off, 0, kSc1);
@@ -104,12 +109,15 @@ __device__ __forceinline__ void set_quarter(f32x16& v, int e4, f32x4 q) {
 }
 
 // A piece's slot in the workspace: its kDTw d-tiles as the register image of
-// the accumulators (each f32x16 stored as four 16-byte columns of 64 lanes),
-// then m of its 32 heads, then l.
+// the accumulators in bf16 (each f32x16 stored as four 8-byte columns of 64
+// lanes), then m of its 32 heads, then l, both fp32.  Exchanging O in bf16
+// halves the bytes that go through memory between the partitions; it adds
+// one rounding (2^-9 relative) to each partition's unnormalised O, while m
+// and l, which set the weights, stay exact.
 template <int D, int P>
 struct Piece {
   static constexpr int kDTw = D / 32 / P;
-  static constexpr int kOBytes = kDTw * 4 * 64 * 16;
+  static constexpr int kOBytes = kDTw * 4 * 64 * 8;
   static constexpr int kBytes = kOBytes + 2 * 32 * 4;
 };
 
@@ -615,7 +623,7 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < kDTw; ++i)
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) store_sc1(r, ((i * 4 + e4) * 64 + lane) * 16, quarter(acc[i], e4));
+      for (int e4 = 0; e4 < 4; ++e4) store_bf16x4_sc1(r, ((i * 4 + e4) * 64 + lane) * 8, quarter(acc[i], e4));
     if (g == 0) {
       store1_sc1(r, Pc::kOBytes + n16 * 4, m0);
       store1_sc1(r, Pc::kOBytes + (16 + n16) * 4, m1);
@@ -656,7 +664,7 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
           const int qc = v * kQ + q;
-          x[b][q] = load_sc1(r, (((i0 + qc / 4) * 4 + qc % 4) * 64 + lane) * 16, so);
+          x[b][q] = load_bf16x4_sc1(r, (((i0 + qc / 4) * 4 + qc % 4) * 64 + lane) * 8, so);
         }
       }
 #pragma unroll
@@ -803,7 +811,7 @@ hipError_t launch_split_shape(const AttnArgs& a, const AttnPlan& p, hipStream_t 
 }  // namespace
 
 size_t split_counters_offset(int32_t N, int32_t D, const AttnPlan& p) {
-  const size_t slot = (size_t)(D / 32 / p.parities) * 4 * 64 * 16 + 2 * 32 * 4;
+  const size_t slot = (size_t)(D / 32 / p.parities) * 4 * 64 * 8 + 2 * 32 * 4;
   return (size_t)N * p.head_groups * p.splits * 4 * slot;
 }
 

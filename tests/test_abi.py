@@ -109,9 +109,9 @@ def test_attn_ex_workspace_checks(lib):
     # decode_base shape: the automatic plan is the split mode, 64 heads a
     # workgroup (4 waves of 32 heads: 2 head blocks x 2 parities), 4
     # partitions of 160 rows: one piece slot per (token, partition, wave) of
-    # 32 heads x 256 fp32 + 32 m + 32 l, then 8 int32 arrival counters per
+    # 32 heads x 256 bf16 + 32 fp32 m + 32 fp32 l, then 8 int32 arrival counters per
     # (token, wave): one per unit of a piece cut into its 8 d-tiles
-    split_need = 64 * 4 * 4 * (32 * 256 * 4 + 2 * 32 * 4) + 64 * 4 * 8 * 4
+    split_need = 64 * 4 * 4 * (32 * 256 * 2 + 2 * 32 * 4) + 64 * 4 * 8 * 4
     assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 0, SPLIT) == split_need
     # the automatic plan keeps rows mode for 640-row slices (no workspace) and
     # splits small batches of slices of 2048 rows and more: 16 tokens x 8
@@ -119,10 +119,10 @@ def test_attn_ex_workspace_checks(lib):
     assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 0, AUTO) == 0
     # 16 tokens of up to 2048 rows: 16 partitions of 128 rows (256 workgroups)
     assert lib.sparse_decode_attn_workspace_size(16, 64, 512, 2048, 0, AUTO) == \
-        16 * 16 * 4 * (32 * 256 * 4 + 2 * 32 * 4) + 16 * 4 * 8 * 4
+        16 * 16 * 4 * (32 * 256 * 2 + 2 * 32 * 4) + 16 * 4 * 8 * 4
     # at most 32 partitions
     assert lib.sparse_decode_attn_workspace_size(2, 64, 512, 65536, 0, SPLIT) == \
-        2 * 32 * 4 * (32 * 256 * 4 + 2 * 32 * 4) + 2 * 4 * 8 * 4
+        2 * 32 * 4 * (32 * 256 * 2 + 2 * 32 * 4) + 2 * 4 * 8 * 4
     assert lib.sparse_decode_attn_workspace_size(2, 64, 512, 65536, 1024, SPLIT) == 0
     # without a capacity bound the automatic plan cannot split: rows mode, no workspace
     assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 0, 0, AUTO) == 0
@@ -261,7 +261,7 @@ def test_fp8_plans_and_ex_checks(lib):
     assert st == OK and i == [SPLIT, 64, 1, 32, 256, 0, 2]
     assert lib.sparse_decode_attn_fp8_workspace_size(8, 64, 512, 8192, 0, AUTO) == \
         lib.sparse_decode_attn_workspace_size(8, 64, 512, 8192, 0, AUTO) == \
-        8 * 32 * 4 * (32 * 256 * 4 + 2 * 32 * 4) + 8 * 4 * 8 * 4
+        8 * 32 * 4 * (32 * 256 * 2 + 2 * 32 * 4) + 8 * 4 * 8 * 4
     assert info(8, 32, 256, 8192)[1][:7] == [SPLIT, 32, 1, 32, 256, 0, 4]
     # no capacity bound, or slices under 2048 rows: no split
     assert info(8, 64, 512)[1][0] == ROWS
