@@ -19,7 +19,8 @@
 // Work: one wave per row, D / 64 entries a lane (entries 2i, 2i+1 of a pair
 // sit in one lane for D >= 128; at D = 64 the partner comes from lane ^ 1).
 // Rows [0, N*H) are q rows (token r / H), rows [N*H, N*H + N) KV rows.  The
-// kernel is bound by HBM: it reads and writes each row once.
+// kernel reads and writes each row once; a wave's life is one row load and
+// the cross-lane sum, so the row's latency sets its throughput.
 #include <math.h>
 
 #include "row_device.h"
@@ -28,53 +29,76 @@
 namespace spd {
 namespace {
 
+// Wave-uniform loads from these (the token's position and state slot) go
+// through the scalar unit, so they do not queue behind the row's vector load.
+typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
+
 template <int D>
 __global__ void __launch_bounds__(256) qk_norm_rope_store_kernel(ProducerArgs a) {
   constexpr int E = D / 64;
+  constexpr int kPairs = E >= 2 ? E / 2 : 1;
   const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t r = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nq = (int64_t)a.N * a.H;
   if (r >= nq + a.N) return;  // wave-uniform
   const bool is_kv = r >= nq;
-  const int t = is_kv ? (int)(r - nq) : (int)(r / a.H);
-  // The row's address does not depend on the position: its load is issued
-  // with the position's (one memory round trip, not two), and its sum of
-  // squares is taken before the position is checked, so the load cannot be
-  // moved below that check.
+  const int t = is_kv ? (int)(r - nq) : (int)(r / a.H);  // wave-uniform
+  // The row's load goes out first; the position (a scalar load) comes back
+  // on its own counter, so the rotary factors it selects, and the weights,
+  // are loaded while the row is still in flight: the row's sum of squares is
+  // the only step that waits for it.
   const uint16_t* src = is_kv ? a.kv + (int64_t)t * D : a.q + r * D;
   float x[E];
   load_bf16_lane<E>(src + lane * E, x);
-  const int p = a.positions[t];
-  const int64_t ring0 = is_kv ? (int64_t)a.state_slot[t] * a.win : 0;
+  const int p = ((ConstI32Ptr)a.positions)[t];
+  const int64_t ring0 = is_kv ? (int64_t)((ConstI32Ptr)a.state_slot)[t] * a.win : 0;
+  const float* w = is_kv ? a.kv_weight : a.q_weight;
+  float wt[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) wt[e] = w[lane * E + e];
+  const bool pos_ok = p >= 0 && (a.rope_dim == 0 || p < a.max_pos);
+  const int o = D - a.rope_dim, half = a.rope_dim >> 1;
+  float cr[kPairs], sr[kPairs];
+#pragma unroll
+  for (int k = 0; k < kPairs; ++k) {
+    cr[k] = 1.f;
+    sr[k] = 0.f;
+  }
+  if (pos_ok && a.rope_dim > 0) {  // the rotary factors go out with the row
+    const float* cs = a.cos_sin + (int64_t)p * a.rope_dim;
+#pragma unroll
+    for (int k = 0; k < kPairs; ++k) {
+      const int d = E >= 2 ? lane * E + 2 * k : lane;
+      if (d >= o) {
+        const int i = (d - o) >> 1;
+        cr[k] = cs[i];
+        sr[k] = cs[half + i];
+      }
+    }
+  }
 
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e) ss += x[e] * x[e];
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  ss = wave_reduce<false>(ss);
 
-  // a position outside the table (when there is one to read): nothing is written
-  if (p < 0 || (a.rope_dim > 0 && p >= a.max_pos)) return;
+  if (!pos_ok) return;  // a position outside the table: nothing is written
   int64_t slot = 0;
   if (is_kv) {
     slot = ring0 + p % a.win;
     if (slot < 0 || slot >= a.num_rows) return;  // outside the pool: nothing is written
   }
   const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
-  const float* w = is_kv ? a.kv_weight : a.q_weight;
   float y[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) y[e] = x[e] * inv * w[lane * E + e];
+  for (int e = 0; e < E; ++e) y[e] = x[e] * inv * wt[e];
 
-  const int o = D - a.rope_dim, half = a.rope_dim >> 1;
-  const float* cs = a.cos_sin + (int64_t)p * a.rope_dim;
   if constexpr (E >= 2) {
 #pragma unroll
     for (int e = 0; e < E; e += 2) {
       const int d = lane * E + e;
       if (d >= o) {
-        const int i = (d - o) >> 1;
-        const float c = cs[i], s = cs[half + i];
+        const float c = cr[e / 2], s = sr[e / 2];
         const float y0 = y[e], y1 = y[e + 1];
         y[e] = y0 * c - y1 * s;
         y[e + 1] = y0 * s + y1 * c;
@@ -83,8 +107,7 @@ __global__ void __launch_bounds__(256) qk_norm_rope_store_kernel(ProducerArgs a)
   } else {
     const float partner = __shfl_xor(y[0], 1);
     if (lane >= o) {
-      const int i = (lane - o) >> 1;
-      const float c = cs[i], s = cs[half + i];
+      const float c = cr[0], s = sr[0];
       y[0] = (lane & 1) == 0 ? y[0] * c - partner * s : partner * s + y[0] * c;
     }
   }

@@ -57,6 +57,36 @@ __device__ __forceinline__ void store_bf16_lane(uint16_t* dst, const float (&y)[
   }
 }
 
+// Sum and maximum of one value over the wave with VALU cross-lane operations
+// only: DPP within each 16-lane row (pairs, quads, then the two mirrors), then
+// v_permlane32_swap and v_permlane16_swap across the rows.  No LDS permute
+// sits in the row's dependent chain, and every lane gets the same bits (each
+// step combines a lane with a partner that combines it back).
+template <int kCtrl>
+__device__ __forceinline__ float rd_dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, false));
+}
+
+template <bool kMax>
+__device__ __forceinline__ float rd_combine(float a, float b) {
+  return kMax ? fmaxf(a, b) : a + b;
+}
+
+template <bool kMax>
+__device__ __forceinline__ float wave_reduce(float v) {
+  v = rd_combine<kMax>(v, rd_dpp<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = rd_combine<kMax>(v, rd_dpp<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = rd_combine<kMax>(v, rd_dpp<0x141>(v));  // row_half_mirror
+  v = rd_combine<kMax>(v, rd_dpp<0x140>(v));  // row_mirror
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = rd_combine<kMax>(__builtin_bit_cast(float, (unsigned)a[0]), __builtin_bit_cast(float, (unsigned)a[1]));
+  const unsigned w = __builtin_bit_cast(unsigned, v);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return rd_combine<kMax>(__builtin_bit_cast(float, (unsigned)b[0]), __builtin_bit_cast(float, (unsigned)b[1]));
+}
+
 // FP8 store of one row held by the wave (x: the lane's E values): amax over
 // the wave; a row with amax < 2^-64 stores scale 0 and zero codes; otherwise
 // scale = amax / 448, inv = 448 / amax (correctly rounded fp32 divisions),
@@ -69,8 +99,7 @@ __device__ __forceinline__ void store_fp8_lane(const float (&x)[E], uint8_t* dst
   float amax = 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(x[e]));
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  amax = wave_reduce<true>(amax);
   unsigned code[(E + 3) / 4];
   float scale = 0.f;
 #pragma unroll
