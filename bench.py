@@ -766,7 +766,9 @@ def main():
         b_prod = 4 * N * H * D + 4 * N * D + 8 * D + 4 * N * rope_dim + 8 * N
         achp = b_prod / (us_prod * 1e-6) / 1e9
         rec["producer"] = {
-            "call": "fused_qk_norm_rope_swa_store", "kernel": "qk_norm_rope_store_kernel<%d>" % D,
+            "call": "fused_qk_norm_rope_swa_store",
+            # the library takes two rows a wave from N*H + N >= 32768 rows, else one
+            "kernel": "qk_norm_rope_store_kernel<%d,%d>" % (D, 2 if N * H + N >= 32768 else 1),
             "rope_dim": rope_dim, "us_per_call": round(us_prod, 3), "bytes_per_call": int(b_prod),
             "achieved_GBps": round(achp, 1), "frac": round(achp / HBM_PEAK_GBPS, 4)}
     if not args.no_cpu_baseline:
