@@ -14,7 +14,8 @@ oracle's producer:
 
 Cases: every supported D, rotary widths 0, part of the row and all of it,
 positions that wrap the ring, in-place q, both pools at once, a decode-base
-batch (N=64, H=64, D=512) and a large batch (N=1024, H=128) sampled."""
+batch (N=64, H=64, D=512), a large batch (N=1024, H=128) and batches with
+a ragged tail where a wave takes two rows."""
 import numpy as np
 import pytest
 import torch
@@ -166,3 +167,20 @@ def test_decode_batches(spd, N, H):
     q, kv, qw, kw, pos, cs, slot = make_case(11 + N, N, H, D, 64, win, n_slots=N)
     slot = np.arange(N, dtype=np.int32)
     run_and_check(spd, (q, kv, qw, kw, pos, cs, slot), win, num_rows=N * win, what="N=%d" % N)
+
+
+@pytest.mark.parametrize("N,H,D", [(255, 128, 128), (257, 128, 64)])
+def test_two_rows_a_wave_with_ragged_tail(spd, N, H, D):
+    """Batches of at least 32768 rows, where a wave takes two consecutive rows:
+    N * H + N odd and not a multiple of eight (waves of the last workgroup with
+    one live row or none), tokens outside the table, in place."""
+    rows = N * H + N
+    assert rows >= 32768 and rows % 8 != 0 and rows % 2 == 1
+    log("case producer two rows a wave N=%d H=%d D=%d" % (N, H, D))
+    win = 16
+    q, kv, qw, kw, pos, cs, slot = make_case(77 + N, N, H, D, 64 if D >= 128 else 32, win,
+                                             n_slots=N + 3)
+    pos[3] = -5
+    pos[N - 1] = 4096
+    run_and_check(spd, (q, kv, qw, kw, pos, cs, slot), win, num_rows=(N + 3) * win,
+                  in_place=True, what="two rows N=%d" % N)
