@@ -48,7 +48,8 @@ typedef enum spd_status {
 SPD_API const char* spd_status_string(spd_status s);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH (0.2.0: SPD_MODE_SPLIT;
- * 0.3.0: sparse_decode_attn_fp8_ex and its split mode). */
+ * 0.3.0: sparse_decode_attn_fp8_ex and its split mode; 0.4.0: split plans
+ * whose partitions the kernel sizes from the slice lengths). */
 SPD_API int spd_version(void);
 
 /*
@@ -115,15 +116,24 @@ SPD_API spd_status sparse_decode_attn(const void* q, const void* unified_kv, int
  *                   four) 16-row streams of each 32-head block; the
  *                   partitions of one (token, head group) are merged inside
  *                   the same kernel, each partition merging a share of the
- *                   columns (no combine kernel).  Up to 32 partitions; the plan
- *                   chooses them (at least 64 rows each) when split_rows is
- *                   0.  Its workspace holds arrival counters: see
+ *                   columns (no combine kernel).  Up to 32 partitions a
+ *                   slice.  With split_rows given, every slice is cut into
+ *                   partitions of that many rows.  With split_rows == 0 and
+ *                   at most 256 (token, head group) pairs (N <= 512), the
+ *                   grid is 256 workgroups, which the kernel deals out as the
+ *                   partitions of this call's slices, sized from kv_indptr: the
+ *                   least partition length (a multiple of 32 rows, 64 when a
+ *                   workgroup takes 32 heads) for which every slice's
+ *                   partitions fit, so a long slice among short ones takes
+ *                   more workgroups.  Otherwise with split_rows == 0 the plan
+ *                   cuts slices only when the batch gives fewer than 256
+ *                   workgroups.  Its workspace holds arrival counters: see
  *                   sparse_decode_attn_ex.
  *   SPD_MODE_AUTO:  SPLIT when split_rows == 0, the batch gives fewer than
  *                   256 HEADS-mode workgroups and max_len >= 2048 (a small
- *                   batch of long slices); else ROWS when split_rows == 0
- *                   and the batch gives fewer than 256 HEADS-mode
- *                   workgroups; else HEADS.
+ *                   batch of long slices, partitions sized from the lengths); else
+ *                   ROWS when split_rows == 0 and the batch gives fewer than
+ *                   256 HEADS-mode workgroups; else HEADS.
  */
 typedef enum spd_mode {
   SPD_MODE_AUTO = 0,
@@ -145,8 +155,10 @@ SPD_API size_t sparse_decode_attn_workspace_size(int32_t N, int32_t H, int32_t D
  * The plan sparse_decode_attn_ex would use for these arguments, for callers
  * that size buffers or report what runs: info[0] = mode actually used
  * (SPD_MODE_HEADS, SPD_MODE_ROWS or SPD_MODE_SPLIT), info[1] = heads per
- * workgroup, info[2] = head groups, info[3] = split-L partitions (1 = none),
- * info[4] = rows per partition, info[5] = 1 when the heads mode runs on
+ * workgroup, info[2] = head groups, info[3] = split-L partitions (1 = none;
+ * for partitions sized in the kernel, the most a slice can take), info[4] =
+ * rows per partition (0 = sized in the kernel from the slice lengths),
+ * info[5] = 1 when the heads mode runs on
  * 32-head waves (64 or 128 heads per workgroup) else 0, info[6] = waves per
  * 32-head block (SPD_MODE_SPLIT: 2, or 4 when a workgroup takes 32 heads,
  * the waves taking alternate 16-row tiles of the same heads; else 1).  info is

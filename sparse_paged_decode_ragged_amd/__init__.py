@@ -173,7 +173,7 @@ def sparse_decode_attn_plan_info(N: int, H: int, D: int, max_len: int = 0, split
     return {"mode": {1: "heads", 2: "rows", 4: "split"}[info[0]], "heads_per_group": info[1],
             "head_groups": info[2], "splits": info[3],
             "split_rows": info[4] if info[3] > 1 else None, "wide": bool(info[5]),
-            "parities": info[6]}
+            "parities": info[6], "balanced": info[0] == 4 and info[3] > 1 and info[4] == 0}
 
 
 def sparse_decode_attn(q: torch.Tensor, unified_kv: torch.Tensor, kv_indices: torch.Tensor,
@@ -388,7 +388,7 @@ def sparse_decode_attn_fp8_plan_info(N: int, H: int, D: int, max_len: int = 0,
     return {"mode": {1: "heads", 2: "rows", 4: "split"}[info[0]], "heads_per_group": info[1],
             "head_groups": info[2], "splits": info[3],
             "split_rows": info[4] if info[3] > 1 else None, "wide_waves": info[5],
-            "parities": info[6]}
+            "parities": info[6], "balanced": info[0] == 4 and info[3] > 1 and info[4] == 0}
 
 
 def sparse_decode_attn_fp8(q: torch.Tensor, kv_fp8: torch.Tensor, kv_scale: torch.Tensor,

@@ -104,7 +104,7 @@ SPD_API const char* spd_status_string(spd_status s) {
   return "SPD_ERR_UNKNOWN";
 }
 
-SPD_API int spd_version(void) { return 300; }
+SPD_API int spd_version(void) { return 400; }
 
 SPD_API int sparse_decode_attn_can_use(int32_t H, int32_t D) {
   return spd::attn_supported(H, D) ? 1 : 0;

@@ -986,6 +986,13 @@ constexpr int kSplitMax = 32;
 // rows mode, of 2048 rows 46.4 us against 49.8 us; N = 8 of 8192 rows 58 us
 // against 150 us).
 constexpr int kSplitAutoLen = 2048;
+// Balanced split plans (no split_rows given, a batch of at most kBalancedSlots
+// (token, head group) pairs): kBalancedSlots workgroups in all, one per CU of
+// the chip, which the kernel deals out as partitions sized from the call's
+// slice lengths, so a long slice among short ones takes more of them.  The
+// kernel's plan search holds at most kBalancedMaxN tokens.
+constexpr int kBalancedSlots = 256;
+constexpr int kBalancedMaxN = 512;
 
 static bool make_split_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t split_rows,
                             AttnPlan* p) {
@@ -996,7 +1003,20 @@ static bool make_split_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, in
   p->heads_per_group = hb1 ? 32 : 64;
   p->waves = 4;
   p->head_groups = (H + p->heads_per_group - 1) / p->heads_per_group;
+  p->bal_slots = 0;
   const long long base = (long long)N * p->head_groups;
+  const int super_rows = 16 * p->parities;  // rows of the kernel's super-tile
+  if (split_rows == 0 && N > 0 && N <= kBalancedMaxN && base <= kBalancedSlots &&
+      max_len > super_rows) {
+    // balanced: partitions of at least one super-tile, at most kSplitMax a
+    // slice (splits reports that bound; the rows are chosen in the kernel)
+    const long long tiles = (max_len + super_rows - 1) / super_rows;
+    p->splits = (int)(tiles < kSplitMax ? tiles : kSplitMax);
+    p->split_rows = 0;
+    p->bal_slots = kBalancedSlots / p->head_groups;
+    p->workspace_bytes = split_workspace_bytes(N, D, *p);
+    return true;
+  }
   long long splits = 1, rows = 0;
   if (split_rows > 0) {
     rows = ((long long)split_rows + 31) / 32 * 32;
@@ -1036,6 +1056,7 @@ bool make_attn_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t sp
       mode != kModeSplit)
     return false;
   p->parities = 1;
+  p->bal_slots = 0;
   if (mode == kModeSplit) return make_split_plan(N, H, D, max_len, split_rows, p);
   if (mode == kModeWide) {  // 32-head waves, no split-L
     if (H % 64 != 0 || split_rows != 0) return false;
@@ -1057,9 +1078,12 @@ bool make_attn_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t sp
   const long long target = 256;
   if (mode == kModeAuto && split_rows == 0 && (long long)N * heads_groups < target &&
       max_len >= kSplitAutoLen) {
-    // a small batch of long slices: partitions merged in-kernel
+    // a small batch of long slices: partitions sized from the lengths, merged
+    // in-kernel.  (At one workgroup per CU already, 256 slices of the ragged
+    // mix, the heads mode is faster: 101.5 us against 106.4 us.)
     if (make_split_plan(N, H, D, max_len, 0, p) && p->splits > 1) return true;
     p->parities = 1;
+    p->bal_slots = 0;
   }
   if (mode == kModeAuto)
     mode = (split_rows == 0 && (long long)N * heads_groups < target) ? kModeRows : kModeHeads;
@@ -1134,6 +1158,7 @@ bool make_fp8_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t spl
   if (mode != kModeAuto && mode != kModeRows && mode != kModeWide && mode != kModeSplit)
     return false;
   p->parities = 1;
+  p->bal_slots = 0;
   // the batch's workgroups without split-L, counted as for the bf16 pool
   const int heads_per = H <= 16 ? 16 : (H <= 32 ? 32 : 64);
   const long long base = (long long)N * ((H + heads_per - 1) / heads_per);
@@ -1145,6 +1170,7 @@ bool make_fp8_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t spl
     if (make_split_plan(N, H, D, max_len, split_rows, p) && (chosen || p->splits > 1)) return true;
     if (chosen) return false;
     p->parities = 1;
+    p->bal_slots = 0;
   }
   if (split_rows != 0) return false;  // only split mode cuts slices
   // 32-head waves (128 heads a workgroup when H % 128 == 0, else 64) once the

@@ -65,6 +65,138 @@ constexpr int kSpinLimit = 1000; // polls (each a memory round trip plus a short
 // another stream holding CUs) is not waited for past this
 constexpr uint64_t kSpinTicks = 2000;  // 20 us
 
+// Balanced plans: a head group's bal_slots workgroups are the partitions of
+// the call's slices, numbered token by token; every partition but a slice's
+// last has R rows, R the least multiple of the super-tile for which they fit
+// (and no slice takes more than kBalMaxParts).  Each wave derives R and its
+// workgroup's (token, partition) from kv_indptr alone, so the grid stays
+// fixed by the host while the split follows this call's lengths.
+constexpr int kBalPer = 8;        // tokens a lane holds (N <= 512)
+constexpr int kBalMaxParts = 32;  // partitions of one slice (the merge's units)
+
+// ceil(a / b) for 0 <= a < 2^31, b >= 1 and a / b <= 32, with rb = 1 / b in
+// fp32: the product is within 2^-16 of a / b, so its truncation lies at most
+// two below the ceiling, which the two integer steps reach exactly (q b stays
+// below 2^32).
+__device__ __forceinline__ int ceil_div_small(int a, int b, float rb) {
+  unsigned q = (unsigned)((float)a * rb);
+  q += q * (unsigned)b < (unsigned)a ? 1u : 0u;
+  q += q * (unsigned)b < (unsigned)a ? 1u : 0u;
+  return (int)q;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off));
+  return v;
+}
+
+struct BalancedItem {
+  int t;       // token, or -1 when the partitions end before this workgroup
+  int c;       // partition of the token
+  int nparts;  // partitions of the token's slice
+  int row0;    // kv_indptr[t]
+  int L;       // rows of the slice
+  int R;       // rows per partition
+};
+
+// Item j (< slots) of a balanced plan over the N <= 64 kBalPer slices of
+// kv_indptr (slots >= N, so one partition a slice always fits).  Lane l holds
+// tokens [l per, l per + per); the result is wave-uniform.
+template <int kSuper>
+__device__ __forceinline__ BalancedItem balanced_item(const int32_t* indptr, int N, int slots,
+                                                      int j, int lane) {
+  static_assert((kSuper & (kSuper - 1)) == 0, "super-tile rows: a power of two");
+  const int per = (N + 63) >> 6;
+  const int t0 = lane * per;
+  int st[kBalPer + 1];
+#pragma unroll
+  for (int i = 0; i <= kBalPer; ++i) st[i] = indptr[t0 + i < N ? t0 + i : N];
+  int lk[kBalPer];  // super-tiles of each slice
+  int mx = 0, sum = 0, nz = 0;
+#pragma unroll
+  for (int i = 0; i < kBalPer; ++i) {
+    const int L = i < per && t0 + i < N ? st[i + 1] - st[i] : 0;
+    lk[i] = L > 0 ? (L - 1) / kSuper + 1 : 0;
+    mx = max(mx, lk[i]);
+    sum += lk[i];
+    nz += lk[i] > 0 ? 1 : 0;
+  }
+  // (the wave sums are uniform; readfirstlane tells the compiler so, which
+  // keeps the search and everything sized by its result in scalar registers)
+  mx = __builtin_amdgcn_readfirstlane(wave_max_i(mx));
+  BalancedItem r{-1, 0, 0, 0, 0, kSuper};
+  if (mx == 0) return r;  // every slice empty
+  const int64_t S = __builtin_amdgcn_readfirstlane(wave_sum_i(sum));  // < 2^27
+  const int n = __builtin_amdgcn_readfirstlane(wave_sum_i(nz));
+  // least k (super-tiles a partition) of at least mx / kBalMaxParts whose
+  // partitions fit.  The count sum_t ceil(lk_t / k) falls as k grows and lies
+  // in [S / k, S / k + n], so it fits from some k in [S / slots, S / (slots -
+  // n)], and at k = mx (one partition a slice)
+  int klo = (mx + kBalMaxParts - 1) / kBalMaxParts, khi = mx;
+  klo = max(klo, (int)((S + slots - 1) / slots));
+  if (slots > n) khi = min(khi, max(klo, (int)((S + (slots - n) - 1) / (slots - n))));
+  klo = min(klo, khi);
+  while (klo < khi) {
+    const int mid = (klo + khi) >> 1;
+    const float rm = 1.0f / (float)mid;
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kBalPer; ++i)
+      if (i < per) cnt += ceil_div_small(lk[i], mid, rm);
+    cnt = __builtin_amdgcn_readfirstlane(wave_sum_i(cnt));
+    if (cnt <= slots)
+      khi = mid;
+    else
+      klo = mid + 1;
+  }
+  const float rk = 1.0f / (float)klo;
+  int np[kBalPer];
+  int tot = 0;
+#pragma unroll
+  for (int i = 0; i < kBalPer; ++i) {
+    np[i] = i < per ? ceil_div_small(lk[i], klo, rk) : 0;
+    tot += np[i];
+  }
+  int incl = tot;  // partitions of lanes 0 .. lane
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  int pre = incl - tot;
+  bool found = false;
+  int ft = 0, fc = 0, fnp = 0, frow0 = 0, fL = 0;
+#pragma unroll
+  for (int i = 0; i < kBalPer; ++i) {
+    if (!found && j >= pre && j < pre + np[i]) {
+      found = true;
+      ft = t0 + i;
+      fc = j - pre;
+      fnp = np[i];
+      frow0 = st[i];
+      fL = st[i + 1] - st[i];
+    }
+    pre += np[i];
+  }
+  const uint64_t m = __builtin_amdgcn_ballot_w64(found);
+  if (m == 0) return r;
+  const int f = __builtin_ctzll(m);
+  r.t = __builtin_amdgcn_readlane(ft, f);
+  r.c = __builtin_amdgcn_readlane(fc, f);
+  r.nparts = __builtin_amdgcn_readlane(fnp, f);
+  r.row0 = __builtin_amdgcn_readlane(frow0, f);
+  r.L = __builtin_amdgcn_readlane(fL, f);
+  r.R = klo * kSuper;
+  return r;
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const void* base) {
   // raw buffer over a piece's slot (< 2 GiB), untyped 32-bit format
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
@@ -169,29 +301,20 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
   __shared__ float sml[kWaves][4][16];  // per wave: m0, m1, l0, l1 of its 32 heads
   __shared__ int sflag[kWaves];
 
-  // Work item (token, head group, partition), partition fastest: the
-  // partitions and head groups of a token are consecutive items, which
-  // xcd_item keeps on one XCD (one L2) and dispatches together.
-  const int item = xcd_item(blockIdx.x, gridDim.x);
-  const int c = item % a.splits;
-  const int th = item / a.splits;
-  const int hg = th % a.head_groups;
-  const int t = th / a.head_groups;
-
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hb = wave / P;
   const int par = wave % P;
   const int n16 = lane & 15;
   const int g = lane >> 4;
-  const int h0 = hg * kHeads + hb * 32;  // first head of this wave (32 heads)
 
   // q of the workgroup's heads is staged once into the last kQStages stages of
   // the ring (rows XOR-swizzled like the tiles, so that the Q^T reads below
   // put 16 heads' same chunk in 16 bank groups), read into registers, and the
   // stages are handed back to the row tiles; rows of heads past H repeat a
-  // valid row.  Its loads go out first, with the sinks: neither depends on the
-  // slice, so their latency overlaps the kv_indptr and index round trips.
+  // valid row.  Its loads go out with the sinks as soon as the token is known:
+  // in a fixed plan first of all, so that their latency overlaps the
+  // kv_indptr and index round trips.
   constexpr int kQBytes = kHeads * kQRowBytes;
   constexpr int kQStages = (kQBytes + kStageBytes - 1) / kStageBytes;
   static_assert(kQStages < kStages, "q staging must leave a stage for the first tiles");
@@ -199,7 +322,7 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
   static_assert(kQLoads % kWaves == 0, "q loads must divide among waves");
   constexpr int kQLoadsPerWave = kQLoads / kWaves;
   unsigned char* sq = smem + (kStages - kQStages) * kStageBytes;
-  {
+  auto issue_q = [&](int t, int hg) {
     constexpr int kRowsPerLd = 1024 / kQRowBytes;
     constexpr int kChunksQ = kQRowBytes / 16;
     const unsigned char* qb = reinterpret_cast<const unsigned char*>(a.q);
@@ -217,21 +340,57 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
       const int hs = hg * kHeads + lane;
       dma_4B(a.sink + (hs < a.H ? hs : a.H - 1), __builtin_amdgcn_readfirstlane(lds_addr(ssink)));
     }
-  }
+  };
 
+  // Work item (token, head group, partition).  Fixed plans: partition
+  // fastest, then head group, so the partitions and head groups of a token
+  // are consecutive items, which xcd_item keeps on one XCD (one L2) and
+  // dispatches together.  Balanced plans: head group slowest, then the
+  // partitions token by token (consecutive again).
+  const int item = xcd_item(blockIdx.x, gridDim.x);
   const ScalarI32Ptr indptr = (ScalarI32Ptr)a.kv_indptr;
-  const int row0 = indptr[t];
-  const int L = indptr[t + 1] - row0;
-  const int nparts = partitions_of(L, a.splits, a.split_rows);
-  if (c >= nparts || L <= 0) {
-    wait_vmcnt<0>();  // no LDS-DMA load may outlive the workgroup
-    // partition 0 of an empty slice: zeros
-    if (c == 0 && L <= 0 && par == 0)
-      zero_heads<D>(a.out, a.H, t, h0, a.H - h0 < 32 ? a.H - h0 : 32, lane, 64);
-    return;
+  int t, hg, c, nparts, row0, L, R;
+  if (a.bal_slots > 0) {
+    hg = item / a.bal_slots;
+    const int j = item - hg * a.bal_slots;
+    const BalancedItem b = balanced_item<kSuper>(a.kv_indptr, a.N, a.bal_slots, j, lane);
+    // the empty slices t = j, j + bal_slots, ... get their zeros here
+    for (int te = j; te < a.N; te += a.bal_slots) {
+      if (par == 0 && indptr[te + 1] - indptr[te] <= 0) {
+        const int hz = hg * kHeads + hb * 32;
+        zero_heads<D>(a.out, a.H, te, hz, a.H - hz < 32 ? a.H - hz : 32, lane, 64);
+      }
+    }
+    if (b.t < 0) return;  // no partition left for this workgroup
+    t = b.t;
+    c = b.c;
+    nparts = b.nparts;
+    row0 = b.row0;
+    L = b.L;
+    R = b.R;
+  } else {
+    c = item % a.splits;
+    const int th0 = item / a.splits;
+    hg = th0 % a.head_groups;
+    t = th0 / a.head_groups;
+    issue_q(t, hg);
+    row0 = indptr[t];
+    L = indptr[t + 1] - row0;
+    nparts = partitions_of(L, a.splits, a.split_rows);
+    R = a.split_rows;
+    if (c >= nparts || L <= 0) {
+      wait_vmcnt<0>();  // no LDS-DMA load may outlive the workgroup
+      // partition 0 of an empty slice: zeros
+      const int hz = hg * kHeads + hb * 32;
+      if (c == 0 && L <= 0 && par == 0)
+        zero_heads<D>(a.out, a.H, t, hz, a.H - hz < 32 ? a.H - hz : 32, lane, 64);
+      return;
+    }
   }
-  const int cb = c * a.split_rows;
-  const int nrows = (c == nparts - 1) ? L - cb : a.split_rows;
+  const int th = t * a.head_groups + hg;
+  const int h0 = hg * kHeads + hb * 32;  // first head of this wave (32 heads)
+  const int cb = c * R;
+  const int nrows = (c == nparts - 1) ? L - cb : R;
   const int32_t* part = a.kv_indices + row0 + cb;
 
   // LDS read offsets of the K and V^T operands: bf16 tiles in the wide
@@ -278,9 +437,23 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
   const int pre = burst0 < kStages - kQStages ? burst0 : kStages - kQStages;
   auto issue_tile0 = [&](int tile) { issue_super(n0, tile); };
   stage_indices(part, 0, n0, sidx, wave, kWaves, lane);
-  wait_vmcnt<0>();
+  if (a.bal_slots > 0) {
+    // q goes out after the indices (the token was known only now): the first
+    // tiles wait for the indices alone, q for its own loads below
+    issue_q(t, hg);
+    if (wave == 0)
+      wait_vmcnt<kQLoadsPerWave + 1>();  // with the sinks
+    else
+      wait_vmcnt<kQLoadsPerWave>();
+  } else {
+    wait_vmcnt<0>();
+  }
   barrier_lds();
   for (int k = 0; k < pre; ++k) issue_tile0(k);
+  if (a.bal_slots > 0) {  // every wave's share of q has landed before any wave reads it
+    wait_outstanding(pre);
+    barrier_lds();
+  }
   bf16x8 q0[kKSteps], q1[kKSteps];  // Q^T operands of head blocks 0 and 1
   {
     // lane (n16, g) of the k-step u operand holds q[h, 32 u + 8 g .. +7]:
@@ -607,10 +780,20 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
   const int64_t slot = (int64_t)Pc::kBytes;
   const int64_t item_bytes = kWaves * slot;
   unsigned char* ws = reinterpret_cast<unsigned char*>(a.ws);
-  unsigned char* ws_th = ws + (int64_t)th * a.splits * item_bytes;  // partition 0's slots
+  // the slot of the (token, head group)'s partition 0 (its partitions' slots
+  // follow it), and the number of slots, behind which the counters start
+  int64_t slot0, n_items;
+  if (a.bal_slots > 0) {
+    const int j = xcd_item(blockIdx.x, gridDim.x) - hg * a.bal_slots;
+    slot0 = (int64_t)hg * a.bal_slots + (j - c);
+    n_items = (int64_t)a.head_groups * a.bal_slots;
+  } else {
+    slot0 = (int64_t)th * a.splits;
+    n_items = (int64_t)a.N * a.head_groups * a.splits;
+  }
+  unsigned char* ws_th = ws + slot0 * item_bytes;
   // kDTw arrival counters a piece (one a unit at the finest cut)
-  int* ctr_th = reinterpret_cast<int*>(ws + (int64_t)a.N * a.head_groups * a.splits * item_bytes) +
-                (int64_t)th * kWaves * kDTw;
+  int* ctr_th = reinterpret_cast<int*>(ws + n_items * item_bytes) + (int64_t)th * kWaves * kDTw;
   const int others = nparts - 1;
   int U = 1;
   while (U < kDTw && 4 * U < nparts) U <<= 1;
@@ -788,9 +971,11 @@ int device_cus() {
 }
 
 template <int D, int HB, int P, bool kFp8>
-hipError_t launch_split_d(const AttnArgs& a0, hipStream_t stream) {
-  const long long items = (long long)a0.N * a0.head_groups * a0.splits;
+hipError_t launch_split_d(const AttnArgs& a0, const AttnPlan& p, hipStream_t stream) {
+  const long long items = p.bal_slots > 0 ? (long long)a0.head_groups * p.bal_slots
+                                          : (long long)a0.N * a0.head_groups * a0.splits;
   AttnArgs a = a0;
+  a.bal_slots = p.bal_slots;
   // one workgroup per CU (the LDS ring and 512 registers a wave): the grid is
   // resident at once when it has no more workgroups than CUs
   a.split_wait = items <= device_cus() ? 1 : 0;
@@ -801,9 +986,9 @@ hipError_t launch_split_d(const AttnArgs& a0, hipStream_t stream) {
 template <int D, bool kFp8>
 hipError_t launch_split_shape(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
   const int hb = p.heads_per_group / 32;
-  if (hb == 2 && p.parities == 2) return launch_split_d<D, 2, 2, kFp8>(a, stream);
+  if (hb == 2 && p.parities == 2) return launch_split_d<D, 2, 2, kFp8>(a, p, stream);
   if constexpr (D >= 128) {
-    if (hb == 1 && p.parities == 4) return launch_split_d<D, 1, 4, kFp8>(a, stream);
+    if (hb == 1 && p.parities == 4) return launch_split_d<D, 1, 4, kFp8>(a, p, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -812,7 +997,9 @@ hipError_t launch_split_shape(const AttnArgs& a, const AttnPlan& p, hipStream_t 
 
 size_t split_counters_offset(int32_t N, int32_t D, const AttnPlan& p) {
   const size_t slot = (size_t)(D / 32 / p.parities) * 4 * 64 * 8 + 2 * 32 * 4;
-  return (size_t)N * p.head_groups * p.splits * 4 * slot;
+  const size_t items = p.bal_slots > 0 ? (size_t)p.head_groups * p.bal_slots
+                                        : (size_t)N * p.head_groups * p.splits;
+  return items * 4 * slot;
 }
 
 size_t split_workspace_bytes(int32_t N, int32_t D, const AttnPlan& p) {

@@ -27,6 +27,8 @@ struct AttnPlan {
   int splits;          // partitions of a slice (1 = no split-L)
   int split_rows;      // rows per partition (multiple of 32); huge when splits == 1
   int parities;        // split mode: waves per head block (2 or 4); 1 otherwise
+  int bal_slots;       // split mode: > 0 for a balanced plan (workgroups per head group,
+                       // partitions sized in the kernel from the slices' lengths); 0 otherwise
   size_t workspace_bytes;
 };
 
@@ -55,6 +57,9 @@ struct AttnArgs {
   // workgroup per CU), so that a merging workgroup may wait a bounded time
   // for the other partitions; 0 = never wait (the last arrival merges)
   int32_t split_wait;
+  // split mode, balanced plan (> 0): the workgroups of a head group, whose
+  // partitions the kernel sizes from kv_indptr (split_rows and splits unused)
+  int32_t bal_slots;
   // Page transform (sparse_decode_attn_paged): when paged != 0 each token's
   // rows are derived from these, as build_decode_indices derives them, and
   // kv_indices / kv_indptr are not read.  win + topk <= kPagedMaxLen, no split.
@@ -85,14 +90,18 @@ constexpr int kPagedMaxLen = 2048;
 
 hipError_t launch_attention(const AttnArgs& args, int D, const AttnPlan& plan, hipStream_t stream);
 
-// Split mode (attn_split.hip): workgroup = (token, 16 * heads_per_group / 16
-// heads, partition), the partitions of a (token, head group) merged by the
-// last to finish.  The workspace holds one softmax state per work item and
-// one arrival counter per (token, head group, wave); the counters must be
-// zero before the first call and every call leaves them zero.
+// Split mode (attn_split.hip): workgroup = (token, heads_per_group heads,
+// partition), the partitions of a (token, head group) merged inside the
+// kernel.  Fixed plans cut every slice into partitions of split_rows rows
+// (grid N x head_groups x splits); balanced plans (bal_slots > 0) give each
+// head group bal_slots workgroups, which the kernel deals out as the
+// partitions of this call's slices.  The workspace holds one softmax state per
+// workgroup and the arrival counters of every (token, head group); the
+// counters must be zero before the first call and every call leaves them
+// zero.
 size_t split_workspace_bytes(int32_t N, int32_t D, const AttnPlan& plan);
-// Offset of the arrival counters in that workspace (N * head_groups * 4 int32
-// from there to its end).
+// Offset of the arrival counters in that workspace (they run from there to
+// its end).
 size_t split_counters_offset(int32_t N, int32_t D, const AttnPlan& plan);
 // fp8: the rows are args.kv8 / args.kv_scale (D >= 128), else args.kv.
 hipError_t launch_split(const AttnArgs& args, int D, const AttnPlan& plan, bool fp8,

@@ -106,23 +106,37 @@ def test_attn_rejects_bad_arguments(lib):
 
 def test_attn_ex_workspace_checks(lib):
     AUTO, HEADS, ROWS, SPLIT = 0, 1, 2, 4
-    # decode_base shape: the automatic plan is the split mode, 64 heads a
-    # workgroup (4 waves of 32 heads: 2 head blocks x 2 parities), 4
-    # partitions of 160 rows: one piece slot per (token, partition, wave) of
-    # 32 heads x 256 bf16 + 32 fp32 m + 32 fp32 l, then 8 int32 arrival counters per
-    # (token, wave): one per unit of a piece cut into its 8 d-tiles
-    split_need = 64 * 4 * 4 * (32 * 256 * 2 + 2 * 32 * 4) + 64 * 4 * 8 * 4
+    # Split mode with no partition length and at most 256 (token, head group)
+    # pairs: 256 workgroups in all (256 / head groups a head group), which the
+    # kernel deals out as partitions sized from the lengths.  One piece slot
+    # per (workgroup, wave) of 32 heads x 256 bf16 + 32 fp32 m + 32 fp32 l,
+    # then 8 int32 arrival counters per (token, head group, wave): one per
+    # unit of a piece cut into its 8 d-tiles
+    piece = 32 * 256 * 2 + 2 * 32 * 4
+    split_need = 256 * 4 * piece + 64 * 4 * 8 * 4
     assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 0, SPLIT) == split_need
     # the automatic plan keeps rows mode for 640-row slices (no workspace) and
-    # splits small batches of slices of 2048 rows and more: 16 tokens x 8
-    # partitions of 256 rows
+    # splits batches of slices of 2048 rows and more
     assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 0, AUTO) == 0
-    # 16 tokens of up to 2048 rows: 16 partitions of 128 rows (256 workgroups)
     assert lib.sparse_decode_attn_workspace_size(16, 64, 512, 2048, 0, AUTO) == \
-        16 * 16 * 4 * (32 * 256 * 2 + 2 * 32 * 4) + 16 * 4 * 8 * 4
-    # at most 32 partitions
+        256 * 4 * piece + 16 * 4 * 8 * 4
+    # 256 tokens (one workgroup each without a split): the automatic plan does
+    # not split; split mode asked for does, on 256 slots
+    assert lib.sparse_decode_attn_workspace_size(256, 64, 512, 2048, 0, AUTO) == 0
+    assert lib.sparse_decode_attn_workspace_size(256, 64, 512, 2048, 0, SPLIT) == \
+        256 * 4 * piece + 256 * 4 * 8 * 4
+    # two head groups (H = 128): 128 slots each; counters per (token, head group)
+    assert lib.sparse_decode_attn_workspace_size(100, 128, 512, 4096, 0, AUTO) == \
+        256 * 4 * piece + 100 * 2 * 4 * 8 * 4
+    # past 256 pairs the automatic plan does not split (heads mode), and an
+    # explicit split mode keeps one partition a slice (no workspace)
+    assert lib.sparse_decode_attn_workspace_size(257, 64, 512, 2048, 0, AUTO) == 0
+    assert lib.sparse_decode_attn_workspace_size(257, 64, 512, 2048, 0, SPLIT) == 0
     assert lib.sparse_decode_attn_workspace_size(2, 64, 512, 65536, 0, SPLIT) == \
-        2 * 32 * 4 * (32 * 256 * 2 + 2 * 32 * 4) + 2 * 4 * 8 * 4
+        256 * 4 * piece + 2 * 4 * 8 * 4
+    # a given partition length: fixed partitions, at most 32 a slice
+    assert lib.sparse_decode_attn_workspace_size(2, 64, 512, 65536, 2048, SPLIT) == \
+        2 * 32 * 4 * piece + 2 * 4 * 8 * 4
     assert lib.sparse_decode_attn_workspace_size(2, 64, 512, 65536, 1024, SPLIT) == 0
     # without a capacity bound the automatic plan cannot split: rows mode, no workspace
     assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 0, 0, AUTO) == 0
@@ -255,14 +269,15 @@ def test_fp8_plans_and_ex_checks(lib):
         st = lib.sparse_decode_attn_fp8_plan_info(N, H, D, max_len, split, mode, out)
         return st, list(out)
 
-    # 8 tokens of 8192 rows: split mode, 64 heads a workgroup, 32 partitions
-    # of 256 rows; the same workspace layout as the bf16 pool's split mode
+    # 8 tokens of 8192 rows: split mode, 64 heads a workgroup, up to 32
+    # partitions a slice sized in the kernel (rows 0); the same workspace
+    # layout as the bf16 pool's split mode: 256 workgroup slots
     st, i = info(8, 64, 512, 8192)
-    assert st == OK and i == [SPLIT, 64, 1, 32, 256, 0, 2]
+    assert st == OK and i == [SPLIT, 64, 1, 32, 0, 0, 2]
     assert lib.sparse_decode_attn_fp8_workspace_size(8, 64, 512, 8192, 0, AUTO) == \
         lib.sparse_decode_attn_workspace_size(8, 64, 512, 8192, 0, AUTO) == \
-        8 * 32 * 4 * (32 * 256 * 2 + 2 * 32 * 4) + 8 * 4 * 8 * 4
-    assert info(8, 32, 256, 8192)[1][:7] == [SPLIT, 32, 1, 32, 256, 0, 4]
+        256 * 4 * (32 * 256 * 2 + 2 * 32 * 4) + 8 * 4 * 8 * 4
+    assert info(8, 32, 256, 8192)[1][:7] == [SPLIT, 32, 1, 32, 0, 0, 4]
     # no capacity bound, or slices under 2048 rows: no split
     assert info(8, 64, 512)[1][0] == ROWS
     assert info(64, 64, 512, 640)[1][0] == ROWS
@@ -271,12 +286,13 @@ def test_fp8_plans_and_ex_checks(lib):
     assert info(1024, 128, 512, 640)[1][:6] == [HEADS, 128, 1, 1, 1 << 30, 4]
     assert info(8192, 64, 512, 640)[1][:6] == [HEADS, 64, 1, 1, 1 << 30, 2]
     assert info(256, 64, 512, 2048)[1][:6] == [HEADS, 64, 1, 1, 1 << 30, 3]
+    assert info(256, 64, 512, 2048, 0, SPLIT)[1][:5] == [SPLIT, 64, 1, 32, 0]
     assert info(255, 64, 512)[1][0] == ROWS
     # explicit modes
     assert info(8, 64, 512, 0, 0, WIDE)[1][5] == 2
     assert info(8, 128, 512, 0, 0, WIDE)[1][5] == 4
     assert info(64, 64, 512, 640, 0, ROWS)[1][0] == ROWS
-    assert info(64, 64, 512, 640, 0, SPLIT)[1][:4] == [SPLIT, 64, 1, 4]
+    assert info(64, 64, 512, 640, 0, SPLIT)[1][:5] == [SPLIT, 64, 1, 20, 0]
     assert info(8, 64, 512, 8192, 1024, AUTO)[1][:5] == [SPLIT, 64, 1, 8, 1024]  # split_rows: split
     assert info(8, 64, 512, 0, 0, HEADS)[0] == UNSUPPORTED     # no FP8 heads kernel
     assert info(8, 64, 64, 0, 0, SPLIT)[0] == UNSUPPORTED
