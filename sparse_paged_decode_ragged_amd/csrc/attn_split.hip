@@ -85,19 +85,29 @@ __device__ __forceinline__ int ceil_div_small(int a, int b, float rb) {
   return (int)q;
 }
 
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+// Sum or maximum over the wave, in every lane: DPP steps within rows of 16
+// lanes, then the two halves and the two quarters swapped across (VALU only,
+// no LDS round trips).
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xf, 0xf, false);
 }
 
-__device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off));
-  return v;
+template <bool kMax>
+__device__ __forceinline__ int wave_reduce_i(int v) {
+  auto op = [](int a, int b) { return kMax ? max(a, b) : a + b; };
+  v = op(v, dpp_i<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = op(v, dpp_i<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = op(v, dpp_i<0x141>(v));  // row_half_mirror
+  v = op(v, dpp_i<0x140>(v));  // row_mirror
+  const auto a = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+  v = op((int)a[0], (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+  return op((int)b[0], (int)b[1]);
 }
 
 struct BalancedItem {
+  bool zero_j; // slice j (j < N) is empty: this workgroup writes its zeros
   int t;       // token, or -1 when the partitions end before this workgroup
   int c;       // partition of the token
   int nparts;  // partitions of the token's slice
@@ -119,7 +129,7 @@ __device__ __forceinline__ BalancedItem balanced_item(const int32_t* indptr, int
 #pragma unroll
   for (int i = 0; i <= kBalPer; ++i) st[i] = indptr[t0 + i < N ? t0 + i : N];
   int lk[kBalPer];  // super-tiles of each slice
-  int mx = 0, sum = 0, nz = 0;
+  int mx = 0, sum = 0, nz = 0, lj = 0;
 #pragma unroll
   for (int i = 0; i < kBalPer; ++i) {
     const int L = i < per && t0 + i < N ? st[i + 1] - st[i] : 0;
@@ -127,21 +137,23 @@ __device__ __forceinline__ BalancedItem balanced_item(const int32_t* indptr, int
     mx = max(mx, lk[i]);
     sum += lk[i];
     nz += lk[i] > 0 ? 1 : 0;
+    lj = t0 + i == j ? lk[i] : lj;  // (in the lane holding token j)
   }
+  const bool zero_j = j < N && __builtin_amdgcn_readlane(lj, j < N ? j / per : 0) == 0;
   // (the wave sums are uniform; readfirstlane tells the compiler so, which
   // keeps the search and everything sized by its result in scalar registers)
-  mx = __builtin_amdgcn_readfirstlane(wave_max_i(mx));
-  BalancedItem r{-1, 0, 0, 0, 0, kSuper};
+  mx = __builtin_amdgcn_readfirstlane(wave_reduce_i<true>(mx));
+  BalancedItem r{zero_j, -1, 0, 0, 0, 0, kSuper};
   if (mx == 0) return r;  // every slice empty
-  const int64_t S = __builtin_amdgcn_readfirstlane(wave_sum_i(sum));  // < 2^27
-  const int n = __builtin_amdgcn_readfirstlane(wave_sum_i(nz));
+  const int S = __builtin_amdgcn_readfirstlane(wave_reduce_i<false>(sum));  // <= 2^26 + N
+  const int n = __builtin_amdgcn_readfirstlane(wave_reduce_i<false>(nz));
   // least k (super-tiles a partition) of at least mx / kBalMaxParts whose
   // partitions fit.  The count sum_t ceil(lk_t / k) falls as k grows and lies
   // in [S / k, S / k + n], so it fits from some k in [S / slots, S / (slots -
   // n)], and at k = mx (one partition a slice)
   int klo = (mx + kBalMaxParts - 1) / kBalMaxParts, khi = mx;
-  klo = max(klo, (int)((S + slots - 1) / slots));
-  if (slots > n) khi = min(khi, max(klo, (int)((S + (slots - n) - 1) / (slots - n))));
+  klo = max(klo, (S + slots - 1) / slots);
+  if (slots > n) khi = min(khi, max(klo, (S + (slots - n) - 1) / (slots - n)));
   klo = min(klo, khi);
   while (klo < khi) {
     const int mid = (klo + khi) >> 1;
@@ -150,7 +162,7 @@ __device__ __forceinline__ BalancedItem balanced_item(const int32_t* indptr, int
 #pragma unroll
     for (int i = 0; i < kBalPer; ++i)
       if (i < per) cnt += ceil_div_small(lk[i], mid, rm);
-    cnt = __builtin_amdgcn_readfirstlane(wave_sum_i(cnt));
+    cnt = __builtin_amdgcn_readfirstlane(wave_reduce_i<false>(cnt));
     if (cnt <= slots)
       khi = mid;
     else
@@ -350,18 +362,27 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
   const int item = xcd_item(blockIdx.x, gridDim.x);
   const ScalarI32Ptr indptr = (ScalarI32Ptr)a.kv_indptr;
   int t, hg, c, nparts, row0, L, R;
+  int tq = -1;  // balanced plans: the token whose q went out before the plan was known
   if (a.bal_slots > 0) {
     hg = item / a.bal_slots;
     const int j = item - hg * a.bal_slots;
+    // q of a guessed token goes out first, so that its latency overlaps the
+    // plan as in a fixed plan: the token of item j if every slice took the
+    // same number of partitions (right for slices of equal length)
+    const int each = min(kBalMaxParts, max(1, a.bal_slots / a.N));
+    tq = min(j / each, a.N - 1);
+    issue_q(tq, hg);
     const BalancedItem b = balanced_item<kSuper>(a.kv_indptr, a.N, a.bal_slots, j, lane);
-    // the empty slices t = j, j + bal_slots, ... get their zeros here
-    for (int te = j; te < a.N; te += a.bal_slots) {
-      if (par == 0 && indptr[te + 1] - indptr[te] <= 0) {
-        const int hz = hg * kHeads + hb * 32;
-        zero_heads<D>(a.out, a.H, te, hz, a.H - hz < 32 ? a.H - hz : 32, lane, 64);
-      }
+    // an empty slice t gets its zeros from workgroup t of the head group
+    // (bal_slots >= N)
+    if (b.zero_j && par == 0) {
+      const int hz = hg * kHeads + hb * 32;
+      zero_heads<D>(a.out, a.H, j, hz, a.H - hz < 32 ? a.H - hz : 32, lane, 64);
     }
-    if (b.t < 0) return;  // no partition left for this workgroup
+    if (b.t < 0) {  // no partition left for this workgroup
+      wait_vmcnt<0>();  // no LDS-DMA load may outlive the workgroup
+      return;
+    }
     t = b.t;
     c = b.c;
     nparts = b.nparts;
@@ -437,20 +458,15 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
   const int pre = burst0 < kStages - kQStages ? burst0 : kStages - kQStages;
   auto issue_tile0 = [&](int tile) { issue_super(n0, tile); };
   stage_indices(part, 0, n0, sidx, wave, kWaves, lane);
-  if (a.bal_slots > 0) {
-    // q goes out after the indices (the token was known only now): the first
-    // tiles wait for the indices alone, q for its own loads below
-    issue_q(t, hg);
-    if (wave == 0)
-      wait_vmcnt<kQLoadsPerWave + 1>();  // with the sinks
-    else
-      wait_vmcnt<kQLoadsPerWave>();
-  } else {
-    wait_vmcnt<0>();
-  }
+  // (balanced plans) a wrong guess: each wave's guessed q loads land before
+  // it loads the right q into the same LDS bytes; the first tiles then go out
+  // before that q has landed, and q is waited for before its LDS copy is read
+  const bool q_late = a.bal_slots > 0 && t != tq;
+  wait_vmcnt<0>();
+  if (q_late) issue_q(t, hg);
   barrier_lds();
   for (int k = 0; k < pre; ++k) issue_tile0(k);
-  if (a.bal_slots > 0) {  // every wave's share of q has landed before any wave reads it
+  if (q_late) {  // every wave's share of q has landed before any wave reads it
     wait_outstanding(pre);
     barrier_lds();
   }
