@@ -13,9 +13,13 @@
 // D = 512) gives one workgroup per (token, head group) for a fraction of the
 // chip, and spreading the heads over several workgroups pulls every gathered
 // row into several CUs.  Here a workgroup is (token, 32 HB heads, partition c
-// of split_rows rows): every gathered row enters one CU (HB = 2: 64 heads) or
-// two (HB = 1, two head groups of a token), and each CU's rows are a quarter
-// or half of what a head-split workgroup would take in.
+// of R rows): every gathered row enters one CU (HB = 2: 64 heads) or two (HB
+// = 1, two head groups of a token), and each CU's rows are a quarter or half
+// of what a head-split workgroup would take in.  R is either fixed by the
+// host (split_rows; grid N x head groups x splits) or chosen by the kernel
+// from the call's slice lengths (balanced plans: 256 workgroups dealt out as
+// the partitions of all slices, token by token), so that a long slice among
+// short ones takes more of the chip.
 //
 // Inside a workgroup: 4 waves of 32 heads (two 16-head MFMA blocks per wave,
 // as in the 32-head-wave heads kernel): HB head blocks x P parities.  A
