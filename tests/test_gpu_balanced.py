@@ -9,7 +9,7 @@ the 256 workgroups, and deals them out token by token; the empty slices get
 their zeros from the workgroups of the same index.  Cases: the ragged length
 mix with a quarter of the slices empty, one long slice among short ones, every
 slice empty, a single slice, slices long enough to take the 32-partition
-limit, two head groups (H = 128) and a partial one (H = 96), 32-head
+limit, two head groups (H = 128), a partial one (H = 96), 16 (H = 1000), 32-head
 workgroups (H <= 32), D = 64 .. 512, calls with different length mixes one
 after another on one workspace (its arrival counters end every call at zero),
 and bit-for-bit repeatability."""
@@ -68,6 +68,8 @@ CASES = [
     ("heads20_d128", 200, 20, 128, 100000, lambda r: ragged_lengths(r, 200, 4000)),
     ("d64", 120, 64, 64, 100000, lambda r: ragged_lengths(r, 120, 3000)),
     ("short", 256, 64, 512, 50000, lambda r: ragged_lengths(r, 256, 40)),
+    # 16 head groups (the last one partial): 16 slots a head group
+    ("heads1000", 12, 1000, 128, 50000, lambda r: ragged_lengths(r, 12, 3000)),
 ]
 
 
