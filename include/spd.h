@@ -174,8 +174,10 @@ SPD_API spd_status sparse_decode_attn_plan_info(int32_t N, int32_t H, int32_t D,
  * every slice length, used only to size the grid and the workspace (a longer
  * slice is still computed correctly, by its last partition); 0 = unknown.
  * split_rows fixes the split-L partition length (rounded up to a multiple of
- * 32, HEADS mode only; SPD_ERR_UNSUPPORTED with SPD_MODE_ROWS); 0 lets the
- * plan choose from N, H and max_len.  mode is an spd_mode.  HEADS-mode
+ * 32; HEADS or SPLIT mode, SPD_ERR_UNSUPPORTED with SPD_MODE_ROWS or
+ * SPD_MODE_WIDE); 0 lets the plan choose from N, H and max_len, and in SPLIT
+ * mode with at most 256 (token, head group) pairs lets the kernel size the
+ * partitions from the slice lengths.  mode is an spd_mode.  HEADS-mode
  * partitions of one token are merged by a combine kernel, SPLIT-mode ones
  * inside the attention kernel (the attention sink is counted once either way).
  * workspace/workspace_bytes: a caller-owned device buffer of at least
