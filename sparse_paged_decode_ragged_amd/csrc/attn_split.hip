@@ -120,18 +120,24 @@ struct BalancedItem {
   int R;       // rows per partition
 };
 
-// Item j (< slots) of a balanced plan over the N <= 64 kBalPer slices of
-// kv_indptr (slots >= N, so one partition a slice always fits).  Lane l holds
-// tokens [l per, l per + per); the result is wave-uniform.
+// The kv_indptr entries lane l holds for a balanced plan over N <= 64 kBalPer
+// slices: tokens [l per, l per + per), per = ceil(N / 64).
+__device__ __forceinline__ void balanced_load(const int32_t* indptr, int N, int lane,
+                                              int (&st)[kBalPer + 1]) {
+  const int t0 = lane * ((N + 63) >> 6);
+#pragma unroll
+  for (int i = 0; i <= kBalPer; ++i) st[i] = indptr[t0 + i < N ? t0 + i : N];
+}
+
+// Item j (< slots) of a balanced plan over the N <= 64 kBalPer slices whose
+// kv_indptr entries balanced_load gave (slots >= N, so one partition a slice
+// always fits).  The result is wave-uniform.
 template <int kSuper>
-__device__ __forceinline__ BalancedItem balanced_item(const int32_t* indptr, int N, int slots,
-                                                      int j, int lane) {
+__device__ __forceinline__ BalancedItem balanced_item(const int (&st)[kBalPer + 1], int N,
+                                                      int slots, int j, int lane) {
   static_assert((kSuper & (kSuper - 1)) == 0, "super-tile rows: a power of two");
   const int per = (N + 63) >> 6;
   const int t0 = lane * per;
-  int st[kBalPer + 1];
-#pragma unroll
-  for (int i = 0; i <= kBalPer; ++i) st[i] = indptr[t0 + i < N ? t0 + i : N];
   int lk[kBalPer];  // super-tiles of each slice
   int mx = 0, sum = 0, nz = 0, lj = 0;
 #pragma unroll
@@ -367,6 +373,9 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
   const ScalarI32Ptr indptr = (ScalarI32Ptr)a.kv_indptr;
   int t, hg, c, nparts, row0, L, R;
   int tq = -1;  // balanced plans: the token whose q went out before the plan was known
+  // balanced plans: the kv_indices offset and count of the indices staged
+  // before the plan was known (-1: none)
+  int spec_row = -1, spec_n = 0;
   if (a.bal_slots > 0) {
     hg = item / a.bal_slots;
     const int j = item - hg * a.bal_slots;
@@ -376,7 +385,26 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
     const int each = min(kBalMaxParts, max(1, a.bal_slots / a.N));
     tq = min(j / each, a.N - 1);
     issue_q(tq, hg);
-    const BalancedItem b = balanced_item<kSuper>(a.kv_indptr, a.N, a.bal_slots, j, lane);
+    int st[kBalPer + 1];  // (the plan's loads, in flight with the guess's)
+    balanced_load(a.kv_indptr, a.N, lane, st);
+    // ... and so do the indices of the partition item j would be if every
+    // slice had the length of slice tq (the plan's choice for equal slices);
+    // they are kept when the plan agrees.  The partition lies inside slice tq.
+    {
+      const int r0 = indptr[tq], lq = indptr[tq + 1] - r0;
+      const int lkq = lq > 0 ? (lq - 1) / kSuper + 1 : 0;
+      const int kg = (lkq + each - 1) / each;
+      const int pg = kg > 0 ? (lkq + kg - 1) / kg : 0;
+      const int cg = j - tq * each;
+      if (lkq > 0 && pg == each && cg >= 0 && cg < pg) {
+        const int rg = kg * kSuper, cbg = cg * rg;
+        const int ng = cg == pg - 1 ? lq - cbg : rg;
+        spec_row = r0 + cbg;
+        spec_n = ng < kSplitIdx ? ng : kSplitIdx;
+        stage_indices(a.kv_indices + spec_row, 0, spec_n, sidx, wave, kWaves, lane);
+      }
+    }
+    const BalancedItem b = balanced_item<kSuper>(st, a.N, a.bal_slots, j, lane);
     // an empty slice t gets its zeros from workgroup t of the head group
     // (bal_slots >= N)
     if (b.zero_j && par == 0) {
@@ -461,7 +489,13 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
   const int burst0 = ntiles0 < kBurst ? ntiles0 : kBurst;  // tiles in flight before the loop
   const int pre = burst0 < kStages - kQStages ? burst0 : kStages - kQStages;
   auto issue_tile0 = [&](int tile) { issue_super(n0, tile); };
-  stage_indices(part, 0, n0, sidx, wave, kWaves, lane);
+  if (spec_row != row0 + cb || spec_n != n0) {
+    if (spec_row >= 0) {  // staged for a wrong guess: those loads land before the restaging
+      wait_vmcnt<0>();
+      barrier_lds();
+    }
+    stage_indices(part, 0, n0, sidx, wave, kWaves, lane);
+  }
   // (balanced plans) a wrong guess: each wave's guessed q loads land before
   // it loads the right q into the same LDS bytes; the first tiles then go out
   // before that q has landed, and q is waited for before its LDS copy is read
