@@ -129,9 +129,9 @@ SPD_API spd_status sparse_decode_attn(const void* q, const void* unified_kv, int
  *                   cuts slices only when the batch gives fewer than 256
  *                   workgroups.  Its workspace holds arrival counters: see
  *                   sparse_decode_attn_ex.
- *   SPD_MODE_AUTO:  SPLIT when split_rows == 0, the batch gives fewer than
- *                   256 HEADS-mode workgroups and max_len >= 2048 (a small
- *                   batch of long slices, partitions sized from the lengths); else
+ *   SPD_MODE_AUTO:  SPLIT when split_rows == 0, the batch gives at most
+ *                   256 HEADS-mode workgroups and max_len >= 2048 (a batch
+ *                   of long slices, partitions sized from the lengths); else
  *                   ROWS when split_rows == 0 and the batch gives fewer than
  *                   256 HEADS-mode workgroups; else HEADS.
  */
@@ -373,7 +373,7 @@ SPD_API spd_status sparse_decode_attn_fp8(const void* q, const void* kv_fp8,
  *                   (D >= 128): partitions of a slice merged inside the
  *                   kernel, each gathered row entering one CU per 64 heads.
  *   SPD_MODE_AUTO:  SPLIT when split_rows != 0, or when D >= 128, the batch
- *                   gives fewer than 256 workgroups of 64 heads (16 or 32
+ *                   gives at most 256 workgroups of 64 heads (16 or 32
  *                   when H is smaller) and max_len >= 2048; else WIDE on 128-head
  *                   workgroups when H % 128 == 0, D >= 128 and N * H / 128 >=
  *                   256; on 64-head workgroups of two waves when H % 64 == 0

@@ -1076,11 +1076,11 @@ bool make_attn_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t sp
   const long long heads_groups = (H + heads_per - 1) / heads_per;
   // Work items the heads mode provides without split-L; the chip has 256 CUs.
   const long long target = 256;
-  if (mode == kModeAuto && split_rows == 0 && (long long)N * heads_groups < target &&
+  if (mode == kModeAuto && split_rows == 0 && (long long)N * heads_groups <= target &&
       max_len >= kSplitAutoLen) {
-    // a small batch of long slices: partitions sized from the lengths, merged
-    // in-kernel.  (At one workgroup per CU already, 256 slices of the ragged
-    // mix, the heads mode is faster: 101.5 us against 106.4 us.)
+    // a batch of at most one workgroup per CU with long slices: partitions
+    // sized from the lengths, merged in-kernel (the ragged mix of 256 slices:
+    // 87.1 us against 101.8 us in heads mode)
     if (make_split_plan(N, H, D, max_len, 0, p) && p->splits > 1) return true;
     p->parities = 1;
     p->bal_slots = 0;
@@ -1165,7 +1165,7 @@ bool make_fp8_plan(int32_t N, int32_t H, int32_t D, int32_t max_len, int32_t spl
   // split mode when asked for, when the automatic plan is given a partition
   // length, or for a small batch of long slices
   const bool chosen = mode == kModeSplit || (mode == kModeAuto && split_rows > 0);
-  if (chosen || (mode == kModeAuto && base < 256 && max_len >= kSplitAutoLen && D >= 128)) {
+  if (chosen || (mode == kModeAuto && base <= 256 && max_len >= kSplitAutoLen && D >= 128)) {
     if (D < 128) return false;
     if (make_split_plan(N, H, D, max_len, split_rows, p) && (chosen || p->splits > 1)) return true;
     if (chosen) return false;

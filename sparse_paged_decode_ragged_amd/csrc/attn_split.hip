@@ -63,11 +63,19 @@ namespace spd {
 namespace {
 
 constexpr int kSplitIdx = 1024;  // row indices staged at a time
-constexpr int kSpinLimit = 1000; // polls (each a memory round trip plus a short sleep)
-// ... and at most this long, on the 100 MHz real-time counter: partners that
-// are resident arrive within a few microseconds; one that is not (a kernel on
-// another stream holding CUs) is not waited for past this
-constexpr uint64_t kSpinTicks = 2000;  // 20 us
+// A merging workgroup waits for its partners at most this long, on the 100
+// MHz real-time counter: partners of equal length that are resident arrive
+// within a few microseconds; one that is not (a kernel on another stream
+// holding CUs) is not waited for past the bound.  A partition shorter than
+// the others of its slice (its last one) waits besides for the rows it lacks,
+// at kSpinTicksPerRow a row (a resident workgroup takes about 0.07 us a row),
+// up to kSpinTicksMax: giving up earlier leaves its units to the last arrival,
+// which merges them one wave at a time (ragged batch in a balanced plan: 107
+// us with a flat 20 us bound, 87 us with the longer one).
+constexpr uint64_t kSpinTicks = 2000;        // 20 us
+constexpr uint64_t kSpinTicksPerRow = 10;    // 0.1 us
+constexpr uint64_t kSpinTicksMax = 100000;   // 1 ms
+constexpr int kSpinLimit = 1 << 20;  // polls (the time bound ends the wait first)
 
 // Balanced plans: a head group's bal_slots workgroups are the partitions of
 // the call's slices, numbered token by token; every partition but a slice's
@@ -444,6 +452,7 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
   const int h0 = hg * kHeads + hb * 32;  // first head of this wave (32 heads)
   const int cb = c * R;
   const int nrows = (c == nparts - 1) ? L - cb : R;
+  const int short_rows = R - nrows;  // > 0 for a slice's shorter last partition
   const int32_t* part = a.kv_indices + row0 + cb;
 
   // LDS read offsets of the K and V^T operands: bf16 tiles in the wide
@@ -983,6 +992,9 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
       int* cu = ctr_of(u);
       int v = 0;
       const uint64_t t_spin = __builtin_amdgcn_s_memrealtime();
+      const uint64_t extra = short_rows > 0 ? (uint64_t)short_rows * kSpinTicksPerRow : 0;
+      const uint64_t spin_ticks =
+          kSpinTicks + extra < kSpinTicksMax ? kSpinTicks + extra : kSpinTicksMax;
       for (int it = 0; a.split_wait && it < kSpinLimit; ++it) {
         // polled with a read-modify-write (max with 0 leaves the count as it
         // is): it is served where the arrivals' adds are, which a plain
@@ -990,7 +1002,7 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
         if (lane == 0) v = __hip_atomic_fetch_max(cu, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         v = __builtin_amdgcn_readfirstlane(v);
         if (v >= others) break;
-        if (__builtin_amdgcn_s_memrealtime() - t_spin > kSpinTicks) break;
+        if (__builtin_amdgcn_s_memrealtime() - t_spin > spin_ticks) break;
         __builtin_amdgcn_s_sleep(2);
       }
       asm volatile("" ::: "memory");

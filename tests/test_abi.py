@@ -120,9 +120,9 @@ def test_attn_ex_workspace_checks(lib):
     assert lib.sparse_decode_attn_workspace_size(64, 64, 512, 640, 0, AUTO) == 0
     assert lib.sparse_decode_attn_workspace_size(16, 64, 512, 2048, 0, AUTO) == \
         256 * 4 * piece + 16 * 4 * 8 * 4
-    # 256 tokens (one workgroup each without a split): the automatic plan does
-    # not split; split mode asked for does, on 256 slots
-    assert lib.sparse_decode_attn_workspace_size(256, 64, 512, 2048, 0, AUTO) == 0
+    # 256 tokens (one workgroup each without a split) still split: 256 slots
+    assert lib.sparse_decode_attn_workspace_size(256, 64, 512, 2048, 0, AUTO) == \
+        256 * 4 * piece + 256 * 4 * 8 * 4
     assert lib.sparse_decode_attn_workspace_size(256, 64, 512, 2048, 0, SPLIT) == \
         256 * 4 * piece + 256 * 4 * 8 * 4
     # two head groups (H = 128): 128 slots each; counters per (token, head group)
@@ -285,8 +285,8 @@ def test_fp8_plans_and_ex_checks(lib):
     # the batch sizes of the 32-head-wave decompositions
     assert info(1024, 128, 512, 640)[1][:6] == [HEADS, 128, 1, 1, 1 << 30, 4]
     assert info(8192, 64, 512, 640)[1][:6] == [HEADS, 64, 1, 1, 1 << 30, 2]
-    assert info(256, 64, 512, 2048)[1][:6] == [HEADS, 64, 1, 1, 1 << 30, 3]
-    assert info(256, 64, 512, 2048, 0, SPLIT)[1][:5] == [SPLIT, 64, 1, 32, 0]
+    assert info(257, 64, 512, 2048)[1][:6] == [HEADS, 64, 1, 1, 1 << 30, 3]
+    assert info(256, 64, 512, 2048)[1][:5] == [SPLIT, 64, 1, 32, 0]   # 256 slices: split
     assert info(255, 64, 512)[1][0] == ROWS
     # explicit modes
     assert info(8, 64, 512, 0, 0, WIDE)[1][5] == 2

@@ -57,9 +57,9 @@ def test_fp8_kernel_name_follows_the_plan():
     # waves (two parities of each head block) when there is one per CU
     assert name(8192, 64, 512, 640) == "attn_wide_fp8_kernel<512,2>"
     assert name(511, 64, 512) == "attn_wide_fp8_kernel<512,4,2>"
-    assert name(256, 64, 512, 2048) == "attn_wide_fp8_kernel<512,4,2>"
-    # fewer than one 64-head workgroup per CU and slices up to 2048 rows: split mode
-    assert name(255, 64, 512, 2048) == "attn_split_kernel<512,2,2,true>"
+    assert name(256, 64, 512, 640) == "attn_wide_fp8_kernel<512,4,2>"
+    # at most one 64-head workgroup per CU and slices up to 2048 rows: split mode
+    assert name(256, 64, 512, 2048) == "attn_split_kernel<512,2,2,true>"
     assert name(255, 64, 512) == "attn_rows_fp8_kernel<512>"
     assert name(256, 64, 64) == "attn_rows_fp8_kernel<64>"
     # a small batch of long slices: split mode over codes

@@ -126,10 +126,13 @@ def test_length_mixes_one_after_another_on_one_workspace(spd):
 
 def test_ragged_config_and_automatic_plan(spd):
     """The ragged configuration (N = 256, H = 64, D = 512, max_len 2048) in
-    split mode, and the automatic plan on its first 200 tokens (fewer than one
-    workgroup per CU: the balanced split); every token checked."""
+    the automatic plan (the balanced split) and in split mode asked for, and
+    the automatic plan on its first 200 tokens; every token checked."""
     w = W.ragged()
-    log("case balanced ragged config, split mode")
+    plan = spd.sparse_decode_attn_plan_info(w.N, w.H, w.D, w.max_len)
+    assert plan["mode"] == "split" and plan["balanced"], plan
+    log("case balanced ragged config, automatic plan and split mode")
+    run_case(spd, w, "ragged auto", max_len=w.max_len, mode=AUTO)
     run_case(spd, w, "ragged split", max_len=w.max_len, mode=SPLIT)
     lengths = list(np.diff(w.kv_indptr)[:200])
     w2 = W.random_csr("bal_ragged200", 808, 200, 64, 512, 200000, lengths)
