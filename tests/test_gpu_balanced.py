@@ -165,3 +165,14 @@ def test_balanced_split_fp8(spd, name, N, H, D, hi):
                                          mode=mode)
         torch.cuda.synchronize()
         assert_close(bf16_to_f64(out), ref, "%s mode %d" % (name, mode))
+
+
+def test_slices_longer_than_max_len(spd):
+    """max_len only sizes the plan: slices longer than it (up to 2.5 x) are
+    still cut from their own lengths and match the oracle."""
+    rng = np.random.default_rng(31)
+    lengths = ragged_lengths(rng, 48, 5000)
+    lengths[5] = 5000
+    w = W.random_csr("bal_over", 931, 48, 64, 256, 100000, lengths)
+    log("case balanced slices past max_len")
+    run_case(spd, w, "past max_len", max_len=2048)
