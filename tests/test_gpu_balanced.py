@@ -8,9 +8,10 @@ its 32- or 64-row super-tile) for which the partitions of all slices fit in
 the 256 workgroups, and deals them out token by token; the empty slices get
 their zeros from the workgroups of the same index.  Cases: the ragged length
 mix with a quarter of the slices empty, one long slice among short ones, every
-slice empty, a single slice, slices long enough to take the 32-partition
-limit, two head groups (H = 128), a partial one (H = 96), 16 (H = 1000), 32-head
-workgroups (H <= 32), D = 64 .. 512, calls with different length mixes one
+slice empty, a single slice, mostly short slices with long and empty ones
+among them, slices long enough to take the 32-partition limit, two head
+groups (H = 128), a partial one (H = 96), 16 (H = 1000), 32-head workgroups
+(H <= 32), D = 64 .. 512, calls with different length mixes one
 after another on one workspace (its arrival counters end every call at zero),
 and bit-for-bit repeatability."""
 import zlib
@@ -37,6 +38,13 @@ def spd():
 def ragged_lengths(rng, N, hi, empty=0.25):
     L = rng.integers(1, hi + 1, size=N)
     L[rng.random(N) < empty] = 0
+    return [int(x) for x in L]
+
+
+def mixed_lengths(rng, N):
+    # a quarter empty, 15 % of 2500-6000 rows, the rest of 1-300 rows
+    u = rng.random(N)
+    L = np.where(u < 0.25, 0, np.where(u < 0.4, rng.integers(2500, 6001, N), rng.integers(1, 301, N)))
     return [int(x) for x in L]
 
 
@@ -68,6 +76,9 @@ CASES = [
     ("heads20_d128", 200, 20, 128, 100000, lambda r: ragged_lengths(r, 200, 4000)),
     ("d64", 120, 64, 64, 100000, lambda r: ragged_lengths(r, 120, 3000)),
     ("short", 256, 64, 512, 50000, lambda r: ragged_lengths(r, 256, 40)),
+    # mostly short slices with long and empty ones among them
+    ("mixed", 256, 64, 512, 200000, lambda r: mixed_lengths(r, 256)),
+    ("mixed_heads128", 128, 128, 256, 100000, lambda r: mixed_lengths(r, 128)),
     # 16 head groups (the last one partial): 16 slots a head group
     ("heads1000", 12, 1000, 128, 50000, lambda r: ragged_lengths(r, 12, 3000)),
 ]
