@@ -184,7 +184,7 @@ def sparse_decode_attn(q: torch.Tensor, unified_kv: torch.Tensor, kv_indices: to
                        plain: bool = False) -> torch.Tensor:
     """out[N, H, D] (bf16) = sparse decode attention; see include/spd.h.
 
-    plain=True calls the spec form ``sparse_decode_attn`` (automatic
+    plain=True calls the plain form ``sparse_decode_attn`` (automatic
     plan, never split-L, no workspace).  Otherwise ``sparse_decode_attn_ex``
     runs with (max_len, split_rows, mode); ``workspace`` (a device tensor of
     at least ``sparse_decode_attn_workspace_size`` bytes) is allocated here
