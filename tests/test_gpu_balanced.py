@@ -13,7 +13,8 @@ among them, slices long enough to take the 32-partition limit, two head
 groups (H = 128), a partial one (H = 96), 16 (H = 1000), 32-head workgroups
 (H <= 32), D = 64 .. 512, calls with different length mixes one
 after another on one workspace (its arrival counters end every call at zero),
-and bit-for-bit repeatability."""
+bit-for-bit repeatability, and 24 seeded random batches (shapes, length
+distributions and empty fractions drawn per seed)."""
 import zlib
 
 import numpy as np
@@ -187,3 +188,38 @@ def test_slices_longer_than_max_len(spd):
     w = W.random_csr("bal_over", 931, 48, 64, 256, 100000, lengths)
     log("case balanced slices past max_len")
     run_case(spd, w, "past max_len", max_len=2048)
+
+
+def random_mix(rng):
+    """A seeded batch shape and length mix for the balanced plan: N tokens of
+    H heads (at most 256 (token, head group) pairs), lengths drawn uniform,
+    exponential, bimodal or equal, some slices empty, one of at least 129 rows."""
+    H, D = [(64, 512), (64, 128), (128, 256), (16, 128), (96, 64)][int(rng.integers(0, 5))]
+    groups = 1 if H <= 64 else (H + 63) // 64
+    N = int(rng.integers(1, 256 // groups + 1))
+    kind = int(rng.integers(0, 4))
+    hi = int(rng.choice([300, 2048, 6000]))
+    if kind == 0:
+        L = rng.integers(1, hi + 1, size=N)
+    elif kind == 1:
+        L = np.minimum(rng.exponential(hi / 4, size=N).astype(np.int64) + 1, 4 * hi)
+    elif kind == 2:
+        L = np.where(rng.random(N) < 0.1, rng.integers(hi, 3 * hi + 1, size=N),
+                     rng.integers(1, 65, size=N))
+    else:
+        L = np.full(N, hi)
+    L[rng.random(N) < rng.choice([0.0, 0.25, 0.6])] = 0
+    L[int(rng.integers(0, N))] = max(129, int(L.max()))
+    return N, H, D, [int(x) for x in L]
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_length_mixes(spd, seed):
+    """Seeded random batches: every token against the oracle, empty slices
+    zero."""
+    rng = np.random.default_rng(1000 + seed)
+    N, H, D, lengths = random_mix(rng)
+    log("case balanced random seed %d: N=%d H=%d D=%d rows=%d max=%d" %
+        (seed, N, H, D, sum(lengths), max(lengths)))
+    w = W.random_csr("bal_rand%d" % seed, 2000 + seed, N, H, D, 60000, lengths)
+    run_case(spd, w, "random mix %d" % seed)
