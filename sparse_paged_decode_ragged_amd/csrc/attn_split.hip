@@ -78,11 +78,14 @@ constexpr uint64_t kSpinTicksMax = 100000;   // 1 ms
 constexpr int kSpinLimit = 1 << 20;  // polls (the time bound ends the wait first)
 
 // Balanced plans: a head group's bal_slots workgroups are the partitions of
-// the call's slices, numbered token by token; every partition but a slice's
-// last has R rows, R the least multiple of the super-tile for which they fit
-// (and no slice takes more than kBalMaxParts).  Each wave derives R and its
-// workgroup's (token, partition) from kv_indptr alone, so the grid stays
-// fixed by the host while the split follows this call's lengths.
+// the call's slices, numbered token by token.  K, the least number of
+// super-tiles for which ceil(lk / K) partitions of every slice (lk its
+// super-tiles) fit, and at least the longest slice's over kBalMaxParts, sets
+// the partition counts; a split slice's super-tiles are then shared evenly
+// by its partitions (ceil(lk / count) each, at most K, the last taking the
+// rest).  Each wave derives the plan and its workgroup's (token, partition)
+// from kv_indptr alone, so the grid stays fixed by the host while the split
+// follows this call's lengths.
 constexpr int kBalPer = 8;        // tokens a lane holds (N <= 512)
 constexpr int kBalMaxParts = 32;  // partitions of one slice (the merge's units)
 
@@ -125,7 +128,7 @@ struct BalancedItem {
   int nparts;  // partitions of the token's slice
   int row0;    // kv_indptr[t]
   int L;       // rows of the slice
-  int R;       // rows per partition
+  int R;       // rows of each partition but the slice's last (which takes the rest)
 };
 
 // The kv_indptr entries lane l holds for a balanced plan over N <= 64 kBalPer
@@ -202,7 +205,7 @@ __device__ __forceinline__ BalancedItem balanced_item(const int (&st)[kBalPer + 
   }
   int pre = incl - tot;
   bool found = false;
-  int ft = 0, fc = 0, fnp = 0, frow0 = 0, fL = 0;
+  int ft = 0, fc = 0, fnp = 0, frow0 = 0, fL = 0, flk = 0;
 #pragma unroll
   for (int i = 0; i < kBalPer; ++i) {
     if (!found && j >= pre && j < pre + np[i]) {
@@ -212,6 +215,7 @@ __device__ __forceinline__ BalancedItem balanced_item(const int (&st)[kBalPer + 
       fnp = np[i];
       frow0 = st[i];
       fL = st[i + 1] - st[i];
+      flk = lk[i];
     }
     pre += np[i];
   }
@@ -223,7 +227,11 @@ __device__ __forceinline__ BalancedItem balanced_item(const int (&st)[kBalPer + 
   r.nparts = __builtin_amdgcn_readlane(fnp, f);
   r.row0 = __builtin_amdgcn_readlane(frow0, f);
   r.L = __builtin_amdgcn_readlane(fL, f);
-  r.R = klo * kSuper;
+  // a split slice's partitions share its super-tiles evenly (at most klo
+  // each), so that a partition that also merges does not take the longest
+  // share of rows as well
+  const int lkf = __builtin_amdgcn_readlane(flk, f);
+  r.R = (r.nparts > 1 ? (lkf + r.nparts - 1) / r.nparts : klo) * kSuper;
   return r;
 }
 
@@ -405,7 +413,7 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
       const int pg = kg > 0 ? (lkq + kg - 1) / kg : 0;
       const int cg = j - tq * each;
       if (lkq > 0 && pg == each && cg >= 0 && cg < pg) {
-        const int rg = kg * kSuper, cbg = cg * rg;
+        const int rg = (pg > 1 ? (lkq + pg - 1) / pg : kg) * kSuper, cbg = cg * rg;
         const int ng = cg == pg - 1 ? lq - cbg : rg;
         spec_row = r0 + cbg;
         spec_n = ng < kSplitIdx ? ng : kSplitIdx;
