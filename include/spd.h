@@ -124,10 +124,13 @@ SPD_API spd_status sparse_decode_attn(const void* q, const void* unified_kv, int
  *                   partitions of this call's slices, sized from kv_indptr: the
  *                   least partition length (a multiple of 32 rows, 64 when a
  *                   workgroup takes 32 heads) for which every slice's
- *                   partitions fit, so a long slice among short ones takes
- *                   more workgroups.  Otherwise with split_rows == 0 the plan
- *                   cuts slices only when the batch gives fewer than 256
- *                   workgroups.  Its workspace holds arrival counters: see
+ *                   partitions fit sets each slice's partition count, and a
+ *                   split slice's rows are then shared evenly among its
+ *                   partitions (in whole 32- or 64-row tiles, the last
+ *                   partition taking the rest), so a long slice among short
+ *                   ones takes more workgroups.  Otherwise with split_rows == 0
+ *                   the plan cuts slices only when the batch gives fewer
+ *                   than 256 workgroups.  Its workspace holds arrival counters: see
  *                   sparse_decode_attn_ex.
  *   SPD_MODE_AUTO:  SPLIT when split_rows == 0, the batch gives at most
  *                   256 HEADS-mode workgroups and max_len >= 2048 (a batch
