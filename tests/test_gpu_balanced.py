@@ -13,8 +13,9 @@ among them, slices long enough to take the 32-partition limit, two head
 groups (H = 128), a partial one (H = 96), 16 (H = 1000), 32-head workgroups
 (H <= 32), D = 64 .. 512, calls with different length mixes one
 after another on one workspace (its arrival counters end every call at zero),
-bit-for-bit repeatability, and 24 seeded random batches (shapes, length
-distributions and empty fractions drawn per seed)."""
+bit-for-bit repeatability, and seeded random batches (shapes, length
+distributions and empty fractions drawn per seed; 24 over bf16 pools, 8 over
+FP8 pools)."""
 import zlib
 
 import numpy as np
@@ -223,3 +224,31 @@ def test_random_length_mixes(spd, seed):
         (seed, N, H, D, sum(lengths), max(lengths)))
     w = W.random_csr("bal_rand%d" % seed, 2000 + seed, N, H, D, 60000, lengths)
     run_case(spd, w, "random mix %d" % seed)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_length_mixes_fp8(spd, seed):
+    """Seeded random batches over an FP8 pool (D >= 128): every token against
+    the oracle's FP8 attention."""
+    rng = np.random.default_rng(3000 + seed)
+    N, H, D, lengths = random_mix(rng)
+    D = max(D, 128)
+    max_len = max(lengths)
+    plan = spd.sparse_decode_attn_fp8_plan_info(N, H, D, max_len, 0, SPLIT)
+    assert plan["mode"] == "split" and plan["balanced"], plan
+    log("case balanced fp8 random seed %d: N=%d H=%d D=%d rows=%d max=%d" %
+        (seed, N, H, D, sum(lengths), max_len))
+    w = W.random_csr("bal_rand8_%d" % seed, 4000 + seed, N, H, D, 60000, lengths)
+    codes, scales = oracle.quantize_fp8(w.kv_bits)
+    ref = oracle.sparse_decode_attn_fp8(w.q_bits, codes, scales, w.kv_indices, w.kv_indptr,
+                                        w.attn_sink, w.softmax_scale)
+    idx, ptr = device_csr(w.kv_indices, w.kv_indptr)
+    out = spd.sparse_decode_attn_fp8(W.device_bits(w.q_bits, dev()), torch.from_numpy(codes).to(dev()),
+                                     torch.from_numpy(scales).to(dev()), idx, ptr,
+                                     torch.from_numpy(w.attn_sink).to(dev()), w.softmax_scale,
+                                     max_len=max_len, mode=SPLIT)
+    torch.cuda.synchronize()
+    assert_close(bf16_to_f64(out), ref, "fp8 random mix %d" % seed)
+    empty = np.nonzero(np.diff(w.kv_indptr) == 0)[0]
+    if len(empty):
+        assert torch.all(out[torch.from_numpy(empty).to(dev())].view(torch.int16) == 0)
