@@ -400,7 +400,10 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
     // same number of partitions (right for slices of equal length)
     const int each = min(kBalMaxParts, max(1, a.bal_slots / a.N));
     tq = min(j / each, a.N - 1);
-    issue_q(tq, hg);
+    // (with one item a slice the guess holds only if no slice before tq is
+    // empty or split, which a padded or ragged batch rarely gives: there q
+    // waits for the check below, and is not loaded at all when it fails)
+    if (each > 1) issue_q(tq, hg);
     int st[kBalPer + 1];  // (the plan's loads, in flight with the guess's)
     balanced_load(a.kv_indptr, a.N, lane, st);
     // ... and so do the indices of the partition item j would be if every
@@ -412,12 +415,16 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
       const int kg = (lkq + each - 1) / each;
       const int pg = kg > 0 ? (lkq + kg - 1) / kg : 0;
       const int cg = j - tq * each;
-      if (lkq > 0 && pg == each && cg >= 0 && cg < pg) {
+      if (lkq > 0 && pg == each && cg >= 0 && cg < pg &&
+          (each > 1 || (int64_t)r0 == (int64_t)tq * lq)) {
+        if (each == 1) issue_q(tq, hg);
         const int rg = (pg > 1 ? (lkq + pg - 1) / pg : kg) * kSuper, cbg = cg * rg;
         const int ng = cg == pg - 1 ? lq - cbg : rg;
         spec_row = r0 + cbg;
         spec_n = ng < kSplitIdx ? ng : kSplitIdx;
         stage_indices(a.kv_indices + spec_row, 0, spec_n, sidx, wave, kWaves, lane);
+      } else if (each == 1) {
+        tq = -1;  // no q went out
       }
     }
     const BalancedItem b = balanced_item<kSuper>(st, a.N, a.bal_slots, j, lane);
