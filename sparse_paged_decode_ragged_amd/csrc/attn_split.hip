@@ -402,7 +402,8 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
     tq = min(j / each, a.N - 1);
     // (with one item a slice the guess holds only if no slice before tq is
     // empty or split, which a padded or ragged batch rarely gives: there q
-    // waits for the check below, and is not loaded at all when it fails)
+    // waits for the check below, and when that fails it goes out with the
+    // indices once the plan is known)
     if (each > 1) issue_q(tq, hg);
     int st[kBalPer + 1];  // (the plan's loads, in flight with the guess's)
     balanced_load(a.kv_indptr, a.N, lane, st);
@@ -444,6 +445,10 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
     row0 = b.row0;
     L = b.L;
     R = b.R;
+    if (tq < 0) {  // nothing was guessed: q goes out now, beside the indices
+      issue_q(t, hg);
+      tq = t;
+    }
   } else {
     c = item % a.splits;
     const int th0 = item / a.splits;
