@@ -395,36 +395,33 @@ __global__ void __launch_bounds__(256) attn_split_kernel(AttnArgs a) {
   if (a.bal_slots > 0) {
     hg = item / a.bal_slots;
     const int j = item - hg * a.bal_slots;
-    // q of a guessed token goes out first, so that its latency overlaps the
-    // plan as in a fixed plan: the token of item j if every slice took the
-    // same number of partitions (right for slices of equal length)
+    // A guess, so that equal slices do not wait for the plan: the token of
+    // item j if every slice took the same number of partitions, and the
+    // partition item j would be if every slice had the length of slice tq
+    // (the plan's choice for equal slices; it lies inside slice tq).  It
+    // holds only if the slices before tq are as long as tq's, which a
+    // padded, ragged or skewed batch rarely gives, so q and the partition's
+    // indices go out after that check (one scalar round trip, beside the
+    // plan's loads) and are kept when the plan agrees; when the check fails
+    // q goes out with the indices once the plan is known.
     const int each = min(kBalMaxParts, max(1, a.bal_slots / a.N));
     tq = min(j / each, a.N - 1);
-    // (with one item a slice the guess holds only if no slice before tq is
-    // empty or split, which a padded or ragged batch rarely gives: there q
-    // waits for the check below, and when that fails it goes out with the
-    // indices once the plan is known)
-    if (each > 1) issue_q(tq, hg);
     int st[kBalPer + 1];  // (the plan's loads, in flight with the guess's)
     balanced_load(a.kv_indptr, a.N, lane, st);
-    // ... and so do the indices of the partition item j would be if every
-    // slice had the length of slice tq (the plan's choice for equal slices);
-    // they are kept when the plan agrees.  The partition lies inside slice tq.
     {
       const int r0 = indptr[tq], lq = indptr[tq + 1] - r0;
       const int lkq = lq > 0 ? (lq - 1) / kSuper + 1 : 0;
       const int kg = (lkq + each - 1) / each;
       const int pg = kg > 0 ? (lkq + kg - 1) / kg : 0;
       const int cg = j - tq * each;
-      if (lkq > 0 && pg == each && cg >= 0 && cg < pg &&
-          (each > 1 || (int64_t)r0 == (int64_t)tq * lq)) {
-        if (each == 1) issue_q(tq, hg);
+      if (lkq > 0 && pg == each && cg >= 0 && cg < pg && (int64_t)r0 == (int64_t)tq * lq) {
+        issue_q(tq, hg);
         const int rg = (pg > 1 ? (lkq + pg - 1) / pg : kg) * kSuper, cbg = cg * rg;
         const int ng = cg == pg - 1 ? lq - cbg : rg;
         spec_row = r0 + cbg;
         spec_n = ng < kSplitIdx ? ng : kSplitIdx;
         stage_indices(a.kv_indices + spec_row, 0, spec_n, sidx, wave, kWaves, lane);
-      } else if (each == 1) {
+      } else {
         tq = -1;  // no q went out
       }
     }
